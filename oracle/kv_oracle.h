@@ -1,0 +1,103 @@
+/*
+ * kv_oracle.h -- plain CPU oracle for paged <-> chunk KV-cache movement.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+ * load or call this code: only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark do.  It shares no header, helper, table or
+ * constant with the GPU library; the two meet only on the byte layouts that
+ * the method defines, and on the seeded synthetic inputs.
+ *
+ * What it computes (sources are the web pages this project is built from,
+ * cited by title and section):
+ *
+ *  - Chunking: a token range [s, e) is cut into C-token chunks (C = 256 by
+ *    default), the last one partial.  "LMCache 源码解析：一个文件讲透KV缓存复用
+ *    机制" (LMCache source walkthrough: cache_engine.py), section "store()：
+ *    一条KV序列如何被分块、键控并批量写入" (how a KV sequence is chunked, keyed
+ *    and written in batch); "LMCache: An Efficient KV Cache Layer for
+ *    Enterprise-Scale LLM Inference" (paper notes), section "方法细节 /
+ *    可配置的块大小" (configurable chunk size).
+ *  - Store = gather: copy the KV of every token of a chunk, for every layer,
+ *    K then V, out of the engine's scattered pages into one contiguous chunk
+ *    buffer laid out [num_layers][2][n_c][num_heads][head_size] (the blob
+ *    shape of "LMCache 中的 KV Cache 压缩：CacheGen 编解码原理..." (CacheGen
+ *    page), section "2. 量化 (Quantization)").
+ *  - Retrieve = scatter of the chunks back into pages, honouring the prefix
+ *    hit rule: hits count from chunk 0 and stop at the first miss (LMCache
+ *    source walkthrough, section "retrieve()：前缀匹配如何在首个未命中处停下").
+ *  - The optional fp8 serde: every element cast to float8 e4m3fn, one byte per
+ *    element ("LMCache 分布式 KV Cache 序列化框架 Serde 双层接口设计与自定义
+ *    扩展实战" (LMCache serde framework page), section "7.1 fp8 量化"), here
+ *    with one fp32 absmax scale per (chunk, layer, K/V): scale = amax / 448,
+ *    q = e4m3(x / scale) rounded to nearest-even and saturated.
+ *
+ * Parity pins (tests marked "not gpu") tie each function to something other
+ * than itself: numpy page-gather + reshape formulations, store-then-retrieve
+ * identity, sentinel invariants, torch's float8_e4m3fn / bfloat16 casts over
+ * exhaustive or large input sets, numpy float32 division and products, and a
+ * closed-form round-trip error bound.
+ */
+#ifndef KV_ORACLE_H
+#define KV_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { KVO_FMT_BF16 = 0, KVO_FMT_FP8 = 1 };
+
+/* The engine's paged pool, in host memory.  For layer l, k[l] and v[l] each
+ * point at uint16 (raw bf16 bits) [num_pages][page_size][num_kv_heads*head_dim]. */
+typedef struct {
+    int32_t num_layers;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t page_size;
+    int32_t chunk_size;
+    int64_t num_pages;
+    uint16_t* const* k;
+    uint16_t* const* v;
+} kvo_pool;
+
+/* Chunk planning over [s, e): count, and tokens of chunk c. */
+int64_t kvo_num_chunks(int64_t s, int64_t e, int32_t chunk_size);
+int64_t kvo_chunk_tokens(int64_t s, int64_t e, int32_t chunk_size, int64_t c);
+/* Exact size in bytes of one chunk holding n_tokens tokens. */
+int64_t kvo_chunk_bytes(const kvo_pool* pool, int64_t n_tokens, int fmt);
+/* Pool row holding token t: block_table[t / P] * P + t % P. */
+int64_t kvo_slot(const int32_t* block_table, int32_t page_size, int64_t t);
+/* Number of leading hit chunks: index of the first 0 in mask, else n_chunks. */
+int64_t kvo_hit_chunks(const uint8_t* mask, int64_t n_chunks);
+
+/* Store (gather) [s, e) into chunks[0 .. num_chunks).  Returns 0, or -1 on a
+ * rejected argument (s not chunk-aligned, e beyond the block table, a page id
+ * out of range, bad format). */
+int kvo_store(const kvo_pool* pool, const int32_t* block_table, int64_t n_bt,
+              int64_t s, int64_t e, uint8_t* const* chunks, int fmt);
+
+/* Retrieve (scatter) the leading hit chunks of [s, e) back into the pool.
+ * layer < 0 moves every layer, else only that layer.  Returns the number of
+ * tokens made available (counted from s), or -1 on a rejected argument
+ * (as for store, plus duplicate page ids among the written pages). */
+int64_t kvo_retrieve(const kvo_pool* pool, const int32_t* block_table, int64_t n_bt,
+                     int64_t s, int64_t e, const uint8_t* mask,
+                     uint8_t* const* chunks, int fmt, int32_t layer);
+
+/* Number formats. */
+uint8_t  kvo_e4m3_encode(float y);       /* OCP E4M3 (fn), RNE, saturating */
+float    kvo_e4m3_decode(uint8_t b);
+uint16_t kvo_bf16_from_float(float y);   /* IEEE-754 round-to-nearest-even */
+float    kvo_float_from_bf16(uint16_t h);
+float    kvo_fp8_scale(float amax);      /* amax == 0 ? 1 : amax / 448 */
+
+/* Array forms of the conversions (for exhaustive checks). */
+void kvo_e4m3_encode_n(const float* y, uint8_t* out, int64_t n);
+void kvo_e4m3_encode_bits_range(uint64_t first_bits, int64_t n, uint8_t* out);
+void kvo_bf16_from_float_n(const float* y, uint16_t* out, int64_t n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KV_ORACLE_H */

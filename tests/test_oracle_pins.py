@@ -1,0 +1,389 @@
+"""Pins of the CPU oracle against things other than itself (no GPU needed).
+
+* printed values of the pages / workload definitions (tests/golden),
+* a numpy page-gather + reshape formulation of store (a different mechanism
+  from the oracle's per-token slot loop),
+* invariants: store-then-retrieve identity, untouched rows keep a sentinel,
+  prefix-hit rule with holes, layer-by-layer equals all layers, byte
+  transparency for arbitrary 16-bit patterns, store leaves the pool unchanged,
+* library routines: torch float8_e4m3fn and bfloat16 casts (exhaustive over
+  the meaningful fp32 range), numpy float32 division and products,
+* the closed-form round-trip error bound of scaled e4m3.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_movement_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "printed_values.json")
+
+
+def _gold():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _pool(w, arr=None):
+    arr = wl.host_pool(w) if arr is None else arr
+    return arr, oracle.Pool.from_array(arr, w.num_kv_heads, w.head_dim, w.chunk_size)
+
+
+def _numpy_gather(arr, bt, s, e, C):
+    """Independent formulation: take whole pages in block-table order, flatten
+    them to a token-major row array, slice [s, e), cut every C rows."""
+    L = arr.shape[0]
+    pages = arr[:, :, np.asarray(bt, np.int64)]            # [L, 2, n_bt, P, E]
+    rows = pages.reshape(L, 2, -1, arr.shape[-1])[:, :, s:e]  # [L, 2, e-s, E]
+    out = []
+    for c0 in range(0, e - s, C):
+        out.append(np.ascontiguousarray(rows[:, :, c0:c0 + C]).view(np.uint8).ravel())
+    return out
+
+
+# ------------------------------------------------------------ printed values
+
+def test_printed_chunk_plan_and_sizes():
+    g = _gold()
+    C = g["chunk_size_default"]["value"]
+    seq = g["sequence_10000"]
+    n = oracle.num_chunks(0, seq["tokens"], C)
+    assert n == seq["full_chunks"] + 1
+    sizes = [oracle.chunk_tokens(0, seq["tokens"], C, c) for c in range(n)]
+    assert sizes[:-1] == [C] * seq["full_chunks"] and sizes[-1] == seq["tail_tokens"]
+    assert oracle.num_chunks(0, 10240, C) == 40 and oracle.chunk_tokens(0, 10240, C, 39) == 256
+    assert oracle.num_chunks(0, 0, C) == 0 and oracle.num_chunks(512, 512, C) == 0
+    assert oracle.num_chunks(0, 1, C) == 1 and oracle.chunk_tokens(0, 1, C, 0) == 1
+
+    s8 = g["llama8b_shape"]
+    P = g["page_tokens"]["value"]
+    arr = np.zeros((s8["layers"], 2, 1, P, s8["kv_heads"] * s8["head_dim"]), np.uint16)
+    pool = oracle.Pool.from_array(arr, s8["kv_heads"], s8["head_dim"], C)
+    lo, hi = g["page_bytes_range"]["value"]
+    page_bytes = P * s8["kv_heads"] * s8["head_dim"] * 2
+    assert lo <= page_bytes <= hi and page_bytes == 32 * 1024
+    assert oracle.chunk_bytes(pool, C, oracle.FMT_BF16) == 32 * 1024 * 1024
+    assert oracle.chunk_bytes(pool, seq["tail_tokens"], oracle.FMT_BF16) == 16 * 32 * 2 * 1024 * 2
+    numel = s8["layers"] * 2 * C * s8["kv_heads"] * s8["head_dim"]
+    bpe = g["fp8_bytes_per_element"]["value"]
+    assert oracle.chunk_bytes(pool, C, oracle.FMT_FP8) == numel * bpe + s8["layers"] * 2 * 4
+
+    s70 = g["llama70b_sequence"]
+    arr70 = np.zeros((s70["layers"], 2, 1, P, s70["kv_heads"] * s70["head_dim"]), np.uint16)
+    pool70 = oracle.Pool.from_array(arr70, s70["kv_heads"], s70["head_dim"], C)
+    n70 = oracle.num_chunks(0, s70["tokens"], C)
+    assert n70 == s70["chunks"]
+    total = sum(oracle.chunk_bytes(pool70, oracle.chunk_tokens(0, s70["tokens"], C, c), oracle.FMT_BF16)
+                for c in range(n70))
+    assert total == s70["kv_bytes"]
+
+
+def test_printed_hit_mask_with_hole():
+    g = _gold()["hit_mask_with_hole"]
+    assert oracle.hit_chunks(g["mask"]) * 256 == g["hit_tokens"]
+    assert oracle.hit_chunks([0, 1, 1]) == 0
+    assert oracle.hit_chunks([1, 1, 1]) == 3
+    assert oracle.hit_chunks([]) == 0
+
+
+def test_slot_formula_against_page_walk():
+    # token t lives in row t % P of page bt[t // P]: walk the pages explicitly
+    bt = np.array([7, 3, 11, 0], np.int32)
+    expected = [p * 16 + r for p in bt for r in range(16)]
+    assert [oracle.slot(bt, 16, t) for t in range(64)] == expected
+
+
+# --------------------------------------------------------------- bf16 moves
+
+@pytest.mark.parametrize("case", ["tiny", "ragged", "multi"])
+def test_store_matches_numpy_page_gather(case):
+    if case == "tiny":
+        w = wl.tiny()
+    elif case == "ragged":
+        # 3 chunks, tail of 37 tokens: last page partly filled; odd head_dim
+        w = wl.custom("ragged", 11, 3, 1, 24, 80, [(0, 549)])
+    else:
+        # several sequences, one starting at a chunk boundary past 0, one empty
+        w = wl.custom("multi", 12, 2, 2, 16, 160, [(0, 300), (256, 700), (512, 512), (0, 17)])
+    arr, pool = _pool(w)
+    before = arr.copy()
+    for sq in w.seqs:
+        chunks = oracle.alloc_chunks(pool, sq.tok_start, sq.tok_end, oracle.FMT_BF16, fill=0xCD)
+        assert oracle.store(pool, sq.block_table, sq.tok_start, sq.tok_end, chunks) == 0
+        exp = _numpy_gather(arr, sq.block_table, sq.tok_start, sq.tok_end, w.chunk_size)
+        assert len(chunks) == len(exp)
+        for a, b in zip(chunks, exp):
+            assert a.size == b.size and np.array_equal(a, b)
+    assert np.array_equal(arr, before), "store must not write the pool"
+
+
+def _slots_of(w, sq, n_tokens):
+    return [oracle.slot(sq.block_table, w.page_size, sq.tok_start + j) for j in range(n_tokens)]
+
+
+@pytest.mark.parametrize("sentinel", [0x0000, 0xA5A5])
+def test_store_clear_retrieve_identity(sentinel):
+    w = wl.custom("rt", 21, 3, 2, 32, 96, [(0, 600), (256, 300)])
+    arr, pool = _pool(w)
+    orig = arr.copy()
+    stored = []
+    for sq in w.seqs:
+        ch = oracle.alloc_chunks(pool, sq.tok_start, sq.tok_end, oracle.FMT_BF16)
+        assert oracle.store(pool, sq.block_table, sq.tok_start, sq.tok_end, ch) == 0
+        stored.append(ch)
+    arr[...] = sentinel
+    touched = np.zeros(arr.shape[2] * arr.shape[3], bool)
+    for sq, ch in zip(w.seqs, stored):
+        n = oracle.retrieve(pool, sq.block_table, sq.tok_start, sq.tok_end, sq.hit_mask, ch)
+        assert n == sq.tok_end - sq.tok_start
+        touched[_slots_of(w, sq, n)] = True
+    flat, oflat = arr.reshape(w.num_layers, 2, -1, w.width), orig.reshape(w.num_layers, 2, -1, w.width)
+    assert np.array_equal(flat[:, :, touched], oflat[:, :, touched])
+    assert (flat[:, :, ~touched] == sentinel).all()
+
+
+def test_retrieve_prefix_hits_and_holes():
+    w = wl.custom("holes", 31, 2, 1, 16, 64, [(0, 1000)])
+    arr, pool = _pool(w)
+    sq = w.seqs[0]
+    ch = oracle.alloc_chunks(pool, 0, 1000, oracle.FMT_BF16)
+    assert oracle.store(pool, sq.block_table, 0, 1000, ch) == 0
+    orig = arr.copy()
+    flat, oflat = arr.reshape(2, 2, -1, w.width), orig.reshape(2, 2, -1, w.width)
+    for mask, n_tok in [([1, 1, 0, 1], 512), ([0, 1, 1, 1], 0), ([1, 0, 0, 0], 256),
+                        ([1, 1, 1, 1], 1000), ([1, 1, 1, 0], 768)]:
+        arr[...] = 0x7E57
+        n = oracle.retrieve(pool, sq.block_table, 0, 1000, np.array(mask, np.uint8), ch)
+        assert n == n_tok
+        hit = _slots_of(w, sq, n_tok)
+        miss = sorted(set(range(flat.shape[2])) - set(hit))
+        assert np.array_equal(flat[:, :, hit], oflat[:, :, hit])
+        assert (flat[:, :, miss] == 0x7E57).all()
+
+
+def test_layer_by_layer_equals_all_layers():
+    w = wl.custom("lw", 41, 4, 2, 16, 64, [(0, 530)])
+    arr, pool = _pool(w)
+    sq = w.seqs[0]
+    ch = oracle.alloc_chunks(pool, 0, 530, oracle.FMT_BF16)
+    assert oracle.store(pool, sq.block_table, 0, 530, ch) == 0
+    arr[...] = 1
+    assert oracle.retrieve(pool, sq.block_table, 0, 530, sq.hit_mask, ch) == 530
+    full = arr.copy()
+    arr[...] = 1
+    for l in range(w.num_layers):
+        before = arr.copy()
+        assert oracle.retrieve(pool, sq.block_table, 0, 530, sq.hit_mask, ch, layer=l) == 530
+        others = [x for x in range(w.num_layers) if x != l]
+        assert np.array_equal(arr[others], before[others]), "a layerwise call wrote another layer"
+    assert np.array_equal(arr, full)
+
+
+def test_byte_transparency_random_bit_patterns():
+    w = wl.custom("bits", 51, 2, 2, 32, 48, [(0, 513)], values="bits")
+    arr, pool = _pool(w)
+    assert (((arr & 0x7F80) == 0x7F80) & ((arr & 0x7F) != 0)).any()   # NaN codes are among them
+    sq = w.seqs[0]
+    orig = arr.copy()
+    ch = oracle.alloc_chunks(pool, 0, 513, oracle.FMT_BF16)
+    assert oracle.store(pool, sq.block_table, 0, 513, ch) == 0
+    exp = _numpy_gather(orig, sq.block_table, 0, 513, 256)
+    assert all(np.array_equal(a, b) for a, b in zip(ch, exp))
+    arr[...] = 0
+    assert oracle.retrieve(pool, sq.block_table, 0, 513, sq.hit_mask, ch) == 513
+    s = _slots_of(w, sq, 513)
+    assert np.array_equal(arr.reshape(2, 2, -1, w.width)[:, :, s], orig.reshape(2, 2, -1, w.width)[:, :, s])
+
+
+def test_rejected_arguments():
+    w = wl.custom("bad", 61, 2, 1, 16, 32, [(0, 300)])
+    arr, pool = _pool(w)
+    bt = w.seqs[0].block_table
+    ch = oracle.alloc_chunks(pool, 0, 300, oracle.FMT_BF16)
+    assert oracle.store(pool, bt, 16, 300, ch) == -1            # start not chunk-aligned
+    assert oracle.store(pool, bt, 0, 16 * bt.size + 1, ch + ch) == -1   # beyond the block table
+    assert oracle.store(pool, bt, 0, 300, ch, fmt=7) == -1
+    bad = bt.copy()
+    bad[3] = 32                                                  # page id out of range
+    assert oracle.store(pool, bad, 0, 300, ch) == -1
+    dup = bt.copy()
+    dup[5] = dup[2]                                              # duplicate page on retrieve
+    assert oracle.store(pool, dup, 0, 300, ch) == 0              # reading twice is fine
+    assert oracle.retrieve(pool, dup, 0, 300, [1, 1], ch) == -1
+    assert oracle.retrieve(pool, dup, 0, 300, [0, 1], ch) == 0   # nothing written, nothing races
+    assert oracle.retrieve(pool, bt, 0, 300, [1, 1], ch, layer=2) == -1
+
+
+# --------------------------------------------------------------- number formats
+
+def _torch_e4m3(y: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(y, np.float32)).clamp(-448.0, 448.0)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_encode_exhaustive_meaningful_range():
+    # every positive fp32 pattern from 2^-12 up to 2^10: covers all subnormal
+    # and normal E4M3 rounding decisions, the ties, and saturation
+    lo = np.float32(2.0 ** -12).view(np.uint32)
+    hi = np.float32(2.0 ** 10).view(np.uint32)
+    step = 1 << 26
+    for b0 in range(int(lo), int(hi), step):
+        n = min(step, int(hi) - b0)
+        got = oracle.e4m3_encode_bits_range(b0, n)
+        y = np.arange(b0, b0 + n, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        exp = _torch_e4m3(y)
+        bad = np.nonzero(got != exp)[0]
+        assert bad.size == 0, (hex(b0 + int(bad[0])), got[bad[0]], exp[bad[0]])
+
+
+def test_e4m3_encode_sampled_everywhere_and_specials():
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    y = bits.view(np.float32)
+    got = oracle.e4m3_encode(y)
+    fin = np.isfinite(y)
+    assert np.array_equal(got[fin], _torch_e4m3(y[fin]))
+    nan = np.isnan(y)
+    assert np.array_equal(got[nan], np.where(np.signbit(y[nan]), 0xFF, 0x7F).astype(np.uint8))
+    sp = np.array([np.inf, -np.inf, 0.0, -0.0, 448.0, 464.0, 464.0001, -480.0, 2.0 ** -10,
+                   1.5 * 2.0 ** -10, 2.0 ** -9, 2.0 ** -6, 1e-30, -1e-45], np.float32)
+    assert list(oracle.e4m3_encode(sp)) == [0x7E, 0xFE, 0x00, 0x80, 0x7E, 0x7E, 0x7E, 0xFE, 0x00,
+                                            0x01, 0x01, 0x08, 0x00, 0x80]
+
+
+def test_e4m3_decode_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.e4m3_decode(codes)
+    exp = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(exp)) and np.isnan(got).sum() == 2
+    ok = ~np.isnan(exp)
+    assert np.array_equal(got[ok].view(np.uint32), exp[ok].view(np.uint32))  # incl. -0
+    # decode then encode is the identity on every non-NaN code
+    assert np.array_equal(oracle.e4m3_encode(got[ok]), codes[ok])
+
+
+def _torch_bf16(y):
+    return torch.from_numpy(np.ascontiguousarray(y, np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+
+
+def test_bf16_rne_against_torch():
+    # exhaustive over chosen binades (subnormal, smallest normals, around 1,
+    # largest normals incl. overflow to inf), sampled elsewhere
+    for exp_field in [0, 1, 2, 126, 127, 128, 200, 253, 254]:
+        b0 = exp_field << 23
+        bits = np.arange(b0, b0 + (1 << 23), dtype=np.uint64).astype(np.uint32)
+        for sign in (0, 0x80000000):
+            y = (bits | np.uint32(sign)).view(np.float32)
+            assert np.array_equal(oracle.bf16_from_float(y), _torch_bf16(y)), exp_field
+    rng = np.random.default_rng(8)
+    y = rng.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    fin = ~np.isnan(y)
+    assert np.array_equal(oracle.bf16_from_float(y[fin]), _torch_bf16(y[fin]))
+    got_nan = oracle.bf16_from_float(y[~fin])
+    assert ((got_nan & 0x7F80) == 0x7F80).all() and ((got_nan & 0x007F) != 0).all()
+
+
+def test_fp8_scale_is_float32_division():
+    rng = np.random.default_rng(9)
+    a = np.abs(rng.standard_normal(20000).astype(np.float32)) * np.float32(30)
+    a = np.concatenate([a, np.float32([1e-38, 3e38, 448.0, 1.0, 2.0 ** -133])])
+    got = np.array([oracle.fp8_scale(float(x)) for x in a], np.float32)
+    assert np.array_equal(got.view(np.uint32), (a / np.float32(448.0)).view(np.uint32))
+    assert oracle.fp8_scale(0.0) == 1.0
+
+
+# ------------------------------------------------------------------ fp8 serde
+
+def _numpy_fp8_store(arr, bt, s, e, C):
+    """Independent formulation of gather + quantise with numpy / torch ops."""
+    L = arr.shape[0]
+    out = []
+    for c0 in range(0, e - s, C):
+        n_c = min(C, e - s - c0)
+        pages = arr[:, :, np.asarray(bt, np.int64)].reshape(L, 2, -1, arr.shape[-1])
+        g = pages[:, :, s + c0:s + c0 + n_c]                       # [L, 2, n_c, E] bf16 bits
+        x = (g.astype(np.uint32) << 16).view(np.float32)
+        amax = np.abs(x).reshape(L, 2, -1).max(axis=2)
+        scale = np.where(amax == 0, np.float32(1), amax / np.float32(448.0)).astype(np.float32)
+        y = x / scale[:, :, None, None]
+        q = _torch_e4m3(y.ravel()).reshape(y.shape)
+        out.append((np.ascontiguousarray(q).ravel(), scale.astype(np.float32).ravel()))
+    return out
+
+
+def test_fp8_store_matches_numpy_formulation():
+    w = wl.custom("fp8", 71, 3, 2, 32, 96, [(0, 600)], outliers=4)
+    arr, pool = _pool(w)
+    sq = w.seqs[0]
+    ch = oracle.alloc_chunks(pool, 0, 600, oracle.FMT_FP8, fill=0xEE)
+    assert oracle.store(pool, sq.block_table, 0, 600, ch, oracle.FMT_FP8) == 0
+    exp = _numpy_fp8_store(arr, sq.block_table, 0, 600, 256)
+    for buf, (q, sc) in zip(ch, exp):
+        assert buf.size == q.size + sc.size * 4
+        assert np.array_equal(buf[:q.size], q)
+        assert np.array_equal(buf[q.size:].view(np.float32).view(np.uint32), sc.view(np.uint32))
+
+
+def test_fp8_retrieve_matches_numpy_formulation_and_error_bound():
+    w = wl.custom("fp8rt", 72, 2, 2, 64, 64, [(0, 520)], outliers=4)
+    arr, pool = _pool(w)
+    orig = arr.copy()
+    sq = w.seqs[0]
+    ch = oracle.alloc_chunks(pool, 0, 520, oracle.FMT_FP8)
+    assert oracle.store(pool, sq.block_table, 0, 520, ch, oracle.FMT_FP8) == 0
+    arr[...] = 0
+    assert oracle.retrieve(pool, sq.block_table, 0, 520, sq.hit_mask, ch, oracle.FMT_FP8) == 520
+    L, E = w.num_layers, w.width
+    slots = _slots_of(w, sq, 520)
+    got = arr.reshape(L, 2, -1, E)[:, :, slots]                       # [L, 2, 520, E]
+    x = (orig.reshape(L, 2, -1, E)[:, :, slots].astype(np.uint32) << 16).view(np.float32)
+    at = 0
+    for c, buf in enumerate(ch):
+        n_c = oracle.chunk_tokens(0, 520, 256, c)
+        q = buf[:L * 2 * n_c * E].reshape(L, 2, n_c, E)
+        sc = buf[L * 2 * n_c * E:].view(np.float32).reshape(L, 2)
+        d = torch.from_numpy(q.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy()
+        prod = (d * sc[:, :, None, None]).astype(np.float32)
+        exp = _torch_bf16(prod.ravel()).reshape(prod.shape)
+        assert np.array_equal(got[:, :, at:at + n_c], exp)
+        # round-trip error bound: |x' - x| <= 2^-4 relative (normal range of
+        # e4m3) or 2^-10 * scale absolute (subnormal range), widened by one
+        # fp32 and one bf16 rounding: (1 + 2^-4)(1 + 2^-24)(1 + 2^-8) - 1
+        xr = (got[:, :, at:at + n_c].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        xo = x[:, :, at:at + n_c].astype(np.float64)
+        floor = (2.0 ** -6) * sc[:, :, None, None].astype(np.float64)
+        rel = np.abs(xr - xo) / np.maximum(np.abs(xo), floor)
+        bound = (1 + 2.0 ** -4) * (1 + 2.0 ** -24) * (1 + 2.0 ** -8) - 1
+        assert rel.max() <= bound <= 0.07
+        at += n_c
+
+
+def test_fp8_zero_group_and_signed_zero():
+    w = wl.custom("zero", 81, 1, 1, 16, 16, [(0, 16)])
+    arr = np.zeros(w.pool_shape(), np.uint16)
+    arr[0, 0, :, :, ::2] = 0x8000                                       # -0 in every other lane
+    _, pool = _pool(w, arr)
+    sq = w.seqs[0]
+    ch = oracle.alloc_chunks(pool, 0, 16, oracle.FMT_FP8)
+    assert oracle.store(pool, sq.block_table, 0, 16, ch, oracle.FMT_FP8) == 0
+    n = 2 * 16 * 16
+    q, sc = ch[0][:n].reshape(2, 16, 16), ch[0][n:].view(np.float32)
+    assert list(sc) == [1.0, 1.0]
+    assert (q[0, :, ::2] == 0x80).all() and (q[0, :, 1::2] == 0).all() and (q[1] == 0).all()
+
+
+def test_store_is_deterministic():
+    w = wl.custom("det", 91, 2, 2, 32, 64, [(0, 700)], outliers=4)
+    arr, pool = _pool(w)
+    sq = w.seqs[0]
+    for fmt in (oracle.FMT_BF16, oracle.FMT_FP8):
+        a = oracle.alloc_chunks(pool, 0, 700, fmt, fill=1)
+        b = oracle.alloc_chunks(pool, 0, 700, fmt, fill=2)
+        assert oracle.store(pool, sq.block_table, 0, 700, a, fmt) == 0
+        assert oracle.store(pool, sq.block_table, 0, 700, b, fmt) == 0
+        assert all(np.array_equal(x, y) for x, y in zip(a, b))
