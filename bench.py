@@ -1,0 +1,395 @@
+#!/usr/bin/env python3
+"""Paged <-> chunk KV gather/scatter throughput on one MI355X.
+
+Default workload (the headline): Llama-3.1-8B KV shape (32 layers, 8 KV
+heads, head_dim 128, bf16), 16-token pages in an 8192-page pool, 8 sequences
+of 10000 tokens.  One step = one batched store (gather of all 8 x 40 chunks,
+one launch) + one batched retrieve with the first 30 chunks of each sequence
+hit (one launch).  Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` = algorithmic bytes moved per step (every
+payload byte read once and written once) / step time, in GB/s (1e9).
+`roofline` is for the dominant kernel (the gather), timed with HIP events on
+the stream it is launched on.  `cpu_baseline` times the CPU oracle on the
+same workload's data on this host's cores.
+
+Other workloads (`--workload layerwise-8b | llama-70b-style | fp8-8b`) print
+their own JSON report line; they are not the headline.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor peak
+METRIC = "paged<->chunk KV gather/scatter GB/s and % of HBM peak (8B KV shape)"
+KERNEL_SOURCES = ["paged_kv_movement_amd/csrc/kv_kernels.hpp", "paged_kv_movement_amd/csrc/kvmove.hip"]
+TRAFFIC_FILE = "profiles/hbm_traffic_gather_llama8b.txt"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per gather launch from the committed rocprofv3 counter
+    summary, if it was taken on the kernel sources as they are now."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ setup
+
+def chunk_plan(paged, seq, fmt):
+    """Sizes of a sequence's chunks from the library (tokens per chunk: the
+    last one holds the remainder)."""
+    n = paged.num_chunks(seq.tok_start, seq.tok_end)
+    toks = [min(paged.chunk_size, seq.tok_end - seq.tok_start - c * paged.chunk_size) for c in range(n)]
+    return [paged.chunk_bytes(t, fmt) for t in toks]
+
+
+def setup(w, fmt):
+    import numpy as np
+    import torch
+    import paged_kv_movement_amd as kvm
+    from paged_kv_movement_amd import workloads as wl
+
+    t = time.time()
+    pool = wl.device_pool(w)
+    paged = kvm.Paged.from_pool(pool, chunk_size=w.chunk_size)
+    sizes = [chunk_plan(paged, sq, fmt) for sq in w.seqs]
+    align = 256
+    total = sum(-(-s // align) * align for ss in sizes for s in ss)
+    arena = torch.empty(total, dtype=torch.uint8, device="cuda")
+    base, at, seqs = arena.data_ptr(), 0, []
+    for sq, ss in zip(w.seqs, sizes):
+        addrs = []
+        for s in ss:
+            addrs.append(base + at)
+            at += -(-s // align) * align
+        bt = torch.from_numpy(np.ascontiguousarray(sq.block_table, np.int32)).cuda()
+        seqs.append(kvm.Seq(bt, sq.tok_start, sq.tok_end,
+                            torch.tensor(addrs, dtype=torch.int64).cuda()))
+    batch = kvm.Batch(paged, seqs).set_masks([sq.hit_mask for sq in w.seqs])
+    torch.cuda.synchronize()
+    log(f"setup {w.name}: pool {pool.numel() * 2 / 1e9:.2f} GB, chunks {total / 1e9:.2f} GB, "
+        f"{time.time() - t:.1f} s")
+    return pool, paged, batch, arena
+
+
+def kv_bytes_per_token(w):
+    return w.num_layers * 2 * w.width * 2
+
+
+def hit_tokens(w):
+    out = []
+    for sq in w.seqs:
+        n_hit = 0
+        while n_hit < len(sq.hit_mask) and sq.hit_mask[n_hit]:
+            n_hit += 1
+        out.append(min(sq.tok_end, sq.tok_start + n_hit * w.chunk_size) - sq.tok_start)
+    return out
+
+
+def timed(stream, fn, reps):
+    """Mean ms of fn() over reps, HIP events on `stream`."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(w, pool, budget_s=20.0):
+    """The oracle, as it stands, on this host: store + retrieve of as many of
+    the workload's sequences as fit in about budget_s, single-threaded."""
+    import numpy as np
+    import oracle
+    t = time.time()
+    arr = pool.view(__import__("torch").int16).cpu().numpy().view(np.uint16).reshape(
+        w.num_layers, 2, w.num_pages, w.page_size, w.width)
+    opool = oracle.Pool.from_array(arr, w.num_kv_heads, w.head_dim, w.chunk_size)
+    log(f"cpu baseline: pool copied to host in {time.time() - t:.1f} s")
+    moved, secs, done = 0, 0.0, 0
+    for sq in w.seqs:
+        ch = oracle.alloc_chunks(opool, sq.tok_start, sq.tok_end, oracle.FMT_BF16)
+        t0 = time.perf_counter()
+        assert oracle.store(opool, sq.block_table, sq.tok_start, sq.tok_end, ch) == 0
+        n = oracle.retrieve(opool, sq.block_table, sq.tok_start, sq.tok_end, sq.hit_mask, ch)
+        secs += time.perf_counter() - t0
+        moved += 2 * ((sq.tok_end - sq.tok_start) + n) * kv_bytes_per_token(w)
+        done += 1
+        del ch
+        if secs >= budget_s:
+            break
+    del arr, opool
+    return {"value": round(moved / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"store + retrieve (30-chunk hit mask) of {done} of {len(w.seqs)} sequences "
+                      f"of the same workload ({moved / 1e9:.2f} GB moved in {secs:.1f} s, single thread)"}
+
+
+# ------------------------------------------------------------------ workloads
+
+def bench_llama8b(args):
+    import torch
+    import paged_kv_movement_amd as kvm
+    from paged_kv_movement_amd import workloads as wl
+
+    w = wl.llama8b()
+    pool, paged, batch, arena = setup(w, kvm.FMT_BF16)
+    stream = torch.cuda.Stream()
+    bpt = kv_bytes_per_token(w)
+    store_tokens = sum(sq.tok_end - sq.tok_start for sq in w.seqs)
+    ret_tokens = sum(hit_tokens(w))
+    store_bytes = 2 * store_tokens * bpt
+    ret_bytes = 2 * ret_tokens * bpt
+
+    def store():
+        kvm.store(paged, batch, stream=stream)
+
+    def retrieve():
+        kvm.retrieve(paged, batch, stream=stream)
+
+    for _ in range(args.warmup):
+        store()
+        retrieve()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        store()
+        ev[i][1].record(stream)
+        ev[i][2].record(stream)
+        retrieve()
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    assert kvm.take_faults() == 0
+
+    step_s = (t1 - t0) / K
+    store_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    ret_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+    value = (store_bytes + ret_bytes) / step_s / 1e9
+    gather_gbps = store_bytes / (store_ms / 1e3) / 1e9
+    scatter_gbps = ret_bytes / (ret_ms / 1e3) / 1e9
+
+    # same-run calibration: a plain contiguous copy of the gather's payload
+    src = pool.view(-1).view(torch.uint8)
+    n = (store_bytes // 2) // 16 * 16
+    copy_ms = timed(stream, lambda: kvm.copy_bytes(arena, src, n, stream=stream), 5)
+    copy_gbps = 2 * n / (copy_ms / 1e3) / 1e9
+    log(f"store {store_ms:.3f} ms ({gather_gbps:.0f} GB/s), retrieve {ret_ms:.3f} ms "
+        f"({scatter_gbps:.0f} GB/s), step {step_s * 1e3:.3f} ms, copy ceiling {copy_gbps:.0f} GB/s")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama3.1-8b KV shape: 8 seqs x 10000 tokens, batched store + retrieve "
+                        "with 30 of 40 chunks hit",
+            "layers": w.num_layers, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+            "page_tokens": w.page_size, "chunk_tokens": w.chunk_size, "pool_pages": w.num_pages,
+            "seqs": len(w.seqs), "tokens_per_seq": 10000, "hit_chunks": 30,
+            "bytes_per_step": store_bytes + ret_bytes,
+            "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+            "tokens_per_s": round((store_tokens + ret_tokens) / step_s, 1),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "kvmove::move_bf16<true,...> (gather)",
+            "achieved": round(gather_gbps, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(gather_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": read_traffic(),
+            "alg_bytes_per_launch": store_bytes,
+            "avg_launch_ms": round(store_ms, 4),
+        },
+        "detail": {
+            "store_ms": round(store_ms, 4), "store_GBps": round(gather_gbps, 2),
+            "retrieve_ms": round(ret_ms, 4), "retrieve_GBps": round(scatter_gbps, 2),
+            "copy_ceiling_GBps": round(copy_gbps, 2),
+            "kernel_source_sha256_16": kernel_source_hash(),
+        },
+    }
+    if not args.no_cpu_baseline:
+        del arena
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(w, pool)
+    return out
+
+
+def bench_layerwise(args):
+    import torch
+    import paged_kv_movement_amd as kvm
+    from paged_kv_movement_amd import workloads as wl
+
+    w = wl.layerwise8b()
+    pool, paged, batch, arena = setup(w, kvm.FMT_BF16)
+    kvm.store(paged, batch)
+    torch.cuda.synchronize()
+    copy, compute = torch.cuda.Stream(), torch.cuda.Stream()
+    x = torch.randn(10240, 4096, device="cuda", dtype=torch.bfloat16)
+    wgt = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16) * 0.01
+    L = w.num_layers
+    events = [torch.cuda.Event() for _ in range(L)]
+
+    def gemms():
+        with torch.cuda.stream(compute):
+            for _ in range(L):
+                torch.mm(x, wgt)
+
+    def copies():
+        for l in range(L):
+            kvm.retrieve_layer(paged, batch, l, stream=copy, event=events[l])
+
+    def both():
+        for l in range(L):
+            kvm.retrieve_layer(paged, batch, l, stream=copy, event=events[l])
+            compute.wait_event(events[l])
+            with torch.cuda.stream(compute):
+                torch.mm(x, wgt)
+
+    def wall(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / reps * 1e3
+
+    reps = max(3, args.steps)
+    t_gemm, t_copy, t_both = wall(gemms, reps), wall(copies, reps), wall(both, reps)
+    layer_ms = timed(copy, lambda: kvm.retrieve_layer(paged, batch, 5, stream=copy), 20)
+    per_layer_bytes = 2 * 10240 * 2 * w.width * 2
+    exposed = t_both - t_gemm
+    return {
+        "metric": "layerwise onload: copy time hidden behind per-layer GEMMs",
+        "workload": "layerwise-8b: 1 seq x 10240 tokens, 32 layers, GEMM 10240x4096x4096 bf16 per layer",
+        "t_gemm_ms": round(t_gemm, 3), "t_copy_ms": round(t_copy, 3), "t_both_ms": round(t_both, 3),
+        "exposed_copy_ms": round(exposed, 3),
+        "overlap_efficiency": round((t_gemm + t_copy - t_both) / t_copy, 4),
+        "layer_scatter_ms": round(layer_ms, 4),
+        "layer_scatter_GBps": round(per_layer_bytes / (layer_ms / 1e3) / 1e9, 2),
+        "layer_scatter_pct_hbm_peak": round(100 * per_layer_bytes / (layer_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 2),
+    }
+
+
+def bench_simple(args, name, fmt):
+    """Store + retrieve GB/s for the 70B-style and fp8 workloads."""
+    import torch
+    import paged_kv_movement_amd as kvm
+    from paged_kv_movement_amd import workloads as wl
+
+    w = wl.ALL[name]()
+    pool, paged, batch, arena = setup(w, fmt)
+    stream = torch.cuda.Stream()
+    tokens = sum(sq.tok_end - sq.tok_start for sq in w.seqs)
+    rtok = sum(hit_tokens(w))
+    elems_st = tokens * w.num_layers * 2 * w.width
+    elems_rt = rtok * w.num_layers * 2 * w.width
+    groups = sum(-(-(sq.tok_end - sq.tok_start) // w.chunk_size) for sq in w.seqs) * w.num_layers * 2
+    if fmt == kvm.FMT_BF16:
+        st_bytes, rt_bytes = 4 * elems_st, 4 * elems_rt
+    else:
+        st_bytes, rt_bytes = 3 * elems_st + 4 * groups, 3 * elems_rt + 4 * groups
+    for _ in range(args.warmup):
+        kvm.store(paged, batch, fmt, stream=stream)
+        kvm.retrieve(paged, batch, fmt=fmt, stream=stream)
+    reps = max(3, args.steps)
+    st_ms = timed(stream, lambda: kvm.store(paged, batch, fmt, stream=stream), reps)
+    rt_ms = timed(stream, lambda: kvm.retrieve(paged, batch, fmt=fmt, stream=stream), reps)
+    assert kvm.take_faults() == 0
+    st, rt = st_bytes / (st_ms / 1e3) / 1e9, rt_bytes / (rt_ms / 1e3) / 1e9
+    return {
+        "metric": "store / retrieve algorithmic GB/s", "workload": name,
+        "format": "bf16" if fmt == kvm.FMT_BF16 else "fp8-e4m3-scaled",
+        "store_ms": round(st_ms, 4), "store_GBps": round(st, 2), "store_pct_hbm_peak": round(100 * st / HBM_PEAK_GBPS, 2),
+        "store_tokens_per_s": round(tokens / (st_ms / 1e3), 1),
+        "retrieve_ms": round(rt_ms, 4), "retrieve_GBps": round(rt, 2),
+        "retrieve_pct_hbm_peak": round(100 * rt / HBM_PEAK_GBPS, 2),
+        "retrieve_tokens_per_s": round(rtok / (rt_ms / 1e3), 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3.1-8b",
+                    choices=["llama3.1-8b", "layerwise-8b", "llama-70b-style", "fp8-8b"])
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle leg (used for profiler runs)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the paged<->chunk movement runs on each GPU's own "
+              "sequences with nothing exchanged, so there is no multi-GPU mode to time "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr, flush=True)
+        sys.exit(2)
+    import torch
+    import paged_kv_movement_amd as kvm
+    kvm.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    log(f"device: {torch.cuda.get_device_name(0)}")
+    if args.workload == "llama3.1-8b":
+        out = bench_llama8b(args)
+    elif args.workload == "layerwise-8b":
+        out = bench_layerwise(args)
+    elif args.workload == "llama-70b-style":
+        out = bench_simple(args, "llama-70b-style", kvm.FMT_BF16)
+    else:
+        out = bench_simple(args, "fp8-8b", kvm.FMT_FP8)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

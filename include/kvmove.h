@@ -1,0 +1,176 @@
+/*
+ * kvmove.h -- C ABI of libkvmove.so: paged <-> chunk KV-cache movement on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * An inference engine keeps each layer's K and V cache in small fixed-size
+ * pages (16 tokens here) scattered through a pool; a KV-cache layer moves it
+ * in large contiguous chunks (256 tokens by default) instead.  This library
+ * is the device-side mover between the two forms:
+ *
+ *   store    (gather)  pages -> chunk buffers, every layer, K then V;
+ *   retrieve (scatter) chunk buffers -> pages, for the leading hit chunks;
+ *   retrieve one layer, then record an event, so compute on another stream
+ *            can start on that layer while the next one is moving;
+ *   optional fp8 serde: quantise to e4m3 on store, dequantise on retrieve.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [paper]  "LMCache: An Efficient KV Cache Layer for Enterprise-Scale LLM
+ *            Inference" (paper notes): section "方法细节" (method details),
+ *            paragraphs on configurable chunk size (a custom GPU kernel copies
+ *            scattered pages into a contiguous streaming buffer as 256-token
+ *            chunks, and splits loaded chunks back into pages) and on the
+ *            layerwise pipeline (separate streams for compute and movement,
+ *            layer i+1 loads while layer i computes); Table 2 (connector
+ *            calls start_load_kv / wait_load_kv(layer)).
+ *   [walk]   "LMCache 源码解析：一个文件讲透KV缓存复用机制" (cache_engine.py
+ *            walkthrough): sections "store()" (chunking, batched gather of
+ *            all chunks in one call), "retrieve()" (hits count from chunk 0
+ *            and stop at the first miss; whole chunks may return more tokens
+ *            than asked), "性能细节" (no transfer when nothing hits),
+ *            "工程实践" (the computed prefix must be a whole number of chunks).
+ *   [blob]   "LMCache 中的 KV Cache 压缩：CacheGen 编解码原理..." (CacheGen
+ *            page), section "2. 量化": a chunk's KV blob is shaped
+ *            [num_layers, 2, num_tokens, num_heads, head_size].
+ *   [serde]  "LMCache 分布式 KV Cache 序列化框架 Serde..." (serde framework
+ *            page), sections "4.2" (exact, layout-only size estimate) and
+ *            "7.1 fp8 量化" (fp8 e4m3 cast, one byte per element, lossy).
+ *
+ * Layouts (all little-endian):
+ *   Pool   For layer l, k_pages[l] / v_pages[l] hold the device address of a
+ *          bf16 array [num_pages][page_size][num_kv_heads][head_dim].  Token t
+ *          of a sequence lives in row t % page_size of page
+ *          block_table[t / page_size].
+ *   Chunk  A chunk of n tokens (n <= chunk_size; only a sequence's last chunk
+ *          is short) is one buffer laid out [num_layers][2][n][H][D] ([blob];
+ *          K before V).  bf16: 2 bytes per element.  fp8: 1 byte per element
+ *          (OCP E4M3, "fn" variant) followed by float32 scales[num_layers][2].
+ *          kv_chunk_bytes() gives the exact size.
+ *
+ * fp8 serde: per (chunk, layer, K/V) group, amax = max |x| (a NaN anywhere
+ * makes it NaN); scale = amax / 448 in float32 (scale = 1 when amax == 0);
+ * q = e4m3(x / scale) with an IEEE float32 division, rounding to nearest-even
+ * and saturating at +-448.  Retrieve writes bf16(float(q) * scale), the
+ * product in float32 and the bf16 rounding to nearest-even.
+ *
+ * Ownership: every buffer is allocated and freed by the caller.  The library
+ * allocates nothing and keeps no state between calls except a per-device
+ * fault word (kv_take_faults).  Host arrays are read only during the call.
+ *
+ * Ordering: every call enqueues work on the given HIP stream (0 = the null
+ * stream) and returns without waiting for it.  Results computed from host
+ * data (out_tokens) are final on return.
+ *
+ * Errors: every int-returning call returns KV_OK or a negative kv_status and
+ * launches nothing on error; kv_last_error() then describes it (per thread).
+ * Device-array contents (page ids, chunk addresses, their 16-byte
+ * alignment) are checked inside the kernels: an offending row group is
+ * skipped and a fault bit is set (kv_take_faults); the kernels never access
+ * memory outside [page 0, page num_pages) of a layer's pool because of a bad
+ * page id.  Chunk capacity cannot be checked: a chunk buffer must hold
+ * kv_chunk_bytes() for its token count.
+ */
+#ifndef KVMOVE_H
+#define KVMOVE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KV_OK = 0,
+    KV_EINVAL = -1, /* malformed argument (null pointer, bad shape, misaligned start, bad format) */
+    KV_ERANGE = -2, /* token range beyond the block table */
+    KV_EHIP = -3    /* the HIP runtime refused a launch or an event record */
+} kv_status;
+
+typedef enum {
+    KV_FMT_BF16 = 0,            /* bf16 copied bit for bit ("naive" serde) */
+    KV_FMT_FP8_E4M3_SCALED = 1  /* e4m3 bytes + one float32 scale per (layer, K/V) */
+} kv_fmt;
+
+/* The engine's paged pool.  All pointers are caller-owned. */
+typedef struct {
+    int32_t num_layers;     /* L  > 0 */
+    int32_t num_kv_heads;   /* H  > 0 */
+    int32_t head_dim;       /* D  > 0; H*D must be a multiple of 8 (16-byte rows) */
+    int32_t page_size;      /* P  > 0 tokens per page (16 in vLLM-style engines) */
+    int32_t chunk_size;     /* C  > 0 tokens per chunk, a multiple of P (256 by default) */
+    int64_t num_pages;      /* pages in each layer's K (and V) pool */
+    const uint64_t* k_pages;/* DEVICE uint64[L]: address of layer l's K pool, 16-byte aligned */
+    const uint64_t* v_pages;/* DEVICE uint64[L]: address of layer l's V pool, 16-byte aligned */
+} kv_paged;
+
+/* One sequence's job. */
+typedef struct {
+    const int32_t* block_table; /* DEVICE int32[n_bt]: page id of tokens [P*i, P*(i+1)) */
+    int64_t n_bt;               /* entries in block_table */
+    int64_t tok_start;          /* first token; a multiple of chunk_size ([walk] "工程实践") */
+    int64_t tok_end;            /* one past the last token; tok_start <= tok_end <= P*n_bt */
+    const uint64_t* chunks;     /* DEVICE uint64[n_chunks]: address of chunk c's buffer,
+                                   16-byte aligned, >= kv_chunk_bytes(tokens of chunk c) */
+} kv_seq;
+
+/* Exact bytes of one chunk holding n_tokens tokens in format fmt ([serde]
+ * "4.2": deterministic, from the layout alone); 0 on a malformed argument. */
+size_t kv_chunk_bytes(const kv_paged* paged, int64_t n_tokens, int fmt);
+
+/* Chunks covering [tok_start, tok_end): ceil((tok_end - tok_start) / C); the
+ * last one holds the remainder ([walk] "store()").  -1 on a malformed argument. */
+int64_t kv_num_chunks(const kv_paged* paged, int64_t tok_start, int64_t tok_end);
+
+/* Store: gather every chunk of every sequence, all layers, K and V, into the
+ * sequences' chunk buffers, in one batched launch ([paper] configurable chunk
+ * size; [walk] "store()").  fmt KV_FMT_FP8_E4M3_SCALED quantises on the way
+ * ([serde] "7.1").  The pool is only read.  Sequences with an empty range are
+ * skipped.  To store a shorter prefix (e.g. after a failed allocation, [walk]
+ * "store()"), pass a smaller tok_end. */
+int kv_store_chunks(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int fmt,
+                    hipStream_t stream);
+
+/* Retrieve: for sequence i, n_hit = index of the first 0 in hit_mask[i][0 ..
+ * n_chunks) (n_chunks if none); scatter chunks [0, n_hit) back into the
+ * sequence's pages, all layers, K and V ([paper] configurable chunk size;
+ * [walk] "retrieve()": a hole ends the hits even if later flags are set).
+ * Page rows outside those chunks are not written.  out_tokens[i] (HOST,
+ * may be NULL) = min(tok_end, tok_start + n_hit*C) - tok_start, which can
+ * exceed what the engine lacked because whole chunks come back.  hit_mask is
+ * a HOST array of n_seqs HOST pointers (an entry may be NULL when the range
+ * is empty).  Nothing is launched when no chunk hits ([walk] "性能细节").
+ * The page ids written by one call must be distinct. */
+int kv_retrieve_chunks(const kv_paged* paged, const kv_seq* seqs,
+                       const uint8_t* const* hit_mask, int n_seqs, int fmt,
+                       int64_t* out_tokens, hipStream_t stream);
+
+/* Layerwise retrieve ([paper] layerwise pipeline; Table 2 start_load_kv /
+ * wait_load_kv(layer)): as kv_retrieve_chunks but writes layer `layer` only,
+ * on copy_stream, then records layer_done (if not NULL) on copy_stream -- also
+ * when nothing hits, so a stream or host waiting on it never hangs.  Calling
+ * it for layers 0 .. L-1 leaves the pool as one kv_retrieve_chunks call does. */
+int kv_retrieve_layer(const kv_paged* paged, const kv_seq* seqs,
+                      const uint8_t* const* hit_mask, int n_seqs, int fmt, int32_t layer,
+                      int64_t* out_tokens, hipStream_t copy_stream, hipEvent_t layer_done);
+
+/* Message for the last non-OK return on this thread ("" if none). */
+const char* kv_last_error(void);
+
+/* Waits for the current device, returns the fault bits the kernels set since
+ * the last call on this device (1: page id out of range, 2: null or
+ * misaligned chunk address, 4: null or misaligned pool address), and clears
+ * them.  Returns -1 (KV_EHIP) if the device cannot be read. */
+int kv_take_faults(void);
+
+/* Measurement aid, not part of the movement path: a plain contiguous
+ * device-to-device copy of `bytes` bytes (a multiple of 16; both addresses
+ * 16-byte aligned) with the same vector width as the movers, used as the
+ * achievable-copy ceiling and to calibrate HBM traffic counters. */
+int kv_copy_bytes(void* dst, const void* src, size_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVMOVE_H */

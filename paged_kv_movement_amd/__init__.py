@@ -1,1 +1,265 @@
-"""MI355X-native paged <-> chunk KV-cache movement (binding over libkvmove.so)."""
+"""MI355X-native paged <-> chunk KV-cache movement: Python binding of libkvmove.so.
+
+Argument marshalling only.  Every byte is moved by the HIP kernels behind the
+C ABI in ``include/kvmove.h``; this module turns torch device tensors,
+streams and events into the raw addresses and handles that ABI takes.  There
+is no fallback: if ``libkvmove.so`` is missing the first call raises.
+
+Typical use::
+
+    import paged_kv_movement_amd as kvm
+    pool = torch.empty(L, 2, num_pages, 16, H, D, dtype=torch.bfloat16, device="cuda")
+    paged = kvm.Paged.from_pool(pool, chunk_size=256)
+    chunks = [torch.empty(paged.chunk_bytes(n), dtype=torch.uint8, device="cuda") for n in ...]
+    batch = kvm.Batch(paged, [kvm.Seq(block_table, 0, 10000, chunks)])
+    kvm.store(paged, batch)                            # gather pages -> chunks
+    n = kvm.retrieve(paged, batch, masks=[hit_mask])   # scatter hit chunks -> pages
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["FMT_BF16", "FMT_FP8", "KvError", "Paged", "Seq", "Batch", "store", "retrieve",
+           "retrieve_layer", "take_faults", "copy_bytes", "library_path", "load"]
+
+FMT_BF16 = 0
+FMT_FP8 = 1
+
+KV_OK, KV_EINVAL, KV_ERANGE, KV_EHIP = 0, -1, -2, -3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkvmove.so")
+_lib = None
+
+
+class KvError(RuntimeError):
+    """A non-OK status from libkvmove (the message is kv_last_error())."""
+
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"kvmove error {code}: {msg}")
+        self.code = code
+
+
+class _KvPaged(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("chunk_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+        ("k_pages", ctypes.c_void_p),
+        ("v_pages", ctypes.c_void_p),
+    ]
+
+
+class _KvSeq(ctypes.Structure):
+    _fields_ = [
+        ("block_table", ctypes.c_void_p),
+        ("n_bt", ctypes.c_int64),
+        ("tok_start", ctypes.c_int64),
+        ("tok_end", ctypes.c_int64),
+        ("chunks", ctypes.c_void_p),
+    ]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libkvmove.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise KvError(KV_EHIP, f"{_LIB_PATH} is missing: build it with "
+                               "`python -m paged_kv_movement_amd.build` (there is no fallback)")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, S = ctypes.POINTER(_KvPaged), ctypes.POINTER(_KvSeq)
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    sig = {
+        "kv_chunk_bytes": (ctypes.c_size_t, [P, i64, ctypes.c_int]),
+        "kv_num_chunks": (i64, [P, i64, i64]),
+        "kv_store_chunks": (ctypes.c_int, [P, S, ctypes.c_int, ctypes.c_int, vp]),
+        "kv_retrieve_chunks": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, vp, vp]),
+        "kv_retrieve_layer": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, i32, vp, vp, vp]),
+        "kv_last_error": (ctypes.c_char_p, []),
+        "kv_take_faults": (ctypes.c_int, []),
+        "kv_copy_bytes": (ctypes.c_int, [vp, vp, ctypes.c_size_t, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != KV_OK:
+        raise KvError(rc, load().kv_last_error().decode())
+
+
+def _stream_handle(stream) -> int | None:
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    h = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return h or None
+
+
+class Paged:
+    """The engine's paged pool: per-layer K and V base addresses on the device.
+
+    ``k_addrs`` / ``v_addrs`` are device int64 tensors [num_layers] holding the
+    address of each layer's bf16 [num_pages][page_size][H][D] K / V pool.
+    """
+
+    def __init__(self, k_addrs, v_addrs, num_layers, num_kv_heads, head_dim, page_size,
+                 chunk_size, num_pages, keepalive=()):
+        self.k_addrs, self.v_addrs = k_addrs, v_addrs
+        self._keep = tuple(keepalive)
+        self.num_layers, self.num_kv_heads, self.head_dim = num_layers, num_kv_heads, head_dim
+        self.page_size, self.chunk_size, self.num_pages = page_size, chunk_size, num_pages
+        self.c = _KvPaged(num_layers, num_kv_heads, head_dim, page_size, chunk_size, num_pages,
+                          k_addrs.data_ptr(), v_addrs.data_ptr())
+
+    @classmethod
+    def from_pool(cls, pool, chunk_size: int = 256) -> "Paged":
+        """From one bf16 tensor [L, 2, num_pages, page_size, H, D] (K at [:, 0], V at [:, 1])."""
+        import torch
+        assert pool.dtype == torch.bfloat16 and pool.is_contiguous() and pool.dim() == 6
+        L, two, n, P, H, D = pool.shape
+        assert two == 2
+        slab = n * P * H * D * pool.element_size()
+        base = pool.data_ptr()
+        k = torch.tensor([base + (2 * l) * slab for l in range(L)], dtype=torch.int64)
+        v = torch.tensor([base + (2 * l + 1) * slab for l in range(L)], dtype=torch.int64)
+        return cls(k.to(pool.device), v.to(pool.device), L, H, D, P, chunk_size, n, keepalive=(pool,))
+
+    @classmethod
+    def from_layers(cls, k_layers, v_layers, chunk_size: int = 256) -> "Paged":
+        """From per-layer bf16 tensors, each [num_pages, page_size, H, D]."""
+        import torch
+        n, P, H, D = k_layers[0].shape
+        for t in list(k_layers) + list(v_layers):
+            assert t.dtype == torch.bfloat16 and t.is_contiguous() and tuple(t.shape) == (n, P, H, D)
+        dev = k_layers[0].device
+        k = torch.tensor([t.data_ptr() for t in k_layers], dtype=torch.int64).to(dev)
+        v = torch.tensor([t.data_ptr() for t in v_layers], dtype=torch.int64).to(dev)
+        return cls(k, v, len(k_layers), H, D, P, chunk_size, n, keepalive=(*k_layers, *v_layers))
+
+    def chunk_bytes(self, n_tokens: int, fmt: int = FMT_BF16) -> int:
+        n = load().kv_chunk_bytes(ctypes.byref(self.c), n_tokens, fmt)
+        if n == 0 and n_tokens > 0:
+            _check(KV_EINVAL)
+        return int(n)
+
+    def num_chunks(self, tok_start: int, tok_end: int) -> int:
+        n = load().kv_num_chunks(ctypes.byref(self.c), tok_start, tok_end)
+        if n < 0:
+            _check(KV_EINVAL)
+        return int(n)
+
+
+class Seq:
+    """One sequence's job: a device int32 block table, a token range and its
+    chunk buffers (device uint8 tensors, or a device int64 tensor of addresses)."""
+
+    def __init__(self, block_table, tok_start: int, tok_end: int, chunks):
+        import torch
+        self.block_table = block_table
+        self.tok_start, self.tok_end = int(tok_start), int(tok_end)
+        if isinstance(chunks, torch.Tensor) and chunks.dtype == torch.int64:
+            self.chunk_addrs, self._chunks = chunks, None
+        else:
+            self._chunks = list(chunks)
+            addrs = torch.tensor([c.data_ptr() for c in self._chunks], dtype=torch.int64)
+            dev = block_table.device if isinstance(block_table, torch.Tensor) else "cuda"
+            self.chunk_addrs = addrs.to(dev)
+        assert block_table.dtype == torch.int32 and block_table.is_contiguous()
+
+    def c(self) -> _KvSeq:
+        return _KvSeq(self.block_table.data_ptr(), self.block_table.numel(), self.tok_start,
+                      self.tok_end, self.chunk_addrs.data_ptr() if self.chunk_addrs.numel() else 0)
+
+
+class Batch:
+    """Prebuilt C descriptors for a list of Seq (reusable across calls)."""
+
+    def __init__(self, paged: Paged, seqs):
+        self.seqs = list(seqs)
+        n = len(self.seqs)
+        self.arr = (_KvSeq * max(1, n))(*[s.c() for s in self.seqs])
+        self.n = n
+        self._mask_bufs = None
+        self._mask_ptrs = None
+        self.out = (ctypes.c_int64 * max(1, n))()
+
+    def set_masks(self, masks):
+        """Host hit masks, one uint8 flag per chunk per sequence."""
+        assert len(masks) == self.n
+        bufs = []
+        for m in masks:
+            b = bytes(int(x) & 0xFF for x in (m.tolist() if hasattr(m, "tolist") else m))
+            bufs.append(ctypes.create_string_buffer(b, max(1, len(b))))
+        self._mask_bufs = bufs
+        self._mask_ptrs = (ctypes.c_void_p * max(1, self.n))(
+            *[ctypes.cast(b, ctypes.c_void_p).value for b in bufs])
+        return self
+
+
+def _batch(paged, seqs) -> Batch:
+    return seqs if isinstance(seqs, Batch) else Batch(paged, seqs)
+
+
+def store(paged: Paged, seqs, fmt: int = FMT_BF16, stream=None) -> None:
+    """Gather every chunk of every sequence (kv_store_chunks)."""
+    b = _batch(paged, seqs)
+    _check(load().kv_store_chunks(ctypes.byref(paged.c), b.arr, b.n, fmt, _stream_handle(stream)))
+
+
+def retrieve(paged: Paged, seqs, masks=None, fmt: int = FMT_BF16, stream=None) -> list:
+    """Scatter the leading hit chunks back into pages (kv_retrieve_chunks).
+    Returns the tokens made available per sequence."""
+    b = _batch(paged, seqs)
+    if masks is not None:
+        b.set_masks(masks)
+    assert b._mask_ptrs is not None, "hit masks are required"
+    _check(load().kv_retrieve_chunks(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n, fmt, b.out,
+                                     _stream_handle(stream)))
+    return [int(b.out[i]) for i in range(b.n)]
+
+
+def retrieve_layer(paged: Paged, seqs, layer: int, masks=None, fmt: int = FMT_BF16,
+                   stream=None, event=None) -> list:
+    """Scatter one layer of the leading hit chunks on ``stream``, then record
+    ``event`` (a torch.cuda.Event) on it (kv_retrieve_layer)."""
+    b = _batch(paged, seqs)
+    if masks is not None:
+        b.set_masks(masks)
+    assert b._mask_ptrs is not None, "hit masks are required"
+    ev = None
+    if event is not None:
+        if not event.cuda_event:        # torch creates the event lazily on first record
+            import torch
+            event.record(stream if stream is not None else torch.cuda.current_stream())
+        ev = event.cuda_event
+    _check(load().kv_retrieve_layer(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n, fmt, layer,
+                                    b.out, _stream_handle(stream), ev))
+    return [int(b.out[i]) for i in range(b.n)]
+
+
+def take_faults() -> int:
+    """Synchronise the device; return and clear the kernels' fault bits."""
+    rc = load().kv_take_faults()
+    if rc < 0:
+        _check(rc)
+    return rc
+
+
+def copy_bytes(dst, src, nbytes: int, stream=None) -> None:
+    """Plain contiguous device copy (measurement aid)."""
+    _check(load().kv_copy_bytes(dst.data_ptr(), src.data_ptr(), nbytes, _stream_handle(stream)))

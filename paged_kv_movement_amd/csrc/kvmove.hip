@@ -1,0 +1,327 @@
+// kvmove.hip -- host side of libkvmove.so: argument checks, unit planning and
+// launches for the C ABI declared in include/kvmove.h.
+//
+// Every entry point validates everything it can see on the host first and
+// returns an error without launching anything; the device-side contents
+// (page ids, chunk addresses) are checked by the kernels themselves.
+#include "kvmove.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kv_kernels.hpp"
+
+namespace {
+
+using namespace kvmove;
+
+// Launch shape of the movers (tuned on MI355X, see the measurement notes).
+constexpr int kMoveBlock = 256;
+constexpr int kMoveVpt = 8;          // 256 x 8 x 16 B = one 32 KiB page unit per pass
+constexpr bool kMoveNtLoad = false;
+constexpr bool kMoveNtStore = false;
+constexpr int kFp8Block = 256;
+constexpr int kCopyBlock = 256;
+constexpr int kCopyVpt = 8;
+// Workgroups per launch: gridDim.x * blockDim.x must stay below 2^32.
+constexpr int64_t kMaxUnits = (int64_t(1) << 24) - 1;
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok()
+{
+    g_last_error.clear();
+    return KV_OK;
+}
+
+int check_paged(const kv_paged* p)
+{
+    if (p == nullptr) return fail(KV_EINVAL, "paged is NULL");
+    if (p->num_layers <= 0 || p->num_kv_heads <= 0 || p->head_dim <= 0)
+        return fail(KV_EINVAL, "num_layers, num_kv_heads and head_dim must be > 0 (got %d, %d, %d)",
+                    p->num_layers, p->num_kv_heads, p->head_dim);
+    const int64_t width = int64_t(p->num_kv_heads) * p->head_dim;
+    if (width % 8 != 0 || width > (int64_t(1) << 30))
+        return fail(KV_EINVAL, "num_kv_heads*head_dim = %lld must be a multiple of 8 (16-byte rows)",
+                    (long long)width);
+    if (p->page_size <= 0 || p->chunk_size <= 0 || p->chunk_size % p->page_size != 0)
+        return fail(KV_EINVAL, "page_size (%d) and chunk_size (%d) must be > 0, chunk a multiple of page",
+                    p->page_size, p->chunk_size);
+    if (p->num_pages <= 0) return fail(KV_EINVAL, "num_pages must be > 0");
+    if (p->k_pages == nullptr || p->v_pages == nullptr)
+        return fail(KV_EINVAL, "k_pages / v_pages address arrays are NULL");
+    return KV_OK;
+}
+
+int check_fmt(int fmt)
+{
+    if (fmt != KV_FMT_BF16 && fmt != KV_FMT_FP8_E4M3_SCALED)
+        return fail(KV_EINVAL, "unknown format %d", fmt);
+    return KV_OK;
+}
+
+int check_seq(const kv_paged* p, const kv_seq* s, int i)
+{
+    if (s->tok_start < 0 || s->tok_end < s->tok_start)
+        return fail(KV_EINVAL, "seq %d: need 0 <= tok_start <= tok_end (got %lld, %lld)", i,
+                    (long long)s->tok_start, (long long)s->tok_end);
+    if (s->tok_start % p->chunk_size != 0)
+        return fail(KV_EINVAL, "seq %d: tok_start %lld is not a multiple of chunk_size %d", i,
+                    (long long)s->tok_start, p->chunk_size);
+    if (s->n_bt < 0 || s->n_bt > INT32_MAX)
+        return fail(KV_EINVAL, "seq %d: n_bt %lld outside [0, 2^31)", i, (long long)s->n_bt);
+    if (s->tok_end > s->n_bt * p->page_size)
+        return fail(KV_ERANGE, "seq %d: tok_end %lld beyond the block table (%lld pages of %d)", i,
+                    (long long)s->tok_end, (long long)s->n_bt, p->page_size);
+    if (s->tok_end > s->tok_start && (s->block_table == nullptr || s->chunks == nullptr))
+        return fail(KV_EINVAL, "seq %d: block_table / chunks is NULL", i);
+    return KV_OK;
+}
+
+int check_seqs(const kv_paged* p, const kv_seq* seqs, int n_seqs)
+{
+    if (n_seqs < 0) return fail(KV_EINVAL, "n_seqs < 0");
+    if (n_seqs > 0 && seqs == nullptr) return fail(KV_EINVAL, "seqs is NULL");
+    for (int i = 0; i < n_seqs; ++i) {
+        int rc = check_seq(p, &seqs[i], i);
+        if (rc != KV_OK) return rc;
+    }
+    return KV_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Leading hit chunks: first 0 in the mask ends the hits.
+int64_t hit_chunks(const uint8_t* mask, int64_t n_chunks)
+{
+    int64_t c = 0;
+    while (c < n_chunks && mask[c] != 0) ++c;
+    return c;
+}
+
+enum class Unit { Page, Group };
+
+using KernelFn = const void*;
+
+// Packs up to kMaxSeqs non-empty sequences per launch, keeping every launch
+// under kMaxUnits units (the kernels index units in 32 bits).  n_tok[i] is the
+// token count moved for sequence i (from its tok_start).
+int launch_units(KernelFn kernel, int block, Unit unit, const kv_paged* p, const kv_seq* seqs,
+                 const int64_t* n_tok, int n_seqs, int32_t layer0, int32_t n_layers,
+                 hipStream_t stream)
+{
+    MoveArgs a{};
+    a.k_pages = reinterpret_cast<uint64_t>(p->k_pages);
+    a.v_pages = reinterpret_cast<uint64_t>(p->v_pages);
+    a.num_pages = p->num_pages;
+    a.width = uint32_t(p->num_kv_heads * p->head_dim);
+    a.page_size = uint32_t(p->page_size);
+    a.chunk_size = uint32_t(p->chunk_size);
+    a.pages_per_chunk = uint32_t(p->chunk_size / p->page_size);
+    a.units_per_chunk = unit == Unit::Page ? uint32_t(n_layers) * 2 * a.pages_per_chunk
+                                           : uint32_t(n_layers) * 2;
+    a.num_layers = uint32_t(p->num_layers);
+    a.layer0 = uint32_t(layer0);
+    a.n_layers = uint32_t(n_layers);
+
+    auto flush = [&](int64_t total) -> int {
+        a.item_base = 0;
+        void* args[] = {&a};
+        hipError_t e = hipLaunchKernel(kernel, dim3((unsigned)total), dim3(block), args, 0, stream);
+        if (e != hipSuccess) return fail(KV_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+        return KV_OK;
+    };
+
+    int64_t total = 0;
+    a.n_seqs = 0;
+    for (int i = 0; i < n_seqs; ++i) {
+        if (n_tok[i] <= 0) continue;
+        const int64_t units = unit == Unit::Page
+                                  ? ceil_div(n_tok[i], p->page_size) * n_layers * 2
+                                  : ceil_div(n_tok[i], p->chunk_size) * n_layers * 2;
+        if (units > kMaxUnits)
+            return fail(KV_EINVAL, "seq %d: %lld work units exceed one launch", i, (long long)units);
+        if (a.n_seqs == kMaxSeqs || total + units > kMaxUnits) {
+            int rc = flush(total);
+            if (rc != KV_OK) return rc;
+            a.n_seqs = 0;
+            total = 0;
+        }
+        SeqArg& s = a.seq[a.n_seqs++];
+        s.bt = reinterpret_cast<uint64_t>(seqs[i].block_table);
+        s.chunks = reinterpret_cast<uint64_t>(seqs[i].chunks);
+        s.first_page = uint32_t(seqs[i].tok_start / p->page_size);
+        s.n_full = uint32_t(n_tok[i] / p->chunk_size);
+        s.tail_tokens = uint32_t(n_tok[i] % p->chunk_size);
+        s.item_begin = uint32_t(total);
+        total += units;
+    }
+    if (a.n_seqs > 0) return flush(total);
+    return KV_OK;
+}
+
+KernelFn gather_kernel(int fmt)
+{
+    if (fmt == KV_FMT_BF16)
+        return reinterpret_cast<KernelFn>(
+            &move_bf16<true, kMoveBlock, kMoveVpt, kMoveNtLoad, kMoveNtStore>);
+    return reinterpret_cast<KernelFn>(&store_fp8<kFp8Block>);
+}
+
+KernelFn scatter_kernel(int fmt)
+{
+    if (fmt == KV_FMT_BF16)
+        return reinterpret_cast<KernelFn>(
+            &move_bf16<false, kMoveBlock, kMoveVpt, kMoveNtLoad, kMoveNtStore>);
+    return reinterpret_cast<KernelFn>(&retrieve_fp8<kFp8Block>);
+}
+
+int block_of(int fmt) { return fmt == KV_FMT_BF16 ? kMoveBlock : kFp8Block; }
+
+// Shared body of the two retrieve entry points.
+int retrieve(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
+             int fmt, int32_t layer0, int32_t n_layers, int64_t* out_tokens, hipStream_t stream)
+{
+    if (n_seqs > 0 && hit_mask == nullptr) return fail(KV_EINVAL, "hit_mask is NULL");
+    int64_t small[64];
+    int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
+    for (int i = 0; i < n_seqs; ++i) {
+        const kv_seq& s = seqs[i];
+        const int64_t n_chunks = ceil_div(s.tok_end - s.tok_start, paged->chunk_size);
+        if (n_chunks > 0 && hit_mask[i] == nullptr) {
+            if (n_tok != small) delete[] n_tok;
+            return fail(KV_EINVAL, "seq %d: hit_mask entry is NULL", i);
+        }
+        const int64_t n_hit = n_chunks > 0 ? hit_chunks(hit_mask[i], n_chunks) : 0;
+        const int64_t end = s.tok_start + n_hit * paged->chunk_size;
+        n_tok[i] = (end < s.tok_end ? end : s.tok_end) - s.tok_start;
+    }
+    int rc = launch_units(scatter_kernel(fmt), block_of(fmt), Unit::Page, paged, seqs, n_tok, n_seqs,
+                          layer0, n_layers, stream);
+    if (rc == KV_OK && out_tokens != nullptr)
+        for (int i = 0; i < n_seqs; ++i) out_tokens[i] = n_tok[i];
+    if (n_tok != small) delete[] n_tok;
+    return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kv_chunk_bytes(const kv_paged* paged, int64_t n_tokens, int fmt)
+{
+    if (check_paged(paged) != KV_OK || check_fmt(fmt) != KV_OK) return 0;
+    if (n_tokens < 0) {
+        fail(KV_EINVAL, "n_tokens < 0");
+        return 0;
+    }
+    const int64_t elems = int64_t(paged->num_layers) * 2 * n_tokens * paged->num_kv_heads * paged->head_dim;
+    if (fmt == KV_FMT_BF16) return size_t(elems) * 2;
+    return size_t(elems) + size_t(paged->num_layers) * 2 * sizeof(float);
+}
+
+int64_t kv_num_chunks(const kv_paged* paged, int64_t tok_start, int64_t tok_end)
+{
+    if (check_paged(paged) != KV_OK) return -1;
+    if (tok_start < 0 || tok_end < tok_start) {
+        fail(KV_EINVAL, "need 0 <= tok_start <= tok_end");
+        return -1;
+    }
+    return ceil_div(tok_end - tok_start, paged->chunk_size);
+}
+
+int kv_store_chunks(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int fmt, hipStream_t stream)
+{
+    int rc = check_paged(paged);
+    if (rc == KV_OK) rc = check_fmt(fmt);
+    if (rc == KV_OK) rc = check_seqs(paged, seqs, n_seqs);
+    if (rc != KV_OK) return rc;
+    int64_t small[64];
+    int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
+    for (int i = 0; i < n_seqs; ++i) n_tok[i] = seqs[i].tok_end - seqs[i].tok_start;
+    rc = launch_units(gather_kernel(fmt), block_of(fmt),
+                      fmt == KV_FMT_BF16 ? Unit::Page : Unit::Group, paged, seqs, n_tok, n_seqs, 0,
+                      paged->num_layers, stream);
+    if (n_tok != small) delete[] n_tok;
+    return rc == KV_OK ? ok() : rc;
+}
+
+int kv_retrieve_chunks(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask,
+                       int n_seqs, int fmt, int64_t* out_tokens, hipStream_t stream)
+{
+    int rc = check_paged(paged);
+    if (rc == KV_OK) rc = check_fmt(fmt);
+    if (rc == KV_OK) rc = check_seqs(paged, seqs, n_seqs);
+    if (rc != KV_OK) return rc;
+    rc = retrieve(paged, seqs, hit_mask, n_seqs, fmt, 0, paged->num_layers, out_tokens, stream);
+    return rc == KV_OK ? ok() : rc;
+}
+
+int kv_retrieve_layer(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask,
+                      int n_seqs, int fmt, int32_t layer, int64_t* out_tokens, hipStream_t copy_stream,
+                      hipEvent_t layer_done)
+{
+    int rc = check_paged(paged);
+    if (rc == KV_OK) rc = check_fmt(fmt);
+    if (rc == KV_OK) rc = check_seqs(paged, seqs, n_seqs);
+    if (rc != KV_OK) return rc;
+    if (layer < 0 || layer >= paged->num_layers)
+        return fail(KV_EINVAL, "layer %d outside [0, %d)", layer, paged->num_layers);
+    rc = retrieve(paged, seqs, hit_mask, n_seqs, fmt, layer, 1, out_tokens, copy_stream);
+    if (rc != KV_OK) return rc;
+    if (layer_done != nullptr) {
+        hipError_t e = hipEventRecord(layer_done, copy_stream);
+        if (e != hipSuccess) return fail(KV_EHIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+    }
+    return ok();
+}
+
+const char* kv_last_error(void) { return g_last_error.c_str(); }
+
+int kv_take_faults(void)
+{
+    hipError_t e = hipDeviceSynchronize();
+    unsigned int v = 0;
+    const unsigned int zero = 0;
+    if (e == hipSuccess) e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_kv_faults), sizeof v, 0, hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(g_kv_faults), &zero, sizeof zero, 0, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail(KV_EHIP, "reading the fault word failed: %s", hipGetErrorString(e));
+    return int(v);
+}
+
+int kv_copy_bytes(void* dst, const void* src, size_t bytes, hipStream_t stream)
+{
+    if (dst == nullptr || src == nullptr) return fail(KV_EINVAL, "dst / src is NULL");
+    if (bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(dst) & 15) || (reinterpret_cast<uintptr_t>(src) & 15))
+        return fail(KV_EINVAL, "kv_copy_bytes needs 16-byte aligned addresses and a multiple of 16 bytes");
+    const int64_t nvec = int64_t(bytes / 16);
+    if (nvec == 0) return ok();
+    const int64_t tile = int64_t(kCopyBlock) * kCopyVpt;
+    const int64_t grid = ceil_div(nvec, tile);
+    if (grid > (int64_t(1) << 31) - 1) return fail(KV_EINVAL, "copy too large");
+    uint64_t s = reinterpret_cast<uint64_t>(src);
+    uint64_t d = reinterpret_cast<uint64_t>(dst);
+    int64_t n = nvec;
+    void* args[] = {&s, &d, &n};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<KernelFn>(&copy_contiguous<kCopyBlock, kCopyVpt>),
+                                   dim3((unsigned)grid), dim3(kCopyBlock), args, 0, stream);
+    if (e != hipSuccess) return fail(KV_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

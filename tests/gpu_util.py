@@ -1,0 +1,122 @@
+"""Plumbing shared by the GPU parity tests: moving workloads between host
+numpy arrays (what the oracle reads) and device tensors (what the HIP path
+reads), and allocating guarded chunk buffers.  No movement arithmetic here
+beyond sizes taken from the library and from the oracle."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_movement_amd as kvm
+
+GUARD = 256          # bytes after each device chunk that must stay untouched
+GUARD_FILL = 0x5A
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_pool_from_host(w, arr):
+    L, _, n, P, E = arr.shape
+    t = torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16)
+    return t.reshape(L, 2, n, P, w.num_kv_heads, w.head_dim).to("cuda")
+
+
+def host_from_dev_pool(pool):
+    L, two, n, P, H, D = pool.shape
+    return pool.view(torch.int16).cpu().numpy().view(np.uint16).reshape(L, 2, n, P, H * D)
+
+
+def oracle_pool(w, arr):
+    return oracle.Pool.from_array(arr, w.num_kv_heads, w.head_dim, w.chunk_size)
+
+
+def chunk_tokens(w, sq):
+    """Token count of each chunk of a sequence, from the oracle."""
+    n = oracle.num_chunks(sq.tok_start, sq.tok_end, w.chunk_size)
+    return [oracle.chunk_tokens(sq.tok_start, sq.tok_end, w.chunk_size, c) for c in range(n)]
+
+
+def alloc_dev_chunks(paged, w, sq, fmt, fill=0x00):
+    """One device uint8 buffer per chunk: the library's exact size + a guard."""
+    bufs, sizes = [], []
+    for n_c in chunk_tokens(w, sq):
+        size = paged.chunk_bytes(n_c, fmt)
+        b = torch.full((size + GUARD,), fill, dtype=torch.uint8, device="cuda")
+        b[size:] = GUARD_FILL
+        bufs.append(b)
+        sizes.append(size)
+    return bufs, sizes
+
+
+def setup_device(w, arr=None, pool=None, fmt=kvm.FMT_BF16, fill=0x00):
+    """Device pool + Paged + per-sequence chunk buffers + a Batch."""
+    if pool is None:
+        pool = dev_pool_from_host(w, arr)
+    paged = kvm.Paged.from_pool(pool, chunk_size=w.chunk_size)
+    seqs, chunk_sets = [], []
+    for sq in w.seqs:
+        bufs, sizes = alloc_dev_chunks(paged, w, sq, fmt, fill)
+        bt = torch.from_numpy(np.ascontiguousarray(sq.block_table, np.int32)).to("cuda")
+        seqs.append(kvm.Seq(bt, sq.tok_start, sq.tok_end, bufs))
+        chunk_sets.append((bufs, sizes))
+    batch = kvm.Batch(paged, seqs).set_masks([sq.hit_mask for sq in w.seqs])
+    return pool, paged, batch, chunk_sets
+
+
+def host_chunks(chunk_set):
+    bufs, sizes = chunk_set
+    out = []
+    for b, s in zip(bufs, sizes):
+        h = b.cpu().numpy()
+        assert (h[s:] == GUARD_FILL).all(), "a kernel wrote past the end of a chunk buffer"
+        out.append(np.ascontiguousarray(h[:s]))
+    return out
+
+
+def first_diff(a, b):
+    d = np.nonzero(a.ravel() != b.ravel())[0]
+    return None if d.size == 0 else (int(d[0]), int(a.ravel()[d[0]]), int(b.ravel()[d[0]]), int(d.size))
+
+
+def equal_blocked(a, b):
+    """np.array_equal without a full-size temporary (pools can be ~20 GB)."""
+    if a.shape != b.shape:
+        return False
+    fa, fb = a.reshape(a.shape[0], -1), b.reshape(b.shape[0], -1)
+    return all(np.array_equal(fa[i], fb[i]) for i in range(fa.shape[0]))
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def check_store(w, arr, chunk_sets, fmt):
+    """Oracle store of every sequence vs the device chunks."""
+    opool = oracle_pool(w, arr)
+    for i, (sq, cs) in enumerate(zip(w.seqs, chunk_sets)):
+        got = host_chunks(cs)
+        exp = oracle.alloc_chunks(opool, sq.tok_start, sq.tok_end, fmt)
+        assert oracle.store(opool, sq.block_table, sq.tok_start, sq.tok_end, exp, fmt) == 0
+        assert len(got) == len(exp)
+        for c, (g, e) in enumerate(zip(got, exp)):
+            assert g.size == e.size, (i, c)
+            assert np.array_equal(g, e), (w.name, "seq", i, "chunk", c, first_diff(g, e))
+
+
+def check_retrieve(w, pool_before, got_pool, chunk_sets, fmt, masks, layer=-1, copy=True):
+    """Oracle retrieve (from the device's chunks) into a copy of the pool as it
+    was before the call (in place when copy=False), vs the device pool after
+    it; returns the oracle's token counts."""
+    exp = pool_before.copy() if copy else pool_before
+    opool = oracle_pool(w, exp)
+    counts = []
+    for sq, cs, m in zip(w.seqs, chunk_sets, masks):
+        ch = host_chunks(cs)
+        counts.append(oracle.retrieve(opool, sq.block_table, sq.tok_start, sq.tok_end, m, ch, fmt,
+                                      layer))
+    assert equal_blocked(got_pool, exp), (w.name, first_diff(got_pool, exp))
+    return counts

@@ -1,0 +1,157 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/kvmove.h declares, and its host-side checks reject malformed calls
+before any HIP call (so these run on a machine with no GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_movement_amd as kvm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvmove.h")
+
+
+def _lib():
+    if not os.path.exists(kvm.library_path()):
+        from paged_kv_movement_amd import build
+        build.build()
+    return kvm.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ["kv_store_chunks", "kv_retrieve_chunks", "kv_retrieve_layer", "kv_chunk_bytes",
+              "kv_num_chunks", "kv_last_error", "kv_take_faults", "kv_copy_bytes"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    _lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", kvm.library_path()], check=True,
+                         capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (kv_[a-z_]+)$", out, flags=re.M))
+    missing = [n for n in _declared_functions() if n not in exported]
+    assert not missing, missing
+    L = _lib()
+    for n in _declared_functions():
+        assert hasattr(L, n)
+
+
+def test_library_is_gfx950_code_object():
+    _lib()
+    out = subprocess.run(["/opt/rocm/llvm/bin/llvm-readelf", "-n", kvm.library_path()],
+                         capture_output=True, text=True)
+    blob = open(kvm.library_path(), "rb").read()
+    assert b"gfx950" in blob
+
+
+def _paged(L=32, H=8, D=128, P=16, C=256, n=8192, k=0x1000, v=0x2000):
+    return kvm._KvPaged(L, H, D, P, C, n, k, v)
+
+
+def test_chunk_bytes_and_num_chunks():
+    L = _lib()
+    p = _paged()
+    assert L.kv_chunk_bytes(ctypes.byref(p), 256, kvm.FMT_BF16) == 32 * 1024 * 1024
+    assert L.kv_chunk_bytes(ctypes.byref(p), 16, kvm.FMT_BF16) == 16 * 32 * 2 * 1024 * 2
+    assert L.kv_chunk_bytes(ctypes.byref(p), 256, kvm.FMT_FP8) == 32 * 2 * 256 * 1024 + 32 * 2 * 4
+    assert L.kv_chunk_bytes(ctypes.byref(p), 0, kvm.FMT_BF16) == 0
+    assert L.kv_chunk_bytes(ctypes.byref(p), 256, 9) == 0
+    assert L.kv_num_chunks(ctypes.byref(p), 0, 10000) == 40
+    assert L.kv_num_chunks(ctypes.byref(p), 0, 10240) == 40
+    assert L.kv_num_chunks(ctypes.byref(p), 512, 513) == 1
+    assert L.kv_num_chunks(ctypes.byref(p), 5, 3) == -1
+
+
+def _seq(s, e, n_bt, bt=0x3000, chunks=0x4000):
+    return kvm._KvSeq(bt, n_bt, s, e, chunks)
+
+
+def _store(p, seqs, fmt=kvm.FMT_BF16):
+    L = _lib()
+    arr = (kvm._KvSeq * max(1, len(seqs)))(*seqs)
+    return L.kv_store_chunks(ctypes.byref(p) if p is not None else None, arr, len(seqs), fmt, None)
+
+
+def test_store_rejections():
+    L = _lib()
+    p = _paged()
+    assert _store(p, [_seq(16, 300, 40)]) == kvm.KV_EINVAL          # start not chunk-aligned
+    assert "multiple of chunk_size" in L.kv_last_error().decode()
+    assert _store(p, [_seq(0, 641, 40)]) == kvm.KV_ERANGE           # beyond 40 pages of 16
+    assert _store(p, [_seq(0, 100, 40)], fmt=3) == kvm.KV_EINVAL
+    assert _store(p, [_seq(300, 200, 40)]) == kvm.KV_EINVAL
+    assert _store(p, [_seq(0, 100, 40, bt=0)]) == kvm.KV_EINVAL
+    assert _store(p, [_seq(0, 100, 40, chunks=0)]) == kvm.KV_EINVAL
+    assert _store(None, [_seq(0, 100, 40)]) == kvm.KV_EINVAL
+    assert _store(_paged(D=3, H=1), [_seq(0, 100, 40)]) == kvm.KV_EINVAL   # 6-byte rows
+    assert _store(_paged(C=250), [_seq(0, 100, 40)]) == kvm.KV_EINVAL      # chunk % page
+    assert _store(_paged(k=0), [_seq(0, 100, 40)]) == kvm.KV_EINVAL
+    # a later bad sequence rejects the whole call before anything is launched
+    assert _store(p, [_seq(0, 100, 40), _seq(0, 100, 2)]) == kvm.KV_ERANGE
+    assert "seq 1" in L.kv_last_error().decode()
+
+
+def test_empty_work_launches_nothing():
+    # no sequences, or only empty ranges: KV_OK with no HIP call (no GPU here)
+    p = _paged()
+    assert _store(p, []) == kvm.KV_OK
+    assert _store(p, [_seq(512, 512, 40), _seq(0, 0, 0, bt=0, chunks=0)]) == kvm.KV_OK
+
+
+def test_retrieve_with_no_hits_launches_nothing():
+    L = _lib()
+    p = _paged()
+    seqs = (kvm._KvSeq * 2)(_seq(0, 1000, 63), _seq(256, 700, 44))
+    m0 = (ctypes.c_uint8 * 4)(0, 1, 1, 1)
+    m1 = (ctypes.c_uint8 * 2)(0, 0)
+    masks = (ctypes.c_void_p * 2)(ctypes.addressof(m0), ctypes.addressof(m1))
+    out = (ctypes.c_int64 * 2)(-7, -7)
+    assert L.kv_retrieve_chunks(ctypes.byref(p), seqs, masks, 2, kvm.FMT_BF16, out, None) == kvm.KV_OK
+    assert list(out) == [0, 0]
+    for layer in (0, 31):
+        out[0] = out[1] = -7
+        assert L.kv_retrieve_layer(ctypes.byref(p), seqs, masks, 2, kvm.FMT_FP8, layer, out, None,
+                                   None) == kvm.KV_OK
+        assert list(out) == [0, 0]
+
+
+def test_retrieve_rejections():
+    L = _lib()
+    p = _paged()
+    seqs = (kvm._KvSeq * 1)(_seq(0, 1000, 63))
+    m = (ctypes.c_uint8 * 4)(1, 1, 0, 1)
+    masks = (ctypes.c_void_p * 1)(ctypes.addressof(m))
+    out = (ctypes.c_int64 * 1)()
+    assert L.kv_retrieve_chunks(ctypes.byref(p), seqs, None, 1, 0, out, None) == kvm.KV_EINVAL
+    nullm = (ctypes.c_void_p * 1)(None)
+    assert L.kv_retrieve_chunks(ctypes.byref(p), seqs, nullm, 1, 0, out, None) == kvm.KV_EINVAL
+    for bad_layer in (-1, 32):
+        assert L.kv_retrieve_layer(ctypes.byref(p), seqs, masks, 1, 0, bad_layer, out, None,
+                                   None) == kvm.KV_EINVAL
+    bad = (kvm._KvSeq * 1)(_seq(100, 1000, 63))
+    assert L.kv_retrieve_chunks(ctypes.byref(p), bad, masks, 1, 0, out, None) == kvm.KV_EINVAL
+
+
+def test_copy_bytes_rejections():
+    L = _lib()
+    assert L.kv_copy_bytes(0x1000, 0x2000, 17, None) == kvm.KV_EINVAL
+    assert L.kv_copy_bytes(0x1008, 0x2000, 32, None) == kvm.KV_EINVAL
+    assert L.kv_copy_bytes(None, 0x2000, 32, None) == kvm.KV_EINVAL
+    assert L.kv_copy_bytes(0x1000, 0x2000, 0, None) == kvm.KV_OK
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(kvm, "_LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(kvm, "_lib", None)
+    with pytest.raises(kvm.KvError, match="no fallback"):
+        kvm.load()

@@ -1,0 +1,309 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
+
+bf16 movement must be bit-exact; fp8 bytes and scales bit-exact; the fp8
+round trip within the closed-form bound.  Every input is seeded (see
+paged_kv_movement_amd/workloads.py); every expected value comes from oracle/.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_movement_amd as kvm
+from paged_kv_movement_amd import workloads as wl
+from gpu_util import (say, host_from_dev_pool, oracle_pool, chunk_tokens, setup_device,
+                      host_chunks, check_store, check_retrieve, sync as _sync)
+
+pytestmark = pytest.mark.gpu
+
+BF16, FP8 = kvm.FMT_BF16, kvm.FMT_FP8
+
+
+def _roundtrip(w, fmt=BF16, fill=0x0000, masks=None):
+    say("case", w.name, "fmt", fmt, "fill", hex(fill))
+    arr = wl.host_pool(w)
+    pool, paged, batch, chunk_sets = setup_device(w, arr, fmt=fmt, fill=0xCD)
+    kvm.store(paged, batch, fmt)
+    _sync()
+    assert kvm.take_faults() == 0
+    assert np.array_equal(host_from_dev_pool(pool), arr), "store wrote the pool"
+    check_store(w, arr, chunk_sets, fmt)
+    masks = masks if masks is not None else [sq.hit_mask for sq in w.seqs]
+    pool.view(torch.int16).fill_(int(np.uint16(fill).view(np.int16)))
+    before = np.full_like(arr, fill)
+    n = kvm.retrieve(paged, batch, masks=masks, fmt=fmt)
+    _sync()
+    assert kvm.take_faults() == 0
+    counts = check_retrieve(w, before, host_from_dev_pool(pool), chunk_sets, fmt, masks)
+    assert n == counts
+    return n
+
+
+# ------------------------------------------------------------------ small cases
+
+def test_tiny_config():
+    # L=2, 2 KV heads, head_dim 64, 64-page pool, one 256-token sequence on a
+    # seeded permutation of pages: store, zero the pages, retrieve, compare
+    n = _roundtrip(wl.tiny(), fill=0x0000)
+    assert n == [256]
+    assert _roundtrip(wl.tiny(), fill=0xA5A5) == [256]
+
+
+SHAPES = [
+    # name, seed, L, H, D, pages, ranges, extra kwargs
+    ("tails", 101, 3, 2, 64, 400, [(0, 1), (0, 15), (0, 16), (0, 17), (0, 255), (0, 257), (0, 511)], {}),
+    ("starts", 102, 2, 4, 32, 300, [(256, 700), (512, 513), (768, 1024), (0, 0), (512, 512)], {}),
+    ("narrow", 103, 5, 1, 8, 200, [(0, 1000), (256, 600)], {}),
+    ("wide", 104, 2, 32, 128, 96, [(0, 530), (0, 300)], {}),
+    ("odd-width", 105, 3, 3, 24, 128, [(0, 777)], {}),
+    ("page32", 106, 2, 2, 64, 200, [(0, 1000), (256, 301)], {"page_size": 32}),
+    ("chunk128", 107, 4, 2, 16, 300, [(0, 1000), (128, 129)], {"chunk_size": 128}),
+    ("page256", 108, 2, 2, 16, 40, [(0, 1000)], {"page_size": 256}),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+@pytest.mark.parametrize("fmt", [BF16, FP8], ids=["bf16", "fp8"])
+def test_shapes_and_tails(shape, fmt):
+    name, seed, L, H, D, pages, ranges, kw = shape
+    w = wl.custom(name, seed, L, H, D, pages, ranges, outliers=2 if fmt == FP8 else 0, **kw)
+    n = _roundtrip(w, fmt=fmt, fill=0x7E57)
+    assert n == [e - s for (s, e) in ranges]
+
+
+def test_many_sequences_span_several_launches():
+    # 70 sequences: more than one launch's worth of sequence slots
+    ranges = [(0, 1 + 37 * i) for i in range(70)]
+    w = wl.custom("many", 111, 2, 2, 32, 6000, ranges)
+    _roundtrip(w, fill=0x1234)
+    w8 = wl.custom("many-fp8", 112, 2, 2, 32, 6000, ranges, outliers=2)
+    _roundtrip(w8, fmt=FP8, fill=0x1234)
+
+
+@pytest.mark.parametrize("fmt", [BF16, FP8], ids=["bf16", "fp8"])
+def test_hit_masks_holes_and_misses(fmt):
+    ranges = [(0, 1000), (0, 1000), (256, 1000), (0, 1000), (0, 600)]
+    masks = [np.array(m, np.uint8) for m in
+             ([1, 1, 0, 1], [0, 1, 1, 1], [1, 0, 1], [1, 1, 1, 1], [1, 1, 1])]
+    w = wl.custom("holes", 121, 3, 2, 32, 400, ranges, masks=masks, outliers=2 if fmt == FP8 else 0)
+    n = _roundtrip(w, fmt=fmt, fill=0xA5A5)
+    assert n == [512, 0, 256, 1000, 600]
+
+
+def test_all_miss_leaves_pool_untouched():
+    ranges = [(0, 700), (256, 900)]
+    masks = [np.zeros(3, np.uint8), np.array([0, 1, 1], np.uint8)]
+    w = wl.custom("miss", 131, 2, 2, 32, 200, ranges, masks=masks)
+    assert _roundtrip(w, fill=0xBEEF) == [0, 0]
+
+
+def test_byte_transparency_random_bits():
+    w = wl.custom("bits", 141, 3, 2, 64, 300, [(0, 1000), (256, 777)], values="bits")
+    _roundtrip(w, fill=0x0000)
+
+
+def test_store_is_deterministic_and_leaves_pool():
+    for fmt in (BF16, FP8):
+        w = wl.custom("det", 151, 2, 2, 64, 200, [(0, 900)], outliers=4)
+        arr = wl.host_pool(w)
+        pool, paged, batch, cs = setup_device(w, arr, fmt=fmt, fill=0x11)
+        kvm.store(paged, batch, fmt)
+        first = [b.clone() for b in cs[0][0]]
+        for b in cs[0][0]:
+            b[: b.numel() - 256].fill_(0x22)
+        kvm.store(paged, batch, fmt)
+        _sync()
+        assert all(torch.equal(a, b) for a, b in zip(first, cs[0][0]))
+
+
+# ------------------------------------------------------------------ layerwise
+
+@pytest.mark.parametrize("fmt", [BF16, FP8], ids=["bf16", "fp8"])
+def test_layerwise_on_copy_stream_equals_full(fmt):
+    w = wl.custom("layers", 161, 6, 2, 32, 300, [(0, 1000), (256, 530)],
+                  masks=[np.array([1, 1, 0, 1], np.uint8), np.array([1, 1], np.uint8)],
+                  outliers=2 if fmt == FP8 else 0)
+    say("case layerwise fmt", fmt)
+    arr = wl.host_pool(w)
+    pool, paged, batch, cs = setup_device(w, arr, fmt=fmt)
+    kvm.store(paged, batch, fmt)
+    _sync()
+    copy = torch.cuda.Stream()
+    events = [torch.cuda.Event() for _ in range(w.num_layers)]
+    pool.view(torch.int16).fill_(0x0F0F)
+    before = host_from_dev_pool(pool)
+    _sync()
+    prev = before
+    for l in range(w.num_layers):
+        n = kvm.retrieve_layer(paged, batch, l, fmt=fmt, stream=copy, event=events[l])
+        assert n == [512, 274]
+        events[l].synchronize()
+        now = host_from_dev_pool(pool)
+        others = [x for x in range(w.num_layers) if x != l]
+        assert np.array_equal(now[others], prev[others]), f"layer {l} call wrote another layer"
+        prev = now
+    masks = [sq.hit_mask for sq in w.seqs]
+    check_retrieve(w, before, prev, cs, fmt, masks)
+    assert kvm.take_faults() == 0
+
+
+def test_layer_event_recorded_without_hits():
+    # the event must be recorded by the call even when nothing hits: record it
+    # early, queue ~ms of work on the copy stream, then check the call moved it
+    w = wl.custom("nohit", 171, 2, 1, 16, 64, [(0, 300)], masks=[np.array([0, 1], np.uint8)])
+    arr = wl.host_pool(w)
+    pool, paged, batch, cs = setup_device(w, arr)
+    s = torch.cuda.Stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    ev = torch.cuda.Event(enable_timing=True)
+    a = torch.randn(4096, 4096, device="cuda")
+    b = torch.randn(4096, 4096, device="cuda")
+    _sync()
+    with torch.cuda.stream(s):
+        t0.record(s)
+        ev.record(s)
+        for _ in range(8):
+            c = torch.mm(a, b)
+    assert kvm.retrieve_layer(paged, batch, 1, stream=s, event=ev) == [0]
+    ev.synchronize()
+    assert t0.elapsed_time(ev) > 0.2, "the layer event was not re-recorded after the queued work"
+    del c
+
+
+# ------------------------------------------------------------------ fp8 specifics
+
+def test_fp8_zero_nan_and_extreme_groups():
+    w = wl.custom("fp8-special", 181, 2, 1, 16, 64, [(0, 40)], masks=[np.array([1], np.uint8)])
+    arr = wl.host_pool(w)
+    bt = w.seqs[0].block_table
+    arr[0, 0, bt[:3]] = 0                       # layer 0 K: all zeros ...
+    arr[0, 0, bt[0], 0, ::2] = 0x8000           # ... with some -0
+    arr[0, 1, bt[1], 5, 3] = 0x7FC1             # layer 0 V: one NaN
+    arr[1, 0, bt[2], 2, 7] = 0x7F80             # layer 1 K: +inf
+    arr[1, 1, bt[:3]] = 0x0001                  # layer 1 V: smallest subnormal everywhere
+    arr[1, 1, bt[0], 0, 0] = 0x8005
+    pool, paged, batch, cs = setup_device(w, arr, fmt=FP8, fill=0xCD)
+    kvm.store(paged, batch, FP8)
+    _sync()
+    got = host_chunks(cs[0])[0]
+    exp = oracle.alloc_chunks(oracle_pool(w, arr), 0, 40, FP8)
+    assert oracle.store(oracle_pool(w, arr), bt, 0, 40, exp, FP8) == 0
+    exp = exp[0]
+    n = 2 * 2 * 40 * w.width
+    # NaN results (x / NaN, inf / inf) may differ in sign or payload between
+    # implementations: there, both sides must give a NaN code / NaN scale
+    nan_e = (exp[:n] & 0x7F) == 0x7F
+    assert np.array_equal(got[:n][~nan_e], exp[:n][~nan_e])
+    assert ((got[:n][nan_e] & 0x7F) == 0x7F).all()
+    se, sg = exp[n:].view(np.float32), got[n:].view(np.float32)
+    assert np.array_equal(np.isnan(se), np.isnan(sg))
+    assert np.array_equal(se[~np.isnan(se)].view(np.uint32), sg[~np.isnan(sg)].view(np.uint32))
+    assert list(np.isnan(se)) == [False, True, False, False]
+    assert se[0] == 1.0 and np.isinf(se[2])
+    pool.view(torch.int16).fill_(0)
+    kvm.retrieve(paged, batch, fmt=FP8)
+    _sync()
+    got = host_from_dev_pool(pool)
+    exp = np.zeros_like(arr)
+    op = oracle_pool(w, exp)
+    assert oracle.retrieve(op, bt, 0, 40, [1], host_chunks(cs[0]), FP8) == 40
+    # NaN codes may differ in payload between implementations: compare NaN-ness there
+    nan_g = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
+    nan_e = ((exp & 0x7F80) == 0x7F80) & ((exp & 0x7F) != 0)
+    assert np.array_equal(nan_g, nan_e)
+    assert np.array_equal(got[~nan_g], exp[~nan_e])
+
+
+def test_fp8_roundtrip_error_bound_small():
+    w = wl.custom("fp8-err", 191, 4, 2, 64, 400, [(0, 1000), (0, 300)], outliers=4)
+    arr = wl.host_pool(w)
+    pool, paged, batch, cs = setup_device(w, arr, fmt=FP8)
+    kvm.store(paged, batch, FP8)
+    orig = pool.clone()
+    pool.zero_()
+    kvm.retrieve(paged, batch, fmt=FP8)
+    _sync()
+    _assert_fp8_bound(w, orig, pool, cs)
+
+
+def _assert_fp8_bound(w, orig, pool, chunk_sets):
+    """max |x' - x| / max(|x|, 2^-6 * scale) over every stored element <= the
+    closed-form bound (1 + 2^-4)(1 + 2^-24)(1 + 2^-8) - 1 < 0.07."""
+    bound = (1 + 2.0 ** -4) * (1 + 2.0 ** -24) * (1 + 2.0 ** -8) - 1
+    L, E, P, C = w.num_layers, w.width, w.page_size, w.chunk_size
+    worst = 0.0
+    for sq, (bufs, sizes) in zip(w.seqs, chunk_sets):
+        bt = torch.from_numpy(sq.block_table.astype(np.int64)).cuda()
+        for c, (b, n_c) in enumerate(zip(bufs, chunk_tokens(w, sq))):
+            scales = b[L * 2 * n_c * E: L * 2 * n_c * E + L * 8].view(torch.float32).view(L, 2)
+            t = sq.tok_start + c * C + torch.arange(n_c, device="cuda")
+            page, row = bt[t // P], t % P
+            for l in range(L):
+                for kv in range(2):
+                    x = orig[l, kv].view(-1, P, E)[page, row].float()
+                    y = pool[l, kv].view(-1, P, E)[page, row].float()
+                    floor = (2.0 ** -6) * scales[l, kv].double()
+                    rel = ((y.double() - x.double()).abs() / torch.maximum(x.double().abs(), floor)).max()
+                    worst = max(worst, float(rel))
+    say("fp8 worst relative error", worst, "bound", bound)
+    assert worst <= bound < 0.07
+
+
+# ------------------------------------------------------------------ faults
+
+def test_bad_page_id_is_skipped_and_reported():
+    w = wl.custom("badpage", 201, 2, 2, 32, 64, [(0, 300)])
+    arr = wl.host_pool(w)
+    w.seqs[0].block_table = w.seqs[0].block_table.copy()
+    good_bt = w.seqs[0].block_table.copy()
+    w.seqs[0].block_table[3] = 64                  # == num_pages: out of range
+    pool, paged, batch, cs = setup_device(w, arr, fill=0xCD)
+    assert kvm.take_faults() == 0
+    kvm.store(paged, batch)
+    assert kvm.take_faults() == 1
+    assert kvm.take_faults() == 0
+    got = host_chunks(cs[0])
+    # every row group except the bad page's is still correct; the bad one untouched
+    w.seqs[0].block_table = good_bt
+    exp = oracle.alloc_chunks(oracle_pool(w, arr), 0, 300, BF16)
+    assert oracle.store(oracle_pool(w, arr), good_bt, 0, 300, exp) == 0
+    E, L = w.width, w.num_layers
+    g0 = got[0].view(np.uint16).reshape(L, 2, 256, E)
+    e0 = exp[0].view(np.uint16).reshape(L, 2, 256, E)
+    assert (g0[:, :, 48:64] == 0xCDCD).all()
+    g0m, e0m = np.delete(g0, range(48, 64), axis=2), np.delete(e0, range(48, 64), axis=2)
+    assert np.array_equal(g0m, e0m)
+    assert np.array_equal(got[1], exp[1])
+
+
+def test_misaligned_or_null_chunk_is_skipped_and_reported():
+    w = wl.custom("badchunk", 211, 2, 2, 32, 64, [(0, 300)])
+    arr = wl.host_pool(w)
+    pool, paged, batch, cs = setup_device(w, arr, fill=0xCD)
+    bufs = cs[0][0]
+    addrs = torch.tensor([bufs[0].data_ptr() + 8, bufs[1].data_ptr()], dtype=torch.int64).cuda()
+    bt = torch.from_numpy(w.seqs[0].block_table).cuda()
+    seq = kvm.Seq(bt, 0, 300, addrs)
+    kvm.store(paged, [seq])
+    assert kvm.take_faults() == 2
+    assert (bufs[0].cpu().numpy()[: cs[0][1][0]] == 0xCD).all()
+    exp = oracle.alloc_chunks(oracle_pool(w, arr), 0, 300, BF16)
+    assert oracle.store(oracle_pool(w, arr), w.seqs[0].block_table, 0, 300, exp) == 0
+    assert np.array_equal(host_chunks(([bufs[1]], [cs[0][1][1]]))[0], exp[1])
+    addrs0 = torch.tensor([0, bufs[1].data_ptr()], dtype=torch.int64).cuda()
+    kvm.store(paged, [kvm.Seq(bt, 0, 300, addrs0)])
+    assert kvm.take_faults() == 2
+
+
+def test_host_rejections_launch_nothing():
+    w = wl.custom("rej", 221, 2, 2, 32, 64, [(0, 300)])
+    arr = wl.host_pool(w)
+    pool, paged, batch, cs = setup_device(w, arr, fill=0xCD)
+    bt = torch.from_numpy(w.seqs[0].block_table).cuda()
+    with pytest.raises(kvm.KvError, match="multiple of chunk_size"):
+        kvm.store(paged, [kvm.Seq(bt, 16, 300, cs[0][0])])
+    with pytest.raises(kvm.KvError) as ei:
+        kvm.store(paged, [kvm.Seq(bt[:2], 0, 300, cs[0][0])])
+    assert ei.value.code == kvm.KV_ERANGE
+    _sync()
+    assert all((b.cpu().numpy() == 0xCD)[: b.numel() - 256].all() for b in cs[0][0])

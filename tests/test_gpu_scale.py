@@ -1,0 +1,157 @@
+"""Parity at the workloads' full sizes, in the launch configuration the
+benchmark times (one store call and one retrieve call over all sequences).
+
+bf16 workloads are compared in full against the oracle; the fp8 workload is
+compared on sampled chunks (the oracle's per-element e4m3 path is slow) plus
+properties that hold at any size: the round-trip error bound over every
+element, and rows outside the hit chunks keeping a sentinel.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_movement_amd as kvm
+from paged_kv_movement_amd import workloads as wl
+from gpu_util import (say, host_from_dev_pool, oracle_pool, chunk_tokens, setup_device, host_chunks,
+                      check_store, check_retrieve, equal_blocked, first_diff, sync)
+
+pytestmark = pytest.mark.gpu
+
+BF16, FP8 = kvm.FMT_BF16, kvm.FMT_FP8
+SENTINEL = 0x7E57
+
+
+def _free():
+    sync()
+    torch.cuda.empty_cache()
+
+
+def _full_bf16(w, expect_tokens):
+    say("case", w.name, "pool GB", w.pool_nbytes() / 1e9)
+    pool = wl.device_pool(w)
+    pool, paged, batch, chunk_sets = setup_device(w, pool=pool, fill=0xCD)
+    kvm.store(paged, batch)                       # one launch over every sequence
+    sync()
+    assert kvm.take_faults() == 0
+    arr = host_from_dev_pool(pool)
+    say("  store done; checking against the oracle")
+    check_store(w, arr, chunk_sets, BF16)
+    del arr
+    pool.view(torch.int16).fill_(SENTINEL)
+    n = kvm.retrieve(paged, batch)                # one launch, masks from the workload
+    sync()
+    assert kvm.take_faults() == 0
+    assert n == expect_tokens
+    say("  retrieve done; checking against the oracle")
+    got = host_from_dev_pool(pool)
+    before = np.full(got.shape, SENTINEL, np.uint16)
+    counts = check_retrieve(w, before, got, chunk_sets, BF16, [s.hit_mask for s in w.seqs],
+                            copy=False)
+    assert counts == expect_tokens
+    del got, before, pool, paged, batch, chunk_sets
+    _free()
+
+
+def test_full_llama8b_store_and_30_chunk_retrieve():
+    # 8 sequences x 10000 tokens (39 full chunks + a 16-token tail), 8192-page
+    # pool; retrieve with the first 30 chunks hit
+    _full_bf16(wl.llama8b(), [30 * 256] * 8)
+
+
+def test_full_llama70b_store_and_retrieve():
+    # 80 layers, one 32768-token sequence (128 chunks) on a 4096-page pool
+    _full_bf16(wl.llama70b(), [32768])
+
+
+def test_full_layerwise_8b_with_compute_stream():
+    # one 10240-token sequence retrieved layer by layer on a copy stream, each
+    # layer's event gating a bf16 GEMM (tokens x 4096 x 4096) on the compute stream
+    w = wl.layerwise8b()
+    say("case", w.name)
+    pool = wl.device_pool(w)
+    pool, paged, batch, chunk_sets = setup_device(w, pool=pool, fill=0xCD)
+    kvm.store(paged, batch)
+    sync()
+    pool.view(torch.int16).fill_(SENTINEL)
+    sync()
+    copy, compute = torch.cuda.Stream(), torch.cuda.Stream()
+    events = [torch.cuda.Event() for _ in range(w.num_layers)]
+    x = torch.randn(10240, 4096, device="cuda", dtype=torch.bfloat16)
+    wgt = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16) * 0.01
+    outs = []
+    for l in range(w.num_layers):
+        assert kvm.retrieve_layer(paged, batch, l, stream=copy, event=events[l]) == [10240]
+        compute.wait_event(events[l])
+        with torch.cuda.stream(compute):
+            outs.append(torch.mm(x, wgt))
+    sync()
+    assert kvm.take_faults() == 0
+    assert all(torch.isfinite(o).all() for o in outs[:2])
+    got = host_from_dev_pool(pool)
+    before = np.full(got.shape, SENTINEL, np.uint16)
+    check_retrieve(w, before, got, chunk_sets, BF16, [s.hit_mask for s in w.seqs], copy=False)
+    del got, before, pool, paged, batch, chunk_sets, outs
+    _free()
+
+
+def test_full_fp8_8b_sampled_chunks_and_bounds():
+    w = wl.fp8_8b()
+    say("case", w.name)
+    pool = wl.device_pool(w)
+    pool, paged, batch, chunk_sets = setup_device(w, pool=pool, fmt=FP8, fill=0xCD)
+    kvm.store(paged, batch, FP8)
+    sync()
+    assert kvm.take_faults() == 0
+    arr = host_from_dev_pool(pool)
+    opool = oracle_pool(w, arr)
+    samples = [(0, 0), (0, 17), (0, 39), (3, 38), (7, 5), (7, 39)]   # (seq, chunk); 39 = tail
+    for si, c in samples:
+        sq = w.seqs[si]
+        s = c * w.chunk_size
+        e = min(sq.tok_end, s + w.chunk_size)
+        exp = oracle.alloc_chunks(opool, s, e, FP8)
+        assert oracle.store(opool, sq.block_table, s, e, exp, FP8) == 0
+        bufs, sizes = chunk_sets[si]
+        got = host_chunks(([bufs[c]], [sizes[c]]))[0]
+        assert np.array_equal(got, exp[0]), (si, c, first_diff(got, exp[0]))
+    say("  sampled fp8 chunks match")
+    # full retrieve (all hit) into a zeroed pool: sampled chunks vs the oracle
+    # and the error bound over every element
+    orig = pool.clone()
+    pool.zero_()
+    assert kvm.retrieve(paged, batch, fmt=FP8) == [10000] * 8
+    sync()
+    got_pool = host_from_dev_pool(pool)
+    for si, c in samples:
+        sq = w.seqs[si]
+        s = c * w.chunk_size
+        e = min(sq.tok_end, s + w.chunk_size)
+        bufs, sizes = chunk_sets[si]
+        ch = host_chunks(([bufs[c]], [sizes[c]]))
+        pages = sq.block_table[s // 16: (e + 15) // 16]
+        # the oracle retrieves this one chunk into a small zeroed pool holding
+        # just its pages, renumbered 0..k-1 (rows do not depend on the page
+        # numbering); the device pool is read back at the real page ids
+        part = np.zeros((w.num_layers, 2, len(pages), 16, w.width), np.uint16)
+        ptmp = oracle.Pool.from_array(part, w.num_kv_heads, w.head_dim, w.chunk_size)
+        padded_bt = np.concatenate([np.zeros(s // 16, np.int32), np.arange(len(pages), dtype=np.int32)])
+        assert oracle.retrieve(ptmp, padded_bt, s, e, [1], ch, FP8) == e - s
+        assert np.array_equal(got_pool[:, :, pages], part), (si, c)
+    del got_pool
+    from test_gpu_parity import _assert_fp8_bound
+    _assert_fp8_bound(w, orig, pool, chunk_sets)
+    # 30-chunk hit mask: rows of chunks >= 30 keep the sentinel, hit rows equal
+    # the all-hit result
+    full = pool.clone()
+    pool.view(torch.int16).fill_(SENTINEL)
+    masks = [np.r_[np.ones(30, np.uint8), np.zeros(10, np.uint8)]] * 8
+    assert kvm.retrieve(paged, batch, masks=masks, fmt=FP8) == [7680] * 8
+    sync()
+    for sq in w.seqs:
+        bt = torch.from_numpy(sq.block_table.astype(np.int64)).cuda()
+        hit, miss = bt[:480], bt[480:]
+        assert torch.equal(pool[:, :, hit], full[:, :, hit])
+        assert (pool[:, :, miss].view(torch.int16) == SENTINEL).all()
+    del pool, orig, full, paged, batch, chunk_sets
+    _free()
