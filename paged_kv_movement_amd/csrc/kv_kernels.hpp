@@ -30,7 +30,6 @@ namespace kvmove {
 
 using u32x4 = __attribute__((ext_vector_type(4))) unsigned int;
 using u32x2 = __attribute__((ext_vector_type(2))) unsigned int;
-using u16x2 = __attribute__((ext_vector_type(2))) unsigned short;
 
 // Global-address-space views: loads and stores through these compile to
 // global_* instructions (no flat aperture checks).
@@ -289,21 +288,27 @@ __global__ __launch_bounds__(kBlock) void store_fp8(MoveArgs a)
     const gvec4* pool_v = reinterpret_cast<const gvec4*>(pool);
 
     // pass 1: absolute maximum as bf16 magnitude bits (integer order equals
-    // magnitude order for non-NaN; NaN codes sort above infinity)
-    u16x2 m2 = {0, 0};
+    // magnitude order for non-NaN; NaN codes sort above infinity).  Plain
+    // 32-bit operations: a packed-u16 form (bit_cast of a vector element into
+    // a u16x2 fed to __builtin_elementwise_max) was compiled by hipcc 7.2 into
+    // a load of only the first dword of each 16-byte vector.
+    uint32_t m1 = 0;
     for (uint32_t pi = 0; pi < n_pages; ++pi) {
         const int64_t page = gptr<const gi32>(sq.bt)[first + pi];
         const uint32_t left = g.n_c - pi * a.page_size;
         const uint32_t nvec = (left < a.page_size ? left : a.page_size) * vrow;
         const gvec4* src = pool_v + page * page_vecs;
         for (uint32_t i = threadIdx.x; i < nvec; i += kBlock) {
-            const u32x4 v = src[i] & 0x7FFF7FFFu;
+            const u32x4 v = src[i];
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, v[k]));
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t lo = v[k] & 0x7FFFu;
+                const uint32_t hi = (v[k] >> 16) & 0x7FFFu;
+                m1 = m1 > lo ? m1 : lo;
+                m1 = m1 > hi ? m1 : hi;
+            }
         }
     }
-    const uint32_t m1 = m2[0] > m2[1] ? m2[0] : m2[1];
     const uint32_t amax_bits = block_max_u32<kBlock>(m1, red);
     const float amax = __uint_as_float(amax_bits << 16);
     const float scale = amax == 0.0f ? 1.0f : amax / 448.0f;
