@@ -6,12 +6,14 @@
 // addresses are wave-uniform and computed in 32-bit scalar arithmetic from
 // constants the host precomputes.
 //
-//   move_bf16<kToChunk>  one workgroup per (sequence, chunk, layer, K/V, page):
-//                        a page's rows are contiguous in the pool and the same
+//   move_bf16<kToChunk>  work unit = (sequence, chunk, layer, K/V, page): a
+//                        page's rows are contiguous in the pool and the same
 //                        rows are contiguous in the chunk ([L][2][n][H*D]
-//                        layout), so each unit is one contiguous copy of
+//                        layout), so a unit is one contiguous copy of
 //                        rows*H*D*2 bytes (32 KiB for a full page at the
-//                        Llama-3.1-8B shape).
+//                        Llama-3.1-8B shape).  Each unit is cut into tiles of
+//                        kBlock*kVpt 16-byte vectors, one workgroup per tile,
+//                        and consecutive tiles are kept on one XCD.
 //   store_fp8            one workgroup per (sequence, chunk, layer, K/V)
 //                        group: pass 1 takes the group's absolute maximum,
 //                        pass 2 re-reads, divides by the scale, encodes e4m3.
@@ -75,6 +77,7 @@ struct MoveArgs {
     uint32_t layer0;          // first layer moved
     uint32_t n_layers;        // layers moved
     uint32_t n_seqs;
+    uint32_t tiles;           // workgroups per page unit (tiled movers; 1 otherwise)
     SeqArg seq[kMaxSeqs];
 };
 
@@ -91,6 +94,16 @@ __device__ __forceinline__ uint32_t find_seq(const MoveArgs& a, uint32_t item)
 }
 
 __device__ __forceinline__ bool bad_addr(uint64_t p) { return p == 0 || (p & 15u) != 0; }
+
+// A value every lane of the wave holds identically, moved into scalar
+// registers (addresses read from device arrays arrive in vector registers;
+// buffer descriptors built from them must be scalar).
+__device__ __forceinline__ uint64_t wave_uniform(uint64_t x)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
 
 // A page unit: rows [j0, j0 + rows) of chunk c, layer l, K/V kv, held by
 // pool page `page`.
@@ -164,23 +177,71 @@ __device__ __forceinline__ void copy_vectors(const gvec4* __restrict__ src, gvec
     }
 }
 
-// Gather (kToChunk) or scatter (!kToChunk) of one page unit, bf16 bit copy.
-template <bool kToChunk, int kBlock, int kVpt, bool kNtLoad, bool kNtStore>
+// Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8).  Renumber them so that each XCD walks one contiguous range of the
+// grid: neighbouring tiles (the pieces of one page, the rows of one chunk)
+// then run on the same XCD, one after the other.  A bijection on
+// [0, 8 * (grid / 8)); the few workgroups past that keep their number.
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t grid)
+{
+    const uint32_t per = grid / 8;
+    return b < per * 8 ? (b % 8) * per + b / 8 : b;
+}
+
+// Cache-policy bits of the buffer instructions (gfx94x/gfx950 encoding of
+// the aux operand): 2 = nt (streaming, do not keep in cache), 16 = sc1.
+enum : int { kCpolNt = 2, kCpolSc1 = 16 };
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(uint64_t base, uint32_t nbytes)
+{
+    // raw buffer: stride 0, range-checked against nbytes (word 3 = gfx9 format)
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), (short)0, (int)nbytes,
+                                             0x00020000);
+}
+
+// Copies nbytes (a multiple of 16, at most kBlock*kVpt*16) from src to dst:
+// kVpt loads in flight per thread, then the stores.  Buffer accesses at or
+// past nbytes are discarded by the hardware range check (loads return 0,
+// stores are dropped), so a partial tile needs no per-vector guard.
+template <int kBlock, int kVpt, int kAuxLoad, int kAuxStore>
+__device__ __forceinline__ void copy_tile(uint64_t src, uint64_t dst, uint32_t nbytes)
+{
+    const __amdgpu_buffer_rsrc_t rs = byte_range(src, nbytes);
+    const __amdgpu_buffer_rsrc_t rd = byte_range(dst, nbytes);
+    u32x4 v[kVpt];
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k)
+        v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (k * kBlock + threadIdx.x) * 16, 0, kAuxLoad);
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k)
+        __builtin_amdgcn_raw_buffer_store_b128(v[k], rd, (k * kBlock + threadIdx.x) * 16, 0, kAuxStore);
+}
+
+// Gather (kToChunk) or scatter (!kToChunk) of one tile of one page unit,
+// bf16 copied bit for bit.  Grid = units * a.tiles.
+template <bool kToChunk, int kBlock, int kVpt, int kAuxLoad, int kAuxStore>
 __global__ __launch_bounds__(kBlock) void move_bf16(MoveArgs a)
 {
-    const PageUnit u = locate_page_unit(a, a.item_base + blockIdx.x);
+    const uint32_t b = xcd_contiguous(blockIdx.x, gridDim.x);
+    const uint32_t unit = b / a.tiles;
+    const uint32_t tile = b - unit * a.tiles;
+    const PageUnit u = locate_page_unit(a, a.item_base + unit);
+    const uint32_t row_bytes = a.width * 2;
+    const uint32_t nbytes = u.rows * row_bytes;
+    const uint32_t lo = tile * (kBlock * kVpt * 16);
+    if (lo >= nbytes) return;                         // tile past a short (tail) page
     if (u.page < 0 || u.page >= a.num_pages) { raise_fault(kFaultPage); return; }
-    const uint64_t pool = gptr<const gu64>(u.kv ? a.v_pages : a.k_pages)[u.l];
-    const uint64_t chunk = gptr<const gu64>(a.seq[u.s].chunks)[u.c];
+    const uint64_t pool = wave_uniform(gptr<const gu64>(u.kv ? a.v_pages : a.k_pages)[u.l]);
+    const uint64_t chunk = wave_uniform(gptr<const gu64>(a.seq[u.s].chunks)[u.c]);
     if (bad_addr(pool)) { raise_fault(kFaultPool); return; }
     if (bad_addr(chunk)) { raise_fault(kFaultChunk); return; }
-    const uint32_t vrow = a.width / 8;                    // 16-byte vectors per token row
-    gvec4* page_v = reinterpret_cast<gvec4*>(pool) + u.page * (int64_t)(a.page_size * vrow);
-    gvec4* chunk_v = reinterpret_cast<gvec4*>(chunk) +
-                     ((int64_t)(u.l * 2 + u.kv) * u.n_c + u.j0) * vrow;
-    const uint32_t nvec = u.rows * vrow;
-    if (kToChunk) copy_vectors<kBlock, kVpt, kNtLoad, kNtStore>(page_v, chunk_v, nvec);
-    else copy_vectors<kBlock, kVpt, kNtLoad, kNtStore>(chunk_v, page_v, nvec);
+    const uint32_t left = nbytes - lo;
+    const uint32_t n = left < kBlock * kVpt * 16 ? left : kBlock * kVpt * 16;
+    const uint64_t page_addr = pool + (uint64_t)u.page * a.page_size * row_bytes + lo;
+    const uint64_t chunk_addr =
+        chunk + ((uint64_t)(u.l * 2 + u.kv) * u.n_c + u.j0) * row_bytes + lo;
+    if (kToChunk) copy_tile<kBlock, kVpt, kAuxLoad, kAuxStore>(page_addr, chunk_addr, n);
+    else copy_tile<kBlock, kVpt, kAuxLoad, kAuxStore>(chunk_addr, page_addr, n);
 }
 
 // ------------------------------------------------------------------ fp8 e4m3
@@ -377,15 +438,14 @@ __global__ __launch_bounds__(kBlock) void retrieve_fp8(MoveArgs a)
 }
 
 // Plain contiguous copy (measurement aid): one tile of kBlock*kVpt vectors
-// per workgroup.
+// per workgroup, the same instruction form as the movers.
 template <int kBlock, int kVpt>
-__global__ __launch_bounds__(kBlock) void copy_contiguous(uint64_t src, uint64_t dst, int64_t nvec)
+__global__ __launch_bounds__(kBlock) void copy_contiguous(uint64_t src, uint64_t dst, int64_t nbytes)
 {
-    const int64_t base = (int64_t)blockIdx.x * kBlock * kVpt;
-    const int64_t left = nvec - base;
-    const uint32_t n = left < (int64_t)kBlock * kVpt ? (uint32_t)left : (uint32_t)(kBlock * kVpt);
-    copy_vectors<kBlock, kVpt, false, false>(reinterpret_cast<const gvec4*>(src) + base,
-                                             reinterpret_cast<gvec4*>(dst) + base, n);
+    const int64_t tile = (int64_t)kBlock * kVpt * 16;
+    const int64_t lo = (int64_t)blockIdx.x * tile;
+    const int64_t left = nbytes - lo;
+    copy_tile<kBlock, kVpt, kCpolNt, kCpolNt>(src + lo, dst + lo, (uint32_t)(left < tile ? left : tile));
 }
 
 }  // namespace kvmove

@@ -19,16 +19,20 @@ namespace {
 
 using namespace kvmove;
 
-// Launch shape of the movers (tuned on MI355X, see the measurement notes).
+// Launch shape of the movers, from sweeps on MI355X at the Llama-3.1-8B
+// shape: 8 KiB tiles (256 threads x 2 vectors of 16 B), streaming (nt)
+// cache policy, sc1 on the gather.
 constexpr int kMoveBlock = 256;
-constexpr int kMoveVpt = 8;          // 256 x 8 x 16 B = one 32 KiB page unit per pass
-constexpr bool kMoveNtLoad = false;
-constexpr bool kMoveNtStore = false;
+constexpr int kMoveVpt = 2;
+constexpr int kGatherAuxLoad = kCpolNt | kCpolSc1;
+constexpr int kGatherAuxStore = kCpolNt | kCpolSc1;
+constexpr int kScatterAuxLoad = kCpolNt;
+constexpr int kScatterAuxStore = kCpolNt;
 constexpr int kFp8Block = 256;
 constexpr int kCopyBlock = 256;
-constexpr int kCopyVpt = 8;
+constexpr int kCopyVpt = 1;
 // Workgroups per launch: gridDim.x * blockDim.x must stay below 2^32.
-constexpr int64_t kMaxUnits = (int64_t(1) << 24) - 1;
+constexpr int64_t kMaxBlocks = (int64_t(1) << 24) - 1;
 
 thread_local std::string g_last_error;
 
@@ -119,11 +123,11 @@ enum class Unit { Page, Group };
 using KernelFn = const void*;
 
 // Packs up to kMaxSeqs non-empty sequences per launch, keeping every launch
-// under kMaxUnits units (the kernels index units in 32 bits).  n_tok[i] is the
+// under kMaxBlocks workgroups (the kernels index units in 32 bits).  n_tok[i] is the
 // token count moved for sequence i (from its tok_start).
-int launch_units(KernelFn kernel, int block, Unit unit, const kv_paged* p, const kv_seq* seqs,
-                 const int64_t* n_tok, int n_seqs, int32_t layer0, int32_t n_layers,
-                 hipStream_t stream)
+int launch_units(KernelFn kernel, int block, int tile_bytes, Unit unit, const kv_paged* p,
+                 const kv_seq* seqs, const int64_t* n_tok, int n_seqs, int32_t layer0,
+                 int32_t n_layers, hipStream_t stream)
 {
     MoveArgs a{};
     a.k_pages = reinterpret_cast<uint64_t>(p->k_pages);
@@ -138,11 +142,16 @@ int launch_units(KernelFn kernel, int block, Unit unit, const kv_paged* p, const
     a.num_layers = uint32_t(p->num_layers);
     a.layer0 = uint32_t(layer0);
     a.n_layers = uint32_t(n_layers);
+    const int64_t page_bytes = int64_t(p->page_size) * a.width * 2;
+    a.tiles = tile_bytes > 0 ? uint32_t(ceil_div(page_bytes, tile_bytes)) : 1u;
+    if (int64_t(a.tiles) > kMaxBlocks) return fail(KV_EINVAL, "page too large for one launch");
+    const int64_t max_units = kMaxBlocks / a.tiles;
 
     auto flush = [&](int64_t total) -> int {
         a.item_base = 0;
         void* args[] = {&a};
-        hipError_t e = hipLaunchKernel(kernel, dim3((unsigned)total), dim3(block), args, 0, stream);
+        hipError_t e = hipLaunchKernel(kernel, dim3(unsigned(total * a.tiles)), dim3(block), args, 0,
+                                       stream);
         if (e != hipSuccess) return fail(KV_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
         return KV_OK;
     };
@@ -154,9 +163,9 @@ int launch_units(KernelFn kernel, int block, Unit unit, const kv_paged* p, const
         const int64_t units = unit == Unit::Page
                                   ? ceil_div(n_tok[i], p->page_size) * n_layers * 2
                                   : ceil_div(n_tok[i], p->chunk_size) * n_layers * 2;
-        if (units > kMaxUnits)
+        if (units > max_units)
             return fail(KV_EINVAL, "seq %d: %lld work units exceed one launch", i, (long long)units);
-        if (a.n_seqs == kMaxSeqs || total + units > kMaxUnits) {
+        if (a.n_seqs == kMaxSeqs || total + units > max_units) {
             int rc = flush(total);
             if (rc != KV_OK) return rc;
             a.n_seqs = 0;
@@ -179,7 +188,7 @@ KernelFn gather_kernel(int fmt)
 {
     if (fmt == KV_FMT_BF16)
         return reinterpret_cast<KernelFn>(
-            &move_bf16<true, kMoveBlock, kMoveVpt, kMoveNtLoad, kMoveNtStore>);
+            &move_bf16<true, kMoveBlock, kMoveVpt, kGatherAuxLoad, kGatherAuxStore>);
     return reinterpret_cast<KernelFn>(&store_fp8<kFp8Block>);
 }
 
@@ -187,11 +196,14 @@ KernelFn scatter_kernel(int fmt)
 {
     if (fmt == KV_FMT_BF16)
         return reinterpret_cast<KernelFn>(
-            &move_bf16<false, kMoveBlock, kMoveVpt, kMoveNtLoad, kMoveNtStore>);
+            &move_bf16<false, kMoveBlock, kMoveVpt, kScatterAuxLoad, kScatterAuxStore>);
     return reinterpret_cast<KernelFn>(&retrieve_fp8<kFp8Block>);
 }
 
 int block_of(int fmt) { return fmt == KV_FMT_BF16 ? kMoveBlock : kFp8Block; }
+
+// Bytes per workgroup of the tiled movers (0: one workgroup per unit).
+int tile_of(int fmt) { return fmt == KV_FMT_BF16 ? kMoveBlock * kMoveVpt * 16 : 0; }
 
 // Shared body of the two retrieve entry points.
 int retrieve(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
@@ -211,8 +223,8 @@ int retrieve(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hi
         const int64_t end = s.tok_start + n_hit * paged->chunk_size;
         n_tok[i] = (end < s.tok_end ? end : s.tok_end) - s.tok_start;
     }
-    int rc = launch_units(scatter_kernel(fmt), block_of(fmt), Unit::Page, paged, seqs, n_tok, n_seqs,
-                          layer0, n_layers, stream);
+    int rc = launch_units(scatter_kernel(fmt), block_of(fmt), tile_of(fmt), Unit::Page, paged, seqs,
+                          n_tok, n_seqs, layer0, n_layers, stream);
     if (rc == KV_OK && out_tokens != nullptr)
         for (int i = 0; i < n_seqs; ++i) out_tokens[i] = n_tok[i];
     if (n_tok != small) delete[] n_tok;
@@ -254,7 +266,7 @@ int kv_store_chunks(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int f
     int64_t small[64];
     int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
     for (int i = 0; i < n_seqs; ++i) n_tok[i] = seqs[i].tok_end - seqs[i].tok_start;
-    rc = launch_units(gather_kernel(fmt), block_of(fmt),
+    rc = launch_units(gather_kernel(fmt), block_of(fmt), tile_of(fmt),
                       fmt == KV_FMT_BF16 ? Unit::Page : Unit::Group, paged, seqs, n_tok, n_seqs, 0,
                       paged->num_layers, stream);
     if (n_tok != small) delete[] n_tok;
@@ -309,14 +321,13 @@ int kv_copy_bytes(void* dst, const void* src, size_t bytes, hipStream_t stream)
     if (dst == nullptr || src == nullptr) return fail(KV_EINVAL, "dst / src is NULL");
     if (bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(dst) & 15) || (reinterpret_cast<uintptr_t>(src) & 15))
         return fail(KV_EINVAL, "kv_copy_bytes needs 16-byte aligned addresses and a multiple of 16 bytes");
-    const int64_t nvec = int64_t(bytes / 16);
-    if (nvec == 0) return ok();
-    const int64_t tile = int64_t(kCopyBlock) * kCopyVpt;
-    const int64_t grid = ceil_div(nvec, tile);
-    if (grid > (int64_t(1) << 31) - 1) return fail(KV_EINVAL, "copy too large");
+    if (bytes == 0) return ok();
+    const int64_t tile = int64_t(kCopyBlock) * kCopyVpt * 16;
+    const int64_t grid = ceil_div(int64_t(bytes), tile);
+    if (grid > kMaxBlocks) return fail(KV_EINVAL, "copy too large for one launch");
     uint64_t s = reinterpret_cast<uint64_t>(src);
     uint64_t d = reinterpret_cast<uint64_t>(dst);
-    int64_t n = nvec;
+    int64_t n = int64_t(bytes);
     void* args[] = {&s, &d, &n};
     hipError_t e = hipLaunchKernel(reinterpret_cast<KernelFn>(&copy_contiguous<kCopyBlock, kCopyVpt>),
                                    dim3((unsigned)grid), dim3(kCopyBlock), args, 0, stream);
