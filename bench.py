@@ -29,7 +29,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor peak
 METRIC = "paged<->chunk KV gather/scatter GB/s and % of HBM peak (8B KV shape)"
-KERNEL_SOURCES = ["paged_kv_movement_amd/csrc/kv_kernels.hpp", "paged_kv_movement_amd/csrc/kvmove.hip"]
+# device sources of the gather kernel (kernel, launch shape, shared helpers)
+KERNEL_SOURCES = ["paged_kv_movement_amd/csrc/kv_common.hpp", "paged_kv_movement_amd/csrc/kv_move_bf16.hpp"]
 TRAFFIC_FILE = "profiles/hbm_traffic_gather_llama8b.txt"
 
 

@@ -1,0 +1,222 @@
+// kv_common.hpp -- shared device code of the paged <-> chunk KV movers
+// (gfx950 / CDNA4): kernel arguments, work-unit decomposition, buffer
+// descriptors, XCD-aware workgroup order, fault reporting.
+//
+// Pure data movement: no matrix cores.  Every kernel streams 16-byte vectors
+// with coalesced accesses along a token row (H*D elements), one workgroup per
+// unit (or tile of a unit) of work; the unit's page id and addresses are
+// wave-uniform and computed in 32-bit scalar arithmetic from constants the
+// host precomputes.
+//
+//   move_bf16<kToChunk>  work unit = (sequence, chunk, layer, K/V, page): a
+//                        page's rows are contiguous in the pool and the same
+//                        rows are contiguous in the chunk ([L][2][n][H*D]
+//                        layout), so a unit is one contiguous copy of
+//                        rows*H*D*2 bytes (32 KiB for a full page at the
+//                        Llama-3.1-8B shape).  Each unit is cut into tiles of
+//                        kBlock*kVpt 16-byte vectors, one workgroup per tile,
+//                        and consecutive tiles are kept on one XCD.
+//   store_fp8            one workgroup per (sequence, chunk, layer, K/V)
+//                        group: pass 1 takes the group's absolute maximum,
+//                        pass 2 re-reads, divides by the scale, encodes e4m3.
+//   retrieve_fp8         page units as move_bf16, decoding e4m3 and scaling.
+//
+// The method these kernels implement is described on the LMCache paper-notes
+// page ("LMCache: An Efficient KV Cache Layer for Enterprise-Scale LLM
+// Inference", section "方法细节": configurable chunk size, layerwise
+// pipeline) and on the serde framework page (section "7.1 fp8 量化").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvmove {
+
+using u32x4 = __attribute__((ext_vector_type(4))) unsigned int;
+using u32x2 = __attribute__((ext_vector_type(2))) unsigned int;
+
+// Global-address-space views: loads and stores through these compile to
+// global_* instructions (no flat aperture checks).
+using gvec4 = __attribute__((address_space(1))) u32x4;
+using gvec2 = __attribute__((address_space(1))) u32x2;
+using gbyte = __attribute__((address_space(1))) uint8_t;
+using gf32 = __attribute__((address_space(1))) float;
+using gi32 = __attribute__((address_space(1))) int32_t;
+using gu64 = __attribute__((address_space(1))) uint64_t;
+
+constexpr int kMaxSeqs = 32;     // sequences per launch (kernel-argument budget)
+
+enum : unsigned { kFaultPage = 1u, kFaultChunk = 2u, kFaultPool = 4u };
+
+// Per-device fault word, set by kernels when a unit is skipped.
+__device__ unsigned int g_kv_faults;
+
+// Device addresses travel as integers (kernel arguments are built by host
+// code) and become global-address-space pointers inside the kernels.
+template <class T>
+__device__ __forceinline__ T* gptr(uint64_t addr) { return reinterpret_cast<T*>(addr); }
+
+struct SeqArg {
+    uint64_t bt;              // block table: int32[]
+    uint64_t chunks;          // chunk addresses: uint64[]
+    uint32_t first_page;      // block-table index of the first token moved
+    uint32_t n_full;          // full chunks moved
+    uint32_t tail_tokens;     // tokens of a trailing partial chunk (0: none)
+    uint32_t item_begin;      // first unit of this sequence in the launch
+};
+
+struct MoveArgs {
+    uint64_t k_pages;         // uint64[L]: layer K pool addresses
+    uint64_t v_pages;         // uint64[L]: layer V pool addresses
+    int64_t num_pages;
+    uint32_t item_base;       // unit index of blockIdx.x == 0
+    uint32_t width;           // H*D elements per token row (multiple of 8)
+    uint32_t page_size;       // P
+    uint32_t chunk_size;      // C (multiple of P)
+    uint32_t pages_per_chunk; // C / P
+    uint32_t units_per_chunk; // units of one full chunk (depends on the kernel)
+    uint32_t num_layers;      // L (chunk layout)
+    uint32_t layer0;          // first layer moved
+    uint32_t n_layers;        // layers moved
+    uint32_t n_seqs;
+    uint32_t tiles;           // workgroups per page unit (tiled movers; 1 otherwise)
+    SeqArg seq[kMaxSeqs];
+};
+
+__device__ __forceinline__ void raise_fault(unsigned bit)
+{
+    if (threadIdx.x == 0) atomicOr(&g_kv_faults, bit);
+}
+
+__device__ __forceinline__ uint32_t find_seq(const MoveArgs& a, uint32_t item)
+{
+    uint32_t s = 0;
+    while (s + 1 < a.n_seqs && item >= a.seq[s + 1].item_begin) ++s;
+    return s;
+}
+
+__device__ __forceinline__ bool bad_addr(uint64_t p) { return p == 0 || (p & 15u) != 0; }
+
+// A value every lane of the wave holds identically, moved into scalar
+// registers (addresses read from device arrays arrive in vector registers;
+// buffer descriptors built from them must be scalar).
+__device__ __forceinline__ uint64_t wave_uniform(uint64_t x)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// A page unit: rows [j0, j0 + rows) of chunk c, layer l, K/V kv, held by
+// pool page `page`.
+struct PageUnit {
+    int64_t page;
+    uint32_t c;
+    uint32_t n_c;    // tokens in chunk c
+    uint32_t j0;     // first row inside the chunk
+    uint32_t rows;
+    uint32_t l;
+    uint32_t kv;
+    uint32_t s;      // sequence slot in the launch
+};
+
+// Units of a sequence run chunk-major: chunk, then layer, then K/V, then page,
+// so consecutive workgroups fill consecutive bytes of a chunk.
+__device__ __forceinline__ PageUnit locate_page_unit(const MoveArgs& a, uint32_t item)
+{
+    PageUnit u;
+    u.s = find_seq(a, item);
+    const SeqArg& sq = a.seq[u.s];
+    uint32_t local = item - sq.item_begin;
+    uint32_t pages_here;
+    if (local < sq.n_full * a.units_per_chunk) {
+        u.c = local / a.units_per_chunk;
+        local -= u.c * a.units_per_chunk;
+        u.n_c = a.chunk_size;
+        pages_here = a.pages_per_chunk;
+    } else {
+        local -= sq.n_full * a.units_per_chunk;
+        u.c = sq.n_full;
+        u.n_c = sq.tail_tokens;
+        pages_here = (sq.tail_tokens + a.page_size - 1) / a.page_size;
+    }
+    const uint32_t per_layer = 2 * pages_here;
+    u.l = a.layer0 + local / per_layer;
+    const uint32_t r = local % per_layer;
+    u.kv = r >= pages_here ? 1u : 0u;
+    const uint32_t pi = r - u.kv * pages_here;
+    u.j0 = pi * a.page_size;
+    const uint32_t left = u.n_c - u.j0;
+    u.rows = left < a.page_size ? left : a.page_size;
+    u.page = gptr<const gi32>(sq.bt)[sq.first_page + u.c * a.pages_per_chunk + pi];
+    return u;
+}
+
+// Streams nvec 16-byte vectors src -> dst: kVpt loads in flight per thread
+// before the matching stores; a strided remainder loop for partial pages.
+template <int kBlock, int kVpt, bool kNtLoad, bool kNtStore>
+__device__ __forceinline__ void copy_vectors(const gvec4* __restrict__ src, gvec4* __restrict__ dst,
+                                             uint32_t nvec)
+{
+    const uint32_t t = threadIdx.x;
+    uint32_t base = 0;
+    for (; base + kBlock * kVpt <= nvec; base += kBlock * kVpt) {
+        u32x4 v[kVpt];
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k) {
+            const gvec4* p = src + base + k * kBlock + t;
+            v[k] = kNtLoad ? __builtin_nontemporal_load(p) : *p;
+        }
+#pragma unroll
+        for (int k = 0; k < kVpt; ++k) {
+            gvec4* p = dst + base + k * kBlock + t;
+            if (kNtStore) __builtin_nontemporal_store(v[k], p); else *p = v[k];
+        }
+    }
+    for (uint32_t i = base + t; i < nvec; i += kBlock) {
+        const u32x4 v = kNtLoad ? __builtin_nontemporal_load(src + i) : src[i];
+        if (kNtStore) __builtin_nontemporal_store(v, dst + i); else dst[i] = v;
+    }
+}
+
+// Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8).  Renumber them so that each XCD walks one contiguous range of the
+// grid: neighbouring tiles (the pieces of one page, the rows of one chunk)
+// then run on the same XCD, one after the other.  A bijection on
+// [0, 8 * (grid / 8)); the few workgroups past that keep their number.
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t grid)
+{
+    const uint32_t per = grid / 8;
+    return b < per * 8 ? (b % 8) * per + b / 8 : b;
+}
+
+// Cache-policy bits of the buffer instructions (gfx94x/gfx950 encoding of
+// the aux operand): 2 = nt (streaming, do not keep in cache), 16 = sc1.
+enum : int { kCpolNt = 2, kCpolSc1 = 16 };
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t byte_range(uint64_t base, uint32_t nbytes)
+{
+    // raw buffer: stride 0, range-checked against nbytes (word 3 = gfx9 format)
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), (short)0, (int)nbytes,
+                                             0x00020000);
+}
+
+// Copies nbytes (a multiple of 16, at most kBlock*kVpt*16) from src to dst:
+// kVpt loads in flight per thread, then the stores.  Buffer accesses at or
+// past nbytes are discarded by the hardware range check (loads return 0,
+// stores are dropped), so a partial tile needs no per-vector guard.
+template <int kBlock, int kVpt, int kAuxLoad, int kAuxStore>
+__device__ __forceinline__ void copy_tile(uint64_t src, uint64_t dst, uint32_t nbytes)
+{
+    const __amdgpu_buffer_rsrc_t rs = byte_range(src, nbytes);
+    const __amdgpu_buffer_rsrc_t rd = byte_range(dst, nbytes);
+    u32x4 v[kVpt];
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k)
+        v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (k * kBlock + threadIdx.x) * 16, 0, kAuxLoad);
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k)
+        __builtin_amdgcn_raw_buffer_store_b128(v[k], rd, (k * kBlock + threadIdx.x) * 16, 0, kAuxStore);
+}
+
+}  // namespace kvmove

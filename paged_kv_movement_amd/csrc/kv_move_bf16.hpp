@@ -1,0 +1,59 @@
+// kv_move_bf16.hpp -- the bf16 movers (gather pages -> chunks, scatter
+// chunks -> pages) and the plain copy used to calibrate measurements.
+#pragma once
+
+#include "kv_common.hpp"
+
+namespace kvmove {
+
+// Launch shape, from sweeps on MI355X at the Llama-3.1-8B KV shape: tiles of
+// 8 KiB (256 threads x 2 vectors of 16 B), four per 32 KiB page; streaming
+// (nt) cache policy, with sc1 on the gather.
+constexpr int kMoveBlock = 256;
+constexpr int kMoveVpt = 2;
+constexpr int kGatherAuxLoad = kCpolNt | kCpolSc1;
+constexpr int kGatherAuxStore = kCpolNt | kCpolSc1;
+constexpr int kScatterAuxLoad = kCpolNt;
+constexpr int kScatterAuxStore = kCpolNt;
+constexpr int kCopyBlock = 256;
+constexpr int kCopyVpt = 1;
+
+// Gather (kToChunk) or scatter (!kToChunk) of one tile of one page unit,
+// bf16 copied bit for bit.  Grid = units * a.tiles.
+template <bool kToChunk, int kBlock, int kVpt, int kAuxLoad, int kAuxStore>
+__global__ __launch_bounds__(kBlock) void move_bf16(MoveArgs a)
+{
+    const uint32_t b = xcd_contiguous(blockIdx.x, gridDim.x);
+    const uint32_t unit = b / a.tiles;
+    const uint32_t tile = b - unit * a.tiles;
+    const PageUnit u = locate_page_unit(a, a.item_base + unit);
+    const uint32_t row_bytes = a.width * 2;
+    const uint32_t nbytes = u.rows * row_bytes;
+    const uint32_t lo = tile * (kBlock * kVpt * 16);
+    if (lo >= nbytes) return;                         // tile past a short (tail) page
+    if (u.page < 0 || u.page >= a.num_pages) { raise_fault(kFaultPage); return; }
+    const uint64_t pool = wave_uniform(gptr<const gu64>(u.kv ? a.v_pages : a.k_pages)[u.l]);
+    const uint64_t chunk = wave_uniform(gptr<const gu64>(a.seq[u.s].chunks)[u.c]);
+    if (bad_addr(pool)) { raise_fault(kFaultPool); return; }
+    if (bad_addr(chunk)) { raise_fault(kFaultChunk); return; }
+    const uint32_t left = nbytes - lo;
+    const uint32_t n = left < kBlock * kVpt * 16 ? left : kBlock * kVpt * 16;
+    const uint64_t page_addr = pool + (uint64_t)u.page * a.page_size * row_bytes + lo;
+    const uint64_t chunk_addr =
+        chunk + ((uint64_t)(u.l * 2 + u.kv) * u.n_c + u.j0) * row_bytes + lo;
+    if (kToChunk) copy_tile<kBlock, kVpt, kAuxLoad, kAuxStore>(page_addr, chunk_addr, n);
+    else copy_tile<kBlock, kVpt, kAuxLoad, kAuxStore>(chunk_addr, page_addr, n);
+}
+
+// Plain contiguous copy (measurement aid): one tile of kBlock*kVpt vectors
+// per workgroup, the same instruction form as the movers.
+template <int kBlock, int kVpt>
+__global__ __launch_bounds__(kBlock) void copy_contiguous(uint64_t src, uint64_t dst, int64_t nbytes)
+{
+    const int64_t tile = (int64_t)kBlock * kVpt * 16;
+    const int64_t lo = (int64_t)blockIdx.x * tile;
+    const int64_t left = nbytes - lo;
+    copy_tile<kBlock, kVpt, kCpolNt, kCpolNt>(src + lo, dst + lo, (uint32_t)(left < tile ? left : tile));
+}
+
+}  // namespace kvmove

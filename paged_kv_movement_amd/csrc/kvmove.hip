@@ -13,24 +13,13 @@
 #include <cstdio>
 #include <string>
 
-#include "kv_kernels.hpp"
+#include "kv_fp8.hpp"
+#include "kv_move_bf16.hpp"
 
 namespace {
 
 using namespace kvmove;
 
-// Launch shape of the movers, from sweeps on MI355X at the Llama-3.1-8B
-// shape: 8 KiB tiles (256 threads x 2 vectors of 16 B), streaming (nt)
-// cache policy, sc1 on the gather.
-constexpr int kMoveBlock = 256;
-constexpr int kMoveVpt = 2;
-constexpr int kGatherAuxLoad = kCpolNt | kCpolSc1;
-constexpr int kGatherAuxStore = kCpolNt | kCpolSc1;
-constexpr int kScatterAuxLoad = kCpolNt;
-constexpr int kScatterAuxStore = kCpolNt;
-constexpr int kFp8Block = 256;
-constexpr int kCopyBlock = 256;
-constexpr int kCopyVpt = 1;
 // Workgroups per launch: gridDim.x * blockDim.x must stay below 2^32.
 constexpr int64_t kMaxBlocks = (int64_t(1) << 24) - 1;
 
