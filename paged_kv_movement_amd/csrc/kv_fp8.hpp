@@ -9,7 +9,10 @@
 
 namespace kvmove {
 
-constexpr int kFp8Block = 256;
+constexpr int kFp8StoreBlock = 512;     // threads per (chunk, layer, K/V) group
+constexpr int kFp8StoreUnroll = 4;     // 16-byte loads in flight per thread
+constexpr int kFp8RetrieveBlock = 256; // tiles of 8 KiB bf16 output
+constexpr int kFp8RetrieveVpt = 2;
 
 // float -> OCP E4M3 ("fn") byte, round to nearest-even, saturating at 448.
 // Integer form of the rounding: in the normal range the e4m3 code is bits
@@ -29,24 +32,6 @@ __device__ __forceinline__ uint32_t e4m3_from_float(float y)
     }
     const float m = __builtin_rintf(__uint_as_float(a) * 512.0f);  // 0 .. 8
     return sign | (uint32_t)m;
-}
-
-// OCP E4M3 byte -> float (exact).
-__device__ __forceinline__ float float_from_e4m3(uint32_t b)
-{
-    const uint32_t sign = (b & 0x80u) << 24;
-    const uint32_t em = b & 0x7Fu;
-    if (em == 0x7Fu) return __uint_as_float(sign | 0x7FC00000u);   // NaN
-    if (em < 8u) return __uint_as_float(sign | __float_as_uint((float)em * 0.001953125f));
-    return __uint_as_float(sign | ((em + (120u << 3)) << 20));
-}
-
-// float -> bf16 bits, round to nearest-even; NaN kept quiet with its sign.
-__device__ __forceinline__ uint32_t bf16_from_float(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
@@ -92,15 +77,47 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* lds)
     return m;
 }
 
+// Quotient x / s for the e4m3 encoder without a division: q0 = x * r with
+// r = 1/s correctly rounded, one fused multiply-add for the exact residual,
+// one to correct q0 (Markstein's correction).  The result is the correctly
+// rounded quotient except for some |x| <= 2^-25; for groups whose amax is a
+// finite bf16 value >= 2^-4 an exhaustive check over every (amax, x) bf16
+// pair showed the e4m3 code always equals that of the IEEE quotient.  The
+// sign is taken from x, which also keeps -0.
+__device__ __forceinline__ float quotient_fast(float x, float s, float r)
+{
+    const float q0 = x * r;
+    const float e = __builtin_fmaf(-q0, s, x);
+    const float q1 = __builtin_fmaf(e, r, q0);
+    return __uint_as_float((__float_as_uint(q1) & 0x7FFFFFFFu) | (__float_as_uint(x) & 0x80000000u));
+}
+
+// Two floats -> two E4M3 bytes (low 16 bits) with the hardware converter,
+// which rounds to nearest-even and matches the OCP encoding for |y| <= 464
+// (checked against the CPU oracle on every float32 in that range); the
+// quotients fed to it stay below 448.0001 in magnitude.
+__device__ __forceinline__ uint32_t e4m3x2(float a, float b)
+{
+    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// amax bits (bf16 magnitude) for which the fast quotient is exact in e4m3
+__device__ __forceinline__ bool fast_quotient_ok(uint32_t amax_bits)
+{
+    return amax_bits >= 0x3D80u && amax_bits < 0x7F80u;     // [2^-4, largest finite]
+}
+
 // Gather + quantise one (chunk, layer, K/V) group into e4m3 bytes + scale.
-template <int kBlock>
+// Pass 1 reads the group's pages and takes max |x|; pass 2 re-reads them
+// (streaming), quantises, and writes 8 bytes per 16-byte input vector.
+template <int kBlock, int kUnroll>
 __global__ __launch_bounds__(kBlock) void store_fp8(MoveArgs a)
 {
     __shared__ uint32_t red[kBlock / 64];
-    const GroupUnit g = locate_group_unit(a, a.item_base + blockIdx.x);
+    const GroupUnit g = locate_group_unit(a, a.item_base + xcd_contiguous(blockIdx.x, gridDim.x));
     const SeqArg& sq = a.seq[g.s];
-    const uint64_t pool = gptr<const gu64>(g.kv ? a.v_pages : a.k_pages)[g.l];
-    const uint64_t chunk = gptr<const gu64>(sq.chunks)[g.c];
+    const uint64_t pool = wave_uniform(gptr<const gu64>(g.kv ? a.v_pages : a.k_pages)[g.l]);
+    const uint64_t chunk = wave_uniform(gptr<const gu64>(sq.chunks)[g.c]);
     if (bad_addr(pool)) { raise_fault(kFaultPool); return; }
     if (bad_addr(chunk)) { raise_fault(kFaultChunk); return; }
     const uint32_t first = sq.first_page + g.c * a.pages_per_chunk;
@@ -109,9 +126,8 @@ __global__ __launch_bounds__(kBlock) void store_fp8(MoveArgs a)
         const int64_t page = gptr<const gi32>(sq.bt)[first + pi];
         if (page < 0 || page >= a.num_pages) { raise_fault(kFaultPage); return; }
     }
-    const uint32_t vrow = a.width / 8;
-    const int64_t page_vecs = (int64_t)a.page_size * vrow;
-    const gvec4* pool_v = reinterpret_cast<const gvec4*>(pool);
+    const uint32_t page_bytes = a.page_size * a.width * 2;
+    constexpr uint32_t kStep = kBlock * kUnroll * 16;
 
     // pass 1: absolute maximum as bf16 magnitude bits (integer order equals
     // magnitude order for non-NaN; NaN codes sort above infinity).  Plain
@@ -122,83 +138,124 @@ __global__ __launch_bounds__(kBlock) void store_fp8(MoveArgs a)
     for (uint32_t pi = 0; pi < n_pages; ++pi) {
         const int64_t page = gptr<const gi32>(sq.bt)[first + pi];
         const uint32_t left = g.n_c - pi * a.page_size;
-        const uint32_t nvec = (left < a.page_size ? left : a.page_size) * vrow;
-        const gvec4* src = pool_v + page * page_vecs;
-        for (uint32_t i = threadIdx.x; i < nvec; i += kBlock) {
-            const u32x4 v = src[i];
+        const uint32_t nb = (left < a.page_size ? left : a.page_size) * a.width * 2;
+        const __amdgpu_buffer_rsrc_t rs = byte_range(pool + (uint64_t)page * page_bytes, nb);
+        for (uint32_t base = 0; base < nb; base += kStep) {
+            u32x4 v[kUnroll];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t lo = v[k] & 0x7FFFu;
-                const uint32_t hi = (v[k] >> 16) & 0x7FFFu;
-                m1 = m1 > lo ? m1 : lo;
-                m1 = m1 > hi ? m1 : hi;
+            for (int k = 0; k < kUnroll; ++k)
+                v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, base + (k * kBlock + threadIdx.x) * 16, 0, 0);
+#pragma unroll
+            for (int k = 0; k < kUnroll; ++k) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t lo = v[k][j] & 0x7FFFu;
+                    const uint32_t hi = (v[k][j] >> 16) & 0x7FFFu;
+                    m1 = m1 > lo ? m1 : lo;
+                    m1 = m1 > hi ? m1 : hi;
+                }
             }
         }
     }
     const uint32_t amax_bits = block_max_u32<kBlock>(m1, red);
     const float amax = __uint_as_float(amax_bits << 16);
     const float scale = amax == 0.0f ? 1.0f : amax / 448.0f;
+    const bool fast = fast_quotient_ok(amax_bits);
+    const float r = 1.0f / scale;
 
     // pass 2: quantise
-    gbyte* out = reinterpret_cast<gbyte*>(chunk) + (int64_t)(g.l * 2 + g.kv) * g.n_c * a.width;
+    const uint64_t out = chunk + (uint64_t)(g.l * 2 + g.kv) * g.n_c * a.width;
     for (uint32_t pi = 0; pi < n_pages; ++pi) {
         const int64_t page = gptr<const gi32>(sq.bt)[first + pi];
         const uint32_t left = g.n_c - pi * a.page_size;
-        const uint32_t nvec = (left < a.page_size ? left : a.page_size) * vrow;
-        const gvec4* src = pool_v + page * page_vecs;
-        gvec2* dst = reinterpret_cast<gvec2*>(out + (int64_t)pi * a.page_size * a.width);
-        for (uint32_t i = threadIdx.x; i < nvec; i += kBlock) {
-            const u32x4 v = src[i];
-            u32x2 q;
+        const uint32_t nb = (left < a.page_size ? left : a.page_size) * a.width * 2;
+        const __amdgpu_buffer_rsrc_t rs = byte_range(pool + (uint64_t)page * page_bytes, nb);
+        const __amdgpu_buffer_rsrc_t rd = byte_range(out + (uint64_t)pi * a.page_size * a.width, nb / 2);
+        for (uint32_t base = 0; base < nb; base += kStep) {
+            u32x4 v[kUnroll];
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const uint32_t b0 = e4m3_from_float(lo_bf16(v[2 * k]) / scale);
-                const uint32_t b1 = e4m3_from_float(hi_bf16(v[2 * k]) / scale);
-                const uint32_t b2 = e4m3_from_float(lo_bf16(v[2 * k + 1]) / scale);
-                const uint32_t b3 = e4m3_from_float(hi_bf16(v[2 * k + 1]) / scale);
-                q[k] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+            for (int k = 0; k < kUnroll; ++k)
+                v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, base + (k * kBlock + threadIdx.x) * 16, 0,
+                                                            kCpolNt);
+#pragma unroll
+            for (int k = 0; k < kUnroll; ++k) {
+                u32x2 q;
+                if (fast) {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const uint32_t w0 = v[k][2 * j], w1 = v[k][2 * j + 1];
+                        const uint32_t p0 = e4m3x2(quotient_fast(lo_bf16(w0), scale, r),
+                                                   quotient_fast(hi_bf16(w0), scale, r));
+                        const uint32_t p1 = e4m3x2(quotient_fast(lo_bf16(w1), scale, r),
+                                                   quotient_fast(hi_bf16(w1), scale, r));
+                        q[j] = p0 | (p1 << 16);
+                    }
+                } else {   // tiny, infinite or NaN amax: IEEE division + exact integer encoder
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const uint32_t b0 = e4m3_from_float(lo_bf16(v[k][2 * j]) / scale);
+                        const uint32_t b1 = e4m3_from_float(hi_bf16(v[k][2 * j]) / scale);
+                        const uint32_t b2 = e4m3_from_float(lo_bf16(v[k][2 * j + 1]) / scale);
+                        const uint32_t b3 = e4m3_from_float(hi_bf16(v[k][2 * j + 1]) / scale);
+                        q[j] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+                    }
+                }
+                __builtin_amdgcn_raw_buffer_store_b64(q, rd, base / 2 + (k * kBlock + threadIdx.x) * 8, 0,
+                                                      kCpolNt);
             }
-            dst[i] = q;
         }
     }
-    if (threadIdx.x == 0) {
-        gf32* scales = reinterpret_cast<gf32*>(reinterpret_cast<gbyte*>(chunk) +
-                                               (int64_t)a.num_layers * 2 * g.n_c * a.width);
-        scales[g.l * 2 + g.kv] = scale;
-    }
+    if (threadIdx.x == 0)
+        gptr<gf32>(chunk + (uint64_t)a.num_layers * 2 * g.n_c * a.width)[g.l * 2 + g.kv] = scale;
 }
 
-// Scatter + dequantise one page unit.
-template <int kBlock>
+// Scatter + dequantise one tile of one page unit: e4m3 decoded by the
+// hardware converter (exact), times the scale in float32, rounded to bf16 by
+// the hardware converter (round to nearest-even; both checked against the
+// CPU oracle, the latter on every float32).  Tiles are kBlock*kVpt*16 bytes
+// of bf16 output; grid = units * a.tiles.
+template <int kBlock, int kVpt>
 __global__ __launch_bounds__(kBlock) void retrieve_fp8(MoveArgs a)
 {
-    const PageUnit u = locate_page_unit(a, a.item_base + blockIdx.x);
+    const uint32_t b = xcd_contiguous(blockIdx.x, gridDim.x);
+    const uint32_t unit = b / a.tiles;
+    const uint32_t tile = b - unit * a.tiles;
+    const PageUnit u = locate_page_unit(a, a.item_base + unit);
+    const uint32_t out_bytes = u.rows * a.width * 2;
+    const uint32_t lo = tile * (kBlock * kVpt * 16);
+    if (lo >= out_bytes) return;
     if (u.page < 0 || u.page >= a.num_pages) { raise_fault(kFaultPage); return; }
-    const uint64_t pool = gptr<const gu64>(u.kv ? a.v_pages : a.k_pages)[u.l];
-    const uint64_t chunk = gptr<const gu64>(a.seq[u.s].chunks)[u.c];
+    const uint64_t pool = wave_uniform(gptr<const gu64>(u.kv ? a.v_pages : a.k_pages)[u.l]);
+    const uint64_t chunk = wave_uniform(gptr<const gu64>(a.seq[u.s].chunks)[u.c]);
     if (bad_addr(pool)) { raise_fault(kFaultPool); return; }
     if (bad_addr(chunk)) { raise_fault(kFaultChunk); return; }
-    const gbyte* cbytes = reinterpret_cast<const gbyte*>(chunk);
-    const float scale = *reinterpret_cast<const gf32*>(
-        cbytes + (int64_t)a.num_layers * 2 * u.n_c * a.width + (u.l * 2 + u.kv) * 4);
-    const gvec2* src = reinterpret_cast<const gvec2*>(
-        cbytes + ((int64_t)(u.l * 2 + u.kv) * u.n_c + u.j0) * a.width);
-    gvec4* dst = reinterpret_cast<gvec4*>(pool) + u.page * (int64_t)(a.page_size * (a.width / 8));
-    const uint32_t nvec = u.rows * (a.width / 8);        // 8 elements each
-    for (uint32_t i = threadIdx.x; i < nvec; i += kBlock) {
-        const u32x2 q = src[i];
+    const float scale = *gptr<const gf32>(chunk + (uint64_t)a.num_layers * 2 * u.n_c * a.width +
+                                          (u.l * 2 + u.kv) * 4);
+    const uint32_t left = out_bytes - lo;
+    const uint32_t n = left < kBlock * kVpt * 16 ? left : kBlock * kVpt * 16;
+    const __amdgpu_buffer_rsrc_t rs =
+        byte_range(chunk + ((uint64_t)(u.l * 2 + u.kv) * u.n_c + u.j0) * a.width + lo / 2, n / 2);
+    const __amdgpu_buffer_rsrc_t rd =
+        byte_range(pool + (uint64_t)u.page * a.page_size * a.width * 2 + lo, n);
+    u32x2 q[kVpt];
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k)
+        q[k] = __builtin_amdgcn_raw_buffer_load_b64(rs, (k * kBlock + threadIdx.x) * 8, 0, kCpolNt);
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k) {
         u32x4 o;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const uint32_t w = q[k];
-            const uint32_t h0 = bf16_from_float(float_from_e4m3(w & 0xFFu) * scale);
-            const uint32_t h1 = bf16_from_float(float_from_e4m3((w >> 8) & 0xFFu) * scale);
-            const uint32_t h2 = bf16_from_float(float_from_e4m3((w >> 16) & 0xFFu) * scale);
-            const uint32_t h3 = bf16_from_float(float_from_e4m3(w >> 24) * scale);
-            o[2 * k] = h0 | (h1 << 16);
-            o[2 * k + 1] = h2 | (h3 << 16);
+        for (int j = 0; j < 2; ++j) {
+            const auto d0 = __builtin_amdgcn_cvt_pk_f32_fp8(q[k][j], false);   // bytes 0, 1
+            const auto d1 = __builtin_amdgcn_cvt_pk_f32_fp8(q[k][j], true);    // bytes 2, 3
+            const __bf16 h0 = (__bf16)(d0[0] * scale), h1 = (__bf16)(d0[1] * scale);
+            const __bf16 h2 = (__bf16)(d1[0] * scale), h3 = (__bf16)(d1[1] * scale);
+            o[2 * j] = __builtin_bit_cast(unsigned short, h0) |
+                       ((uint32_t)__builtin_bit_cast(unsigned short, h1) << 16);
+            o[2 * j + 1] = __builtin_bit_cast(unsigned short, h2) |
+                           ((uint32_t)__builtin_bit_cast(unsigned short, h3) << 16);
         }
-        dst[i] = o;
+        __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * kBlock + threadIdx.x) * 16, 0, kCpolNt);
     }
 }
 

@@ -173,26 +173,30 @@ int launch_units(KernelFn kernel, int block, int tile_bytes, Unit unit, const kv
     return KV_OK;
 }
 
-KernelFn gather_kernel(int fmt)
+struct Launch {
+    KernelFn kernel;
+    int block;        // threads per workgroup
+    int tile_bytes;   // bytes of page-side data per workgroup (0: one workgroup per unit)
+};
+
+Launch gather_launch(int fmt)
 {
     if (fmt == KV_FMT_BF16)
-        return reinterpret_cast<KernelFn>(
-            &move_bf16<true, kMoveBlock, kMoveVpt, kGatherAuxLoad, kGatherAuxStore>);
-    return reinterpret_cast<KernelFn>(&store_fp8<kFp8Block>);
+        return {reinterpret_cast<KernelFn>(
+                    &move_bf16<true, kMoveBlock, kMoveVpt, kGatherAuxLoad, kGatherAuxStore>),
+                kMoveBlock, kMoveBlock * kMoveVpt * 16};
+    return {reinterpret_cast<KernelFn>(&store_fp8<kFp8StoreBlock, kFp8StoreUnroll>), kFp8StoreBlock, 0};
 }
 
-KernelFn scatter_kernel(int fmt)
+Launch scatter_launch(int fmt)
 {
     if (fmt == KV_FMT_BF16)
-        return reinterpret_cast<KernelFn>(
-            &move_bf16<false, kMoveBlock, kMoveVpt, kScatterAuxLoad, kScatterAuxStore>);
-    return reinterpret_cast<KernelFn>(&retrieve_fp8<kFp8Block>);
+        return {reinterpret_cast<KernelFn>(
+                    &move_bf16<false, kMoveBlock, kMoveVpt, kScatterAuxLoad, kScatterAuxStore>),
+                kMoveBlock, kMoveBlock * kMoveVpt * 16};
+    return {reinterpret_cast<KernelFn>(&retrieve_fp8<kFp8RetrieveBlock, kFp8RetrieveVpt>),
+            kFp8RetrieveBlock, kFp8RetrieveBlock * kFp8RetrieveVpt * 16};
 }
-
-int block_of(int fmt) { return fmt == KV_FMT_BF16 ? kMoveBlock : kFp8Block; }
-
-// Bytes per workgroup of the tiled movers (0: one workgroup per unit).
-int tile_of(int fmt) { return fmt == KV_FMT_BF16 ? kMoveBlock * kMoveVpt * 16 : 0; }
 
 // Shared body of the two retrieve entry points.
 int retrieve(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
@@ -212,8 +216,9 @@ int retrieve(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hi
         const int64_t end = s.tok_start + n_hit * paged->chunk_size;
         n_tok[i] = (end < s.tok_end ? end : s.tok_end) - s.tok_start;
     }
-    int rc = launch_units(scatter_kernel(fmt), block_of(fmt), tile_of(fmt), Unit::Page, paged, seqs,
-                          n_tok, n_seqs, layer0, n_layers, stream);
+    const Launch L = scatter_launch(fmt);
+    int rc = launch_units(L.kernel, L.block, L.tile_bytes, Unit::Page, paged, seqs, n_tok, n_seqs,
+                          layer0, n_layers, stream);
     if (rc == KV_OK && out_tokens != nullptr)
         for (int i = 0; i < n_seqs; ++i) out_tokens[i] = n_tok[i];
     if (n_tok != small) delete[] n_tok;
@@ -255,9 +260,9 @@ int kv_store_chunks(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int f
     int64_t small[64];
     int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
     for (int i = 0; i < n_seqs; ++i) n_tok[i] = seqs[i].tok_end - seqs[i].tok_start;
-    rc = launch_units(gather_kernel(fmt), block_of(fmt), tile_of(fmt),
-                      fmt == KV_FMT_BF16 ? Unit::Page : Unit::Group, paged, seqs, n_tok, n_seqs, 0,
-                      paged->num_layers, stream);
+    const Launch L = gather_launch(fmt);
+    rc = launch_units(L.kernel, L.block, L.tile_bytes, fmt == KV_FMT_BF16 ? Unit::Page : Unit::Group,
+                      paged, seqs, n_tok, n_seqs, 0, paged->num_layers, stream);
     if (n_tok != small) delete[] n_tok;
     return rc == KV_OK ? ok() : rc;
 }

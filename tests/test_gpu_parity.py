@@ -307,3 +307,41 @@ def test_host_rejections_launch_nothing():
     assert ei.value.code == kvm.KV_ERANGE
     _sync()
     assert all((b.cpu().numpy() == 0xCD)[: b.numel() - 256].all() for b in cs[0][0])
+
+
+def test_fp8_every_bf16_value_under_many_amax():
+    # Each (chunk, K/V) group holds its amax followed by every bf16 value of
+    # magnitude <= amax, both signs; the amax values span the whole bf16
+    # range, on both sides of 2^-4 (where the kernel switches between its
+    # quotient forms) and include subnormal, zero-only and largest-finite groups.
+    rng = np.random.default_rng(17)
+    amax = [0x3D80, 0x3D81, 0x3E00, 0x3F80, 0x3FC0, 0x4000, 0x40A0, 0x4120, 0x42A0, 0x4300, 0x4780,
+            0x5000, 0x6000, 0x7000, 0x7F00, 0x7F7F, 0x3D7F, 0x3C00, 0x3000, 0x1000, 0x0080, 0x0001, 0x0000]
+    amax += [int(x) for x in rng.integers(0x3D80, 0x7F7F, size=9)]
+    n_groups = len(amax)                       # 32 groups = 16 chunks x (K, V), one layer
+    n_chunks = n_groups // 2
+    T = n_chunks * 256
+    w = wl.custom("fp8-all-values", 231, 1, 8, 128, T // 16 + 8, [(0, T)])
+    E = w.width
+    logical = np.zeros((2, T, E), np.uint16)   # [kv, token, channel]
+    for gi, a in enumerate(amax):
+        c, kv = gi // 2, gi % 2
+        vals = np.arange(0, a + 1, dtype=np.uint32)
+        body = np.concatenate([[a], vals, vals | 0x8000]).astype(np.uint16)
+        grp = np.zeros(256 * E, np.uint16)
+        grp[:body.size] = body
+        logical[kv, c * 256:(c + 1) * 256] = grp.reshape(256, E)
+    arr = np.zeros(w.pool_shape(), np.uint16)
+    bt = w.seqs[0].block_table
+    t = np.arange(T)
+    for kv in range(2):
+        arr[0, kv][bt[t // 16], t % 16] = logical[kv]
+    pool, paged, batch, cs = setup_device(w, arr, fmt=FP8, fill=0xCD)
+    kvm.store(paged, batch, FP8)
+    _sync()
+    assert kvm.take_faults() == 0
+    check_store(w, arr, cs, FP8)
+    pool.view(torch.int16).fill_(0x7E57)
+    assert kvm.retrieve(paged, batch, fmt=FP8) == [T]
+    _sync()
+    check_retrieve(w, np.full_like(arr, 0x7E57), host_from_dev_pool(pool), cs, FP8, [w.seqs[0].hit_mask])
