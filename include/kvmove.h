@@ -150,10 +150,15 @@ int kv_retrieve_chunks(const kv_paged* paged, const kv_seq* seqs,
  * wait_load_kv(layer)): as kv_retrieve_chunks but writes layer `layer` only,
  * on copy_stream, then records layer_done (if not NULL) on copy_stream -- also
  * when nothing hits, so a stream or host waiting on it never hangs.  Calling
- * it for layers 0 .. L-1 leaves the pool as one kv_retrieve_chunks call does. */
+ * it for layers 0 .. L-1 leaves the pool as one kv_retrieve_chunks call does.
+ * max_workgroups = 0 launches one workgroup per 8 KiB tile (fastest when the
+ * GPU is otherwise idle); a positive value caps the grid, each workgroup then
+ * moving a contiguous run of tiles, so the scatter occupies few wave slots
+ * while compute on another stream runs beside it. */
 int kv_retrieve_layer(const kv_paged* paged, const kv_seq* seqs,
                       const uint8_t* const* hit_mask, int n_seqs, int fmt, int32_t layer,
-                      int64_t* out_tokens, hipStream_t copy_stream, hipEvent_t layer_done);
+                      int64_t* out_tokens, int32_t max_workgroups, hipStream_t copy_stream,
+                      hipEvent_t layer_done);
 
 /* Message for the last non-OK return on this thread ("" if none). */
 const char* kv_last_error(void);

@@ -84,7 +84,7 @@ def load():
         "kv_num_chunks": (i64, [P, i64, i64]),
         "kv_store_chunks": (ctypes.c_int, [P, S, ctypes.c_int, ctypes.c_int, vp]),
         "kv_retrieve_chunks": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, vp, vp]),
-        "kv_retrieve_layer": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, i32, vp, vp, vp]),
+        "kv_retrieve_layer": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, i32, vp, i32, vp, vp]),
         "kv_last_error": (ctypes.c_char_p, []),
         "kv_take_faults": (ctypes.c_int, []),
         "kv_copy_bytes": (ctypes.c_int, [vp, vp, ctypes.c_size_t, vp]),
@@ -234,9 +234,11 @@ def retrieve(paged: Paged, seqs, masks=None, fmt: int = FMT_BF16, stream=None) -
 
 
 def retrieve_layer(paged: Paged, seqs, layer: int, masks=None, fmt: int = FMT_BF16,
-                   stream=None, event=None) -> list:
+                   stream=None, event=None, max_workgroups: int = 0) -> list:
     """Scatter one layer of the leading hit chunks on ``stream``, then record
-    ``event`` (a torch.cuda.Event) on it (kv_retrieve_layer)."""
+    ``event`` (a torch.cuda.Event) on it (kv_retrieve_layer).  A positive
+    ``max_workgroups`` caps the grid so compute on another stream keeps most
+    of the GPU."""
     b = _batch(paged, seqs)
     if masks is not None:
         b.set_masks(masks)
@@ -248,7 +250,7 @@ def retrieve_layer(paged: Paged, seqs, layer: int, masks=None, fmt: int = FMT_BF
             event.record(stream if stream is not None else torch.cuda.current_stream())
         ev = event.cuda_event
     _check(load().kv_retrieve_layer(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n, fmt, layer,
-                                    b.out, _stream_handle(stream), ev))
+                                    b.out, max_workgroups, _stream_handle(stream), ev))
     return [int(b.out[i]) for i in range(b.n)]
 
 

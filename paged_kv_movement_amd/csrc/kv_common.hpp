@@ -79,7 +79,9 @@ struct MoveArgs {
     uint32_t layer0;          // first layer moved
     uint32_t n_layers;        // layers moved
     uint32_t n_seqs;
-    uint32_t tiles;           // workgroups per page unit (tiled movers; 1 otherwise)
+    uint32_t tiles;           // tiles per page unit (tiled movers; 1 otherwise)
+    uint32_t total_tiles;     // tiles in this launch; a workgroup may take several
+    uint32_t pad_;
     SeqArg seq[kMaxSeqs];
 };
 
@@ -188,6 +190,22 @@ __device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t grid)
 {
     const uint32_t per = grid / 8;
     return b < per * 8 ? (b % 8) * per + b / 8 : b;
+}
+
+// Tiles [first, last) of this workgroup.  With one workgroup per tile (the
+// default launch) that is a single tile; with a capped grid each workgroup
+// walks a contiguous run of tiles, and the runs stay XCD-contiguous.
+struct TileRange {
+    uint32_t first, last;
+};
+
+__device__ __forceinline__ TileRange my_tiles(uint32_t total)
+{
+    const uint32_t w = xcd_contiguous(blockIdx.x, gridDim.x);
+    const uint32_t per = (total + gridDim.x - 1) / gridDim.x;
+    const uint32_t first = w * per;
+    const uint32_t last = first + per < total ? first + per : total;
+    return {first, last};
 }
 
 // Cache-policy bits of the buffer instructions (gfx94x/gfx950 encoding of

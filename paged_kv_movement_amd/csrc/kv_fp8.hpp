@@ -213,11 +213,11 @@ __global__ __launch_bounds__(kBlock) void store_fp8(MoveArgs a)
 // hardware converter (exact), times the scale in float32, rounded to bf16 by
 // the hardware converter (round to nearest-even; both checked against the
 // CPU oracle, the latter on every float32).  Tiles are kBlock*kVpt*16 bytes
-// of bf16 output; grid = units * a.tiles.
+// of bf16 output; grid = units * a.tiles, or fewer workgroups each taking
+// a contiguous run of tiles.
 template <int kBlock, int kVpt>
-__global__ __launch_bounds__(kBlock) void retrieve_fp8(MoveArgs a)
+__device__ __forceinline__ void retrieve_fp8_tile(const MoveArgs& a, uint32_t b)
 {
-    const uint32_t b = xcd_contiguous(blockIdx.x, gridDim.x);
     const uint32_t unit = b / a.tiles;
     const uint32_t tile = b - unit * a.tiles;
     const PageUnit u = locate_page_unit(a, a.item_base + unit);
@@ -257,6 +257,13 @@ __global__ __launch_bounds__(kBlock) void retrieve_fp8(MoveArgs a)
         }
         __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * kBlock + threadIdx.x) * 16, 0, kCpolNt);
     }
+}
+
+template <int kBlock, int kVpt>
+__global__ __launch_bounds__(kBlock) void retrieve_fp8(MoveArgs a)
+{
+    const TileRange r = my_tiles(a.total_tiles);
+    for (uint32_t b = r.first; b < r.last; ++b) retrieve_fp8_tile<kBlock, kVpt>(a, b);
 }
 
 }  // namespace kvmove

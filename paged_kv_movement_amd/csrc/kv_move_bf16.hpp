@@ -19,11 +19,10 @@ constexpr int kCopyBlock = 256;
 constexpr int kCopyVpt = 1;
 
 // Gather (kToChunk) or scatter (!kToChunk) of one tile of one page unit,
-// bf16 copied bit for bit.  Grid = units * a.tiles.
+// bf16 copied bit for bit.
 template <bool kToChunk, int kBlock, int kVpt, int kAuxLoad, int kAuxStore>
-__global__ __launch_bounds__(kBlock) void move_bf16(MoveArgs a)
+__device__ __forceinline__ void move_tile(const MoveArgs& a, uint32_t b)
 {
-    const uint32_t b = xcd_contiguous(blockIdx.x, gridDim.x);
     const uint32_t unit = b / a.tiles;
     const uint32_t tile = b - unit * a.tiles;
     const PageUnit u = locate_page_unit(a, a.item_base + unit);
@@ -43,6 +42,16 @@ __global__ __launch_bounds__(kBlock) void move_bf16(MoveArgs a)
         chunk + ((uint64_t)(u.l * 2 + u.kv) * u.n_c + u.j0) * row_bytes + lo;
     if (kToChunk) copy_tile<kBlock, kVpt, kAuxLoad, kAuxStore>(page_addr, chunk_addr, n);
     else copy_tile<kBlock, kVpt, kAuxLoad, kAuxStore>(chunk_addr, page_addr, n);
+}
+
+// Grid = one workgroup per tile (units * a.tiles), or fewer workgroups that
+// each take a contiguous run of tiles.
+template <bool kToChunk, int kBlock, int kVpt, int kAuxLoad, int kAuxStore>
+__global__ __launch_bounds__(kBlock) void move_bf16(MoveArgs a)
+{
+    const TileRange r = my_tiles(a.total_tiles);
+    for (uint32_t b = r.first; b < r.last; ++b)
+        move_tile<kToChunk, kBlock, kVpt, kAuxLoad, kAuxStore>(a, b);
 }
 
 // Plain contiguous copy (measurement aid): one tile of kBlock*kVpt vectors

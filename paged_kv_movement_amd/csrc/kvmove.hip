@@ -116,7 +116,7 @@ using KernelFn = const void*;
 // token count moved for sequence i (from its tok_start).
 int launch_units(KernelFn kernel, int block, int tile_bytes, Unit unit, const kv_paged* p,
                  const kv_seq* seqs, const int64_t* n_tok, int n_seqs, int32_t layer0,
-                 int32_t n_layers, hipStream_t stream)
+                 int32_t n_layers, hipStream_t stream, int32_t max_workgroups = 0)
 {
     MoveArgs a{};
     a.k_pages = reinterpret_cast<uint64_t>(p->k_pages);
@@ -138,9 +138,11 @@ int launch_units(KernelFn kernel, int block, int tile_bytes, Unit unit, const kv
 
     auto flush = [&](int64_t total) -> int {
         a.item_base = 0;
+        a.total_tiles = uint32_t(total * a.tiles);
+        int64_t grid = a.total_tiles;
+        if (max_workgroups > 0 && grid > max_workgroups) grid = max_workgroups;
         void* args[] = {&a};
-        hipError_t e = hipLaunchKernel(kernel, dim3(unsigned(total * a.tiles)), dim3(block), args, 0,
-                                       stream);
+        hipError_t e = hipLaunchKernel(kernel, dim3(unsigned(grid)), dim3(block), args, 0, stream);
         if (e != hipSuccess) return fail(KV_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
         return KV_OK;
     };
@@ -200,7 +202,8 @@ Launch scatter_launch(int fmt)
 
 // Shared body of the two retrieve entry points.
 int retrieve(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
-             int fmt, int32_t layer0, int32_t n_layers, int64_t* out_tokens, hipStream_t stream)
+             int fmt, int32_t layer0, int32_t n_layers, int64_t* out_tokens, hipStream_t stream,
+             int32_t max_workgroups = 0)
 {
     if (n_seqs > 0 && hit_mask == nullptr) return fail(KV_EINVAL, "hit_mask is NULL");
     int64_t small[64];
@@ -218,7 +221,7 @@ int retrieve(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hi
     }
     const Launch L = scatter_launch(fmt);
     int rc = launch_units(L.kernel, L.block, L.tile_bytes, Unit::Page, paged, seqs, n_tok, n_seqs,
-                          layer0, n_layers, stream);
+                          layer0, n_layers, stream, max_workgroups);
     if (rc == KV_OK && out_tokens != nullptr)
         for (int i = 0; i < n_seqs; ++i) out_tokens[i] = n_tok[i];
     if (n_tok != small) delete[] n_tok;
@@ -279,8 +282,8 @@ int kv_retrieve_chunks(const kv_paged* paged, const kv_seq* seqs, const uint8_t*
 }
 
 int kv_retrieve_layer(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask,
-                      int n_seqs, int fmt, int32_t layer, int64_t* out_tokens, hipStream_t copy_stream,
-                      hipEvent_t layer_done)
+                      int n_seqs, int fmt, int32_t layer, int64_t* out_tokens, int32_t max_workgroups,
+                      hipStream_t copy_stream, hipEvent_t layer_done)
 {
     int rc = check_paged(paged);
     if (rc == KV_OK) rc = check_fmt(fmt);
@@ -288,7 +291,8 @@ int kv_retrieve_layer(const kv_paged* paged, const kv_seq* seqs, const uint8_t* 
     if (rc != KV_OK) return rc;
     if (layer < 0 || layer >= paged->num_layers)
         return fail(KV_EINVAL, "layer %d outside [0, %d)", layer, paged->num_layers);
-    rc = retrieve(paged, seqs, hit_mask, n_seqs, fmt, layer, 1, out_tokens, copy_stream);
+    if (max_workgroups < 0) return fail(KV_EINVAL, "max_workgroups < 0");
+    rc = retrieve(paged, seqs, hit_mask, n_seqs, fmt, layer, 1, out_tokens, copy_stream, max_workgroups);
     if (rc != KV_OK) return rc;
     if (layer_done != nullptr) {
         hipError_t e = hipEventRecord(layer_done, copy_stream);

@@ -120,7 +120,7 @@ def test_retrieve_with_no_hits_launches_nothing():
     assert list(out) == [0, 0]
     for layer in (0, 31):
         out[0] = out[1] = -7
-        assert L.kv_retrieve_layer(ctypes.byref(p), seqs, masks, 2, kvm.FMT_FP8, layer, out, None,
+        assert L.kv_retrieve_layer(ctypes.byref(p), seqs, masks, 2, kvm.FMT_FP8, layer, out, 0, None,
                                    None) == kvm.KV_OK
         assert list(out) == [0, 0]
 
@@ -136,8 +136,10 @@ def test_retrieve_rejections():
     nullm = (ctypes.c_void_p * 1)(None)
     assert L.kv_retrieve_chunks(ctypes.byref(p), seqs, nullm, 1, 0, out, None) == kvm.KV_EINVAL
     for bad_layer in (-1, 32):
-        assert L.kv_retrieve_layer(ctypes.byref(p), seqs, masks, 1, 0, bad_layer, out, None,
+        assert L.kv_retrieve_layer(ctypes.byref(p), seqs, masks, 1, 0, bad_layer, out, 0, None,
                                    None) == kvm.KV_EINVAL
+    assert L.kv_retrieve_layer(ctypes.byref(p), seqs, masks, 1, 0, 0, out, -5, None,
+                               None) == kvm.KV_EINVAL
     bad = (kvm._KvSeq * 1)(_seq(100, 1000, 63))
     assert L.kv_retrieve_chunks(ctypes.byref(p), bad, masks, 1, 0, out, None) == kvm.KV_EINVAL
 
