@@ -262,6 +262,10 @@ __device__ __forceinline__ void retrieve_fp8_tile(const MoveArgs& a, uint32_t b)
 template <int kBlock, int kVpt>
 __global__ __launch_bounds__(kBlock) void retrieve_fp8(MoveArgs a)
 {
+    if (gridDim.x >= a.total_tiles) {         // one workgroup per tile: straight-line code
+        retrieve_fp8_tile<kBlock, kVpt>(a, xcd_contiguous(blockIdx.x, gridDim.x));
+        return;
+    }
     const TileRange r = my_tiles(a.total_tiles);
     for (uint32_t b = r.first; b < r.last; ++b) retrieve_fp8_tile<kBlock, kVpt>(a, b);
 }

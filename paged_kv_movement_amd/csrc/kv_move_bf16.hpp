@@ -49,6 +49,10 @@ __device__ __forceinline__ void move_tile(const MoveArgs& a, uint32_t b)
 template <bool kToChunk, int kBlock, int kVpt, int kAuxLoad, int kAuxStore>
 __global__ __launch_bounds__(kBlock) void move_bf16(MoveArgs a)
 {
+    if (gridDim.x >= a.total_tiles) {         // one workgroup per tile: straight-line code
+        move_tile<kToChunk, kBlock, kVpt, kAuxLoad, kAuxStore>(a, xcd_contiguous(blockIdx.x, gridDim.x));
+        return;
+    }
     const TileRange r = my_tiles(a.total_tiles);
     for (uint32_t b = r.first; b < r.last; ++b)
         move_tile<kToChunk, kBlock, kVpt, kAuxLoad, kAuxStore>(a, b);
