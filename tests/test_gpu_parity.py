@@ -345,3 +345,70 @@ def test_fp8_every_bf16_value_under_many_amax():
     assert kvm.retrieve(paged, batch, fmt=FP8) == [T]
     _sync()
     check_retrieve(w, np.full_like(arr, 0x7E57), host_from_dev_pool(pool), cs, FP8, [w.seqs[0].hit_mask])
+
+
+@pytest.mark.parametrize("fmt", [BF16, FP8], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("cap", [1, 7, 64])
+def test_layerwise_with_capped_grid(fmt, cap):
+    # a capped grid makes each workgroup walk a run of tiles; the result must
+    # not depend on the cap
+    w = wl.custom("capped", 241, 4, 2, 64, 300, [(0, 1000), (256, 531), (0, 17)],
+                  masks=[np.array([1, 1, 0, 1], np.uint8), np.array([1, 1], np.uint8),
+                         np.array([1], np.uint8)], outliers=2 if fmt == FP8 else 0)
+    say("case capped layerwise", cap, fmt)
+    arr = wl.host_pool(w)
+    pool, paged, batch, cs = setup_device(w, arr, fmt=fmt)
+    kvm.store(paged, batch, fmt)
+    pool.view(torch.int16).fill_(0x2A2A)
+    _sync()
+    s = torch.cuda.Stream()
+    for l in range(w.num_layers):
+        assert kvm.retrieve_layer(paged, batch, l, fmt=fmt, stream=s, max_workgroups=cap) == [512, 275, 17]
+    torch.cuda.synchronize()
+    assert kvm.take_faults() == 0
+    before = np.full_like(arr, 0x2A2A)
+    check_retrieve(w, before, host_from_dev_pool(pool), cs, fmt, [sq.hit_mask for sq in w.seqs])
+
+
+def test_pool_from_per_layer_tensors():
+    # an engine may keep one K and one V tensor per layer at unrelated addresses
+    w = wl.custom("layers-separate", 251, 3, 2, 32, 80, [(0, 700), (256, 300)])
+    arr = wl.host_pool(w)
+    L, _, n, P, E = arr.shape
+    k_layers, v_layers = [], []
+    for l in range(L):
+        pad = torch.empty(4096 * (l + 1), dtype=torch.uint8, device="cuda")   # unrelated allocations between layers
+        k_layers.append(torch.from_numpy(arr[l, 0].view(np.int16)).view(torch.bfloat16)
+                        .reshape(n, P, w.num_kv_heads, w.head_dim).cuda())
+        v_layers.append(torch.from_numpy(arr[l, 1].view(np.int16)).view(torch.bfloat16)
+                        .reshape(n, P, w.num_kv_heads, w.head_dim).cuda())
+        del pad
+    paged = kvm.Paged.from_layers(k_layers, v_layers, chunk_size=w.chunk_size)
+    from gpu_util import alloc_dev_chunks
+    seqs, sets = [], []
+    for sq in w.seqs:
+        bufs, sizes = alloc_dev_chunks(paged, w, sq, BF16, fill=0xCD)
+        seqs.append(kvm.Seq(torch.from_numpy(sq.block_table).cuda(), sq.tok_start, sq.tok_end, bufs))
+        sets.append((bufs, sizes))
+    batch = kvm.Batch(paged, seqs).set_masks([sq.hit_mask for sq in w.seqs])
+    kvm.store(paged, batch)
+    _sync()
+    check_store(w, arr, sets, BF16)
+    for t in k_layers + v_layers:
+        t.view(torch.int16).fill_(0x1111)
+    assert kvm.retrieve(paged, batch) == [700, 44]
+    _sync()
+    got = np.stack([np.stack([k.view(torch.int16).cpu().numpy().view(np.uint16).reshape(n, P, E),
+                              v.view(torch.int16).cpu().numpy().view(np.uint16).reshape(n, P, E)])
+                    for k, v in zip(k_layers, v_layers)])
+    check_retrieve(w, np.full_like(arr, 0x1111), got, sets, BF16, [sq.hit_mask for sq in w.seqs])
+
+
+def test_copy_bytes_is_a_plain_copy():
+    src = torch.randint(0, 256, (3 * 4096 * 1024 + 48,), dtype=torch.uint8, device="cuda")
+    dst = torch.full_like(src, 7)
+    n = src.numel() - 32
+    kvm.copy_bytes(dst, src, n)
+    _sync()
+    assert torch.equal(dst[:n], src[:n])
+    assert (dst[n:] == 7).all()
