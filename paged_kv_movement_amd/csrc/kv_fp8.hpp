@@ -9,8 +9,16 @@
 
 namespace kvmove {
 
-constexpr int kFp8StoreBlock = 512;     // threads per (chunk, layer, K/V) group
-constexpr int kFp8StoreUnroll = 4;     // 16-byte loads in flight per thread
+constexpr int kFp8StoreBlock = 512;     // two-pass store: threads per (chunk, layer, K/V) group
+constexpr int kFp8StoreUnroll = 4;     // two-pass store: 16-byte loads in flight per thread
+// single-pass store: the whole group on chip, 1024 threads x (26 vectors in
+// VGPRs + 6 vectors in LDS) = 32768 16-byte vectors = 512 KiB, one
+// (256-token chunk, layer, K/V) group at the Llama-3.1-8B shape.
+constexpr int kOnchipBlock = 1024;
+constexpr int kOnchipRegSlots = 26;
+constexpr int kOnchipLdsSlots = 6;
+constexpr int kOnchipMaxPages = 64;
+constexpr uint32_t kOnchipMaxVectors = uint32_t(kOnchipBlock) * (kOnchipRegSlots + kOnchipLdsSlots);
 constexpr int kFp8RetrieveBlock = 256; // tiles of 8 KiB bf16 output
 constexpr int kFp8RetrieveVpt = 2;
 
@@ -107,9 +115,132 @@ __device__ __forceinline__ bool fast_quotient_ok(uint32_t amax_bits)
     return amax_bits >= 0x3D80u && amax_bits < 0x7F80u;     // [2^-4, largest finite]
 }
 
-// Gather + quantise one (chunk, layer, K/V) group into e4m3 bytes + scale.
-// Pass 1 reads the group's pages and takes max |x|; pass 2 re-reads them
-// (streaming), quantises, and writes 8 bytes per 16-byte input vector.
+// Eight bf16 values (one 16-byte vector) -> eight e4m3 bytes.  `fast`
+// selects the division-free quotient (exact in e4m3 for the group's amax,
+// see quotient_fast); otherwise IEEE division and the integer encoder.
+__device__ __forceinline__ u32x2 quantize8(const u32x4 x, float scale, float r, bool fast)
+{
+    u32x2 q;
+    if (fast) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t w0 = x[2 * j], w1 = x[2 * j + 1];
+            const uint32_t p0 = e4m3x2(quotient_fast(lo_bf16(w0), scale, r), quotient_fast(hi_bf16(w0), scale, r));
+            const uint32_t p1 = e4m3x2(quotient_fast(lo_bf16(w1), scale, r), quotient_fast(hi_bf16(w1), scale, r));
+            q[j] = p0 | (p1 << 16);
+        }
+    } else {   // tiny, infinite or NaN amax
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t b0 = e4m3_from_float(lo_bf16(x[2 * j]) / scale);
+            const uint32_t b1 = e4m3_from_float(hi_bf16(x[2 * j]) / scale);
+            const uint32_t b2 = e4m3_from_float(lo_bf16(x[2 * j + 1]) / scale);
+            const uint32_t b3 = e4m3_from_float(hi_bf16(x[2 * j + 1]) / scale);
+            q[j] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        }
+    }
+    return q;
+}
+
+__device__ __forceinline__ uint32_t max_magnitude(uint32_t m, const u32x4 x)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = x[j] & 0x7FFFu;
+        const uint32_t hi = (x[j] >> 16) & 0x7FFFu;
+        m = m > lo ? m : lo;
+        m = m > hi ? m : hi;
+    }
+    return m;
+}
+
+// Single-pass gather + quantise of one (chunk, layer, K/V) group that fits
+// on chip (at most kOnchipMaxVectors 16-byte vectors, kOnchipMaxPages
+// pages): every vector is read from HBM once -- kOnchipRegSlots per thread
+// into VGPRs, kOnchipLdsSlots per thread straight into LDS -- the group
+// maximum is reduced, and the quantised bytes are written from the chip.
+// One workgroup per group; vector v of the group (token-major, 8 elements)
+// is held by thread v % 1024 in slot v / 1024.
+__global__ __launch_bounds__(kOnchipBlock) void store_fp8_onchip(MoveArgs a)
+{
+    constexpr int B = kOnchipBlock;
+    __shared__ u32x4 lds[kOnchipLdsSlots * B];
+    __shared__ uint32_t red[B / 64];
+    __shared__ int32_t pages[kOnchipMaxPages];
+    const GroupUnit g = locate_group_unit(a, a.item_base + xcd_contiguous(blockIdx.x, gridDim.x));
+    const SeqArg& sq = a.seq[g.s];
+    const uint64_t pool = wave_uniform(gptr<const gu64>(g.kv ? a.v_pages : a.k_pages)[g.l]);
+    const uint64_t chunk = wave_uniform(gptr<const gu64>(sq.chunks)[g.c]);
+    if (bad_addr(pool)) { raise_fault(kFaultPool); return; }
+    if (bad_addr(chunk)) { raise_fault(kFaultChunk); return; }
+    const uint32_t first = sq.first_page + g.c * a.pages_per_chunk;
+    const uint32_t n_pages = (g.n_c + a.page_size - 1) / a.page_size;
+    if (threadIdx.x < n_pages) pages[threadIdx.x] = gptr<const gi32>(sq.bt)[first + threadIdx.x];
+    __syncthreads();
+    for (uint32_t pi = 0; pi < n_pages; ++pi) {       // same verdict in every thread
+        if (pages[pi] < 0 || pages[pi] >= a.num_pages) { raise_fault(kFaultPage); return; }
+    }
+    const uint32_t page_vecs = a.page_size * (a.width / 8);
+    const uint64_t page_bytes = (uint64_t)page_vecs * 16;
+    const uint32_t total = g.n_c * (a.width / 8);
+    const uint32_t wave = threadIdx.x / 64;
+    auto src_of = [&](uint32_t v) {
+        const uint32_t pi = v / page_vecs;
+        return reinterpret_cast<const gvec4*>(pool + (uint64_t)pages[pi] * page_bytes) + (v - pi * page_vecs);
+    };
+
+    // LDS slots: direct-to-LDS loads (each lane's 16 bytes land at
+    // base + lane * 16, base uniform per wave)
+#pragma unroll
+    for (int k = 0; k < kOnchipLdsSlots; ++k) {
+        const uint32_t v = (kOnchipRegSlots + k) * B + threadIdx.x;
+        if (v < total)
+            __builtin_amdgcn_global_load_lds(src_of(v),
+                                             (__attribute__((address_space(3))) void*)&lds[k * B + wave * 64],
+                                             16, 0, 0);
+    }
+    u32x4 reg[kOnchipRegSlots];
+#pragma unroll
+    for (int k = 0; k < kOnchipRegSlots; ++k) {
+        const uint32_t v = k * B + threadIdx.x;
+        reg[k] = u32x4{0u, 0u, 0u, 0u};                   // zero is neutral for the maximum
+        if (v < total) reg[k] = __builtin_nontemporal_load(src_of(v));
+    }
+    uint32_t m1 = 0;
+#pragma unroll
+    for (int k = 0; k < kOnchipRegSlots; ++k) m1 = max_magnitude(m1, reg[k]);
+    __builtin_amdgcn_s_waitcnt(0);                        // the LDS loads have landed
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kOnchipLdsSlots; ++k) {
+        const uint32_t v = (kOnchipRegSlots + k) * B + threadIdx.x;
+        if (v < total) m1 = max_magnitude(m1, lds[k * B + threadIdx.x]);
+    }
+    const uint32_t amax_bits = block_max_u32<B>(m1, red);
+    const float amax = __uint_as_float(amax_bits << 16);
+    const float scale = amax == 0.0f ? 1.0f : amax / 448.0f;
+    const bool fast = fast_quotient_ok(amax_bits);
+    const float r = 1.0f / scale;
+
+    gvec2* dst = reinterpret_cast<gvec2*>(chunk + (uint64_t)(g.l * 2 + g.kv) * g.n_c * a.width);
+#pragma unroll
+    for (int k = 0; k < kOnchipRegSlots; ++k) {
+        const uint32_t v = k * B + threadIdx.x;
+        if (v < total) __builtin_nontemporal_store(quantize8(reg[k], scale, r, fast), dst + v);
+    }
+#pragma unroll
+    for (int k = 0; k < kOnchipLdsSlots; ++k) {
+        const uint32_t v = (kOnchipRegSlots + k) * B + threadIdx.x;
+        if (v < total) __builtin_nontemporal_store(quantize8(lds[k * B + threadIdx.x], scale, r, fast), dst + v);
+    }
+    if (threadIdx.x == 0)
+        gptr<gf32>(chunk + (uint64_t)a.num_layers * 2 * g.n_c * a.width)[g.l * 2 + g.kv] = scale;
+}
+
+// Gather + quantise one (chunk, layer, K/V) group of any size into e4m3
+// bytes + scale, in two passes: pass 1 reads the group's pages and takes
+// max |x|; pass 2 re-reads them (streaming), quantises, and writes 8 bytes
+// per 16-byte input vector.  Used for groups too large for store_fp8_onchip.
 template <int kBlock, int kUnroll>
 __global__ __launch_bounds__(kBlock) void store_fp8(MoveArgs a)
 {
@@ -146,15 +277,7 @@ __global__ __launch_bounds__(kBlock) void store_fp8(MoveArgs a)
             for (int k = 0; k < kUnroll; ++k)
                 v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, base + (k * kBlock + threadIdx.x) * 16, 0, 0);
 #pragma unroll
-            for (int k = 0; k < kUnroll; ++k) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t lo = v[k][j] & 0x7FFFu;
-                    const uint32_t hi = (v[k][j] >> 16) & 0x7FFFu;
-                    m1 = m1 > lo ? m1 : lo;
-                    m1 = m1 > hi ? m1 : hi;
-                }
-            }
+            for (int k = 0; k < kUnroll; ++k) m1 = max_magnitude(m1, v[k]);
         }
     }
     const uint32_t amax_bits = block_max_u32<kBlock>(m1, red);
@@ -178,31 +301,9 @@ __global__ __launch_bounds__(kBlock) void store_fp8(MoveArgs a)
                 v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, base + (k * kBlock + threadIdx.x) * 16, 0,
                                                             kCpolNt);
 #pragma unroll
-            for (int k = 0; k < kUnroll; ++k) {
-                u32x2 q;
-                if (fast) {
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const uint32_t w0 = v[k][2 * j], w1 = v[k][2 * j + 1];
-                        const uint32_t p0 = e4m3x2(quotient_fast(lo_bf16(w0), scale, r),
-                                                   quotient_fast(hi_bf16(w0), scale, r));
-                        const uint32_t p1 = e4m3x2(quotient_fast(lo_bf16(w1), scale, r),
-                                                   quotient_fast(hi_bf16(w1), scale, r));
-                        q[j] = p0 | (p1 << 16);
-                    }
-                } else {   // tiny, infinite or NaN amax: IEEE division + exact integer encoder
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const uint32_t b0 = e4m3_from_float(lo_bf16(v[k][2 * j]) / scale);
-                        const uint32_t b1 = e4m3_from_float(hi_bf16(v[k][2 * j]) / scale);
-                        const uint32_t b2 = e4m3_from_float(lo_bf16(v[k][2 * j + 1]) / scale);
-                        const uint32_t b3 = e4m3_from_float(hi_bf16(v[k][2 * j + 1]) / scale);
-                        q[j] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
-                    }
-                }
-                __builtin_amdgcn_raw_buffer_store_b64(q, rd, base / 2 + (k * kBlock + threadIdx.x) * 8, 0,
-                                                      kCpolNt);
-            }
+            for (int k = 0; k < kUnroll; ++k)
+                __builtin_amdgcn_raw_buffer_store_b64(quantize8(v[k], scale, r, fast), rd,
+                                                      base / 2 + (k * kBlock + threadIdx.x) * 8, 0, kCpolNt);
         }
     }
     if (threadIdx.x == 0)

@@ -181,12 +181,16 @@ struct Launch {
     int tile_bytes;   // bytes of page-side data per workgroup (0: one workgroup per unit)
 };
 
-Launch gather_launch(int fmt)
+Launch gather_launch(const kv_paged* p, int fmt)
 {
     if (fmt == KV_FMT_BF16)
         return {reinterpret_cast<KernelFn>(
                     &move_bf16<true, kMoveBlock, kMoveVpt, kGatherAuxLoad, kGatherAuxStore>),
                 kMoveBlock, kMoveBlock * kMoveVpt * 16};
+    // a whole (chunk, layer, K/V) group on chip when it fits, else two passes
+    const int64_t group_vectors = int64_t(p->chunk_size) * p->num_kv_heads * p->head_dim / 8;
+    if (group_vectors <= int64_t(kOnchipMaxVectors) && p->chunk_size / p->page_size <= kOnchipMaxPages)
+        return {reinterpret_cast<KernelFn>(&store_fp8_onchip), kOnchipBlock, 0};
     return {reinterpret_cast<KernelFn>(&store_fp8<kFp8StoreBlock, kFp8StoreUnroll>), kFp8StoreBlock, 0};
 }
 
@@ -263,7 +267,7 @@ int kv_store_chunks(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int f
     int64_t small[64];
     int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
     for (int i = 0; i < n_seqs; ++i) n_tok[i] = seqs[i].tok_end - seqs[i].tok_start;
-    const Launch L = gather_launch(fmt);
+    const Launch L = gather_launch(paged, fmt);
     rc = launch_units(L.kernel, L.block, L.tile_bytes, fmt == KV_FMT_BF16 ? Unit::Page : Unit::Group,
                       paged, seqs, n_tok, n_seqs, 0, paged->num_layers, stream);
     if (n_tok != small) delete[] n_tok;
