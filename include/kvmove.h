@@ -9,8 +9,8 @@
  *
  *   store    (gather)  pages -> chunk buffers, every layer, K then V;
  *   retrieve (scatter) chunk buffers -> pages, for the leading hit chunks;
- *   retrieve one layer, then record an event, so compute on another stream
- *            can start on that layer while the next one is moving;
+ *   store / retrieve one layer, then record an event, so compute on another
+ *            stream overlaps the movement of the neighbouring layer;
  *   optional fp8 serde: quantise to e4m3 on store, dequantise on retrieve.
  *
  * Sources (web pages, cited by title and section):
@@ -132,6 +132,17 @@ int64_t kv_num_chunks(const kv_paged* paged, int64_t tok_start, int64_t tok_end)
 int kv_store_chunks(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int fmt,
                     hipStream_t stream);
 
+/* Layerwise store ([paper] layerwise pipeline; Table 2 start_store_kv /
+ * wait_store_kv(layer)): as kv_store_chunks but gathers layer `layer` only
+ * (its K and V sections of every chunk; for fp8 also its two scales), on
+ * stream, then records layer_done (if not NULL) on stream.  Calling it for
+ * layers 0 .. L-1 fills the chunks as one kv_store_chunks call does.  Chunks
+ * that are already stored are skipped by giving a later tok_start or an
+ * earlier tok_end.  max_workgroups as for kv_retrieve_layer (bf16 only; the
+ * fp8 store runs one workgroup per (chunk, K/V) group and ignores it). */
+int kv_store_layer(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int fmt, int32_t layer,
+                   int32_t max_workgroups, hipStream_t stream, hipEvent_t layer_done);
+
 /* Retrieve: for sequence i, n_hit = index of the first 0 in hit_mask[i][0 ..
  * n_chunks) (n_chunks if none); scatter chunks [0, n_hit) back into the
  * sequence's pages, all layers, K and V ([paper] configurable chunk size;
@@ -154,7 +165,8 @@ int kv_retrieve_chunks(const kv_paged* paged, const kv_seq* seqs,
  * max_workgroups = 0 launches one workgroup per 8 KiB tile (fastest when the
  * GPU is otherwise idle); a positive value caps the grid, each workgroup then
  * moving a contiguous run of tiles, so the scatter occupies few wave slots
- * while compute on another stream runs beside it. */
+ * while compute on another stream runs beside it (page-unit kernels: bf16
+ * and the fp8 retrieve). */
 int kv_retrieve_layer(const kv_paged* paged, const kv_seq* seqs,
                       const uint8_t* const* hit_mask, int n_seqs, int fmt, int32_t layer,
                       int64_t* out_tokens, int32_t max_workgroups, hipStream_t copy_stream,

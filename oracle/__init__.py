@@ -71,7 +71,7 @@ def _bind(L):
         "kvo_chunk_bytes": (i64, [P, i64, ctypes.c_int]),
         "kvo_slot": (i64, [vp, i32, i64]),
         "kvo_hit_chunks": (i64, [vp, i64]),
-        "kvo_store": (ctypes.c_int, [P, vp, i64, i64, i64, vp, ctypes.c_int]),
+        "kvo_store": (ctypes.c_int, [P, vp, i64, i64, i64, vp, ctypes.c_int, i32]),
         "kvo_retrieve": (i64, [P, vp, i64, i64, i64, vp, vp, ctypes.c_int, i32]),
         "kvo_e4m3_encode": (u8, [f32]),
         "kvo_e4m3_decode": (f32, [u8]),
@@ -161,11 +161,13 @@ def _chunk_ptrs(chunks):
     return (ctypes.c_void_p * max(1, len(chunks)))(*[_ptr(a) for a in chunks])
 
 
-def store(pool: Pool, block_table, s: int, e: int, chunks, fmt: int = FMT_BF16) -> int:
-    """Gather [s, e) into ``chunks`` (list from alloc_chunks).  Returns 0 or -1."""
+def store(pool: Pool, block_table, s: int, e: int, chunks, fmt: int = FMT_BF16,
+          layer: int = -1) -> int:
+    """Gather [s, e) into ``chunks`` (list from alloc_chunks); one layer only
+    when layer >= 0.  Returns 0 or -1."""
     bt = np.ascontiguousarray(block_table, dtype=np.int32)
     ptrs = _chunk_ptrs(chunks)
-    return int(lib().kvo_store(ctypes.byref(pool.c), _ptr(bt), bt.size, s, e, ptrs, fmt))
+    return int(lib().kvo_store(ctypes.byref(pool.c), _ptr(bt), bt.size, s, e, ptrs, fmt, layer))
 
 
 def retrieve(pool: Pool, block_table, s: int, e: int, mask, chunks, fmt: int = FMT_BF16,

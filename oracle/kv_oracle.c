@@ -216,11 +216,14 @@ static int64_t chunk_index(const kvo_pool* p, int l, int kv, int64_t n_c, int64_
 /* Store: the paper notes (section "可配置的块大小") describe a GPU kernel that
  * copies KV from scattered paged memory into a contiguous buffer, grouping
  * pages of all layers into 256-token chunks; the LMCache walkthrough's store()
- * gathers every chunk of the request in one batched call. */
+ * gathers every chunk of the request in one batched call.  The layerwise
+ * variant (paper notes, section "层级流水线" and Table 2's start_store_kv /
+ * wait_store_kv(layer)) stores one layer per call. */
 int kvo_store(const kvo_pool* p, const int32_t* bt, int64_t n_bt,
-              int64_t s, int64_t e, uint8_t* const* chunks, int fmt)
+              int64_t s, int64_t e, uint8_t* const* chunks, int fmt, int32_t layer)
 {
     if (check_args(p, bt, n_bt, s, e, fmt) != 0) return -1;
+    if (layer >= p->num_layers) return -1;
     int64_t width = (int64_t)p->num_kv_heads * p->head_dim;
     int64_t n_chunks = kvo_num_chunks(s, e, p->chunk_size);
     for (int64_t c = 0; c < n_chunks; c++) {
@@ -231,6 +234,7 @@ int kvo_store(const kvo_pool* p, const int32_t* bt, int64_t n_bt,
         int64_t t0 = s + c * p->chunk_size;
         uint8_t* buf = chunks[c];
         for (int l = 0; l < p->num_layers; l++) {
+            if (layer >= 0 && l != layer) continue;
             for (int kv = 0; kv < 2; kv++) {
                 if (fmt == KVO_FMT_BF16) {
                     for (int64_t j = 0; j < n_c; j++) {

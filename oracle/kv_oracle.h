@@ -71,11 +71,13 @@ int64_t kvo_slot(const int32_t* block_table, int32_t page_size, int64_t t);
 /* Number of leading hit chunks: index of the first 0 in mask, else n_chunks. */
 int64_t kvo_hit_chunks(const uint8_t* mask, int64_t n_chunks);
 
-/* Store (gather) [s, e) into chunks[0 .. num_chunks).  Returns 0, or -1 on a
- * rejected argument (s not chunk-aligned, e beyond the block table, a page id
- * out of range, bad format). */
+/* Store (gather) [s, e) into chunks[0 .. num_chunks).  layer < 0 stores every
+ * layer, else only that layer's K and V sections of each chunk (the rest of
+ * the chunk buffers is left as it was).  Returns 0, or -1 on a rejected
+ * argument (s not chunk-aligned, e beyond the block table, a page id out of
+ * range, bad format or layer). */
 int kvo_store(const kvo_pool* pool, const int32_t* block_table, int64_t n_bt,
-              int64_t s, int64_t e, uint8_t* const* chunks, int fmt);
+              int64_t s, int64_t e, uint8_t* const* chunks, int fmt, int32_t layer);
 
 /* Retrieve (scatter) the leading hit chunks of [s, e) back into the pool.
  * layer < 0 moves every layer, else only that layer.  Returns the number of

@@ -20,8 +20,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["FMT_BF16", "FMT_FP8", "KvError", "Paged", "Seq", "Batch", "store", "retrieve",
-           "retrieve_layer", "take_faults", "copy_bytes", "library_path", "load"]
+__all__ = ["FMT_BF16", "FMT_FP8", "KvError", "Paged", "Seq", "Batch", "store", "store_layer",
+           "retrieve", "retrieve_layer", "take_faults", "copy_bytes", "library_path", "load"]
 
 FMT_BF16 = 0
 FMT_FP8 = 1
@@ -83,6 +83,7 @@ def load():
         "kv_chunk_bytes": (ctypes.c_size_t, [P, i64, ctypes.c_int]),
         "kv_num_chunks": (i64, [P, i64, i64]),
         "kv_store_chunks": (ctypes.c_int, [P, S, ctypes.c_int, ctypes.c_int, vp]),
+        "kv_store_layer": (ctypes.c_int, [P, S, ctypes.c_int, ctypes.c_int, i32, i32, vp, vp]),
         "kv_retrieve_chunks": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, vp, vp]),
         "kv_retrieve_layer": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, i32, vp, i32, vp, vp]),
         "kv_last_error": (ctypes.c_char_p, []),
@@ -221,6 +222,24 @@ def store(paged: Paged, seqs, fmt: int = FMT_BF16, stream=None) -> None:
     _check(load().kv_store_chunks(ctypes.byref(paged.c), b.arr, b.n, fmt, _stream_handle(stream)))
 
 
+def _event_handle(event, stream):
+    if event is None:
+        return None
+    if not event.cuda_event:        # torch creates the event lazily on first record
+        import torch
+        event.record(stream if stream is not None else torch.cuda.current_stream())
+    return event.cuda_event
+
+
+def store_layer(paged: Paged, seqs, layer: int, fmt: int = FMT_BF16, stream=None, event=None,
+                max_workgroups: int = 0) -> None:
+    """Gather one layer of every chunk on ``stream``, then record ``event``
+    (a torch.cuda.Event) on it (kv_store_layer)."""
+    b = _batch(paged, seqs)
+    _check(load().kv_store_layer(ctypes.byref(paged.c), b.arr, b.n, fmt, layer, max_workgroups,
+                                 _stream_handle(stream), _event_handle(event, stream)))
+
+
 def retrieve(paged: Paged, seqs, masks=None, fmt: int = FMT_BF16, stream=None) -> list:
     """Scatter the leading hit chunks back into pages (kv_retrieve_chunks).
     Returns the tokens made available per sequence."""
@@ -243,14 +262,9 @@ def retrieve_layer(paged: Paged, seqs, layer: int, masks=None, fmt: int = FMT_BF
     if masks is not None:
         b.set_masks(masks)
     assert b._mask_ptrs is not None, "hit masks are required"
-    ev = None
-    if event is not None:
-        if not event.cuda_event:        # torch creates the event lazily on first record
-            import torch
-            event.record(stream if stream is not None else torch.cuda.current_stream())
-        ev = event.cuda_event
     _check(load().kv_retrieve_layer(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n, fmt, layer,
-                                    b.out, max_workgroups, _stream_handle(stream), ev))
+                                    b.out, max_workgroups, _stream_handle(stream),
+                                    _event_handle(event, stream)))
     return [int(b.out[i]) for i in range(b.n)]
 
 

@@ -140,7 +140,9 @@ int launch_units(KernelFn kernel, int block, int tile_bytes, Unit unit, const kv
         a.item_base = 0;
         a.total_tiles = uint32_t(total * a.tiles);
         int64_t grid = a.total_tiles;
-        if (max_workgroups > 0 && grid > max_workgroups) grid = max_workgroups;
+        // only the tiled movers walk runs of tiles; group kernels need one
+        // workgroup per group
+        if (unit == Unit::Page && max_workgroups > 0 && grid > max_workgroups) grid = max_workgroups;
         void* args[] = {&a};
         hipError_t e = hipLaunchKernel(kernel, dim3(unsigned(grid)), dim3(block), args, 0, stream);
         if (e != hipSuccess) return fail(KV_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -272,6 +274,31 @@ int kv_store_chunks(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int f
                       paged, seqs, n_tok, n_seqs, 0, paged->num_layers, stream);
     if (n_tok != small) delete[] n_tok;
     return rc == KV_OK ? ok() : rc;
+}
+
+int kv_store_layer(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int fmt, int32_t layer,
+                   int32_t max_workgroups, hipStream_t stream, hipEvent_t layer_done)
+{
+    int rc = check_paged(paged);
+    if (rc == KV_OK) rc = check_fmt(fmt);
+    if (rc == KV_OK) rc = check_seqs(paged, seqs, n_seqs);
+    if (rc != KV_OK) return rc;
+    if (layer < 0 || layer >= paged->num_layers)
+        return fail(KV_EINVAL, "layer %d outside [0, %d)", layer, paged->num_layers);
+    if (max_workgroups < 0) return fail(KV_EINVAL, "max_workgroups < 0");
+    int64_t small[64];
+    int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
+    for (int i = 0; i < n_seqs; ++i) n_tok[i] = seqs[i].tok_end - seqs[i].tok_start;
+    const Launch L = gather_launch(paged, fmt);
+    rc = launch_units(L.kernel, L.block, L.tile_bytes, fmt == KV_FMT_BF16 ? Unit::Page : Unit::Group,
+                      paged, seqs, n_tok, n_seqs, layer, 1, stream, max_workgroups);
+    if (n_tok != small) delete[] n_tok;
+    if (rc != KV_OK) return rc;
+    if (layer_done != nullptr) {
+        hipError_t e = hipEventRecord(layer_done, stream);
+        if (e != hipSuccess) return fail(KV_EHIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+    }
+    return ok();
 }
 
 int kv_retrieve_chunks(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask,

@@ -29,7 +29,7 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ["kv_store_chunks", "kv_retrieve_chunks", "kv_retrieve_layer", "kv_chunk_bytes",
+    for n in ["kv_store_chunks", "kv_store_layer", "kv_retrieve_chunks", "kv_retrieve_layer", "kv_chunk_bytes",
               "kv_num_chunks", "kv_last_error", "kv_take_faults", "kv_copy_bytes"]:
         assert n in names
 
@@ -99,6 +99,19 @@ def test_store_rejections():
     # a later bad sequence rejects the whole call before anything is launched
     assert _store(p, [_seq(0, 100, 40), _seq(0, 100, 2)]) == kvm.KV_ERANGE
     assert "seq 1" in L.kv_last_error().decode()
+
+
+def test_store_layer_rejections_and_empty_work():
+    L = _lib()
+    p = _paged()
+    ok = (kvm._KvSeq * 1)(_seq(0, 100, 40))
+    for bad_layer in (-1, 32):
+        assert L.kv_store_layer(ctypes.byref(p), ok, 1, 0, bad_layer, 0, None, None) == kvm.KV_EINVAL
+    assert L.kv_store_layer(ctypes.byref(p), ok, 1, 0, 3, -1, None, None) == kvm.KV_EINVAL
+    bad = (kvm._KvSeq * 1)(_seq(16, 100, 40))
+    assert L.kv_store_layer(ctypes.byref(p), bad, 1, 0, 3, 0, None, None) == kvm.KV_EINVAL
+    empty = (kvm._KvSeq * 1)(_seq(256, 256, 40))
+    assert L.kv_store_layer(ctypes.byref(p), empty, 1, 1, 3, 0, None, None) == kvm.KV_OK
 
 
 def test_empty_work_launches_nothing():

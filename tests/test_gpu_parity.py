@@ -412,3 +412,34 @@ def test_copy_bytes_is_a_plain_copy():
     _sync()
     assert torch.equal(dst[:n], src[:n])
     assert (dst[n:] == 7).all()
+
+
+@pytest.mark.parametrize("fmt", [BF16, FP8], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("cap", [0, 5])
+def test_layerwise_store_equals_full_store(fmt, cap):
+    # storing layer by layer on a side stream (each call recording its event)
+    # fills the chunks exactly as one full store; before its layer is stored,
+    # a chunk section keeps what it held
+    w = wl.custom("store-layers", 261, 5, 2, 32, 300, [(0, 1000), (256, 531), (0, 17)],
+                  outliers=2 if fmt == FP8 else 0)
+    say("case layerwise store", fmt, cap)
+    arr = wl.host_pool(w)
+    pool, paged, batch, cs = setup_device(w, arr, fmt=fmt, fill=0xC3)
+    s = torch.cuda.Stream()
+    events = [torch.cuda.Event() for _ in range(w.num_layers)]
+    for l in range(w.num_layers):
+        kvm.store_layer(paged, batch, l, fmt=fmt, stream=s, event=events[l], max_workgroups=cap)
+        events[l].synchronize()
+        if l == 1:
+            # layers >= 2 untouched so far: compare against an oracle store of
+            # layers 0 and 1 into buffers of the same fill
+            opool = oracle_pool(w, arr)
+            for sq, chunk_set in zip(w.seqs, cs):
+                exp = oracle.alloc_chunks(opool, sq.tok_start, sq.tok_end, fmt, fill=0xC3)
+                for ll in (0, 1):
+                    assert oracle.store(opool, sq.block_table, sq.tok_start, sq.tok_end, exp, fmt, ll) == 0
+                got = host_chunks(chunk_set)
+                assert all(np.array_equal(g, e) for g, e in zip(got, exp))
+    torch.cuda.synchronize()
+    assert kvm.take_faults() == 0
+    check_store(w, arr, cs, fmt)

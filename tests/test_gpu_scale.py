@@ -158,3 +158,30 @@ def test_full_fp8_8b_sampled_chunks_and_bounds():
         assert (pool[:, :, miss].view(torch.int16) == SENTINEL).all()
     del pool, orig, full, paged, batch, chunk_sets
     _free()
+
+
+def test_full_layerwise_store_8b_behind_compute():
+    # prefill-style: layer l's KV is stored on a copy stream once layer l's
+    # GEMM (the producer) is done, while layer l+1 computes
+    w = wl.layerwise8b()
+    say("case", w.name, "layerwise store")
+    pool = wl.device_pool(w)
+    pool, paged, batch, chunk_sets = setup_device(w, pool=pool, fill=0xCD)
+    copy, compute = torch.cuda.Stream(), torch.cuda.Stream()
+    done = [torch.cuda.Event() for _ in range(w.num_layers)]
+    stored = [torch.cuda.Event() for _ in range(w.num_layers)]
+    x = torch.randn(10240, 4096, device="cuda", dtype=torch.bfloat16)
+    wgt = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16) * 0.01
+    sync()
+    for l in range(w.num_layers):
+        with torch.cuda.stream(compute):
+            torch.mm(x, wgt)
+            done[l].record(compute)
+        copy.wait_event(done[l])
+        kvm.store_layer(paged, batch, l, stream=copy, event=stored[l], max_workgroups=0 if l == 0 else 128)
+    sync()
+    assert kvm.take_faults() == 0
+    arr = host_from_dev_pool(pool)
+    check_store(w, arr, chunk_sets, BF16)
+    del arr, pool, paged, batch, chunk_sets
+    _free()

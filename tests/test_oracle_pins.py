@@ -207,6 +207,7 @@ def test_rejected_arguments():
     assert oracle.store(pool, bt, 16, 300, ch) == -1            # start not chunk-aligned
     assert oracle.store(pool, bt, 0, 16 * bt.size + 1, ch + ch) == -1   # beyond the block table
     assert oracle.store(pool, bt, 0, 300, ch, fmt=7) == -1
+    assert oracle.store(pool, bt, 0, 300, ch, layer=2) == -1          # no layer 2
     bad = bt.copy()
     bad[3] = 32                                                  # page id out of range
     assert oracle.store(pool, bad, 0, 300, ch) == -1
@@ -387,3 +388,30 @@ def test_store_is_deterministic():
         assert oracle.store(pool, sq.block_table, 0, 700, a, fmt) == 0
         assert oracle.store(pool, sq.block_table, 0, 700, b, fmt) == 0
         assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("fmt", [oracle.FMT_BF16, oracle.FMT_FP8])
+def test_layer_by_layer_store_equals_full_store(fmt):
+    # storing layers 0..L-1 one call at a time fills the chunks exactly as one
+    # full store does, and each call writes only its own layer's sections
+    w = wl.custom("lws", 42, 4, 2, 16, 64, [(0, 530)], outliers=2)
+    arr, pool = _pool(w)
+    sq = w.seqs[0]
+    full = oracle.alloc_chunks(pool, 0, 530, fmt, fill=0x5C)
+    assert oracle.store(pool, sq.block_table, 0, 530, full, fmt) == 0
+    part = oracle.alloc_chunks(pool, 0, 530, fmt, fill=0x5C)
+    E = w.width
+    for l in range(w.num_layers):
+        before = [c.copy() for c in part]
+        assert oracle.store(pool, sq.block_table, 0, 530, part, fmt, layer=l) == 0
+        for c, (b, a) in enumerate(zip(before, part)):
+            n_c = oracle.chunk_tokens(0, 530, 256, c)
+            bpe = 2 if fmt == oracle.FMT_BF16 else 1
+            sec = 2 * n_c * E * bpe                          # bytes of one layer's K and V sections
+            changed = np.nonzero(b != a)[0]
+            payload = w.num_layers * sec
+            in_sections = (changed >= l * sec) & (changed < (l + 1) * sec)
+            in_scales = (changed >= payload + 8 * l) & (changed < payload + 8 * (l + 1))
+            assert (in_sections | in_scales).all(), "a layer call wrote outside its layer"
+    assert all(np.array_equal(a, b) for a, b in zip(full, part))
+    assert oracle.store(pool, sq.block_table, 0, 530, part, fmt, layer=4) == -1
