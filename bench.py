@@ -14,8 +14,8 @@ the stream it is launched on.  `cpu_baseline` times the CPU oracle on the
 same workload's data on this host's cores.
 
 Other workloads (`--workload layerwise-8b | layerwise-store-8b |
-llama-70b-style | fp8-8b`) print their own JSON report line; they are not the
-headline.
+llama-70b-style | fp8-8b | offload-8b`) print their own JSON report line; they
+are not the headline.
 """
 import argparse
 import hashlib
@@ -29,6 +29,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor peak
+PCIE_PEAK_GBPS = 63.0           # PCIe 5.0 x16 host link, one direction, after 128b/130b coding
 METRIC = "paged<->chunk KV gather/scatter GB/s and % of HBM peak (8B KV shape)"
 # device sources of the gather kernel (kernel, launch shape, shared helpers)
 KERNEL_SOURCES = ["paged_kv_movement_amd/csrc/kv_common.hpp", "paged_kv_movement_amd/csrc/kv_move_bf16.hpp"]
@@ -76,19 +77,25 @@ def chunk_plan(paged, seq, fmt):
     return [paged.chunk_bytes(t, fmt) for t in toks]
 
 
-def setup(w, fmt):
+def setup(w, fmt, where="device", pool=None):
+    """Device pool (made here unless given), chunk buffers carved from one
+    arena in device memory or, for where="host", in pinned host memory."""
     import numpy as np
     import torch
     import paged_kv_movement_amd as kvm
     from paged_kv_movement_amd import workloads as wl
 
     t = time.time()
-    pool = wl.device_pool(w)
+    if pool is None:
+        pool = wl.device_pool(w)
     paged = kvm.Paged.from_pool(pool, chunk_size=w.chunk_size)
     sizes = [chunk_plan(paged, sq, fmt) for sq in w.seqs]
     align = 256
     total = sum(-(-s // align) * align for ss in sizes for s in ss)
-    arena = torch.empty(total, dtype=torch.uint8, device="cuda")
+    if where == "host":
+        arena = torch.empty(total, dtype=torch.uint8, pin_memory=True)
+    else:
+        arena = torch.empty(total, dtype=torch.uint8, device="cuda")
     base, at, seqs = arena.data_ptr(), 0, []
     for sq, ss in zip(w.seqs, sizes):
         addrs = []
@@ -100,8 +107,8 @@ def setup(w, fmt):
                             torch.tensor(addrs, dtype=torch.int64).cuda()))
     batch = kvm.Batch(paged, seqs).set_masks([sq.hit_mask for sq in w.seqs])
     torch.cuda.synchronize()
-    log(f"setup {w.name}: pool {pool.numel() * 2 / 1e9:.2f} GB, chunks {total / 1e9:.2f} GB, "
-        f"{time.time() - t:.1f} s")
+    log(f"setup {w.name}: pool {pool.numel() * 2 / 1e9:.2f} GB, chunks {total / 1e9:.2f} GB in {where} "
+        f"memory, {time.time() - t:.1f} s")
     return pool, paged, batch, arena
 
 
@@ -422,6 +429,189 @@ def bench_layerwise_store(args):
             "variants": variants}
 
 
+def bench_offload(args):
+    """Offload to / onload from pinned host memory at the 8B shape.
+
+    The chunk buffers live in pinned host memory and the same store / retrieve
+    kernels write / read them over PCIe.  Reported next to it: the link's own
+    ceiling (one 1 GiB hipMemcpy each way), the staged alternative (gather
+    into device chunks, then copy each chunk; copy each chunk, then scatter),
+    fp8 chunks (half the bytes on the link), a duplex run (offload of four
+    sequences while the other four onload), and the layerwise onload from
+    host behind the per-layer GEMMs."""
+    import numpy as np
+    import torch
+    import paged_kv_movement_amd as kvm
+    from paged_kv_movement_amd import workloads as wl
+
+    w = wl.llama8b()
+    reps = max(3, args.steps)
+    stream = torch.cuda.Stream()
+    pool, paged, hb, harena = setup(w, kvm.FMT_BF16, "host")
+    _, _, db, darena = setup(w, kvm.FMT_BF16, "device", pool=pool)
+    tokens = sum(sq.tok_end - sq.tok_start for sq in w.seqs)
+    rtok = sum(hit_tokens(w))
+    per_tok = kv_bytes_per_token(w)
+    out = {"metric": "offload / onload GB/s over PCIe (chunks in pinned host memory)",
+           "workload": "offload-8b: llama3.1-8b KV shape, 8 seqs x 10000 tokens, 30-chunk hit mask",
+           "pcie_gen5_x16_GBps": PCIE_PEAK_GBPS}
+
+    def gbps(nbytes, ms):
+        return round(nbytes / (ms / 1e3) / 1e9, 2)
+
+    # link ceiling: 1 GiB pinned <-> device copies
+    big_d = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    big_h = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    with torch.cuda.stream(stream):
+        big_d.copy_(big_h, non_blocking=True)
+        big_h.copy_(big_d, non_blocking=True)
+        h2d = timed(stream, lambda: big_d.copy_(big_h, non_blocking=True), reps)
+        d2h = timed(stream, lambda: big_h.copy_(big_d, non_blocking=True), reps)
+    out["link_ceiling"] = {"h2d_GBps": gbps(1 << 30, h2d), "d2h_GBps": gbps(1 << 30, d2h)}
+    del big_d, big_h
+
+    for _ in range(args.warmup):
+        kvm.store(paged, hb, stream=stream)
+        kvm.retrieve(paged, hb, stream=stream)
+    st = timed(stream, lambda: kvm.store(paged, hb, stream=stream), reps)
+    rt = timed(stream, lambda: kvm.retrieve(paged, hb, stream=stream), reps)
+    out["offload"] = {"ms": round(st, 3), "GBps_link": gbps(tokens * per_tok, st),
+                      "pct_of_link_ceiling": round(100 * tokens * per_tok / (st / 1e3) / 1e9
+                                                   / out["link_ceiling"]["d2h_GBps"], 1),
+                      "tokens_per_s": round(tokens / (st / 1e3), 1)}
+    out["onload"] = {"ms": round(rt, 3), "GBps_link": gbps(rtok * per_tok, rt),
+                     "pct_of_link_ceiling": round(100 * rtok * per_tok / (rt / 1e3) / 1e9
+                                                  / out["link_ceiling"]["h2d_GBps"], 1),
+                     "tokens_per_s": round(rtok / (rt / 1e3), 1)}
+    log(f"offload {out['offload']}  onload {out['onload']}")
+
+    # staged alternative: device chunks plus one copy per chunk
+    nbytes = darena.numel()
+
+    def staged_offload():
+        kvm.store(paged, db, stream=stream)
+        with torch.cuda.stream(stream):
+            harena.copy_(darena, non_blocking=True)
+
+    def staged_onload():
+        with torch.cuda.stream(stream):
+            darena.copy_(harena, non_blocking=True)
+        kvm.retrieve(paged, db, stream=stream)
+
+    so, sn = timed(stream, staged_offload, reps), timed(stream, staged_onload, reps)
+    out["staged_offload"] = {"ms": round(so, 3), "GBps_link": gbps(tokens * per_tok, so),
+                             "note": "gather into device chunks, then one device-to-host copy of all of them"}
+    out["staged_onload"] = {"ms": round(sn, 3), "GBps_link": gbps(rtok * per_tok, sn),
+                            "note": "one host-to-device copy of all chunks, then the scatter"}
+    del darena, db
+    torch.cuda.empty_cache()
+
+    # duplex: sequences 0-3 offload while 4-7 onload
+    a, b = kvm.Batch(paged, hb.seqs[:4]), kvm.Batch(paged, hb.seqs[4:])
+    a.set_masks([sq.hit_mask for sq in w.seqs[:4]])
+    b.set_masks([sq.hit_mask for sq in w.seqs[4:]])
+    other = torch.cuda.Stream()
+
+    def duplex():
+        other.wait_stream(stream)
+        kvm.store(paged, a, stream=stream)
+        kvm.retrieve(paged, b, stream=other)
+        stream.wait_stream(other)
+
+    du = timed(stream, duplex, reps)
+    du_bytes = (sum(sq.tok_end - sq.tok_start for sq in w.seqs[:4]) + sum(hit_tokens(w)[4:])) * per_tok
+    out["duplex"] = {"ms": round(du, 3), "GBps_link_both_directions": gbps(du_bytes, du)}
+    log(f"staged {out['staged_offload']} {out['staged_onload']} duplex {out['duplex']}")
+
+    # fp8 chunks on the link
+    del harena, hb
+    _, _, fb, farena = setup(w, kvm.FMT_FP8, "host", pool=pool)
+    for _ in range(args.warmup):
+        kvm.store(paged, fb, kvm.FMT_FP8, stream=stream)
+    fst = timed(stream, lambda: kvm.store(paged, fb, kvm.FMT_FP8, stream=stream), reps)
+    frt = timed(stream, lambda: kvm.retrieve(paged, fb, fmt=kvm.FMT_FP8, stream=stream), reps)
+    fb_st = sum(kvm_chunk_total(paged, sq, kvm.FMT_FP8, None) for sq in w.seqs)
+    fb_rt = sum(kvm_chunk_total(paged, sq, kvm.FMT_FP8, sq.hit_mask) for sq in w.seqs)
+    out["fp8_offload"] = {"ms": round(fst, 3), "GBps_link": gbps(fb_st, fst), "tokens_per_s": round(tokens / (fst / 1e3), 1)}
+    out["fp8_onload"] = {"ms": round(frt, 3), "GBps_link": gbps(fb_rt, frt), "tokens_per_s": round(rtok / (frt / 1e3), 1)}
+    log(f"fp8 {out['fp8_offload']} {out['fp8_onload']}")
+    assert kvm.take_faults() == 0
+    del fb, farena, pool, paged
+    torch.cuda.empty_cache()
+    # the two streams already made: a third and fourth would share a
+    # hardware queue with one of them and run in order with it
+    out["layerwise_onload_from_host"] = layerwise_from_host(args, copy=stream, compute=other)
+    return out
+
+
+def kvm_chunk_total(paged, sq, fmt, mask):
+    """Exact bytes of a sequence's chunks (only the leading hit ones if mask)."""
+    n = -(-(sq.tok_end - sq.tok_start) // paged.chunk_size)
+    if mask is not None:
+        m = list(mask) + [0]
+        n = m.index(0) if 0 in m[:n] else n
+    return sum(paged.chunk_bytes(min(paged.chunk_size, sq.tok_end - sq.tok_start - c * paged.chunk_size), fmt)
+               for c in range(n))
+
+
+def layerwise_from_host(args, copy, compute):
+    """Layer-by-layer onload of one 10240-token sequence whose chunks are in
+    pinned host memory, each layer's event gating that layer's GEMM."""
+    import torch
+    import paged_kv_movement_amd as kvm
+    from paged_kv_movement_amd import workloads as wl
+
+    w = wl.layerwise8b()
+    pool, paged, batch, arena = setup(w, kvm.FMT_BF16, "host")
+    kvm.store(paged, batch)
+    torch.cuda.synchronize()
+    x = torch.randn(10240, 4096, device="cuda", dtype=torch.bfloat16)
+    wgt = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16) * 0.01
+    L = w.num_layers
+    evs = [torch.cuda.Event() for _ in range(L)]
+    layer_bytes = 10240 * 2 * w.width * 2
+    reps = max(2, min(args.steps, 3))
+
+    def wall(fn):
+        fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / reps * 1e3
+
+    def gemms():
+        with torch.cuda.stream(compute):
+            for _ in range(L):
+                torch.mm(x, wgt)
+
+    t_gemm = wall(gemms)
+    variants = []
+    for cap in (16, 32, 64, 0):
+        def copies():
+            for l in range(L):
+                kvm.retrieve_layer(paged, batch, l, stream=copy, max_workgroups=cap)
+
+        def both():
+            for l in range(L):
+                kvm.retrieve_layer(paged, batch, l, stream=copy, event=evs[l], max_workgroups=cap)
+                compute.wait_event(evs[l])
+                with torch.cuda.stream(compute):
+                    torch.mm(x, wgt)
+
+        t_copy, t_both = wall(copies), wall(both)
+        variants.append({"max_workgroups": cap, "t_copy_ms": round(t_copy, 3), "t_both_ms": round(t_both, 3),
+                         "layer_GBps_link": round(L * layer_bytes / (t_copy / 1e3) / 1e9, 2),
+                         "exposed_ms": round(t_both - max(t_gemm, t_copy), 3),
+                         "gemm_hidden_fraction": round((t_gemm + t_copy - t_both) / t_gemm, 4)})
+        log(f"layerwise from host cap {cap}: {variants[-1]}")
+    assert kvm.take_faults() == 0
+    return {"workload": "1 seq x 10240 tokens, 32 layers, chunks in pinned host memory, "
+                        "GEMM 10240x4096x4096 bf16 per layer",
+            "t_gemm_ms": round(t_gemm, 3), "variants": variants}
+
+
 def bench_simple(args, name, fmt):
     """Store + retrieve GB/s for the 70B-style and fp8 workloads."""
     import torch
@@ -465,7 +655,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3.1-8b",
-                    choices=["llama3.1-8b", "layerwise-8b", "layerwise-store-8b", "llama-70b-style", "fp8-8b"])
+                    choices=["llama3.1-8b", "layerwise-8b", "layerwise-store-8b", "llama-70b-style", "fp8-8b",
+                             "offload-8b"])
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (used for profiler runs)")
     args = ap.parse_args()
@@ -486,6 +677,8 @@ def main():
         out = bench_layerwise(args)
     elif args.workload == "layerwise-store-8b":
         out = bench_layerwise_store(args)
+    elif args.workload == "offload-8b":
+        out = bench_offload(args)
     elif args.workload == "llama-70b-style":
         out = bench_simple(args, "llama-70b-style", kvm.FMT_BF16)
     else:

@@ -46,6 +46,17 @@
  *          (OCP E4M3, "fn" variant) followed by float32 scales[num_layers][2].
  *          kv_chunk_bytes() gives the exact size.
  *
+ * Where chunks live: a chunk buffer is either device memory or pinned host
+ * memory that the device addresses directly (hipHostMalloc, or torch's
+ * pin_memory=True).  With host buffers, store is the offload to CPU memory
+ * and retrieve the onload from it: the kernels' own loads and stores cross
+ * PCIe, with no staging buffer and no separate DMA step.  [paper] gathers
+ * into a GPU streaming buffer and then copies that to CPU memory ("方法细节",
+ * configurable-chunk-size paragraph); its section "实验结果", component-level
+ * evaluation and Table 5, reports the load bandwidth from CPU memory that
+ * this path is measured against.  Pageable host memory is not addressable
+ * by the device and must not be passed.
+ *
  * fp8 serde: per (chunk, layer, K/V) group, amax = max |x| (a NaN anywhere
  * makes it NaN); scale = amax / 448 in float32 (scale = 1 when amax == 0);
  * q = e4m3(x / scale) with an IEEE float32 division, rounding to nearest-even
@@ -111,8 +122,9 @@ typedef struct {
     int64_t n_bt;               /* entries in block_table */
     int64_t tok_start;          /* first token; a multiple of chunk_size ([walk] "工程实践") */
     int64_t tok_end;            /* one past the last token; tok_start <= tok_end <= P*n_bt */
-    const uint64_t* chunks;     /* DEVICE uint64[n_chunks]: address of chunk c's buffer,
-                                   16-byte aligned, >= kv_chunk_bytes(tokens of chunk c) */
+    const uint64_t* chunks;     /* DEVICE uint64[n_chunks]: address of chunk c's buffer
+                                   (device or pinned host memory), 16-byte aligned,
+                                   >= kv_chunk_bytes(tokens of chunk c) */
 } kv_seq;
 
 /* Exact bytes of one chunk holding n_tokens tokens in format fmt ([serde]
@@ -166,7 +178,11 @@ int kv_retrieve_chunks(const kv_paged* paged, const kv_seq* seqs,
  * GPU is otherwise idle); a positive value caps the grid, each workgroup then
  * moving a contiguous run of tiles, so the scatter occupies few wave slots
  * while compute on another stream runs beside it (page-unit kernels: bf16
- * and the fp8 retrieve). */
+ * and the fp8 retrieve).  From host chunks the scatter is bound by PCIe, and
+ * a cap of 32 workgroups already moves at the link's rate.  Overlap needs
+ * copy_stream and the compute stream on different hardware queues: HIP
+ * spreads a process's streams over a few queues (GPU_MAX_HW_QUEUES, 4 by
+ * default), and two streams that share a queue run in order. */
 int kv_retrieve_layer(const kv_paged* paged, const kv_seq* seqs,
                       const uint8_t* const* hit_mask, int n_seqs, int fmt, int32_t layer,
                       int64_t* out_tokens, int32_t max_workgroups, hipStream_t copy_stream,

@@ -14,6 +14,9 @@ Typical use::
     batch = kvm.Batch(paged, [kvm.Seq(block_table, 0, 10000, chunks)])
     kvm.store(paged, batch)                            # gather pages -> chunks
     n = kvm.retrieve(paged, batch, masks=[hit_mask])   # scatter hit chunks -> pages
+
+Chunk tensors made with ``pin_memory=True`` instead of on the device turn the
+same calls into the offload to host memory and the onload from it.
 """
 from __future__ import annotations
 
@@ -167,7 +170,13 @@ class Paged:
 
 class Seq:
     """One sequence's job: a device int32 block table, a token range and its
-    chunk buffers (device uint8 tensors, or a device int64 tensor of addresses)."""
+    chunk buffers (device int64 tensor of addresses, or uint8 tensors).
+
+    A chunk tensor lives either in device memory or in pinned host memory
+    (``pin_memory=True``): the kernels address pinned host memory directly,
+    so a store into host chunks is the offload and a retrieve from them the
+    onload, both over PCIe with no staging copy.  Pageable host tensors are
+    refused, since the GPU cannot reach them."""
 
     def __init__(self, block_table, tok_start: int, tok_end: int, chunks):
         import torch
@@ -177,6 +186,12 @@ class Seq:
             self.chunk_addrs, self._chunks = chunks, None
         else:
             self._chunks = list(chunks)
+            for i, c in enumerate(self._chunks):
+                if not c.is_contiguous():
+                    raise KvError(KV_EINVAL, f"chunk {i} is not contiguous")
+                if not (c.is_cuda or c.is_pinned()):
+                    raise KvError(KV_EINVAL, f"chunk {i} is pageable host memory; "
+                                             "use a device tensor or pin_memory=True")
             addrs = torch.tensor([c.data_ptr() for c in self._chunks], dtype=torch.int64)
             dev = block_table.device if isinstance(block_table, torch.Tensor) else "cuda"
             self.chunk_addrs = addrs.to(dev)

@@ -40,26 +40,32 @@ def chunk_tokens(w, sq):
     return [oracle.chunk_tokens(sq.tok_start, sq.tok_end, w.chunk_size, c) for c in range(n)]
 
 
-def alloc_dev_chunks(paged, w, sq, fmt, fill=0x00):
-    """One device uint8 buffer per chunk: the library's exact size + a guard."""
+def alloc_dev_chunks(paged, w, sq, fmt, fill=0x00, where="device"):
+    """One uint8 buffer per chunk: the library's exact size + a guard.  In
+    device memory, or in pinned host memory when where == "host"."""
     bufs, sizes = [], []
     for n_c in chunk_tokens(w, sq):
         size = paged.chunk_bytes(n_c, fmt)
-        b = torch.full((size + GUARD,), fill, dtype=torch.uint8, device="cuda")
+        if where == "host":
+            b = torch.empty((size + GUARD,), dtype=torch.uint8, pin_memory=True)
+            b.fill_(fill)
+        else:
+            b = torch.full((size + GUARD,), fill, dtype=torch.uint8, device="cuda")
         b[size:] = GUARD_FILL
         bufs.append(b)
         sizes.append(size)
     return bufs, sizes
 
 
-def setup_device(w, arr=None, pool=None, fmt=kvm.FMT_BF16, fill=0x00):
-    """Device pool + Paged + per-sequence chunk buffers + a Batch."""
+def setup_device(w, arr=None, pool=None, fmt=kvm.FMT_BF16, fill=0x00, where="device"):
+    """Device pool + Paged + per-sequence chunk buffers + a Batch.  Chunk
+    buffers are in device memory, or pinned host memory for where="host"."""
     if pool is None:
         pool = dev_pool_from_host(w, arr)
     paged = kvm.Paged.from_pool(pool, chunk_size=w.chunk_size)
     seqs, chunk_sets = [], []
     for sq in w.seqs:
-        bufs, sizes = alloc_dev_chunks(paged, w, sq, fmt, fill)
+        bufs, sizes = alloc_dev_chunks(paged, w, sq, fmt, fill, where)
         bt = torch.from_numpy(np.ascontiguousarray(sq.block_table, np.int32)).to("cuda")
         seqs.append(kvm.Seq(bt, sq.tok_start, sq.tok_end, bufs))
         chunk_sets.append((bufs, sizes))

@@ -170,3 +170,15 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(kvm, "_lib", None)
     with pytest.raises(kvm.KvError, match="no fallback"):
         kvm.load()
+
+
+def test_binding_refuses_pageable_host_chunks():
+    # the GPU cannot address pageable host memory: the binding refuses it
+    # before any call (device and pinned host tensors are accepted)
+    import torch
+    bt = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(kvm.KvError, match="pageable"):
+        kvm.Seq(bt, 0, 64, [torch.empty(1 << 16, dtype=torch.uint8)])
+    with pytest.raises(kvm.KvError, match="contiguous"):
+        t = torch.empty(1 << 16, dtype=torch.uint8, device="meta")
+        kvm.Seq(bt, 0, 64, [t[::2]])

@@ -11,12 +11,13 @@ import torch
 import oracle
 import paged_kv_movement_amd as kvm
 from paged_kv_movement_amd import workloads as wl
-from gpu_util import (say, host_from_dev_pool, oracle_pool, chunk_tokens, setup_device,
-                      host_chunks, check_store, check_retrieve, sync as _sync)
+from gpu_util import (say, dev_pool_from_host, host_from_dev_pool, oracle_pool, chunk_tokens,
+                      setup_device, host_chunks, check_store, check_retrieve, sync as _sync)
 
 pytestmark = pytest.mark.gpu
 
 BF16, FP8 = kvm.FMT_BF16, kvm.FMT_FP8
+SENTINEL = 0x7E57
 
 
 def _roundtrip(w, fmt=BF16, fill=0x0000, masks=None):
@@ -443,3 +444,118 @@ def test_layerwise_store_equals_full_store(fmt, cap):
     torch.cuda.synchronize()
     assert kvm.take_faults() == 0
     check_store(w, arr, cs, fmt)
+
+
+def test_consumer_waiting_on_layer_event_sees_the_whole_layer():
+    # the compute stream waits on layer l's event and then copies layer l of
+    # the pool; the scatter runs on a one-workgroup grid (milliseconds per
+    # layer), so an event recorded too early would let the copy see sentinels
+    w = wl.custom("event-order", 271, 4, 8, 128, 1024, [(0, 4096), (0, 1000)])
+    say("case", w.name)
+    arr = wl.host_pool(w)
+    pool, paged, batch, cs = setup_device(w, arr)
+    kvm.store(paged, batch)
+    torch.cuda.synchronize()
+    pool.view(torch.int16).fill_(SENTINEL)
+    copy, compute = torch.cuda.Stream(), torch.cuda.Stream()
+    events = [torch.cuda.Event() for _ in range(w.num_layers)]
+    torch.cuda.synchronize()
+    snaps = []
+    for l in range(w.num_layers):
+        kvm.retrieve_layer(paged, batch, l, stream=copy, event=events[l], max_workgroups=1)
+        compute.wait_event(events[l])
+        with torch.cuda.stream(compute):
+            snaps.append(pool[l].clone())
+    torch.cuda.synchronize()
+    assert kvm.take_faults() == 0
+    for l in range(w.num_layers):
+        assert torch.equal(snaps[l].view(torch.int16), pool[l].view(torch.int16)), l
+    got = host_from_dev_pool(pool)
+    check_retrieve(w, np.full(got.shape, SENTINEL, np.uint16), got, cs, BF16,
+                   [s.hit_mask for s in w.seqs], copy=False)
+
+
+@pytest.mark.parametrize("fmt", [BF16, FP8], ids=["bf16", "fp8"])
+def test_store_waiting_on_producer_event_sees_the_layer(fmt):
+    # the producer (compute stream) writes layer l of the pool after a GEMM and
+    # records its event; the layer store on the copy stream waits on it, so the
+    # chunks must hold the produced values, never the sentinel left before
+    w = wl.custom("producer-order", 272, 4, 8, 128, 1024, [(0, 4096), (256, 1300)],
+                  outliers=2 if fmt == FP8 else 0)
+    say("case", w.name, fmt)
+    arr = wl.host_pool(w)
+    src = dev_pool_from_host(w, arr)
+    pool, paged, batch, cs = setup_device(w, arr, fmt=fmt, fill=0xC3)
+    pool.view(torch.int16).fill_(SENTINEL)
+    x = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    copy, compute = torch.cuda.Stream(), torch.cuda.Stream()
+    done = [torch.cuda.Event() for _ in range(w.num_layers)]
+    torch.cuda.synchronize()
+    for l in range(w.num_layers):
+        with torch.cuda.stream(compute):
+            torch.mm(x, x)
+            pool[l].copy_(src[l])
+            done[l].record(compute)
+        copy.wait_event(done[l])
+        kvm.store_layer(paged, batch, l, fmt=fmt, stream=copy)
+    torch.cuda.synchronize()
+    assert kvm.take_faults() == 0
+    check_store(w, arr, cs, fmt)
+
+
+@pytest.mark.parametrize("fmt", [BF16, FP8], ids=["bf16", "fp8"])
+def test_host_chunks_offload_and_onload(fmt):
+    # chunk buffers in pinned host memory: the store writes them over PCIe
+    # (offload) and the retrieve reads them back (onload), bit for bit as
+    # with device chunks; guards after each host buffer stay untouched
+    w = wl.custom("host-chunks", 281, 3, 4, 64, 400, [(0, 1000), (256, 1555), (0, 17)],
+                  masks=[[1, 1, 0, 1], [1, 1, 1, 1, 1, 1], [1]], outliers=2 if fmt == FP8 else 0)
+    say("case", w.name, fmt)
+    arr = wl.host_pool(w)
+    pool, paged, batch, cs = setup_device(w, arr, fmt=fmt, fill=0xCD, where="host")
+    assert all(b.is_pinned() for b in cs[0][0])
+    kvm.store(paged, batch, fmt)
+    _sync()
+    assert kvm.take_faults() == 0
+    check_store(w, arr, cs, fmt)
+    masks = [s.hit_mask for s in w.seqs]
+    pool.view(torch.int16).fill_(0x7E57)
+    n = kvm.retrieve(paged, batch, fmt=fmt)
+    _sync()
+    assert kvm.take_faults() == 0
+    got = host_from_dev_pool(pool)
+    assert n == check_retrieve(w, np.full(got.shape, 0x7E57, np.uint16), got, cs, fmt, masks)
+    # layer by layer from host chunks, on a side stream with a capped grid
+    pool.view(torch.int16).fill_(0x7E57)
+    s = torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    for l in range(w.num_layers):
+        kvm.retrieve_layer(paged, batch, l, fmt=fmt, stream=s, event=ev, max_workgroups=3)
+    ev.synchronize()
+    assert kvm.take_faults() == 0
+    assert np.array_equal(host_from_dev_pool(pool), got)
+
+
+def test_host_and_device_chunks_in_one_call():
+    # one batch whose sequences keep their chunks in different memories
+    w = wl.custom("mixed-chunks", 282, 2, 2, 64, 200, [(0, 700), (0, 300)])
+    arr = wl.host_pool(w)
+    pool = dev_pool_from_host(w, arr)
+    paged = kvm.Paged.from_pool(pool, chunk_size=w.chunk_size)
+    from gpu_util import alloc_dev_chunks
+    seqs, cs = [], []
+    for sq, where in zip(w.seqs, ["host", "device"]):
+        bufs, sizes = alloc_dev_chunks(paged, w, sq, BF16, 0, where)
+        bt = torch.from_numpy(np.ascontiguousarray(sq.block_table, np.int32)).cuda()
+        seqs.append(kvm.Seq(bt, sq.tok_start, sq.tok_end, bufs))
+        cs.append((bufs, sizes))
+    batch = kvm.Batch(paged, seqs).set_masks([s.hit_mask for s in w.seqs])
+    kvm.store(paged, batch)
+    _sync()
+    check_store(w, arr, cs, BF16)
+    pool.zero_()
+    assert kvm.retrieve(paged, batch) == [700, 300]
+    _sync()
+    assert kvm.take_faults() == 0
+    got = host_from_dev_pool(pool)
+    check_retrieve(w, np.zeros(got.shape, np.uint16), got, cs, BF16, [s.hit_mask for s in w.seqs])

@@ -25,12 +25,13 @@ SENTINEL = 0x7E57
 def _free():
     sync()
     torch.cuda.empty_cache()
+    torch._C._host_emptyCache()     # give back pinned host blocks too
 
 
-def _full_bf16(w, expect_tokens):
-    say("case", w.name, "pool GB", w.pool_nbytes() / 1e9)
+def _full_bf16(w, expect_tokens, where="device"):
+    say("case", w.name, "pool GB", w.pool_nbytes() / 1e9, "chunks in", where)
     pool = wl.device_pool(w)
-    pool, paged, batch, chunk_sets = setup_device(w, pool=pool, fill=0xCD)
+    pool, paged, batch, chunk_sets = setup_device(w, pool=pool, fill=0xCD, where=where)
     kvm.store(paged, batch)                       # one launch over every sequence
     sync()
     assert kvm.take_faults() == 0
@@ -57,6 +58,12 @@ def test_full_llama8b_store_and_30_chunk_retrieve():
     # 8 sequences x 10000 tokens (39 full chunks + a 16-token tail), 8192-page
     # pool; retrieve with the first 30 chunks hit
     _full_bf16(wl.llama8b(), [30 * 256] * 8)
+
+
+def test_full_llama8b_offload_to_host_and_onload():
+    # the same workload with every chunk in pinned host memory: the store is
+    # the offload over PCIe, the retrieve the onload
+    _full_bf16(wl.llama8b(), [30 * 256] * 8, where="host")
 
 
 def test_full_llama70b_store_and_retrieve():
