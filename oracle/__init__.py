@@ -23,8 +23,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kv_oracle.c")
 _LIB = os.path.join(_HERE, "libkvoracle.so")
 
-FMT_BF16 = 0
-FMT_FP8 = 1
+FMT_BF16 = 0          # K and V bf16
+FMT_FP8 = 1           # K and V e4m3, one float32 scale per (layer, K/V)
+FMT_FP8_E5M2 = 2      # K and V e5m2, one float32 scale per (layer, K/V)
+FMT_K16_V8 = 3        # K bf16, V e4m3, one float32 scale per layer
 
 _lib = None
 
@@ -78,6 +80,11 @@ def _bind(L):
         "kvo_bf16_from_float": (ctypes.c_uint16, [f32]),
         "kvo_float_from_bf16": (f32, [ctypes.c_uint16]),
         "kvo_fp8_scale": (f32, [f32]),
+        "kvo_e5m2_scale": (f32, [f32]),
+        "kvo_e5m2_encode": (u8, [f32]),
+        "kvo_e5m2_decode": (f32, [u8]),
+        "kvo_e5m2_encode_n": (None, [vp, vp, i64]),
+        "kvo_e5m2_encode_bits_range": (None, [ctypes.c_uint64, i64, vp]),
         "kvo_e4m3_encode_n": (None, [vp, vp, i64]),
         "kvo_e4m3_encode_bits_range": (None, [ctypes.c_uint64, i64, vp]),
         "kvo_bf16_from_float_n": (None, [vp, vp, i64]),
@@ -197,6 +204,29 @@ def e4m3_decode(b) -> np.ndarray:
     b = np.asarray(b, dtype=np.uint8)
     L = lib()
     return np.array([L.kvo_e4m3_decode(int(x)) for x in b.ravel()], dtype=np.float32).reshape(b.shape)
+
+
+def e5m2_encode(y) -> np.ndarray:
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(y.shape, dtype=np.uint8)
+    lib().kvo_e5m2_encode_n(_ptr(y), _ptr(out), y.size)
+    return out
+
+
+def e5m2_encode_bits_range(first_bits: int, n: int) -> np.ndarray:
+    out = np.empty(n, dtype=np.uint8)
+    lib().kvo_e5m2_encode_bits_range(first_bits, n, _ptr(out))
+    return out
+
+
+def e5m2_decode(b) -> np.ndarray:
+    b = np.asarray(b, dtype=np.uint8)
+    L = lib()
+    return np.array([L.kvo_e5m2_decode(int(x)) for x in b.ravel()], dtype=np.float32).reshape(b.shape)
+
+
+def e5m2_scale(amax: float) -> float:
+    return float(lib().kvo_e5m2_scale(amax))
 
 
 def bf16_from_float(y) -> np.ndarray:

@@ -37,15 +37,67 @@ int64_t kvo_chunk_tokens(int64_t s, int64_t e, int32_t chunk_size, int64_t c)
     return last > first ? last - first : 0;
 }
 
-/* Exact serialized size: 2 bytes per bf16 element, or, for fp8, 1 byte per
- * element (serde page, section "7.1 fp8 量化": the estimate is exactly the
- * element count) plus one fp32 scale per (layer, K/V). */
+/* How a chunk of format fmt holds K (kv = 0) or V (kv = 1): copied bf16, or
+ * quantised to one of the two fp8 encodings the serde page offers (section
+ * "7.1 fp8 量化": e4m3fn by default, e5m2 on request); the asymmetric format
+ * keeps K at 16 bits and V at 8 (section "7.3"). */
+enum { PART_BF16, PART_E4M3, PART_E5M2 };
+
+static int part_kind(int fmt, int kv)
+{
+    switch (fmt) {
+    case KVO_FMT_BF16: return PART_BF16;
+    case KVO_FMT_FP8: return PART_E4M3;
+    case KVO_FMT_FP8_E5M2: return PART_E5M2;
+    case KVO_FMT_K16_V8: return kv == 0 ? PART_BF16 : PART_E4M3;
+    }
+    return -1;
+}
+
+static int valid_fmt(int fmt)
+{
+    return fmt == KVO_FMT_BF16 || fmt == KVO_FMT_FP8 || fmt == KVO_FMT_FP8_E5M2 || fmt == KVO_FMT_K16_V8;
+}
+
+/* Bytes per element of a part: bf16 2; fp8 1 (serde page, section "7.1":
+ * one byte per element). */
+static int64_t part_bytes(int kind) { return kind == PART_BF16 ? 2 : 1; }
+
+/* Byte offset of the (l, kv) section of a chunk of n_c tokens: the sections
+ * run layer by layer, K before V, each n_c rows of the part's type. */
+static int64_t section_offset(const kvo_pool* p, int fmt, int l, int kv, int64_t n_c)
+{
+    int64_t width = (int64_t)p->num_kv_heads * p->head_dim;
+    int64_t off = 0;
+    for (int ll = 0; ll < p->num_layers; ll++) {
+        for (int k = 0; k < 2; k++) {
+            if (ll == l && k == kv) return off;
+            off += n_c * width * part_bytes(part_kind(fmt, k));
+        }
+    }
+    return off;      /* (l, kv) = (num_layers, 0): the end of the payload */
+}
+
+/* Byte offset of the float32 scale of a quantised (l, kv) part: the scales
+ * follow the payload, one per quantised part, in the sections' order. */
+static int64_t scale_offset(const kvo_pool* p, int fmt, int l, int kv, int64_t n_c)
+{
+    int64_t off = section_offset(p, fmt, p->num_layers, 0, n_c);
+    for (int ll = 0; ll < p->num_layers; ll++) {
+        for (int k = 0; k < 2; k++) {
+            if (ll == l && k == kv) return off;
+            if (part_kind(fmt, k) != PART_BF16) off += 4;
+        }
+    }
+    return off;
+}
+
+/* Exact serialized size (serde page, section "4.2": the estimate follows from
+ * the layout alone, with no slack): the sections plus the scales. */
 int64_t kvo_chunk_bytes(const kvo_pool* p, int64_t n_tokens, int fmt)
 {
-    int64_t elems = (int64_t)p->num_layers * 2 * n_tokens * p->num_kv_heads * p->head_dim;
-    if (fmt == KVO_FMT_BF16) return elems * 2;
-    if (fmt == KVO_FMT_FP8) return elems + (int64_t)p->num_layers * 2 * 4;
-    return -1;
+    if (!valid_fmt(fmt)) return -1;
+    return scale_offset(p, fmt, p->num_layers, 0, n_tokens);
 }
 
 /* The connector hands the mover the addresses of the pages that hold a
@@ -145,6 +197,48 @@ uint8_t kvo_e4m3_encode(float y)
     return (uint8_t)(sign | (uint8_t)((E + 7) << 3) | (uint8_t)mant);
 }
 
+/* OCP 8-bit floating point, E5M2: exponent bias 15, 2 mantissa bits,
+ * S.11111.00 is infinity and S.11111.{01,10,11} NaN, largest finite
+ * 57344 = S.11110.11, smallest normal 2^-14, subnormals m * 2^-16 for
+ * m = 1..3.  Closed-form decode. */
+float kvo_e5m2_decode(uint8_t b)
+{
+    int s = b >> 7, e = (b >> 2) & 31, m = b & 3;
+    double v;
+    if (e == 31) {
+        if (m == 0) return s ? -INFINITY : INFINITY;
+        return s ? -NAN : NAN;
+    }
+    if (e == 0) v = m * ldexp(1.0, -16);
+    else v = (1.0 + m / 4.0) * ldexp(1.0, e - 15);
+    return (float)(s ? -v : v);
+}
+
+/* float -> E5M2, round-to-nearest-even over normals and subnormals,
+ * saturating: a magnitude that rounds above 57344, and infinity, become
+ * 57344 (the saturating reading is the same as for E4M3).  +-0 keep their
+ * sign; NaN becomes S.11111.11. */
+uint8_t kvo_e5m2_encode(float y)
+{
+    uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    if (isnan(y)) return (uint8_t)(sign | 0x7F);
+    if (isinf(y)) return (uint8_t)(sign | 0x7B);
+    double a = fabs((double)y);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);                 /* a in [2^(e-1), 2^e) */
+    int E = e - 1;
+    if (E < -14) E = -14;         /* below 2^-14 the subnormal spacing 2^-16 holds */
+    double q = ldexp(1.0, E - 2); /* spacing of E5M2 values around a */
+    double v = nearbyint(a / q) * q;   /* ties to even */
+    if (v > 57344.0) return (uint8_t)(sign | 0x7B);
+    if (v < ldexp(1.0, -14)) return (uint8_t)(sign | (uint8_t)(v / ldexp(1.0, -16)));
+    frexp(v, &e);
+    E = e - 1;
+    int mant = (int)((v / ldexp(1.0, E) - 1.0) * 4.0);
+    return (uint8_t)(sign | (uint8_t)((E + 15) << 2) | (uint8_t)mant);
+}
+
 /* One scale per (chunk, layer, K/V) group: the group's absolute maximum
  * mapped onto E4M3's largest finite value, so the group spans [-448, 448].
  * An all-zero group takes scale 1 (its elements encode as signed zeros). */
@@ -152,6 +246,28 @@ float kvo_fp8_scale(float amax)
 {
     if (amax == 0.0f) return 1.0f;
     return amax / 448.0f;
+}
+
+/* As kvo_fp8_scale, for E5M2's largest finite value. */
+float kvo_e5m2_scale(float amax)
+{
+    if (amax == 0.0f) return 1.0f;
+    return amax / 57344.0f;
+}
+
+void kvo_e5m2_encode_n(const float* y, uint8_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = kvo_e5m2_encode(y[i]);
+}
+
+void kvo_e5m2_encode_bits_range(uint64_t first_bits, int64_t n, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; i++) {
+        uint32_t bits = (uint32_t)(first_bits + (uint64_t)i);
+        float y;
+        memcpy(&y, &bits, 4);
+        out[i] = kvo_e5m2_encode(y);
+    }
 }
 
 void kvo_e4m3_encode_n(const float* y, uint8_t* out, int64_t n)
@@ -184,7 +300,7 @@ static int check_args(const kvo_pool* p, const int32_t* bt, int64_t n_bt,
     if (p == NULL || bt == NULL) return -1;
     if (p->num_layers <= 0 || p->num_kv_heads <= 0 || p->head_dim <= 0) return -1;
     if (p->page_size <= 0 || p->chunk_size <= 0 || p->num_pages <= 0) return -1;
-    if (fmt != KVO_FMT_BF16 && fmt != KVO_FMT_FP8) return -1;
+    if (!valid_fmt(fmt)) return -1;
     /* the already-computed prefix must be a whole number of chunks (LMCache
      * source walkthrough, section "工程实践": the count of False mask entries
      * must be a multiple of chunk_size, else ValueError) */
@@ -205,13 +321,10 @@ static uint16_t* pool_elem(const kvo_pool* p, int l, int kv, int64_t row, int64_
     return base + row * width + i;
 }
 
-/* Byte offset of element (l, kv, j, i) inside a chunk of n_c tokens laid out
- * [layers][K,V][tokens][heads * head_size], in units of elements. */
-static int64_t chunk_index(const kvo_pool* p, int l, int kv, int64_t n_c, int64_t j, int64_t i)
-{
-    int64_t width = (int64_t)p->num_kv_heads * p->head_dim;
-    return (((int64_t)l * 2 + kv) * n_c + j) * width + i;
-}
+/* Inside the (l, kv) section of a chunk, element (j, i) -- token j of the
+ * chunk, element i of its row -- sits at byte (j * width + i) * element size.
+ * For bf16 everywhere this is the blob [layers][K,V][tokens][heads *
+ * head_size] of the CacheGen page, section "2. 量化". */
 
 /* Store: the paper notes (section "可配置的块大小") describe a GPU kernel that
  * copies KV from scattered paged memory into a contiguous buffer, grouping
@@ -236,12 +349,15 @@ int kvo_store(const kvo_pool* p, const int32_t* bt, int64_t n_bt,
         for (int l = 0; l < p->num_layers; l++) {
             if (layer >= 0 && l != layer) continue;
             for (int kv = 0; kv < 2; kv++) {
-                if (fmt == KVO_FMT_BF16) {
+                int kind = part_kind(fmt, kv);
+                uint8_t* sec = buf + section_offset(p, fmt, l, kv, n_c);
+                int64_t eb = part_bytes(kind);
+                if (kind == PART_BF16) {
                     for (int64_t j = 0; j < n_c; j++) {
                         int64_t row = kvo_slot(bt, p->page_size, t0 + j);
                         for (int64_t i = 0; i < width; i++) {
                             uint16_t x = *pool_elem(p, l, kv, row, i);
-                            memcpy(buf + 2 * chunk_index(p, l, kv, n_c, j, i), &x, 2);
+                            memcpy(sec + (j * width + i) * eb, &x, 2);
                         }
                     }
                 } else {
@@ -257,18 +373,17 @@ int kvo_store(const kvo_pool* p, const int32_t* bt, int64_t n_bt,
                         }
                     }
                     if (saw_nan) amax = NAN;
-                    float scale = kvo_fp8_scale(amax);
+                    float scale = kind == PART_E4M3 ? kvo_fp8_scale(amax) : kvo_e5m2_scale(amax);
                     for (int64_t j = 0; j < n_c; j++) {
                         int64_t row = kvo_slot(bt, p->page_size, t0 + j);
                         for (int64_t i = 0; i < width; i++) {
                             float x = kvo_float_from_bf16(*pool_elem(p, l, kv, row, i));
                             float y = x / scale;          /* binary32 division */
-                            buf[chunk_index(p, l, kv, n_c, j, i)] = kvo_e4m3_encode(y);
+                            sec[(j * width + i) * eb] =
+                                kind == PART_E4M3 ? kvo_e4m3_encode(y) : kvo_e5m2_encode(y);
                         }
                     }
-                    /* scales follow the payload as float32[layers][K,V] */
-                    int64_t payload = (int64_t)p->num_layers * 2 * n_c * width;
-                    memcpy(buf + payload + 4 * ((int64_t)l * 2 + kv), &scale, 4);
+                    memcpy(buf + scale_offset(p, fmt, l, kv, n_c), &scale, 4);
                 }
             }
         }
@@ -310,20 +425,23 @@ int64_t kvo_retrieve(const kvo_pool* p, const int32_t* bt, int64_t n_bt,
         int64_t n_c = kvo_chunk_tokens(s, e, p->chunk_size, c);
         int64_t t0 = s + c * p->chunk_size;
         const uint8_t* buf = chunks[c];
-        int64_t payload = (int64_t)p->num_layers * 2 * n_c * width;
         for (int l = 0; l < p->num_layers; l++) {
             if (layer >= 0 && l != layer) continue;
             for (int kv = 0; kv < 2; kv++) {
+                int kind = part_kind(fmt, kv);
+                const uint8_t* sec = buf + section_offset(p, fmt, l, kv, n_c);
+                int64_t eb = part_bytes(kind);
                 float scale = 1.0f;
-                if (fmt == KVO_FMT_FP8) memcpy(&scale, buf + payload + 4 * ((int64_t)l * 2 + kv), 4);
+                if (kind != PART_BF16) memcpy(&scale, buf + scale_offset(p, fmt, l, kv, n_c), 4);
                 for (int64_t j = 0; j < n_c; j++) {
                     int64_t row = kvo_slot(bt, p->page_size, t0 + j);
                     for (int64_t i = 0; i < width; i++) {
+                        const uint8_t* src = sec + (j * width + i) * eb;
                         uint16_t x;
-                        if (fmt == KVO_FMT_BF16) {
-                            memcpy(&x, buf + 2 * chunk_index(p, l, kv, n_c, j, i), 2);
+                        if (kind == PART_BF16) {
+                            memcpy(&x, src, 2);
                         } else {
-                            float d = kvo_e4m3_decode(buf[chunk_index(p, l, kv, n_c, j, i)]);
+                            float d = kind == PART_E4M3 ? kvo_e4m3_decode(*src) : kvo_e5m2_decode(*src);
                             float prod = d * scale;       /* binary32 product */
                             x = kvo_bf16_from_float(prod);
                         }

@@ -25,11 +25,14 @@
  *  - Retrieve = scatter of the chunks back into pages, honouring the prefix
  *    hit rule: hits count from chunk 0 and stop at the first miss (LMCache
  *    source walkthrough, section "retrieve()：前缀匹配如何在首个未命中处停下").
- *  - The optional fp8 serde: every element cast to float8 e4m3fn, one byte per
- *    element ("LMCache 分布式 KV Cache 序列化框架 Serde 双层接口设计与自定义
- *    扩展实战" (LMCache serde framework page), section "7.1 fp8 量化"), here
- *    with one fp32 absmax scale per (chunk, layer, K/V): scale = amax / 448,
- *    q = e4m3(x / scale) rounded to nearest-even and saturated.
+ *  - The optional fp8 serde: every element cast to float8 e4m3fn (default)
+ *    or e5m2, one byte per element ("LMCache 分布式 KV Cache 序列化框架 Serde
+ *    双层接口设计与自定义扩展实战" (LMCache serde framework page), section
+ *    "7.1 fp8 量化"), here with one fp32 absmax scale per (chunk, layer, K/V):
+ *    scale = amax / fmax (448 for e4m3, 57344 for e5m2), q = fp8(x / scale)
+ *    rounded to nearest-even and saturated.
+ *  - The asymmetric K16/V8 serde named on the same page (section "7.3":
+ *    K kept at 16 bits, V at 8): K copied as bf16, V quantised as scaled e4m3.
  *
  * Parity pins (tests marked "not gpu") tie each function to something other
  * than itself: numpy page-gather + reshape formulations, store-then-retrieve
@@ -46,7 +49,16 @@
 extern "C" {
 #endif
 
-enum { KVO_FMT_BF16 = 0, KVO_FMT_FP8 = 1 };
+/* Chunk formats.  A chunk of n tokens holds, for each layer in order, its K
+ * section then its V section, each n * H * D elements of the part's type
+ * (bf16: 2 bytes, fp8: 1 byte), then one float32 scale for each quantised
+ * (layer, K/V) part in the same order. */
+enum {
+    KVO_FMT_BF16 = 0,       /* K bf16, V bf16 */
+    KVO_FMT_FP8 = 1,        /* K e4m3, V e4m3, scales [L][2] */
+    KVO_FMT_FP8_E5M2 = 2,   /* K e5m2, V e5m2, scales [L][2] */
+    KVO_FMT_K16_V8 = 3      /* K bf16, V e4m3, scales [L] */
+};
 
 /* The engine's paged pool, in host memory.  For layer l, k[l] and v[l] each
  * point at uint16 (raw bf16 bits) [num_pages][page_size][num_kv_heads*head_dim]. */
@@ -90,13 +102,18 @@ int64_t kvo_retrieve(const kvo_pool* pool, const int32_t* block_table, int64_t n
 /* Number formats. */
 uint8_t  kvo_e4m3_encode(float y);       /* OCP E4M3 (fn), RNE, saturating */
 float    kvo_e4m3_decode(uint8_t b);
+uint8_t  kvo_e5m2_encode(float y);       /* OCP E5M2, RNE, saturating (infinity too) */
+float    kvo_e5m2_decode(uint8_t b);
 uint16_t kvo_bf16_from_float(float y);   /* IEEE-754 round-to-nearest-even */
 float    kvo_float_from_bf16(uint16_t h);
 float    kvo_fp8_scale(float amax);      /* amax == 0 ? 1 : amax / 448 */
+float    kvo_e5m2_scale(float amax);     /* amax == 0 ? 1 : amax / 57344 */
 
 /* Array forms of the conversions (for exhaustive checks). */
 void kvo_e4m3_encode_n(const float* y, uint8_t* out, int64_t n);
 void kvo_e4m3_encode_bits_range(uint64_t first_bits, int64_t n, uint8_t* out);
+void kvo_e5m2_encode_n(const float* y, uint8_t* out, int64_t n);
+void kvo_e5m2_encode_bits_range(uint64_t first_bits, int64_t n, uint8_t* out);
 void kvo_bf16_from_float_n(const float* y, uint16_t* out, int64_t n);
 
 #ifdef __cplusplus

@@ -226,19 +226,29 @@ def _torch_e4m3(y: np.ndarray) -> np.ndarray:
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
+def _exhaustive(encode_range, torch_cast, lo, hi):
+    """Every positive fp32 pattern in [lo, hi): oracle vs the torch cast, in
+    blocks spread over threads (the oracle's ctypes calls release the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+    lo, hi = int(np.float32(lo).view(np.uint32)), int(np.float32(hi).view(np.uint32))
+    step = 1 << 23
+
+    def block(b0):
+        n = min(step, hi - b0)
+        got = encode_range(b0, n)
+        y = np.arange(b0, b0 + n, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        bad = np.nonzero(got != torch_cast(y))[0]
+        return None if bad.size == 0 else (hex(b0 + int(bad[0])), int(got[bad[0]]))
+
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        fails = [r for r in ex.map(block, range(lo, hi, step)) if r is not None]
+    assert not fails, fails[:3]
+
+
 def test_e4m3_encode_exhaustive_meaningful_range():
     # every positive fp32 pattern from 2^-12 up to 2^10: covers all subnormal
     # and normal E4M3 rounding decisions, the ties, and saturation
-    lo = np.float32(2.0 ** -12).view(np.uint32)
-    hi = np.float32(2.0 ** 10).view(np.uint32)
-    step = 1 << 26
-    for b0 in range(int(lo), int(hi), step):
-        n = min(step, int(hi) - b0)
-        got = oracle.e4m3_encode_bits_range(b0, n)
-        y = np.arange(b0, b0 + n, dtype=np.uint64).astype(np.uint32).view(np.float32)
-        exp = _torch_e4m3(y)
-        bad = np.nonzero(got != exp)[0]
-        assert bad.size == 0, (hex(b0 + int(bad[0])), got[bad[0]], exp[bad[0]])
+    _exhaustive(oracle.e4m3_encode_bits_range, _torch_e4m3, 2.0 ** -12, 2.0 ** 10)
 
 
 def test_e4m3_encode_sampled_everywhere_and_specials():
@@ -265,6 +275,44 @@ def test_e4m3_decode_all_codes():
     assert np.array_equal(got[ok].view(np.uint32), exp[ok].view(np.uint32))  # incl. -0
     # decode then encode is the identity on every non-NaN code
     assert np.array_equal(oracle.e4m3_encode(got[ok]), codes[ok])
+
+
+def _torch_e5m2(y: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(y, np.float32)).clamp(-57344.0, 57344.0)
+    return t.to(torch.float8_e5m2).view(torch.uint8).numpy()
+
+
+def test_e5m2_encode_exhaustive_meaningful_range():
+    # every positive fp32 pattern from 2^-18 up to 2^17: all subnormal (step
+    # 2^-16) and normal E5M2 rounding decisions, the ties, and saturation
+    # above 57344 (the cast is clamped first, torch's own cast overflows)
+    _exhaustive(oracle.e5m2_encode_bits_range, _torch_e5m2, 2.0 ** -18, 2.0 ** 17)
+
+
+def test_e5m2_encode_sampled_everywhere_and_specials():
+    rng = np.random.default_rng(17)
+    bits = rng.integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    y = bits.view(np.float32)
+    got = oracle.e5m2_encode(y)
+    fin = np.isfinite(y)
+    assert np.array_equal(got[fin], _torch_e5m2(y[fin]))
+    nan = np.isnan(y)
+    assert np.array_equal(got[nan], np.where(np.signbit(y[nan]), 0xFF, 0x7F).astype(np.uint8))
+    sp = np.array([np.inf, -np.inf, 0.0, -0.0, 57344.0, 59391.0, 59392.0, -65536.0, 2.0 ** -17,
+                   1.5 * 2.0 ** -16, 2.0 ** -16, 2.0 ** -14, 1.0, 1e-30], np.float32)
+    assert list(oracle.e5m2_encode(sp)) == [0x7B, 0xFB, 0x00, 0x80, 0x7B, 0x7B, 0x7B, 0xFB, 0x00,
+                                            0x02, 0x01, 0x04, 0x3C, 0x00]
+
+
+def test_e5m2_decode_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.e5m2_decode(codes)
+    exp = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float32).numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(exp)) and np.isnan(got).sum() == 6
+    ok = ~np.isnan(exp)
+    assert np.array_equal(got[ok].view(np.uint32), exp[ok].view(np.uint32))  # incl. -0 and inf
+    fin = ok & np.isfinite(exp)
+    assert np.array_equal(oracle.e5m2_encode(got[fin]), codes[fin])
 
 
 def _torch_bf16(y):
@@ -296,6 +344,9 @@ def test_fp8_scale_is_float32_division():
     got = np.array([oracle.fp8_scale(float(x)) for x in a], np.float32)
     assert np.array_equal(got.view(np.uint32), (a / np.float32(448.0)).view(np.uint32))
     assert oracle.fp8_scale(0.0) == 1.0
+    got5 = np.array([oracle.e5m2_scale(float(x)) for x in a], np.float32)
+    assert np.array_equal(got5.view(np.uint32), (a / np.float32(57344.0)).view(np.uint32))
+    assert oracle.e5m2_scale(0.0) == 1.0
 
 
 # ------------------------------------------------------------------ fp8 serde
@@ -378,6 +429,119 @@ def test_fp8_zero_group_and_signed_zero():
     assert (q[0, :, ::2] == 0x80).all() and (q[0, :, 1::2] == 0).all() and (q[1] == 0).all()
 
 
+# ------------------------------------------- e5m2 and asymmetric K16/V8 formats
+
+_PARTS = {oracle.FMT_BF16: ("bf16", "bf16"), oracle.FMT_FP8: ("e4m3", "e4m3"),
+          oracle.FMT_FP8_E5M2: ("e5m2", "e5m2"), oracle.FMT_K16_V8: ("bf16", "e4m3")}
+_FMAX = {"e4m3": np.float32(448.0), "e5m2": np.float32(57344.0)}
+_CAST = {"e4m3": _torch_e4m3, "e5m2": _torch_e5m2}
+_VIEW = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}
+# closed-form round-trip bound of a quantised part: half a unit in the last
+# place of the fp8 significand (2^-4 for 3 mantissa bits, 2^-3 for 2),
+# widened by the fp32 product and the bf16 rounding
+_BOUND = {k: (1 + 2.0 ** -m) * (1 + 2.0 ** -24) * (1 + 2.0 ** -8) - 1 for k, m in (("e4m3", 4), ("e5m2", 3))}
+
+
+def _numpy_store_any(arr, bt, s, e, C, fmt):
+    """Independent formulation of a format's chunk bytes: whole pages gathered
+    with numpy, each (layer, K/V) part appended in order -- raw bf16 bytes, or
+    fp8 codes from numpy's amax, a float32 division and the torch cast --
+    then the float32 scales of the quantised parts."""
+    L, E = arr.shape[0], arr.shape[-1]
+    rows = arr[:, :, np.asarray(bt, np.int64)].reshape(L, 2, -1, E)
+    out = []
+    for c0 in range(0, e - s, C):
+        g = rows[:, :, s + c0:min(s + c0 + C, e)]
+        parts, scales = [], []
+        for l in range(L):
+            for kv in range(2):
+                kind = _PARTS[fmt][kv]
+                if kind == "bf16":
+                    parts.append(np.ascontiguousarray(g[l, kv]).view(np.uint8).ravel())
+                    continue
+                x = (g[l, kv].astype(np.uint32) << 16).view(np.float32)
+                amax = np.abs(x).max()
+                scale = np.float32(1.0) if amax == 0 else np.float32(amax / _FMAX[kind])
+                parts.append(_CAST[kind]((x / scale).ravel()))
+                scales.append(scale)
+        out.append(np.concatenate(parts + [np.array(scales, np.float32).view(np.uint8)]))
+    return out
+
+
+@pytest.mark.parametrize("fmt", [oracle.FMT_BF16, oracle.FMT_FP8, oracle.FMT_FP8_E5M2, oracle.FMT_K16_V8])
+def test_store_any_format_matches_numpy_formulation(fmt):
+    w = wl.custom("anyfmt", 73, 3, 2, 32, 96, [(0, 600), (256, 531)], outliers=4)
+    arr, pool = _pool(w)
+    for sq in w.seqs:
+        ch = oracle.alloc_chunks(pool, sq.tok_start, sq.tok_end, fmt, fill=0xEE)
+        assert oracle.store(pool, sq.block_table, sq.tok_start, sq.tok_end, ch, fmt) == 0
+        exp = _numpy_store_any(arr, sq.block_table, sq.tok_start, sq.tok_end, 256, fmt)
+        assert len(ch) == len(exp)
+        for got, e in zip(ch, exp):
+            assert got.size == e.size and np.array_equal(got, e)
+
+
+def test_chunk_bytes_of_every_format_from_the_layout():
+    # L layers x (K + V) sections of n*E elements at each part's width, plus a
+    # float32 scale per quantised part and layer
+    pool = oracle.Pool(32, 8, 128, 16, 256, 1, [np.zeros(16 * 1024, np.uint16)] * 32,
+                       [np.zeros(16 * 1024, np.uint16)] * 32)
+    for n in (256, 16, 1):
+        ne = n * 1024 * 32
+        assert oracle.chunk_bytes(pool, n, oracle.FMT_BF16) == ne * 4
+        assert oracle.chunk_bytes(pool, n, oracle.FMT_FP8) == ne * 2 + 32 * 2 * 4
+        assert oracle.chunk_bytes(pool, n, oracle.FMT_FP8_E5M2) == ne * 2 + 32 * 2 * 4
+        assert oracle.chunk_bytes(pool, n, oracle.FMT_K16_V8) == ne * 3 + 32 * 4
+    assert oracle.chunk_bytes(pool, 256, 9) == -1
+
+
+@pytest.mark.parametrize("fmt", [oracle.FMT_FP8, oracle.FMT_FP8_E5M2, oracle.FMT_K16_V8])
+def test_retrieve_any_format_matches_numpy_formulation_and_bounds(fmt):
+    w = wl.custom("anyrt", 75, 2, 2, 64, 64, [(0, 520)], outliers=4)
+    arr, pool = _pool(w)
+    orig = arr.copy()
+    sq = w.seqs[0]
+    ch = oracle.alloc_chunks(pool, 0, 520, fmt)
+    assert oracle.store(pool, sq.block_table, 0, 520, ch, fmt) == 0
+    arr[...] = 0
+    assert oracle.retrieve(pool, sq.block_table, 0, 520, sq.hit_mask, ch, fmt) == 520
+    L, E = w.num_layers, w.width
+    slots = _slots_of(w, sq, 520)
+    got = arr.reshape(L, 2, -1, E)[:, :, slots]
+    x = (orig.reshape(L, 2, -1, E)[:, :, slots].astype(np.uint32) << 16).view(np.float32)
+    at = 0
+    for c, buf in enumerate(ch):
+        n_c = oracle.chunk_tokens(0, 520, 256, c)
+        kinds = _PARTS[fmt]
+        widths = [2 if k == "bf16" else 1 for k in kinds]
+        payload = L * n_c * E * sum(widths)
+        scales = buf[payload:].view(np.float32)
+        off, si = 0, 0
+        for l in range(L):
+            for kv in range(2):
+                nb = n_c * E * widths[kv]
+                sec = buf[off:off + nb]
+                off += nb
+                g = got[l, kv, at:at + n_c]
+                xo = x[l, kv, at:at + n_c].astype(np.float64)
+                if kinds[kv] == "bf16":
+                    assert np.array_equal(g, sec.view(np.uint16).reshape(n_c, E))
+                    assert np.array_equal(g, orig.reshape(L, 2, -1, E)[l, kv, slots[at:at + n_c]])
+                    continue
+                sc = scales[si]
+                si += 1
+                d = torch.from_numpy(sec.copy()).view(_VIEW[kinds[kv]]).to(torch.float32).numpy()
+                exp = _torch_bf16((d * sc).astype(np.float32)).reshape(n_c, E)
+                assert np.array_equal(g, exp)
+                xr = (g.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                floor = {"e4m3": 2.0 ** -6, "e5m2": 2.0 ** -14}[kinds[kv]] * float(sc)
+                rel = np.abs(xr - xo) / np.maximum(np.abs(xo), floor)
+                assert rel.max() <= _BOUND[kinds[kv]], (l, kv, rel.max())
+        assert si == scales.size
+        at += n_c
+    assert _BOUND["e4m3"] <= 0.07 and _BOUND["e5m2"] <= 0.13
+
+
 def test_store_is_deterministic():
     w = wl.custom("det", 91, 2, 2, 32, 64, [(0, 700)], outliers=4)
     arr, pool = _pool(w)
@@ -390,7 +554,7 @@ def test_store_is_deterministic():
         assert all(np.array_equal(x, y) for x, y in zip(a, b))
 
 
-@pytest.mark.parametrize("fmt", [oracle.FMT_BF16, oracle.FMT_FP8])
+@pytest.mark.parametrize("fmt", [oracle.FMT_BF16, oracle.FMT_FP8, oracle.FMT_FP8_E5M2, oracle.FMT_K16_V8])
 def test_layer_by_layer_store_equals_full_store(fmt):
     # storing layers 0..L-1 one call at a time fills the chunks exactly as one
     # full store does, and each call writes only its own layer's sections
@@ -406,12 +570,13 @@ def test_layer_by_layer_store_equals_full_store(fmt):
         assert oracle.store(pool, sq.block_table, 0, 530, part, fmt, layer=l) == 0
         for c, (b, a) in enumerate(zip(before, part)):
             n_c = oracle.chunk_tokens(0, 530, 256, c)
-            bpe = 2 if fmt == oracle.FMT_BF16 else 1
-            sec = 2 * n_c * E * bpe                          # bytes of one layer's K and V sections
+            widths = [2 if k == "bf16" else 1 for k in _PARTS[fmt]]
+            n_q = sum(k != "bf16" for k in _PARTS[fmt])     # scales per layer
+            sec = n_c * E * sum(widths)                      # bytes of one layer's K and V sections
             changed = np.nonzero(b != a)[0]
             payload = w.num_layers * sec
             in_sections = (changed >= l * sec) & (changed < (l + 1) * sec)
-            in_scales = (changed >= payload + 8 * l) & (changed < payload + 8 * (l + 1))
+            in_scales = (changed >= payload + 4 * n_q * l) & (changed < payload + 4 * n_q * (l + 1))
             assert (in_sections | in_scales).all(), "a layer call wrote outside its layer"
     assert all(np.array_equal(a, b) for a, b in zip(full, part))
     assert oracle.store(pool, sq.block_table, 0, 530, part, fmt, layer=4) == -1
