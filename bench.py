@@ -14,8 +14,8 @@ the stream it is launched on.  `cpu_baseline` times the CPU oracle on the
 same workload's data on this host's cores.
 
 Other workloads (`--workload layerwise-8b | layerwise-store-8b |
-llama-70b-style | fp8-8b | offload-8b`) print their own JSON report line; they
-are not the headline.
+llama-70b-style | fp8-8b | e5m2-8b | k16v8-8b | offload-8b`) print their own
+JSON report line; they are not the headline.
 """
 import argparse
 import hashlib
@@ -612,8 +612,14 @@ def layerwise_from_host(args, copy, compute):
             "t_gemm_ms": round(t_gemm, 3), "variants": variants}
 
 
+FORMAT_NAMES = {0: "bf16", 1: "fp8-e4m3-scaled", 2: "fp8-e5m2-scaled", 3: "k16-v8"}
+# chunk bytes per K element and per V element of each format
+PART_BYTES = {0: (2, 2), 1: (1, 1), 2: (1, 1), 3: (2, 1)}
+
+
 def bench_simple(args, name, fmt):
-    """Store + retrieve GB/s for the 70B-style and fp8 workloads."""
+    """Store + retrieve GB/s for the 70B-style workload and the quantised
+    formats (the fp8 workload's inputs)."""
     import torch
     import paged_kv_movement_amd as kvm
     from paged_kv_movement_amd import workloads as wl
@@ -623,13 +629,16 @@ def bench_simple(args, name, fmt):
     stream = torch.cuda.Stream()
     tokens = sum(sq.tok_end - sq.tok_start for sq in w.seqs)
     rtok = sum(hit_tokens(w))
-    elems_st = tokens * w.num_layers * 2 * w.width
-    elems_rt = rtok * w.num_layers * 2 * w.width
-    groups = sum(-(-(sq.tok_end - sq.tok_start) // w.chunk_size) for sq in w.seqs) * w.num_layers * 2
-    if fmt == kvm.FMT_BF16:
-        st_bytes, rt_bytes = 4 * elems_st, 4 * elems_rt
-    else:
-        st_bytes, rt_bytes = 3 * elems_st + 4 * groups, 3 * elems_rt + 4 * groups
+    # per token and part: 2 bytes of bf16 on the pool side, the part's element
+    # size on the chunk side; plus one float32 scale per quantised group
+    part_elems_st = tokens * w.num_layers * w.width
+    part_elems_rt = rtok * w.num_layers * w.width
+    chunks_st = sum(-(-(sq.tok_end - sq.tok_start) // w.chunk_size) for sq in w.seqs)
+    chunks_rt = sum(-(-t // w.chunk_size) for t in hit_tokens(w))
+    n_q = sum(b == 1 for b in PART_BYTES[fmt])
+    per_elem = sum(2 + b for b in PART_BYTES[fmt])
+    st_bytes = per_elem * part_elems_st + 4 * n_q * w.num_layers * chunks_st
+    rt_bytes = per_elem * part_elems_rt + 4 * n_q * w.num_layers * chunks_rt
     for _ in range(args.warmup):
         kvm.store(paged, batch, fmt, stream=stream)
         kvm.retrieve(paged, batch, fmt=fmt, stream=stream)
@@ -640,7 +649,7 @@ def bench_simple(args, name, fmt):
     st, rt = st_bytes / (st_ms / 1e3) / 1e9, rt_bytes / (rt_ms / 1e3) / 1e9
     return {
         "metric": "store / retrieve algorithmic GB/s", "workload": name,
-        "format": "bf16" if fmt == kvm.FMT_BF16 else "fp8-e4m3-scaled",
+        "format": FORMAT_NAMES[fmt],
         "store_ms": round(st_ms, 4), "store_GBps": round(st, 2), "store_pct_hbm_peak": round(100 * st / HBM_PEAK_GBPS, 2),
         "store_tokens_per_s": round(tokens / (st_ms / 1e3), 1),
         "retrieve_ms": round(rt_ms, 4), "retrieve_GBps": round(rt, 2),
@@ -656,6 +665,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3.1-8b",
                     choices=["llama3.1-8b", "layerwise-8b", "layerwise-store-8b", "llama-70b-style", "fp8-8b",
+                             "e5m2-8b", "k16v8-8b",
                              "offload-8b"])
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (used for profiler runs)")
@@ -681,6 +691,10 @@ def main():
         out = bench_offload(args)
     elif args.workload == "llama-70b-style":
         out = bench_simple(args, "llama-70b-style", kvm.FMT_BF16)
+    elif args.workload == "e5m2-8b":
+        out = bench_simple(args, "fp8-8b", kvm.FMT_FP8_E5M2)
+    elif args.workload == "k16v8-8b":
+        out = bench_simple(args, "fp8-8b", kvm.FMT_K16_V8)
     else:
         out = bench_simple(args, "fp8-8b", kvm.FMT_FP8)
     print(json.dumps(out), flush=True)

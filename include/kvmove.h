@@ -41,9 +41,18 @@
  *          of a sequence lives in row t % page_size of page
  *          block_table[t / page_size].
  *   Chunk  A chunk of n tokens (n <= chunk_size; only a sequence's last chunk
- *          is short) is one buffer laid out [num_layers][2][n][H][D] ([blob];
- *          K before V).  bf16: 2 bytes per element.  fp8: 1 byte per element
- *          (OCP E4M3, "fn" variant) followed by float32 scales[num_layers][2].
+ *          is short) is one buffer holding, layer by layer, the layer's K
+ *          section and then its V section, each n rows of H*D elements, then
+ *          one float32 scale per quantised (layer, K/V) part in the same
+ *          order.  Elements are 2 bytes (bf16, copied bit for bit) or 1 byte
+ *          (fp8) according to the format:
+ *            KV_FMT_BF16             K bf16, V bf16: exactly the blob
+ *                                    [num_layers][2][n][H][D] of [blob];
+ *            KV_FMT_FP8_E4M3_SCALED  K and V OCP E4M3 ("fn"), scales [L][2];
+ *            KV_FMT_FP8_E5M2_SCALED  K and V OCP E5M2, scales [L][2];
+ *            KV_FMT_K16_V8           K bf16, V E4M3, scales [L] ([serde]
+ *                                    section "7.3" names this asymmetric
+ *                                    K16/V8 serde).
  *          kv_chunk_bytes() gives the exact size.
  *
  * Where chunks live: a chunk buffer is either device memory or pinned host
@@ -57,11 +66,14 @@
  * this path is measured against.  Pageable host memory is not addressable
  * by the device and must not be passed.
  *
- * fp8 serde: per (chunk, layer, K/V) group, amax = max |x| (a NaN anywhere
- * makes it NaN); scale = amax / 448 in float32 (scale = 1 when amax == 0);
- * q = e4m3(x / scale) with an IEEE float32 division, rounding to nearest-even
- * and saturating at +-448.  Retrieve writes bf16(float(q) * scale), the
- * product in float32 and the bf16 rounding to nearest-even.
+ * fp8 serde: per quantised (chunk, layer, K/V) group, amax = max |x| (a NaN
+ * anywhere makes it NaN); scale = amax / fmax in float32 with fmax = 448
+ * (E4M3) or 57344 (E5M2), and scale = 1 when amax == 0; q = fp8(x / scale)
+ * with an IEEE float32 division, rounding to nearest-even and saturating at
+ * +-fmax (infinity too).  Retrieve writes bf16(float(q) * scale), the product
+ * in float32 and the bf16 rounding to nearest-even.  [serde] section "7.1"
+ * casts to e4m3 (default) or e5m2 without a scale; the scale is this
+ * library's addition.
  *
  * Ownership: every buffer is allocated and freed by the caller.  The library
  * allocates nothing and keeps no state between calls except a per-device
@@ -101,7 +113,9 @@ typedef enum {
 
 typedef enum {
     KV_FMT_BF16 = 0,            /* bf16 copied bit for bit ("naive" serde) */
-    KV_FMT_FP8_E4M3_SCALED = 1  /* e4m3 bytes + one float32 scale per (layer, K/V) */
+    KV_FMT_FP8_E4M3_SCALED = 1, /* e4m3 bytes + one float32 scale per (layer, K/V) */
+    KV_FMT_FP8_E5M2_SCALED = 2, /* e5m2 bytes + one float32 scale per (layer, K/V) */
+    KV_FMT_K16_V8 = 3           /* K bf16, V e4m3 bytes + one float32 scale per layer */
 } kv_fmt;
 
 /* The engine's paged pool.  All pointers are caller-owned. */

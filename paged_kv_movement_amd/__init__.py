@@ -23,11 +23,13 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["FMT_BF16", "FMT_FP8", "KvError", "Paged", "Seq", "Batch", "store", "store_layer",
+__all__ = ["FMT_BF16", "FMT_FP8", "FMT_FP8_E5M2", "FMT_K16_V8", "KvError", "Paged", "Seq", "Batch", "store", "store_layer",
            "retrieve", "retrieve_layer", "take_faults", "copy_bytes", "library_path", "load"]
 
-FMT_BF16 = 0
-FMT_FP8 = 1
+FMT_BF16 = 0          # K and V bf16, copied bit for bit
+FMT_FP8 = 1           # K and V e4m3 + one float32 scale per (layer, K/V)
+FMT_FP8_E5M2 = 2      # K and V e5m2 + one float32 scale per (layer, K/V)
+FMT_K16_V8 = 3        # K bf16, V e4m3 + one float32 scale per layer
 
 KV_OK, KV_EINVAL, KV_ERANGE, KV_EHIP = 0, -1, -2, -3
 

@@ -10,16 +10,23 @@
 //
 //   move_bf16<kToChunk>  work unit = (sequence, chunk, layer, K/V, page): a
 //                        page's rows are contiguous in the pool and the same
-//                        rows are contiguous in the chunk ([L][2][n][H*D]
-//                        layout), so a unit is one contiguous copy of
-//                        rows*H*D*2 bytes (32 KiB for a full page at the
-//                        Llama-3.1-8B shape).  Each unit is cut into tiles of
-//                        kBlock*kVpt 16-byte vectors, one workgroup per tile,
-//                        and consecutive tiles are kept on one XCD.
-//   store_fp8            one workgroup per (sequence, chunk, layer, K/V)
-//                        group: pass 1 takes the group's absolute maximum,
-//                        pass 2 re-reads, divides by the scale, encodes e4m3.
-//   retrieve_fp8         page units as move_bf16, decoding e4m3 and scaling.
+//                        rows are contiguous in the chunk (each layer holds
+//                        its K section, then its V section, of n rows), so a
+//                        unit is one contiguous copy of rows*H*D*2 bytes
+//                        (32 KiB for a full page at the Llama-3.1-8B shape).
+//                        Each unit is cut into tiles of kBlock*kVpt 16-byte
+//                        vectors, one workgroup per tile, and consecutive
+//                        tiles are kept on one XCD.
+//   store_fp8_onchip,    one workgroup per (sequence, chunk, layer, K/V)
+//   store_fp8            group: the group's absolute maximum, then every
+//                        element divided by the scale and encoded (e4m3 or
+//                        e5m2).
+//   retrieve_fp8         page units as move_bf16, decoding and scaling.
+//
+// A chunk format says, for K and for V, how many bytes an element takes (2:
+// bf16 copied, 1: fp8) and how many float32 scales per layer follow the
+// payload; a launch moves the K part, the V part or both, so a format that
+// keeps K in bf16 and V in fp8 runs one kernel of each kind.
 //
 // The method these kernels implement is described on the LMCache paper-notes
 // page ("LMCache: An Efficient KV Cache Layer for Enterprise-Scale LLM
@@ -81,9 +88,31 @@ struct MoveArgs {
     uint32_t n_seqs;
     uint32_t tiles;           // tiles per page unit (tiled movers; 1 otherwise)
     uint32_t total_tiles;     // tiles in this launch; a workgroup may take several
+    uint32_t kv0;             // first part moved: 0 = K, 1 = V
+    uint32_t n_kv;            // parts moved (1 or 2)
+    uint32_t elt_k;           // chunk bytes per K element (2: bf16, 1: fp8)
+    uint32_t elt_v;           // chunk bytes per V element
+    uint32_t n_scaled;        // float32 scales per layer after the payload (quantised parts)
     uint32_t pad_;
     SeqArg seq[kMaxSeqs];
 };
+
+// Byte offset, in a chunk of n_c tokens, of layer l's K (kv = 0) or V
+// (kv = 1) section: layer by layer, K before V, n_c rows of the part's
+// element size each.
+__device__ __forceinline__ uint64_t section_offset(const MoveArgs& a, uint32_t l, uint32_t kv, uint32_t n_c)
+{
+    return ((uint64_t)l * (a.elt_k + a.elt_v) + kv * a.elt_k) * n_c * a.width;
+}
+
+// Byte offset of the float32 scale of quantised part (l, kv): the scales
+// follow the payload in (layer, K/V) order, one per quantised part -- index
+// 2l + kv when both parts are quantised, l when only V is.
+__device__ __forceinline__ uint64_t scale_offset(const MoveArgs& a, uint32_t l, uint32_t kv, uint32_t n_c)
+{
+    return (uint64_t)a.num_layers * (a.elt_k + a.elt_v) * n_c * a.width +
+           (l * a.n_scaled + kv + a.n_scaled - 2) * 4;
+}
 
 __device__ __forceinline__ void raise_fault(unsigned bit)
 {
@@ -122,8 +151,9 @@ struct PageUnit {
     uint32_t s;      // sequence slot in the launch
 };
 
-// Units of a sequence run chunk-major: chunk, then layer, then K/V, then page,
-// so consecutive workgroups fill consecutive bytes of a chunk.
+// Units of a sequence run chunk-major: chunk, then layer, then K/V (the n_kv
+// parts from kv0), then page, so consecutive workgroups fill consecutive
+// bytes of a chunk.
 __device__ __forceinline__ PageUnit locate_page_unit(const MoveArgs& a, uint32_t item)
 {
     PageUnit u;
@@ -142,11 +172,12 @@ __device__ __forceinline__ PageUnit locate_page_unit(const MoveArgs& a, uint32_t
         u.n_c = sq.tail_tokens;
         pages_here = (sq.tail_tokens + a.page_size - 1) / a.page_size;
     }
-    const uint32_t per_layer = 2 * pages_here;
+    const uint32_t per_layer = a.n_kv * pages_here;
     u.l = a.layer0 + local / per_layer;
     const uint32_t r = local % per_layer;
-    u.kv = r >= pages_here ? 1u : 0u;
-    const uint32_t pi = r - u.kv * pages_here;
+    const uint32_t k = r >= pages_here ? 1u : 0u;     // second part (n_kv == 2 only)
+    u.kv = a.kv0 + k;
+    const uint32_t pi = r - k * pages_here;
     u.j0 = pi * a.page_size;
     const uint32_t left = u.n_c - u.j0;
     u.rows = left < a.page_size ? left : a.page_size;

@@ -1,8 +1,9 @@
-// kv_fp8.hpp -- fused fp8 serde movers: gather + quantise to OCP E4M3 with
-// one float32 absmax scale per (chunk, layer, K/V) group, and scatter +
-// dequantise.  The serde framework page ("LMCache 分布式 KV Cache 序列化框架
-// Serde...", section "7.1 fp8 量化") casts every element to e4m3, one byte
-// per element; the per-group scale is this library's addition.
+// kv_fp8.hpp -- fused fp8 serde movers: gather + quantise to OCP E4M3 or
+// E5M2 with one float32 absmax scale per (chunk, layer, K/V) group, and
+// scatter + dequantise.  The serde framework page ("LMCache 分布式 KV Cache
+// 序列化框架 Serde...", section "7.1 fp8 量化") casts every element to e4m3
+// (default) or e5m2, one byte per element; the per-group scale is this
+// library's addition.  kE5M2 selects the encoding throughout.
 #pragma once
 
 #include "kv_common.hpp"
@@ -42,6 +43,33 @@ __device__ __forceinline__ uint32_t e4m3_from_float(float y)
     return sign | (uint32_t)m;
 }
 
+// float -> OCP E5M2 byte, round to nearest-even, saturating at 57344 (also
+// for infinity).  Normal range: bits [30:21] of the binary32 pattern
+// re-biased (exponent bias 127 -> 15), rounded at bit 21; below 2^-14 the
+// value is a multiple of 2^-16, rounded with v_rndne_f32 after an exact
+// scaling by 65536.
+__device__ __forceinline__ uint32_t e5m2_from_float(float y)
+{
+    const uint32_t u = __float_as_uint(y);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return sign | 0x7Fu;                      // NaN
+    if (a >= 0x47600000u) return sign | 0x7Bu;                     // >= 57344, inf: saturate
+    if (a >= 0x38800000u) {                                        // >= 2^-14: normal
+        const uint32_t r = a + 0xFFFFFu + ((a >> 21) & 1u);
+        return sign | ((r >> 21) - (112u << 2));
+    }
+    const float m = __builtin_rintf(__uint_as_float(a) * 65536.0f);  // 0 .. 4
+    return sign | (uint32_t)m;
+}
+
+// Largest finite value of the encoding: the group maximum maps onto it.
+template <bool kE5M2>
+__device__ __forceinline__ float fp8_max() { return kE5M2 ? 57344.0f : 448.0f; }
+
+template <bool kE5M2>
+__device__ __forceinline__ uint32_t fp8_from_float(float y) { return kE5M2 ? e5m2_from_float(y) : e4m3_from_float(y); }
+
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -60,10 +88,10 @@ __device__ __forceinline__ GroupUnit locate_group_unit(const MoveArgs& a, uint32
     g.s = find_seq(a, item);
     const SeqArg& sq = a.seq[g.s];
     const uint32_t local = item - sq.item_begin;
-    g.c = local / a.units_per_chunk;                 // units_per_chunk = 2 * n_layers
+    g.c = local / a.units_per_chunk;                 // units_per_chunk = n_kv * n_layers
     const uint32_t r = local - g.c * a.units_per_chunk;
-    g.l = a.layer0 + (r >> 1);
-    g.kv = r & 1u;
+    g.l = a.layer0 + (a.n_kv == 2 ? r >> 1 : r);
+    g.kv = a.kv0 + (a.n_kv == 2 ? r & 1u : 0u);
     g.n_c = g.c < sq.n_full ? a.chunk_size : sq.tail_tokens;
     return g;
 }
@@ -85,13 +113,13 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* lds)
     return m;
 }
 
-// Quotient x / s for the e4m3 encoder without a division: q0 = x * r with
+// Quotient x / s for the fp8 encoder without a division: q0 = x * r with
 // r = 1/s correctly rounded, one fused multiply-add for the exact residual,
 // one to correct q0 (Markstein's correction).  The result is the correctly
 // rounded quotient except for some |x| <= 2^-25; for groups whose amax is a
 // finite bf16 value >= 2^-4 an exhaustive check over every (amax, x) bf16
-// pair showed the e4m3 code always equals that of the IEEE quotient.  The
-// sign is taken from x, which also keeps -0.
+// pair showed the e4m3 code, and the e5m2 code, always equal those of the
+// IEEE quotient.  The sign is taken from x, which also keeps -0.
 __device__ __forceinline__ float quotient_fast(float x, float s, float r)
 {
     const float q0 = x * r;
@@ -100,13 +128,17 @@ __device__ __forceinline__ float quotient_fast(float x, float s, float r)
     return __uint_as_float((__float_as_uint(q1) & 0x7FFFFFFFu) | (__float_as_uint(x) & 0x80000000u));
 }
 
-// Two floats -> two E4M3 bytes (low 16 bits) with the hardware converter,
+// Two floats -> two fp8 bytes (low 16 bits) with the hardware converter,
 // which rounds to nearest-even and matches the OCP encoding for |y| <= 464
-// (checked against the CPU oracle on every float32 in that range); the
-// quotients fed to it stay below 448.0001 in magnitude.
-__device__ __forceinline__ uint32_t e4m3x2(float a, float b)
+// (E4M3) and |y| < 59392 (E5M2; above, it overflows to infinity instead of
+// saturating) -- checked against the CPU oracle on every float32 in those
+// ranges.  The quotients fed to it stay within the scale's target maximum
+// (448, 57344) plus a few units in the last place.
+template <bool kE5M2>
+__device__ __forceinline__ uint32_t fp8x2(float a, float b)
 {
-    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+    return (kE5M2 ? __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false)
+                  : __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
 }
 
 // amax bits (bf16 magnitude) for which the fast quotient is exact in e4m3
@@ -115,9 +147,11 @@ __device__ __forceinline__ bool fast_quotient_ok(uint32_t amax_bits)
     return amax_bits >= 0x3D80u && amax_bits < 0x7F80u;     // [2^-4, largest finite]
 }
 
-// Eight bf16 values (one 16-byte vector) -> eight e4m3 bytes.  `fast`
-// selects the division-free quotient (exact in e4m3 for the group's amax,
-// see quotient_fast); otherwise IEEE division and the integer encoder.
+// Eight bf16 values (one 16-byte vector) -> eight fp8 bytes.  `fast`
+// selects the division-free quotient (exact in both encodings for the
+// group's amax, see quotient_fast); otherwise IEEE division and the integer
+// encoder.
+template <bool kE5M2>
 __device__ __forceinline__ u32x2 quantize8(const u32x4 x, float scale, float r, bool fast)
 {
     u32x2 q;
@@ -125,17 +159,19 @@ __device__ __forceinline__ u32x2 quantize8(const u32x4 x, float scale, float r, 
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const uint32_t w0 = x[2 * j], w1 = x[2 * j + 1];
-            const uint32_t p0 = e4m3x2(quotient_fast(lo_bf16(w0), scale, r), quotient_fast(hi_bf16(w0), scale, r));
-            const uint32_t p1 = e4m3x2(quotient_fast(lo_bf16(w1), scale, r), quotient_fast(hi_bf16(w1), scale, r));
+            const uint32_t p0 =
+                fp8x2<kE5M2>(quotient_fast(lo_bf16(w0), scale, r), quotient_fast(hi_bf16(w0), scale, r));
+            const uint32_t p1 =
+                fp8x2<kE5M2>(quotient_fast(lo_bf16(w1), scale, r), quotient_fast(hi_bf16(w1), scale, r));
             q[j] = p0 | (p1 << 16);
         }
     } else {   // tiny, infinite or NaN amax
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const uint32_t b0 = e4m3_from_float(lo_bf16(x[2 * j]) / scale);
-            const uint32_t b1 = e4m3_from_float(hi_bf16(x[2 * j]) / scale);
-            const uint32_t b2 = e4m3_from_float(lo_bf16(x[2 * j + 1]) / scale);
-            const uint32_t b3 = e4m3_from_float(hi_bf16(x[2 * j + 1]) / scale);
+            const uint32_t b0 = fp8_from_float<kE5M2>(lo_bf16(x[2 * j]) / scale);
+            const uint32_t b1 = fp8_from_float<kE5M2>(hi_bf16(x[2 * j]) / scale);
+            const uint32_t b2 = fp8_from_float<kE5M2>(lo_bf16(x[2 * j + 1]) / scale);
+            const uint32_t b3 = fp8_from_float<kE5M2>(hi_bf16(x[2 * j + 1]) / scale);
             q[j] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
         }
     }
@@ -154,6 +190,17 @@ __device__ __forceinline__ uint32_t max_magnitude(uint32_t m, const u32x4 x)
     return m;
 }
 
+// Address of 16-byte vector v of a group (token-major) whose pool pages are
+// listed in `pages`, page_vecs vectors per page.  (A plain function: a
+// lambda returning this address-space-qualified pointer inside a template
+// kernel made hipcc 7.2 drop the kernel's host-side launch stub.)
+__device__ __forceinline__ const gvec4* group_vector(uint64_t pool, const int32_t* pages, uint32_t page_vecs,
+                                                     uint64_t page_bytes, uint32_t v)
+{
+    const uint32_t pi = v / page_vecs;
+    return reinterpret_cast<const gvec4*>(pool + (uint64_t)pages[pi] * page_bytes) + (v - pi * page_vecs);
+}
+
 // Single-pass gather + quantise of one (chunk, layer, K/V) group that fits
 // on chip (at most kOnchipMaxVectors 16-byte vectors, kOnchipMaxPages
 // pages): every vector is read from HBM once -- kOnchipRegSlots per thread
@@ -161,6 +208,7 @@ __device__ __forceinline__ uint32_t max_magnitude(uint32_t m, const u32x4 x)
 // maximum is reduced, and the quantised bytes are written from the chip.
 // One workgroup per group; vector v of the group (token-major, 8 elements)
 // is held by thread v % 1024 in slot v / 1024.
+template <bool kE5M2>
 __global__ __launch_bounds__(kOnchipBlock) void store_fp8_onchip(MoveArgs a)
 {
     constexpr int B = kOnchipBlock;
@@ -184,10 +232,6 @@ __global__ __launch_bounds__(kOnchipBlock) void store_fp8_onchip(MoveArgs a)
     const uint64_t page_bytes = (uint64_t)page_vecs * 16;
     const uint32_t total = g.n_c * (a.width / 8);
     const uint32_t wave = threadIdx.x / 64;
-    auto src_of = [&](uint32_t v) {
-        const uint32_t pi = v / page_vecs;
-        return reinterpret_cast<const gvec4*>(pool + (uint64_t)pages[pi] * page_bytes) + (v - pi * page_vecs);
-    };
 
     // LDS slots: direct-to-LDS loads (each lane's 16 bytes land at
     // base + lane * 16, base uniform per wave)
@@ -195,7 +239,7 @@ __global__ __launch_bounds__(kOnchipBlock) void store_fp8_onchip(MoveArgs a)
     for (int k = 0; k < kOnchipLdsSlots; ++k) {
         const uint32_t v = (kOnchipRegSlots + k) * B + threadIdx.x;
         if (v < total)
-            __builtin_amdgcn_global_load_lds(src_of(v),
+            __builtin_amdgcn_global_load_lds(group_vector(pool, pages, page_vecs, page_bytes, v),
                                              (__attribute__((address_space(3))) void*)&lds[k * B + wave * 64],
                                              16, 0, 0);
     }
@@ -204,7 +248,7 @@ __global__ __launch_bounds__(kOnchipBlock) void store_fp8_onchip(MoveArgs a)
     for (int k = 0; k < kOnchipRegSlots; ++k) {
         const uint32_t v = k * B + threadIdx.x;
         reg[k] = u32x4{0u, 0u, 0u, 0u};                   // zero is neutral for the maximum
-        if (v < total) reg[k] = __builtin_nontemporal_load(src_of(v));
+        if (v < total) reg[k] = __builtin_nontemporal_load(group_vector(pool, pages, page_vecs, page_bytes, v));
     }
     uint32_t m1 = 0;
 #pragma unroll
@@ -218,30 +262,30 @@ __global__ __launch_bounds__(kOnchipBlock) void store_fp8_onchip(MoveArgs a)
     }
     const uint32_t amax_bits = block_max_u32<B>(m1, red);
     const float amax = __uint_as_float(amax_bits << 16);
-    const float scale = amax == 0.0f ? 1.0f : amax / 448.0f;
+    const float scale = amax == 0.0f ? 1.0f : amax / fp8_max<kE5M2>();
     const bool fast = fast_quotient_ok(amax_bits);
     const float r = 1.0f / scale;
 
-    gvec2* dst = reinterpret_cast<gvec2*>(chunk + (uint64_t)(g.l * 2 + g.kv) * g.n_c * a.width);
+    gvec2* dst = reinterpret_cast<gvec2*>(chunk + section_offset(a, g.l, g.kv, g.n_c));
 #pragma unroll
     for (int k = 0; k < kOnchipRegSlots; ++k) {
         const uint32_t v = k * B + threadIdx.x;
-        if (v < total) __builtin_nontemporal_store(quantize8(reg[k], scale, r, fast), dst + v);
+        if (v < total) __builtin_nontemporal_store(quantize8<kE5M2>(reg[k], scale, r, fast), dst + v);
     }
 #pragma unroll
     for (int k = 0; k < kOnchipLdsSlots; ++k) {
         const uint32_t v = (kOnchipRegSlots + k) * B + threadIdx.x;
-        if (v < total) __builtin_nontemporal_store(quantize8(lds[k * B + threadIdx.x], scale, r, fast), dst + v);
+        if (v < total)
+            __builtin_nontemporal_store(quantize8<kE5M2>(lds[k * B + threadIdx.x], scale, r, fast), dst + v);
     }
-    if (threadIdx.x == 0)
-        gptr<gf32>(chunk + (uint64_t)a.num_layers * 2 * g.n_c * a.width)[g.l * 2 + g.kv] = scale;
+    if (threadIdx.x == 0) *gptr<gf32>(chunk + scale_offset(a, g.l, g.kv, g.n_c)) = scale;
 }
 
-// Gather + quantise one (chunk, layer, K/V) group of any size into e4m3
+// Gather + quantise one (chunk, layer, K/V) group of any size into fp8
 // bytes + scale, in two passes: pass 1 reads the group's pages and takes
 // max |x|; pass 2 re-reads them (streaming), quantises, and writes 8 bytes
 // per 16-byte input vector.  Used for groups too large for store_fp8_onchip.
-template <int kBlock, int kUnroll>
+template <int kBlock, int kUnroll, bool kE5M2>
 __global__ __launch_bounds__(kBlock) void store_fp8(MoveArgs a)
 {
     __shared__ uint32_t red[kBlock / 64];
@@ -282,12 +326,12 @@ __global__ __launch_bounds__(kBlock) void store_fp8(MoveArgs a)
     }
     const uint32_t amax_bits = block_max_u32<kBlock>(m1, red);
     const float amax = __uint_as_float(amax_bits << 16);
-    const float scale = amax == 0.0f ? 1.0f : amax / 448.0f;
+    const float scale = amax == 0.0f ? 1.0f : amax / fp8_max<kE5M2>();
     const bool fast = fast_quotient_ok(amax_bits);
     const float r = 1.0f / scale;
 
     // pass 2: quantise
-    const uint64_t out = chunk + (uint64_t)(g.l * 2 + g.kv) * g.n_c * a.width;
+    const uint64_t out = chunk + section_offset(a, g.l, g.kv, g.n_c);
     for (uint32_t pi = 0; pi < n_pages; ++pi) {
         const int64_t page = gptr<const gi32>(sq.bt)[first + pi];
         const uint32_t left = g.n_c - pi * a.page_size;
@@ -302,21 +346,20 @@ __global__ __launch_bounds__(kBlock) void store_fp8(MoveArgs a)
                                                             kCpolNt);
 #pragma unroll
             for (int k = 0; k < kUnroll; ++k)
-                __builtin_amdgcn_raw_buffer_store_b64(quantize8(v[k], scale, r, fast), rd,
+                __builtin_amdgcn_raw_buffer_store_b64(quantize8<kE5M2>(v[k], scale, r, fast), rd,
                                                       base / 2 + (k * kBlock + threadIdx.x) * 8, 0, kCpolNt);
         }
     }
-    if (threadIdx.x == 0)
-        gptr<gf32>(chunk + (uint64_t)a.num_layers * 2 * g.n_c * a.width)[g.l * 2 + g.kv] = scale;
+    if (threadIdx.x == 0) *gptr<gf32>(chunk + scale_offset(a, g.l, g.kv, g.n_c)) = scale;
 }
 
-// Scatter + dequantise one tile of one page unit: e4m3 decoded by the
-// hardware converter (exact), times the scale in float32, rounded to bf16 by
-// the hardware converter (round to nearest-even; both checked against the
-// CPU oracle, the latter on every float32).  Tiles are kBlock*kVpt*16 bytes
-// of bf16 output; grid = units * a.tiles, or fewer workgroups each taking
-// a contiguous run of tiles.
-template <int kBlock, int kVpt>
+// Scatter + dequantise one tile of one page unit: fp8 decoded by the
+// hardware converter (exact; all 256 codes of both encodings checked against
+// the CPU oracle), times the scale in float32, rounded to bf16 by the
+// hardware converter (round to nearest-even; checked on every float32).
+// Tiles are kBlock*kVpt*16 bytes of bf16 output; grid = units * a.tiles, or
+// fewer workgroups each taking a contiguous run of tiles.
+template <int kBlock, int kVpt, bool kE5M2>
 __device__ __forceinline__ void retrieve_fp8_tile(const MoveArgs& a, uint32_t b)
 {
     const uint32_t unit = b / a.tiles;
@@ -330,12 +373,11 @@ __device__ __forceinline__ void retrieve_fp8_tile(const MoveArgs& a, uint32_t b)
     const uint64_t chunk = wave_uniform(gptr<const gu64>(a.seq[u.s].chunks)[u.c]);
     if (bad_addr(pool)) { raise_fault(kFaultPool); return; }
     if (bad_addr(chunk)) { raise_fault(kFaultChunk); return; }
-    const float scale = *gptr<const gf32>(chunk + (uint64_t)a.num_layers * 2 * u.n_c * a.width +
-                                          (u.l * 2 + u.kv) * 4);
+    const float scale = *gptr<const gf32>(chunk + scale_offset(a, u.l, u.kv, u.n_c));
     const uint32_t left = out_bytes - lo;
     const uint32_t n = left < kBlock * kVpt * 16 ? left : kBlock * kVpt * 16;
     const __amdgpu_buffer_rsrc_t rs =
-        byte_range(chunk + ((uint64_t)(u.l * 2 + u.kv) * u.n_c + u.j0) * a.width + lo / 2, n / 2);
+        byte_range(chunk + section_offset(a, u.l, u.kv, u.n_c) + (uint64_t)u.j0 * a.width + lo / 2, n / 2);
     const __amdgpu_buffer_rsrc_t rd =
         byte_range(pool + (uint64_t)u.page * a.page_size * a.width * 2 + lo, n);
     u32x2 q[kVpt];
@@ -347,8 +389,10 @@ __device__ __forceinline__ void retrieve_fp8_tile(const MoveArgs& a, uint32_t b)
         u32x4 o;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const auto d0 = __builtin_amdgcn_cvt_pk_f32_fp8(q[k][j], false);   // bytes 0, 1
-            const auto d1 = __builtin_amdgcn_cvt_pk_f32_fp8(q[k][j], true);    // bytes 2, 3
+            const auto d0 = kE5M2 ? __builtin_amdgcn_cvt_pk_f32_bf8(q[k][j], false)    // bytes 0, 1
+                                  : __builtin_amdgcn_cvt_pk_f32_fp8(q[k][j], false);
+            const auto d1 = kE5M2 ? __builtin_amdgcn_cvt_pk_f32_bf8(q[k][j], true)     // bytes 2, 3
+                                  : __builtin_amdgcn_cvt_pk_f32_fp8(q[k][j], true);
             const __bf16 h0 = (__bf16)(d0[0] * scale), h1 = (__bf16)(d0[1] * scale);
             const __bf16 h2 = (__bf16)(d1[0] * scale), h3 = (__bf16)(d1[1] * scale);
             o[2 * j] = __builtin_bit_cast(unsigned short, h0) |
@@ -360,15 +404,15 @@ __device__ __forceinline__ void retrieve_fp8_tile(const MoveArgs& a, uint32_t b)
     }
 }
 
-template <int kBlock, int kVpt>
+template <int kBlock, int kVpt, bool kE5M2>
 __global__ __launch_bounds__(kBlock) void retrieve_fp8(MoveArgs a)
 {
     if (gridDim.x >= a.total_tiles) {         // one workgroup per tile: straight-line code
-        retrieve_fp8_tile<kBlock, kVpt>(a, xcd_contiguous(blockIdx.x, gridDim.x));
+        retrieve_fp8_tile<kBlock, kVpt, kE5M2>(a, xcd_contiguous(blockIdx.x, gridDim.x));
         return;
     }
     const TileRange r = my_tiles(a.total_tiles);
-    for (uint32_t b = r.first; b < r.last; ++b) retrieve_fp8_tile<kBlock, kVpt>(a, b);
+    for (uint32_t b = r.first; b < r.last; ++b) retrieve_fp8_tile<kBlock, kVpt, kE5M2>(a, b);
 }
 
 }  // namespace kvmove

@@ -19,7 +19,7 @@ constexpr int kCopyBlock = 256;
 constexpr int kCopyVpt = 1;
 
 // Gather (kToChunk) or scatter (!kToChunk) of one tile of one page unit,
-// bf16 copied bit for bit.
+// bf16 copied bit for bit (the chunk part moved holds 2-byte elements).
 template <bool kToChunk, int kBlock, int kVpt, int kAuxLoad, int kAuxStore>
 __device__ __forceinline__ void move_tile(const MoveArgs& a, uint32_t b)
 {
@@ -38,8 +38,7 @@ __device__ __forceinline__ void move_tile(const MoveArgs& a, uint32_t b)
     const uint32_t left = nbytes - lo;
     const uint32_t n = left < kBlock * kVpt * 16 ? left : kBlock * kVpt * 16;
     const uint64_t page_addr = pool + (uint64_t)u.page * a.page_size * row_bytes + lo;
-    const uint64_t chunk_addr =
-        chunk + ((uint64_t)(u.l * 2 + u.kv) * u.n_c + u.j0) * row_bytes + lo;
+    const uint64_t chunk_addr = chunk + section_offset(a, u.l, u.kv, u.n_c) + (uint64_t)u.j0 * row_bytes + lo;
     if (kToChunk) copy_tile<kBlock, kVpt, kAuxLoad, kAuxStore>(page_addr, chunk_addr, n);
     else copy_tile<kBlock, kVpt, kAuxLoad, kAuxStore>(chunk_addr, page_addr, n);
 }

@@ -63,9 +63,26 @@ int check_paged(const kv_paged* p)
 
 int check_fmt(int fmt)
 {
-    if (fmt != KV_FMT_BF16 && fmt != KV_FMT_FP8_E4M3_SCALED)
+    if (fmt != KV_FMT_BF16 && fmt != KV_FMT_FP8_E4M3_SCALED && fmt != KV_FMT_FP8_E5M2_SCALED &&
+        fmt != KV_FMT_K16_V8)
         return fail(KV_EINVAL, "unknown format %d", fmt);
     return KV_OK;
+}
+
+// How a format holds K and V in a chunk: bytes per element of each part
+// and float32 scales per layer (one per quantised part).
+struct Layout {
+    uint32_t elt_k, elt_v, n_scaled;
+};
+
+Layout layout_of(int fmt)
+{
+    switch (fmt) {
+    case KV_FMT_BF16: return {2, 2, 0};
+    case KV_FMT_FP8_E4M3_SCALED:
+    case KV_FMT_FP8_E5M2_SCALED: return {1, 1, 2};
+    default: return {2, 1, 1};        // KV_FMT_K16_V8
+    }
 }
 
 int check_seq(const kv_paged* p, const kv_seq* s, int i)
@@ -111,14 +128,39 @@ enum class Unit { Page, Group };
 
 using KernelFn = const void*;
 
+// One kernel launch of an operation: the kernel, its shape, and the K/V
+// parts of the chunk it moves.
+struct Launch {
+    KernelFn kernel;
+    int block;        // threads per workgroup
+    int tile_bytes;   // bytes of page-side data per workgroup (0: one workgroup per unit)
+    Unit unit;
+    uint32_t kv0, n_kv;
+};
+
+// The launches of one store or retrieve: one, or one per part when K and V
+// are held differently.
+struct Plan {
+    Launch part[2];
+    int n;
+};
+
 // Packs up to kMaxSeqs non-empty sequences per launch, keeping every launch
 // under kMaxBlocks workgroups (the kernels index units in 32 bits).  n_tok[i] is the
 // token count moved for sequence i (from its tok_start).
-int launch_units(KernelFn kernel, int block, int tile_bytes, Unit unit, const kv_paged* p,
-                 const kv_seq* seqs, const int64_t* n_tok, int n_seqs, int32_t layer0,
-                 int32_t n_layers, hipStream_t stream, int32_t max_workgroups = 0)
+int launch_units(const Launch& L, const Layout& lay, const kv_paged* p, const kv_seq* seqs,
+                 const int64_t* n_tok, int n_seqs, int32_t layer0, int32_t n_layers, hipStream_t stream,
+                 int32_t max_workgroups = 0)
 {
+    const KernelFn kernel = L.kernel;
+    const int block = L.block, tile_bytes = L.tile_bytes;
+    const Unit unit = L.unit;
     MoveArgs a{};
+    a.kv0 = L.kv0;
+    a.n_kv = L.n_kv;
+    a.elt_k = lay.elt_k;
+    a.elt_v = lay.elt_v;
+    a.n_scaled = lay.n_scaled;
     a.k_pages = reinterpret_cast<uint64_t>(p->k_pages);
     a.v_pages = reinterpret_cast<uint64_t>(p->v_pages);
     a.num_pages = p->num_pages;
@@ -126,8 +168,8 @@ int launch_units(KernelFn kernel, int block, int tile_bytes, Unit unit, const kv
     a.page_size = uint32_t(p->page_size);
     a.chunk_size = uint32_t(p->chunk_size);
     a.pages_per_chunk = uint32_t(p->chunk_size / p->page_size);
-    a.units_per_chunk = unit == Unit::Page ? uint32_t(n_layers) * 2 * a.pages_per_chunk
-                                           : uint32_t(n_layers) * 2;
+    a.units_per_chunk = unit == Unit::Page ? uint32_t(n_layers) * L.n_kv * a.pages_per_chunk
+                                           : uint32_t(n_layers) * L.n_kv;
     a.num_layers = uint32_t(p->num_layers);
     a.layer0 = uint32_t(layer0);
     a.n_layers = uint32_t(n_layers);
@@ -154,8 +196,8 @@ int launch_units(KernelFn kernel, int block, int tile_bytes, Unit unit, const kv
     for (int i = 0; i < n_seqs; ++i) {
         if (n_tok[i] <= 0) continue;
         const int64_t units = unit == Unit::Page
-                                  ? ceil_div(n_tok[i], p->page_size) * n_layers * 2
-                                  : ceil_div(n_tok[i], p->chunk_size) * n_layers * 2;
+                                  ? ceil_div(n_tok[i], p->page_size) * n_layers * L.n_kv
+                                  : ceil_div(n_tok[i], p->chunk_size) * n_layers * L.n_kv;
         if (units > max_units)
             return fail(KV_EINVAL, "seq %d: %lld work units exceed one launch", i, (long long)units);
         if (a.n_seqs == kMaxSeqs || total + units > max_units) {
@@ -177,33 +219,67 @@ int launch_units(KernelFn kernel, int block, int tile_bytes, Unit unit, const kv
     return KV_OK;
 }
 
-struct Launch {
-    KernelFn kernel;
-    int block;        // threads per workgroup
-    int tile_bytes;   // bytes of page-side data per workgroup (0: one workgroup per unit)
-};
-
-Launch gather_launch(const kv_paged* p, int fmt)
+Launch bf16_launch(bool to_chunk, uint32_t kv0, uint32_t n_kv)
 {
-    if (fmt == KV_FMT_BF16)
-        return {reinterpret_cast<KernelFn>(
-                    &move_bf16<true, kMoveBlock, kMoveVpt, kGatherAuxLoad, kGatherAuxStore>),
-                kMoveBlock, kMoveBlock * kMoveVpt * 16};
-    // a whole (chunk, layer, K/V) group on chip when it fits, else two passes
-    const int64_t group_vectors = int64_t(p->chunk_size) * p->num_kv_heads * p->head_dim / 8;
-    if (group_vectors <= int64_t(kOnchipMaxVectors) && p->chunk_size / p->page_size <= kOnchipMaxPages)
-        return {reinterpret_cast<KernelFn>(&store_fp8_onchip), kOnchipBlock, 0};
-    return {reinterpret_cast<KernelFn>(&store_fp8<kFp8StoreBlock, kFp8StoreUnroll>), kFp8StoreBlock, 0};
+    const KernelFn k =
+        to_chunk ? reinterpret_cast<KernelFn>(&move_bf16<true, kMoveBlock, kMoveVpt, kGatherAuxLoad, kGatherAuxStore>)
+                 : reinterpret_cast<KernelFn>(
+                       &move_bf16<false, kMoveBlock, kMoveVpt, kScatterAuxLoad, kScatterAuxStore>);
+    return {k, kMoveBlock, kMoveBlock * kMoveVpt * 16, Unit::Page, kv0, n_kv};
 }
 
-Launch scatter_launch(int fmt)
+// Gather + quantise: a whole (chunk, layer, K/V) group on chip when it fits,
+// else two passes.
+Launch quantise_launch(const kv_paged* p, bool e5m2, uint32_t kv0, uint32_t n_kv)
 {
-    if (fmt == KV_FMT_BF16)
-        return {reinterpret_cast<KernelFn>(
-                    &move_bf16<false, kMoveBlock, kMoveVpt, kScatterAuxLoad, kScatterAuxStore>),
-                kMoveBlock, kMoveBlock * kMoveVpt * 16};
-    return {reinterpret_cast<KernelFn>(&retrieve_fp8<kFp8RetrieveBlock, kFp8RetrieveVpt>),
-            kFp8RetrieveBlock, kFp8RetrieveBlock * kFp8RetrieveVpt * 16};
+    const int64_t group_vectors = int64_t(p->chunk_size) * p->num_kv_heads * p->head_dim / 8;
+    if (group_vectors <= int64_t(kOnchipMaxVectors) && p->chunk_size / p->page_size <= kOnchipMaxPages) {
+        const KernelFn k = e5m2 ? reinterpret_cast<KernelFn>(&store_fp8_onchip<true>)
+                                : reinterpret_cast<KernelFn>(&store_fp8_onchip<false>);
+        return {k, kOnchipBlock, 0, Unit::Group, kv0, n_kv};
+    }
+    const KernelFn k = e5m2 ? reinterpret_cast<KernelFn>(&store_fp8<kFp8StoreBlock, kFp8StoreUnroll, true>)
+                            : reinterpret_cast<KernelFn>(&store_fp8<kFp8StoreBlock, kFp8StoreUnroll, false>);
+    return {k, kFp8StoreBlock, 0, Unit::Group, kv0, n_kv};
+}
+
+Launch dequantise_launch(bool e5m2, uint32_t kv0, uint32_t n_kv)
+{
+    const KernelFn k = e5m2 ? reinterpret_cast<KernelFn>(&retrieve_fp8<kFp8RetrieveBlock, kFp8RetrieveVpt, true>)
+                            : reinterpret_cast<KernelFn>(&retrieve_fp8<kFp8RetrieveBlock, kFp8RetrieveVpt, false>);
+    return {k, kFp8RetrieveBlock, kFp8RetrieveBlock * kFp8RetrieveVpt * 16, Unit::Page, kv0, n_kv};
+}
+
+Plan gather_plan(const kv_paged* p, int fmt)
+{
+    switch (fmt) {
+    case KV_FMT_BF16: return {{bf16_launch(true, 0, 2)}, 1};
+    case KV_FMT_FP8_E4M3_SCALED: return {{quantise_launch(p, false, 0, 2)}, 1};
+    case KV_FMT_FP8_E5M2_SCALED: return {{quantise_launch(p, true, 0, 2)}, 1};
+    default: return {{bf16_launch(true, 0, 1), quantise_launch(p, false, 1, 1)}, 2};   // K16_V8
+    }
+}
+
+Plan scatter_plan(int fmt)
+{
+    switch (fmt) {
+    case KV_FMT_BF16: return {{bf16_launch(false, 0, 2)}, 1};
+    case KV_FMT_FP8_E4M3_SCALED: return {{dequantise_launch(false, 0, 2)}, 1};
+    case KV_FMT_FP8_E5M2_SCALED: return {{dequantise_launch(true, 0, 2)}, 1};
+    default: return {{bf16_launch(false, 0, 1), dequantise_launch(false, 1, 1)}, 2};  // K16_V8
+    }
+}
+
+int run_plan(const Plan& plan, int fmt, const kv_paged* p, const kv_seq* seqs, const int64_t* n_tok,
+             int n_seqs, int32_t layer0, int32_t n_layers, hipStream_t stream, int32_t max_workgroups)
+{
+    const Layout lay = layout_of(fmt);
+    for (int k = 0; k < plan.n; ++k) {
+        const int rc = launch_units(plan.part[k], lay, p, seqs, n_tok, n_seqs, layer0, n_layers, stream,
+                                    max_workgroups);
+        if (rc != KV_OK) return rc;
+    }
+    return KV_OK;
 }
 
 // Shared body of the two retrieve entry points.
@@ -225,9 +301,8 @@ int retrieve(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hi
         const int64_t end = s.tok_start + n_hit * paged->chunk_size;
         n_tok[i] = (end < s.tok_end ? end : s.tok_end) - s.tok_start;
     }
-    const Launch L = scatter_launch(fmt);
-    int rc = launch_units(L.kernel, L.block, L.tile_bytes, Unit::Page, paged, seqs, n_tok, n_seqs,
-                          layer0, n_layers, stream, max_workgroups);
+    int rc = run_plan(scatter_plan(fmt), fmt, paged, seqs, n_tok, n_seqs, layer0, n_layers, stream,
+                      max_workgroups);
     if (rc == KV_OK && out_tokens != nullptr)
         for (int i = 0; i < n_seqs; ++i) out_tokens[i] = n_tok[i];
     if (n_tok != small) delete[] n_tok;
@@ -245,9 +320,9 @@ size_t kv_chunk_bytes(const kv_paged* paged, int64_t n_tokens, int fmt)
         fail(KV_EINVAL, "n_tokens < 0");
         return 0;
     }
-    const int64_t elems = int64_t(paged->num_layers) * 2 * n_tokens * paged->num_kv_heads * paged->head_dim;
-    if (fmt == KV_FMT_BF16) return size_t(elems) * 2;
-    return size_t(elems) + size_t(paged->num_layers) * 2 * sizeof(float);
+    const Layout lay = layout_of(fmt);
+    const int64_t part = int64_t(paged->num_layers) * n_tokens * paged->num_kv_heads * paged->head_dim;
+    return size_t(part) * (lay.elt_k + lay.elt_v) + size_t(paged->num_layers) * lay.n_scaled * sizeof(float);
 }
 
 int64_t kv_num_chunks(const kv_paged* paged, int64_t tok_start, int64_t tok_end)
@@ -269,9 +344,7 @@ int kv_store_chunks(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int f
     int64_t small[64];
     int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
     for (int i = 0; i < n_seqs; ++i) n_tok[i] = seqs[i].tok_end - seqs[i].tok_start;
-    const Launch L = gather_launch(paged, fmt);
-    rc = launch_units(L.kernel, L.block, L.tile_bytes, fmt == KV_FMT_BF16 ? Unit::Page : Unit::Group,
-                      paged, seqs, n_tok, n_seqs, 0, paged->num_layers, stream);
+    rc = run_plan(gather_plan(paged, fmt), fmt, paged, seqs, n_tok, n_seqs, 0, paged->num_layers, stream, 0);
     if (n_tok != small) delete[] n_tok;
     return rc == KV_OK ? ok() : rc;
 }
@@ -289,9 +362,7 @@ int kv_store_layer(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int fm
     int64_t small[64];
     int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
     for (int i = 0; i < n_seqs; ++i) n_tok[i] = seqs[i].tok_end - seqs[i].tok_start;
-    const Launch L = gather_launch(paged, fmt);
-    rc = launch_units(L.kernel, L.block, L.tile_bytes, fmt == KV_FMT_BF16 ? Unit::Page : Unit::Group,
-                      paged, seqs, n_tok, n_seqs, layer, 1, stream, max_workgroups);
+    rc = run_plan(gather_plan(paged, fmt), fmt, paged, seqs, n_tok, n_seqs, layer, 1, stream, max_workgroups);
     if (n_tok != small) delete[] n_tok;
     if (rc != KV_OK) return rc;
     if (layer_done != nullptr) {

@@ -64,8 +64,12 @@ def test_chunk_bytes_and_num_chunks():
     assert L.kv_chunk_bytes(ctypes.byref(p), 256, kvm.FMT_BF16) == 32 * 1024 * 1024
     assert L.kv_chunk_bytes(ctypes.byref(p), 16, kvm.FMT_BF16) == 16 * 32 * 2 * 1024 * 2
     assert L.kv_chunk_bytes(ctypes.byref(p), 256, kvm.FMT_FP8) == 32 * 2 * 256 * 1024 + 32 * 2 * 4
+    assert L.kv_chunk_bytes(ctypes.byref(p), 256, kvm.FMT_FP8_E5M2) == 32 * 2 * 256 * 1024 + 32 * 2 * 4
+    assert L.kv_chunk_bytes(ctypes.byref(p), 256, kvm.FMT_K16_V8) == 32 * 3 * 256 * 1024 + 32 * 4
+    assert L.kv_chunk_bytes(ctypes.byref(p), 16, kvm.FMT_K16_V8) == 32 * 3 * 16 * 1024 + 32 * 4
     assert L.kv_chunk_bytes(ctypes.byref(p), 0, kvm.FMT_BF16) == 0
     assert L.kv_chunk_bytes(ctypes.byref(p), 256, 9) == 0
+    assert L.kv_chunk_bytes(ctypes.byref(p), 256, 4) == 0
     assert L.kv_num_chunks(ctypes.byref(p), 0, 10000) == 40
     assert L.kv_num_chunks(ctypes.byref(p), 0, 10240) == 40
     assert L.kv_num_chunks(ctypes.byref(p), 512, 513) == 1
@@ -88,7 +92,8 @@ def test_store_rejections():
     assert _store(p, [_seq(16, 300, 40)]) == kvm.KV_EINVAL          # start not chunk-aligned
     assert "multiple of chunk_size" in L.kv_last_error().decode()
     assert _store(p, [_seq(0, 641, 40)]) == kvm.KV_ERANGE           # beyond 40 pages of 16
-    assert _store(p, [_seq(0, 100, 40)], fmt=3) == kvm.KV_EINVAL
+    assert _store(p, [_seq(0, 100, 40)], fmt=4) == kvm.KV_EINVAL
+    assert _store(p, [_seq(0, 100, 40)], fmt=-1) == kvm.KV_EINVAL
     assert _store(p, [_seq(300, 200, 40)]) == kvm.KV_EINVAL
     assert _store(p, [_seq(0, 100, 40, bt=0)]) == kvm.KV_EINVAL
     assert _store(p, [_seq(0, 100, 40, chunks=0)]) == kvm.KV_EINVAL

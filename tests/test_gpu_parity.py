@@ -16,8 +16,14 @@ from gpu_util import (say, dev_pool_from_host, host_from_dev_pool, oracle_pool, 
 
 pytestmark = pytest.mark.gpu
 
-BF16, FP8 = kvm.FMT_BF16, kvm.FMT_FP8
+BF16, FP8, E5M2, K16V8 = kvm.FMT_BF16, kvm.FMT_FP8, kvm.FMT_FP8_E5M2, kvm.FMT_K16_V8
 SENTINEL = 0x7E57
+ALL_FMTS = dict(argvalues=[BF16, FP8, E5M2, K16V8], ids=["bf16", "fp8", "e5m2", "k16v8"])
+FP8_FMTS = dict(argvalues=[FP8, E5M2], ids=["fp8", "e5m2"])
+
+
+def _outliers(fmt):
+    return 0 if fmt == BF16 else 2
 
 
 def _roundtrip(w, fmt=BF16, fill=0x0000, masks=None):
@@ -64,10 +70,10 @@ SHAPES = [
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
-@pytest.mark.parametrize("fmt", [BF16, FP8], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", **ALL_FMTS)
 def test_shapes_and_tails(shape, fmt):
     name, seed, L, H, D, pages, ranges, kw = shape
-    w = wl.custom(name, seed, L, H, D, pages, ranges, outliers=2 if fmt == FP8 else 0, **kw)
+    w = wl.custom(name, seed, L, H, D, pages, ranges, outliers=_outliers(fmt), **kw)
     n = _roundtrip(w, fmt=fmt, fill=0x7E57)
     assert n == [e - s for (s, e) in ranges]
 
@@ -77,16 +83,17 @@ def test_many_sequences_span_several_launches():
     ranges = [(0, 1 + 37 * i) for i in range(70)]
     w = wl.custom("many", 111, 2, 2, 32, 6000, ranges)
     _roundtrip(w, fill=0x1234)
-    w8 = wl.custom("many-fp8", 112, 2, 2, 32, 6000, ranges, outliers=2)
-    _roundtrip(w8, fmt=FP8, fill=0x1234)
+    for fmt in (FP8, E5M2, K16V8):
+        w8 = wl.custom("many-q", 112, 2, 2, 32, 6000, ranges, outliers=2)
+        _roundtrip(w8, fmt=fmt, fill=0x1234)
 
 
-@pytest.mark.parametrize("fmt", [BF16, FP8], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", **ALL_FMTS)
 def test_hit_masks_holes_and_misses(fmt):
     ranges = [(0, 1000), (0, 1000), (256, 1000), (0, 1000), (0, 600)]
     masks = [np.array(m, np.uint8) for m in
              ([1, 1, 0, 1], [0, 1, 1, 1], [1, 0, 1], [1, 1, 1, 1], [1, 1, 1])]
-    w = wl.custom("holes", 121, 3, 2, 32, 400, ranges, masks=masks, outliers=2 if fmt == FP8 else 0)
+    w = wl.custom("holes", 121, 3, 2, 32, 400, ranges, masks=masks, outliers=_outliers(fmt))
     n = _roundtrip(w, fmt=fmt, fill=0xA5A5)
     assert n == [512, 0, 256, 1000, 600]
 
@@ -104,7 +111,7 @@ def test_byte_transparency_random_bits():
 
 
 def test_store_is_deterministic_and_leaves_pool():
-    for fmt in (BF16, FP8):
+    for fmt in (BF16, FP8, E5M2, K16V8):
         w = wl.custom("det", 151, 2, 2, 64, 200, [(0, 900)], outliers=4)
         arr = wl.host_pool(w)
         pool, paged, batch, cs = setup_device(w, arr, fmt=fmt, fill=0x11)
@@ -119,11 +126,11 @@ def test_store_is_deterministic_and_leaves_pool():
 
 # ------------------------------------------------------------------ layerwise
 
-@pytest.mark.parametrize("fmt", [BF16, FP8], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", **ALL_FMTS)
 def test_layerwise_on_copy_stream_equals_full(fmt):
     w = wl.custom("layers", 161, 6, 2, 32, 300, [(0, 1000), (256, 530)],
                   masks=[np.array([1, 1, 0, 1], np.uint8), np.array([1, 1], np.uint8)],
-                  outliers=2 if fmt == FP8 else 0)
+                  outliers=_outliers(fmt))
     say("case layerwise fmt", fmt)
     arr = wl.host_pool(w)
     pool, paged, batch, cs = setup_device(w, arr, fmt=fmt)
@@ -173,7 +180,8 @@ def test_layer_event_recorded_without_hits():
 
 # ------------------------------------------------------------------ fp8 specifics
 
-def test_fp8_zero_nan_and_extreme_groups():
+@pytest.mark.parametrize("fmt", **FP8_FMTS)
+def test_fp8_zero_nan_and_extreme_groups(fmt):
     w = wl.custom("fp8-special", 181, 2, 1, 16, 64, [(0, 40)], masks=[np.array([1], np.uint8)])
     arr = wl.host_pool(w)
     bt = w.seqs[0].block_table
@@ -183,12 +191,12 @@ def test_fp8_zero_nan_and_extreme_groups():
     arr[1, 0, bt[2], 2, 7] = 0x7F80             # layer 1 K: +inf
     arr[1, 1, bt[:3]] = 0x0001                  # layer 1 V: smallest subnormal everywhere
     arr[1, 1, bt[0], 0, 0] = 0x8005
-    pool, paged, batch, cs = setup_device(w, arr, fmt=FP8, fill=0xCD)
-    kvm.store(paged, batch, FP8)
+    pool, paged, batch, cs = setup_device(w, arr, fmt=fmt, fill=0xCD)
+    kvm.store(paged, batch, fmt)
     _sync()
     got = host_chunks(cs[0])[0]
-    exp = oracle.alloc_chunks(oracle_pool(w, arr), 0, 40, FP8)
-    assert oracle.store(oracle_pool(w, arr), bt, 0, 40, exp, FP8) == 0
+    exp = oracle.alloc_chunks(oracle_pool(w, arr), 0, 40, fmt)
+    assert oracle.store(oracle_pool(w, arr), bt, 0, 40, exp, fmt) == 0
     exp = exp[0]
     n = 2 * 2 * 40 * w.width
     # NaN results (x / NaN, inf / inf) may differ in sign or payload between
@@ -202,12 +210,12 @@ def test_fp8_zero_nan_and_extreme_groups():
     assert list(np.isnan(se)) == [False, True, False, False]
     assert se[0] == 1.0 and np.isinf(se[2])
     pool.view(torch.int16).fill_(0)
-    kvm.retrieve(paged, batch, fmt=FP8)
+    kvm.retrieve(paged, batch, fmt=fmt)
     _sync()
     got = host_from_dev_pool(pool)
     exp = np.zeros_like(arr)
     op = oracle_pool(w, exp)
-    assert oracle.retrieve(op, bt, 0, 40, [1], host_chunks(cs[0]), FP8) == 40
+    assert oracle.retrieve(op, bt, 0, 40, [1], host_chunks(cs[0]), fmt) == 40
     # NaN codes may differ in payload between implementations: compare NaN-ness there
     nan_g = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
     nan_e = ((exp & 0x7F80) == 0x7F80) & ((exp & 0x7F) != 0)
@@ -215,39 +223,60 @@ def test_fp8_zero_nan_and_extreme_groups():
     assert np.array_equal(got[~nan_g], exp[~nan_e])
 
 
-def test_fp8_roundtrip_error_bound_small():
+@pytest.mark.parametrize("fmt", [FP8, E5M2, K16V8], ids=["fp8", "e5m2", "k16v8"])
+def test_fp8_roundtrip_error_bound_small(fmt):
     w = wl.custom("fp8-err", 191, 4, 2, 64, 400, [(0, 1000), (0, 300)], outliers=4)
     arr = wl.host_pool(w)
-    pool, paged, batch, cs = setup_device(w, arr, fmt=FP8)
-    kvm.store(paged, batch, FP8)
+    pool, paged, batch, cs = setup_device(w, arr, fmt=fmt)
+    kvm.store(paged, batch, fmt)
     orig = pool.clone()
     pool.zero_()
-    kvm.retrieve(paged, batch, fmt=FP8)
+    kvm.retrieve(paged, batch, fmt=fmt)
     _sync()
-    _assert_fp8_bound(w, orig, pool, cs)
+    _assert_fp8_bound(w, orig, pool, cs, fmt)
 
 
-def _assert_fp8_bound(w, orig, pool, chunk_sets):
-    """max |x' - x| / max(|x|, 2^-6 * scale) over every stored element <= the
-    closed-form bound (1 + 2^-4)(1 + 2^-24)(1 + 2^-8) - 1 < 0.07."""
-    bound = (1 + 2.0 ** -4) * (1 + 2.0 ** -24) * (1 + 2.0 ** -8) - 1
+# How each format holds K and V: (element kind of K, of V).  Quantised parts
+# carry a float32 scale each, after the payload, in (layer, K/V) order.
+PARTS = {BF16: ("bf16", "bf16"), FP8: ("e4m3", "e4m3"), E5M2: ("e5m2", "e5m2"), K16V8: ("bf16", "e4m3")}
+# closed-form round-trip bound of a quantised part, and its subnormal floor
+# (smallest normal of the encoding, relative to the scale)
+BOUND = {"e4m3": (1 + 2.0 ** -4) * (1 + 2.0 ** -24) * (1 + 2.0 ** -8) - 1,
+         "e5m2": (1 + 2.0 ** -3) * (1 + 2.0 ** -24) * (1 + 2.0 ** -8) - 1}
+FLOOR = {"e4m3": 2.0 ** -6, "e5m2": 2.0 ** -14}
+
+
+def _assert_fp8_bound(w, orig, pool, chunk_sets, fmt=FP8):
+    """max |x' - x| / max(|x|, floor * scale) over every stored element of a
+    quantised part <= the part's closed-form bound (e4m3: 0.0667, e5m2:
+    0.1295); bf16 parts come back exactly."""
     L, E, P, C = w.num_layers, w.width, w.page_size, w.chunk_size
-    worst = 0.0
+    kinds = PARTS[fmt]
+    n_q = sum(k != "bf16" for k in kinds)
+    worst = {k: 0.0 for k in kinds}
     for sq, (bufs, sizes) in zip(w.seqs, chunk_sets):
         bt = torch.from_numpy(sq.block_table.astype(np.int64)).cuda()
         for c, (b, n_c) in enumerate(zip(bufs, chunk_tokens(w, sq))):
-            scales = b[L * 2 * n_c * E: L * 2 * n_c * E + L * 8].view(torch.float32).view(L, 2)
+            payload = L * n_c * E * sum(2 if k == "bf16" else 1 for k in kinds)
+            scales = b[payload: payload + L * n_q * 4].view(torch.float32).view(L, n_q)
             t = sq.tok_start + c * C + torch.arange(n_c, device="cuda")
             page, row = bt[t // P], t % P
             for l in range(L):
                 for kv in range(2):
-                    x = orig[l, kv].view(-1, P, E)[page, row].float()
-                    y = pool[l, kv].view(-1, P, E)[page, row].float()
-                    floor = (2.0 ** -6) * scales[l, kv].double()
-                    rel = ((y.double() - x.double()).abs() / torch.maximum(x.double().abs(), floor)).max()
-                    worst = max(worst, float(rel))
-    say("fp8 worst relative error", worst, "bound", bound)
-    assert worst <= bound < 0.07
+                    x = orig[l, kv].view(-1, P, E)[page, row]
+                    y = pool[l, kv].view(-1, P, E)[page, row]
+                    if kinds[kv] == "bf16":
+                        assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (l, kv)
+                        continue
+                    x, y = x.double(), y.double()
+                    floor = FLOOR[kinds[kv]] * scales[l, kv if n_q == 2 else 0].double()
+                    rel = ((y - x).abs() / torch.maximum(x.abs(), floor)).max()
+                    worst[kinds[kv]] = max(worst[kinds[kv]], float(rel))
+    say("fp8 worst relative error", worst)
+    for k, v in worst.items():
+        if k != "bf16":
+            assert v <= BOUND[k], (k, v)
+    assert BOUND["e4m3"] < 0.07
 
 
 # ------------------------------------------------------------------ faults
@@ -310,7 +339,8 @@ def test_host_rejections_launch_nothing():
     assert all((b.cpu().numpy() == 0xCD)[: b.numel() - 256].all() for b in cs[0][0])
 
 
-def test_fp8_every_bf16_value_under_many_amax():
+@pytest.mark.parametrize("fmt", **FP8_FMTS)
+def test_fp8_every_bf16_value_under_many_amax(fmt):
     # Each (chunk, K/V) group holds its amax followed by every bf16 value of
     # magnitude <= amax, both signs; the amax values span the whole bf16
     # range, on both sides of 2^-4 (where the kernel switches between its
@@ -337,25 +367,25 @@ def test_fp8_every_bf16_value_under_many_amax():
     t = np.arange(T)
     for kv in range(2):
         arr[0, kv][bt[t // 16], t % 16] = logical[kv]
-    pool, paged, batch, cs = setup_device(w, arr, fmt=FP8, fill=0xCD)
-    kvm.store(paged, batch, FP8)
+    pool, paged, batch, cs = setup_device(w, arr, fmt=fmt, fill=0xCD)
+    kvm.store(paged, batch, fmt)
     _sync()
     assert kvm.take_faults() == 0
-    check_store(w, arr, cs, FP8)
+    check_store(w, arr, cs, fmt)
     pool.view(torch.int16).fill_(0x7E57)
-    assert kvm.retrieve(paged, batch, fmt=FP8) == [T]
+    assert kvm.retrieve(paged, batch, fmt=fmt) == [T]
     _sync()
-    check_retrieve(w, np.full_like(arr, 0x7E57), host_from_dev_pool(pool), cs, FP8, [w.seqs[0].hit_mask])
+    check_retrieve(w, np.full_like(arr, 0x7E57), host_from_dev_pool(pool), cs, fmt, [w.seqs[0].hit_mask])
 
 
-@pytest.mark.parametrize("fmt", [BF16, FP8], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", **ALL_FMTS)
 @pytest.mark.parametrize("cap", [1, 7, 64])
 def test_layerwise_with_capped_grid(fmt, cap):
     # a capped grid makes each workgroup walk a run of tiles; the result must
     # not depend on the cap
     w = wl.custom("capped", 241, 4, 2, 64, 300, [(0, 1000), (256, 531), (0, 17)],
                   masks=[np.array([1, 1, 0, 1], np.uint8), np.array([1, 1], np.uint8),
-                         np.array([1], np.uint8)], outliers=2 if fmt == FP8 else 0)
+                         np.array([1], np.uint8)], outliers=_outliers(fmt))
     say("case capped layerwise", cap, fmt)
     arr = wl.host_pool(w)
     pool, paged, batch, cs = setup_device(w, arr, fmt=fmt)
@@ -415,14 +445,14 @@ def test_copy_bytes_is_a_plain_copy():
     assert (dst[n:] == 7).all()
 
 
-@pytest.mark.parametrize("fmt", [BF16, FP8], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", **ALL_FMTS)
 @pytest.mark.parametrize("cap", [0, 5])
 def test_layerwise_store_equals_full_store(fmt, cap):
     # storing layer by layer on a side stream (each call recording its event)
     # fills the chunks exactly as one full store; before its layer is stored,
     # a chunk section keeps what it held
     w = wl.custom("store-layers", 261, 5, 2, 32, 300, [(0, 1000), (256, 531), (0, 17)],
-                  outliers=2 if fmt == FP8 else 0)
+                  outliers=_outliers(fmt))
     say("case layerwise store", fmt, cap)
     arr = wl.host_pool(w)
     pool, paged, batch, cs = setup_device(w, arr, fmt=fmt, fill=0xC3)
@@ -446,15 +476,17 @@ def test_layerwise_store_equals_full_store(fmt, cap):
     check_store(w, arr, cs, fmt)
 
 
-def test_consumer_waiting_on_layer_event_sees_the_whole_layer():
+@pytest.mark.parametrize("fmt", [BF16, K16V8], ids=["bf16", "k16v8"])
+def test_consumer_waiting_on_layer_event_sees_the_whole_layer(fmt):
     # the compute stream waits on layer l's event and then copies layer l of
     # the pool; the scatter runs on a one-workgroup grid (milliseconds per
-    # layer), so an event recorded too early would let the copy see sentinels
-    w = wl.custom("event-order", 271, 4, 8, 128, 1024, [(0, 4096), (0, 1000)])
-    say("case", w.name)
+    # layer), so an event recorded too early -- for k16v8, after the K launch
+    # but before the V launch -- would let the copy see sentinels
+    w = wl.custom("event-order", 271, 4, 8, 128, 1024, [(0, 4096), (0, 1000)], outliers=_outliers(fmt))
+    say("case", w.name, fmt)
     arr = wl.host_pool(w)
-    pool, paged, batch, cs = setup_device(w, arr)
-    kvm.store(paged, batch)
+    pool, paged, batch, cs = setup_device(w, arr, fmt=fmt)
+    kvm.store(paged, batch, fmt)
     torch.cuda.synchronize()
     pool.view(torch.int16).fill_(SENTINEL)
     copy, compute = torch.cuda.Stream(), torch.cuda.Stream()
@@ -462,7 +494,7 @@ def test_consumer_waiting_on_layer_event_sees_the_whole_layer():
     torch.cuda.synchronize()
     snaps = []
     for l in range(w.num_layers):
-        kvm.retrieve_layer(paged, batch, l, stream=copy, event=events[l], max_workgroups=1)
+        kvm.retrieve_layer(paged, batch, l, fmt=fmt, stream=copy, event=events[l], max_workgroups=1)
         compute.wait_event(events[l])
         with torch.cuda.stream(compute):
             snaps.append(pool[l].clone())
@@ -471,17 +503,17 @@ def test_consumer_waiting_on_layer_event_sees_the_whole_layer():
     for l in range(w.num_layers):
         assert torch.equal(snaps[l].view(torch.int16), pool[l].view(torch.int16)), l
     got = host_from_dev_pool(pool)
-    check_retrieve(w, np.full(got.shape, SENTINEL, np.uint16), got, cs, BF16,
+    check_retrieve(w, np.full(got.shape, SENTINEL, np.uint16), got, cs, fmt,
                    [s.hit_mask for s in w.seqs], copy=False)
 
 
-@pytest.mark.parametrize("fmt", [BF16, FP8], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", [BF16, FP8, K16V8], ids=["bf16", "fp8", "k16v8"])
 def test_store_waiting_on_producer_event_sees_the_layer(fmt):
     # the producer (compute stream) writes layer l of the pool after a GEMM and
     # records its event; the layer store on the copy stream waits on it, so the
     # chunks must hold the produced values, never the sentinel left before
     w = wl.custom("producer-order", 272, 4, 8, 128, 1024, [(0, 4096), (256, 1300)],
-                  outliers=2 if fmt == FP8 else 0)
+                  outliers=_outliers(fmt))
     say("case", w.name, fmt)
     arr = wl.host_pool(w)
     src = dev_pool_from_host(w, arr)
@@ -503,13 +535,13 @@ def test_store_waiting_on_producer_event_sees_the_layer(fmt):
     check_store(w, arr, cs, fmt)
 
 
-@pytest.mark.parametrize("fmt", [BF16, FP8], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", **ALL_FMTS)
 def test_host_chunks_offload_and_onload(fmt):
     # chunk buffers in pinned host memory: the store writes them over PCIe
     # (offload) and the retrieve reads them back (onload), bit for bit as
     # with device chunks; guards after each host buffer stay untouched
     w = wl.custom("host-chunks", 281, 3, 4, 64, 400, [(0, 1000), (256, 1555), (0, 17)],
-                  masks=[[1, 1, 0, 1], [1, 1, 1, 1, 1, 1], [1]], outliers=2 if fmt == FP8 else 0)
+                  masks=[[1, 1, 0, 1], [1, 1, 1, 1, 1, 1], [1]], outliers=_outliers(fmt))
     say("case", w.name, fmt)
     arr = wl.host_pool(w)
     pool, paged, batch, cs = setup_device(w, arr, fmt=fmt, fill=0xCD, where="host")

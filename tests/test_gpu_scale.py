@@ -18,7 +18,7 @@ from gpu_util import (say, host_from_dev_pool, oracle_pool, chunk_tokens, setup_
 
 pytestmark = pytest.mark.gpu
 
-BF16, FP8 = kvm.FMT_BF16, kvm.FMT_FP8
+BF16, FP8, E5M2, K16V8 = kvm.FMT_BF16, kvm.FMT_FP8, kvm.FMT_FP8_E5M2, kvm.FMT_K16_V8
 SENTINEL = 0x7E57
 
 
@@ -105,12 +105,13 @@ def test_full_layerwise_8b_with_compute_stream():
     _free()
 
 
-def test_full_fp8_8b_sampled_chunks_and_bounds():
+@pytest.mark.parametrize("fmt", [FP8, E5M2, K16V8], ids=["fp8", "e5m2", "k16v8"])
+def test_full_fp8_8b_sampled_chunks_and_bounds(fmt):
     w = wl.fp8_8b()
-    say("case", w.name)
+    say("case", w.name, fmt)
     pool = wl.device_pool(w)
-    pool, paged, batch, chunk_sets = setup_device(w, pool=pool, fmt=FP8, fill=0xCD)
-    kvm.store(paged, batch, FP8)
+    pool, paged, batch, chunk_sets = setup_device(w, pool=pool, fmt=fmt, fill=0xCD)
+    kvm.store(paged, batch, fmt)
     sync()
     assert kvm.take_faults() == 0
     arr = host_from_dev_pool(pool)
@@ -120,8 +121,8 @@ def test_full_fp8_8b_sampled_chunks_and_bounds():
         sq = w.seqs[si]
         s = c * w.chunk_size
         e = min(sq.tok_end, s + w.chunk_size)
-        exp = oracle.alloc_chunks(opool, s, e, FP8)
-        assert oracle.store(opool, sq.block_table, s, e, exp, FP8) == 0
+        exp = oracle.alloc_chunks(opool, s, e, fmt)
+        assert oracle.store(opool, sq.block_table, s, e, exp, fmt) == 0
         bufs, sizes = chunk_sets[si]
         got = host_chunks(([bufs[c]], [sizes[c]]))[0]
         assert np.array_equal(got, exp[0]), (si, c, first_diff(got, exp[0]))
@@ -130,7 +131,7 @@ def test_full_fp8_8b_sampled_chunks_and_bounds():
     # and the error bound over every element
     orig = pool.clone()
     pool.zero_()
-    assert kvm.retrieve(paged, batch, fmt=FP8) == [10000] * 8
+    assert kvm.retrieve(paged, batch, fmt=fmt) == [10000] * 8
     sync()
     got_pool = host_from_dev_pool(pool)
     for si, c in samples:
@@ -146,17 +147,17 @@ def test_full_fp8_8b_sampled_chunks_and_bounds():
         part = np.zeros((w.num_layers, 2, len(pages), 16, w.width), np.uint16)
         ptmp = oracle.Pool.from_array(part, w.num_kv_heads, w.head_dim, w.chunk_size)
         padded_bt = np.concatenate([np.zeros(s // 16, np.int32), np.arange(len(pages), dtype=np.int32)])
-        assert oracle.retrieve(ptmp, padded_bt, s, e, [1], ch, FP8) == e - s
+        assert oracle.retrieve(ptmp, padded_bt, s, e, [1], ch, fmt) == e - s
         assert np.array_equal(got_pool[:, :, pages], part), (si, c)
     del got_pool
     from test_gpu_parity import _assert_fp8_bound
-    _assert_fp8_bound(w, orig, pool, chunk_sets)
+    _assert_fp8_bound(w, orig, pool, chunk_sets, fmt)
     # 30-chunk hit mask: rows of chunks >= 30 keep the sentinel, hit rows equal
     # the all-hit result
     full = pool.clone()
     pool.view(torch.int16).fill_(SENTINEL)
     masks = [np.r_[np.ones(30, np.uint8), np.zeros(10, np.uint8)]] * 8
-    assert kvm.retrieve(paged, batch, masks=masks, fmt=FP8) == [7680] * 8
+    assert kvm.retrieve(paged, batch, masks=masks, fmt=fmt) == [7680] * 8
     sync()
     for sq in w.seqs:
         bt = torch.from_numpy(sq.block_table.astype(np.int64)).cuda()
