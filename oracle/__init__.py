@@ -27,6 +27,7 @@ FMT_BF16 = 0          # K and V bf16
 FMT_FP8 = 1           # K and V e4m3, one float32 scale per (layer, K/V)
 FMT_FP8_E5M2 = 2      # K and V e5m2, one float32 scale per (layer, K/V)
 FMT_K16_V8 = 3        # K bf16, V e4m3, one float32 scale per layer
+FMT_CACHEGEN = 4      # CacheGen symbols u8 [L][2][n][E], then float32 max1 [L][2][n]
 
 _lib = None
 
@@ -75,6 +76,8 @@ def _bind(L):
         "kvo_hit_chunks": (i64, [vp, i64]),
         "kvo_store": (ctypes.c_int, [P, vp, i64, i64, i64, vp, ctypes.c_int, i32]),
         "kvo_retrieve": (i64, [P, vp, i64, i64, i64, vp, vp, ctypes.c_int, i32]),
+        "kvo_store_cachegen": (ctypes.c_int, [P, vp, i64, i64, i64, vp, vp, vp]),
+        "kvo_retrieve_cachegen": (i64, [P, vp, i64, i64, i64, vp, vp, vp, vp]),
         "kvo_e4m3_encode": (u8, [f32]),
         "kvo_e4m3_decode": (f32, [u8]),
         "kvo_bf16_from_float": (ctypes.c_uint16, [f32]),
@@ -185,6 +188,30 @@ def retrieve(pool: Pool, block_table, s: int, e: int, mask, chunks, fmt: int = F
     ptrs = _chunk_ptrs(chunks)
     return int(lib().kvo_retrieve(ctypes.byref(pool.c), _ptr(bt), bt.size, s, e,
                                   _ptr(m) if m.size else None, ptrs, fmt, layer))
+
+
+def _bins(b, n):
+    a = np.ascontiguousarray(b, dtype=np.int32)
+    assert a.size == n
+    return a
+
+
+def store_cachegen(pool: Pool, block_table, s: int, e: int, chunks, key_bins, value_bins) -> int:
+    """CacheGen quantiser: gather + quantise [s, e) into ``chunks`` (from
+    alloc_chunks(..., FMT_CACHEGEN)).  Returns 0 or -1."""
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    kb, vb = _bins(key_bins, pool.num_layers), _bins(value_bins, pool.num_layers)
+    return int(lib().kvo_store_cachegen(ctypes.byref(pool.c), _ptr(bt), bt.size, s, e, _chunk_ptrs(chunks),
+                                        _ptr(kb), _ptr(vb)))
+
+
+def retrieve_cachegen(pool: Pool, block_table, s: int, e: int, mask, chunks, key_bins, value_bins) -> int:
+    """Dequantise + scatter the leading hit chunks.  Returns tokens or -1."""
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    m = np.ascontiguousarray(mask if mask is not None else [], dtype=np.uint8)
+    kb, vb = _bins(key_bins, pool.num_layers), _bins(value_bins, pool.num_layers)
+    return int(lib().kvo_retrieve_cachegen(ctypes.byref(pool.c), _ptr(bt), bt.size, s, e,
+                                           _ptr(m) if m.size else None, _chunk_ptrs(chunks), _ptr(kb), _ptr(vb)))
 
 
 def e4m3_encode(y) -> np.ndarray:

@@ -96,6 +96,11 @@ static int64_t scale_offset(const kvo_pool* p, int fmt, int l, int kv, int64_t n
  * the layout alone, with no slack): the sections plus the scales. */
 int64_t kvo_chunk_bytes(const kvo_pool* p, int64_t n_tokens, int fmt)
 {
+    if (fmt == KVO_FMT_CACHEGEN) {
+        /* one byte per symbol, then one float32 max1 per (layer, K/V, token) */
+        int64_t rows = (int64_t)p->num_layers * 2 * n_tokens;
+        return rows * p->num_kv_heads * p->head_dim + rows * 4;
+    }
     if (!valid_fmt(fmt)) return -1;
     return scale_offset(p, fmt, p->num_layers, 0, n_tokens);
 }
@@ -446,6 +451,137 @@ int64_t kvo_retrieve(const kvo_pool* p, const int32_t* bt, int64_t n_bt,
                             x = kvo_bf16_from_float(prod);
                         }
                         *pool_elem(p, l, kv, row, i) = x;
+                    }
+                }
+            }
+        }
+    }
+    return tokens;
+}
+
+/* ------------------------------------------------- CacheGen quantiser */
+
+/* The CacheGen page (section "2. 量化") quantises K and V, each viewed as
+ * [layers][tokens][channels], layer by layer with that layer's bin count:
+ * MAX = bins / 2 - 1; max1 = max |x| over a token's channels; the symbol is
+ * round(x * (MAX / max1) + MAX), rounded half to even as torch.round does,
+ * and max1 is kept for the inverse (q - MAX) / MAX * max1.  All arithmetic
+ * in float32, one rounding per operation.  Readings: an all-zero row
+ * (max1 == 0) gives every element the symbol MAX (the division by zero has
+ * no value there); a NaN from the arithmetic also gives MAX. */
+static int cachegen_max(const int32_t* bins, int l)
+{
+    return bins[l] / 2 - 1;
+}
+
+static int check_bins(const kvo_pool* p, const int32_t* key_bins, const int32_t* value_bins)
+{
+    if (key_bins == NULL || value_bins == NULL) return -1;
+    for (int l = 0; l < p->num_layers; l++) {
+        if (key_bins[l] < 4 || key_bins[l] > 129) return -1;
+        if (value_bins[l] < 4 || value_bins[l] > 129) return -1;
+    }
+    return 0;
+}
+
+/* Chunk of n_c tokens: symbols u8 [L][2][n_c][width], then float32
+ * max1 [L][2][n_c]. */
+static int64_t cg_row(const kvo_pool* p, int l, int kv, int64_t n_c, int64_t j)
+{
+    return ((int64_t)l * 2 + kv) * n_c + j;
+}
+
+int kvo_store_cachegen(const kvo_pool* p, const int32_t* bt, int64_t n_bt,
+                       int64_t s, int64_t e, uint8_t* const* chunks,
+                       const int32_t* key_bins, const int32_t* value_bins)
+{
+    if (check_args(p, bt, n_bt, s, e, KVO_FMT_BF16) != 0) return -1;
+    if (check_bins(p, key_bins, value_bins) != 0) return -1;
+    int64_t width = (int64_t)p->num_kv_heads * p->head_dim;
+    int64_t n_chunks = kvo_num_chunks(s, e, p->chunk_size);
+    for (int64_t c = 0; c < n_chunks; c++) {
+        if (chunks[c] == NULL) return -1;
+    }
+    for (int64_t c = 0; c < n_chunks; c++) {
+        int64_t n_c = kvo_chunk_tokens(s, e, p->chunk_size, c);
+        int64_t t0 = s + c * p->chunk_size;
+        uint8_t* buf = chunks[c];
+        uint8_t* max_area = buf + (int64_t)p->num_layers * 2 * n_c * width;
+        for (int l = 0; l < p->num_layers; l++) {
+            for (int kv = 0; kv < 2; kv++) {
+                int MAX = cachegen_max(kv == 0 ? key_bins : value_bins, l);
+                for (int64_t j = 0; j < n_c; j++) {
+                    int64_t row = kvo_slot(bt, p->page_size, t0 + j);
+                    float max1 = 0.0f;
+                    int saw_nan = 0;
+                    for (int64_t i = 0; i < width; i++) {
+                        float x = kvo_float_from_bf16(*pool_elem(p, l, kv, row, i));
+                        if (isnan(x)) saw_nan = 1;
+                        else if (fabsf(x) > max1) max1 = fabsf(x);
+                    }
+                    if (saw_nan) max1 = NAN;
+                    float factor = max1 == 0.0f ? 0.0f : (float)MAX / max1;
+                    uint8_t* out = buf + cg_row(p, l, kv, n_c, j) * width;
+                    for (int64_t i = 0; i < width; i++) {
+                        float x = kvo_float_from_bf16(*pool_elem(p, l, kv, row, i));
+                        float scaled = x * factor;              /* binary32 product */
+                        float y = scaled + (float)MAX;          /* binary32 sum */
+                        int q;
+                        if (isnan(y)) q = MAX;
+                        else {
+                            float r = nearbyintf(y);            /* ties to even */
+                            q = r < 0.0f ? 0 : r > 2.0f * MAX ? 2 * MAX : (int)r;
+                        }
+                        out[i] = (uint8_t)q;
+                    }
+                    memcpy(max_area + 4 * cg_row(p, l, kv, n_c, j), &max1, 4);
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+int64_t kvo_retrieve_cachegen(const kvo_pool* p, const int32_t* bt, int64_t n_bt,
+                              int64_t s, int64_t e, const uint8_t* mask, uint8_t* const* chunks,
+                              const int32_t* key_bins, const int32_t* value_bins)
+{
+    if (check_args(p, bt, n_bt, s, e, KVO_FMT_BF16) != 0) return -1;
+    if (check_bins(p, key_bins, value_bins) != 0) return -1;
+    int64_t width = (int64_t)p->num_kv_heads * p->head_dim;
+    int64_t n_chunks = kvo_num_chunks(s, e, p->chunk_size);
+    if (n_chunks > 0 && mask == NULL) return -1;
+    int64_t n_hit = kvo_hit_chunks(mask, n_chunks);
+    int64_t tokens = 0;
+    for (int64_t c = 0; c < n_hit; c++) tokens += kvo_chunk_tokens(s, e, p->chunk_size, c);
+    for (int64_t c = 0; c < n_hit; c++) {
+        if (chunks[c] == NULL) return -1;
+    }
+    int64_t first_page = s / p->page_size;
+    int64_t n_pages = (tokens + p->page_size - 1) / p->page_size;
+    for (int64_t a = 0; a < n_pages; a++) {
+        for (int64_t b = a + 1; b < n_pages; b++) {
+            if (bt[first_page + a] == bt[first_page + b]) return -1;
+        }
+    }
+    for (int64_t c = 0; c < n_hit; c++) {
+        int64_t n_c = kvo_chunk_tokens(s, e, p->chunk_size, c);
+        int64_t t0 = s + c * p->chunk_size;
+        const uint8_t* buf = chunks[c];
+        const uint8_t* max_area = buf + (int64_t)p->num_layers * 2 * n_c * width;
+        for (int l = 0; l < p->num_layers; l++) {
+            for (int kv = 0; kv < 2; kv++) {
+                int MAX = cachegen_max(kv == 0 ? key_bins : value_bins, l);
+                for (int64_t j = 0; j < n_c; j++) {
+                    int64_t row = kvo_slot(bt, p->page_size, t0 + j);
+                    float max1;
+                    memcpy(&max1, max_area + 4 * cg_row(p, l, kv, n_c, j), 4);
+                    const uint8_t* in = buf + cg_row(p, l, kv, n_c, j) * width;
+                    for (int64_t i = 0; i < width; i++) {
+                        float centred = (float)in[i] - (float)MAX;   /* exact */
+                        float unit = centred / (float)MAX;           /* binary32 quotient */
+                        float x = unit * max1;                       /* binary32 product */
+                        *pool_elem(p, l, kv, row, i) = kvo_bf16_from_float(x);
                     }
                 }
             }

@@ -33,6 +33,12 @@
  *    rounded to nearest-even and saturated.
  *  - The asymmetric K16/V8 serde named on the same page (section "7.3":
  *    K kept at 16 bits, V at 8): K copied as bf16, V quantised as scaled e4m3.
+ *  - The CacheGen quantiser (CacheGen page, section "2. 量化"): per layer a
+ *    bin count for K and one for V, MAX = bins / 2 - 1; per token row the
+ *    absolute maximum max1 over its channels; symbol
+ *    q = round(x * (MAX / max1) + MAX), kept with max1; dequantised as
+ *    (q - MAX) / MAX * max1.  Only the quantiser, not the CDF and
+ *    arithmetic coding that follow it on that page.
  *
  * Parity pins (tests marked "not gpu") tie each function to something other
  * than itself: numpy page-gather + reshape formulations, store-then-retrieve
@@ -57,7 +63,8 @@ enum {
     KVO_FMT_BF16 = 0,       /* K bf16, V bf16 */
     KVO_FMT_FP8 = 1,        /* K e4m3, V e4m3, scales [L][2] */
     KVO_FMT_FP8_E5M2 = 2,   /* K e5m2, V e5m2, scales [L][2] */
-    KVO_FMT_K16_V8 = 3      /* K bf16, V e4m3, scales [L] */
+    KVO_FMT_K16_V8 = 3,     /* K bf16, V e4m3, scales [L] */
+    KVO_FMT_CACHEGEN = 4    /* symbols u8 [L][2][n][H*D], then float32 max1 [L][2][n] */
 };
 
 /* The engine's paged pool, in host memory.  For layer l, k[l] and v[l] each
@@ -98,6 +105,17 @@ int kvo_store(const kvo_pool* pool, const int32_t* block_table, int64_t n_bt,
 int64_t kvo_retrieve(const kvo_pool* pool, const int32_t* block_table, int64_t n_bt,
                      int64_t s, int64_t e, const uint8_t* mask,
                      uint8_t* const* chunks, int fmt, int32_t layer);
+
+/* CacheGen quantiser: as kvo_store / kvo_retrieve in format KVO_FMT_CACHEGEN,
+ * with per-layer bin counts key_bins[L] and value_bins[L], each in [4, 129]
+ * (so every symbol 0 .. 2*MAX fits the page's int8).  Rejections as for
+ * kvo_store / kvo_retrieve, plus a bin count out of range. */
+int kvo_store_cachegen(const kvo_pool* pool, const int32_t* block_table, int64_t n_bt,
+                       int64_t s, int64_t e, uint8_t* const* chunks,
+                       const int32_t* key_bins, const int32_t* value_bins);
+int64_t kvo_retrieve_cachegen(const kvo_pool* pool, const int32_t* block_table, int64_t n_bt,
+                              int64_t s, int64_t e, const uint8_t* mask, uint8_t* const* chunks,
+                              const int32_t* key_bins, const int32_t* value_bins);
 
 /* Number formats. */
 uint8_t  kvo_e4m3_encode(float y);       /* OCP E4M3 (fn), RNE, saturating */

@@ -580,3 +580,130 @@ def test_layer_by_layer_store_equals_full_store(fmt):
             assert (in_sections | in_scales).all(), "a layer call wrote outside its layer"
     assert all(np.array_equal(a, b) for a, b in zip(full, part))
     assert oracle.store(pool, sq.block_table, 0, 530, part, fmt, layer=4) == -1
+
+
+# ------------------------------------------------------- CacheGen quantiser
+
+def _torch_cachegen_store(arr, bt, s, e, C, key_bins, value_bins):
+    """The quantiser as the CacheGen page writes it, in torch float32 ops:
+    MAX = bins // 2 - 1 per layer; max1 = amax(|x|) over a token's channels;
+    q = round(x * (MAX / max1) + MAX) (torch.round: half to even).  A zero
+    row takes factor 0 (every symbol MAX)."""
+    L, E = arr.shape[0], arr.shape[-1]
+    rows = arr[:, :, np.asarray(bt, np.int64)].reshape(L, 2, -1, E)
+    out = []
+    for c0 in range(0, e - s, C):
+        g = rows[:, :, s + c0:min(s + c0 + C, e)]
+        syms, maxes = [], []
+        for l in range(L):
+            for kv in range(2):
+                MAX = float((key_bins if kv == 0 else value_bins)[l] // 2 - 1)
+                x = torch.from_numpy((g[l, kv].astype(np.uint32) << 16).view(np.float32).copy())
+                max1 = torch.amax(torch.abs(x), dim=-1, keepdim=True)
+                # MAX is a tensor on the page (indexed by layer), so this is a
+                # tensor / tensor division; a Python float over a tensor would
+                # go through torch's reciprocal-and-multiply instead
+                factor = torch.where(max1 == 0, torch.zeros_like(max1), torch.full_like(max1, MAX) / max1)
+                q = torch.round(x * factor + MAX).clamp(0, 2 * MAX).to(torch.uint8)
+                syms.append(q.numpy().ravel())
+                maxes.append(max1.numpy().ravel())
+        out.append(np.concatenate(syms + [np.concatenate(maxes).astype(np.float32).view(np.uint8)]))
+    return out
+
+
+def _cg_bins(L, seed):
+    rng = np.random.default_rng(seed)
+    return rng.integers(4, 130, size=L).astype(np.int32), rng.integers(4, 130, size=L).astype(np.int32)
+
+
+def test_cachegen_store_matches_torch_formulation():
+    w = wl.custom("cg", 301, 4, 2, 32, 96, [(0, 600), (256, 531)], outliers=4)
+    arr, pool = _pool(w)
+    kb, vb = _cg_bins(w.num_layers, 5)
+    kb[0], vb[0] = 4, 129                                  # both ends of the bin range
+    for sq in w.seqs:
+        ch = oracle.alloc_chunks(pool, sq.tok_start, sq.tok_end, oracle.FMT_CACHEGEN, fill=0xEE)
+        assert oracle.store_cachegen(pool, sq.block_table, sq.tok_start, sq.tok_end, ch, kb, vb) == 0
+        exp = _torch_cachegen_store(arr, sq.block_table, sq.tok_start, sq.tok_end, 256, kb, vb)
+        for got, e in zip(ch, exp):
+            assert got.size == e.size and np.array_equal(got, e)
+
+
+def test_cachegen_layout_symbols_and_extremes():
+    # sizes from the layout; every symbol of layer l lies in [0, 2*MAX_l]; the
+    # element that sets a row's max1 lands on 0 or 2*MAX; a zero row is all MAX
+    w = wl.custom("cgx", 302, 3, 2, 32, 64, [(0, 300)])
+    arr = wl.host_pool(w)
+    bt = w.seqs[0].block_table
+    arr[1, 0, bt[0], 3] = 0                                # layer 1 K, token 3: zero row
+    arr[1, 0, bt[0], 4, ::3] = 0x8000                      # token 4: -0 mixed in
+    _, pool = _pool(w, arr)
+    kb, vb = np.int32([8, 32, 129]), np.int32([4, 16, 64])
+    ch = oracle.alloc_chunks(pool, 0, 300, oracle.FMT_CACHEGEN)
+    L, E = w.num_layers, w.width
+    assert [c.size for c in ch] == [L * 2 * n * E + L * 2 * n * 4 for n in (256, 44)]
+    assert oracle.store_cachegen(pool, bt, 0, 300, ch, kb, vb) == 0
+    n = 256
+    sym = ch[0][:L * 2 * n * E].reshape(L, 2, n, E)
+    mx = ch[0][L * 2 * n * E:].view(np.float32).reshape(L, 2, n)
+    x = (arr.reshape(L, 2, -1, E)[:, :, [oracle.slot(bt, 16, t) for t in range(n)]].astype(np.uint32) << 16).view(np.float32)
+    for l in range(L):
+        for kv, bins in ((0, kb), (1, vb)):
+            MAX = bins[l] // 2 - 1
+            assert sym[l, kv].max() <= 2 * MAX
+            assert np.array_equal(mx[l, kv], np.abs(x[l, kv]).max(axis=1))
+            for j in range(n):
+                if mx[l, kv, j] == 0:
+                    assert (sym[l, kv, j] == MAX).all()
+                    continue
+                i = int(np.argmax(np.abs(x[l, kv, j])))
+                assert sym[l, kv, j, i] == (2 * MAX if x[l, kv, j, i] > 0 else 0)
+    assert mx[1, 0, 3] == 0 and (sym[1, 0, 3] == kb[1] // 2 - 1).all()
+
+
+def test_cachegen_retrieve_matches_torch_and_error_bound():
+    w = wl.custom("cgr", 303, 3, 2, 64, 96, [(0, 700)], masks=[np.array([1, 1, 0], np.uint8)], outliers=4)
+    arr, pool = _pool(w)
+    orig = arr.copy()
+    sq = w.seqs[0]
+    kb, vb = _cg_bins(w.num_layers, 6)
+    ch = oracle.alloc_chunks(pool, 0, 700, oracle.FMT_CACHEGEN)
+    assert oracle.store_cachegen(pool, sq.block_table, 0, 700, ch, kb, vb) == 0
+    arr[...] = 0xA5A5
+    assert oracle.retrieve_cachegen(pool, sq.block_table, 0, 700, sq.hit_mask, ch, kb, vb) == 512
+    L, E = w.num_layers, w.width
+    slots = _slots_of(w, sq, 700)
+    got = arr.reshape(L, 2, -1, E)
+    for c in range(2):                                      # the two hit chunks
+        n = 256
+        sym = ch[c][:L * 2 * n * E].reshape(L, 2, n, E)
+        mx = ch[c][L * 2 * n * E:].view(np.float32).reshape(L, 2, n)
+        rows = slots[c * 256:(c + 1) * 256]
+        for l in range(L):
+            for kv, bins in ((0, kb), (1, vb)):
+                MAX = float(bins[l] // 2 - 1)
+                q = torch.from_numpy(sym[l, kv].astype(np.float32))
+                m1 = torch.from_numpy(mx[l, kv].copy())[:, None]
+                mt = torch.full_like(m1, MAX)               # a tensor, as on the page
+                val = (q - mt) / mt * m1                     # the page's inverse, float32
+                exp = val.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+                g = got[l, kv, rows]
+                assert np.array_equal(g, exp), (c, l, kv)
+                # half a quantisation step, widened by the float32 steps and the bf16 rounding
+                xo = (orig.reshape(L, 2, -1, E)[l, kv, rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                xr = (g.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                bound = mx[l, kv].astype(np.float64)[:, None] * (0.5 / MAX + 2.0 ** -8 + 2.0 ** -20)
+                assert (np.abs(xr - xo) <= bound).all(), (c, l, kv)
+    # rows of the missed chunk keep the sentinel
+    assert (got[:, :, slots[512:]] == 0xA5A5).all()
+
+
+def test_cachegen_rejects_bins_out_of_range():
+    w = wl.custom("cgb", 304, 2, 1, 16, 32, [(0, 40)])
+    _, pool = _pool(w)
+    sq = w.seqs[0]
+    ch = oracle.alloc_chunks(pool, 0, 40, oracle.FMT_CACHEGEN)
+    for kb, vb in (([3, 8], [8, 8]), ([8, 130], [8, 8]), ([8, 8], [8, 2])):
+        assert oracle.store_cachegen(pool, sq.block_table, 0, 40, ch, kb, vb) == -1
+        assert oracle.retrieve_cachegen(pool, sq.block_table, 0, 40, [1], ch, kb, vb) == -1
+    assert oracle.store_cachegen(pool, sq.block_table, 0, 40, ch, [4, 129], [129, 4]) == 0
