@@ -14,8 +14,8 @@ the stream it is launched on.  `cpu_baseline` times the CPU oracle on the
 same workload's data on this host's cores.
 
 Other workloads (`--workload layerwise-8b | layerwise-store-8b |
-llama-70b-style | fp8-8b | e5m2-8b | k16v8-8b | offload-8b`) print their own
-JSON report line; they are not the headline.
+llama-70b-style | fp8-8b | e5m2-8b | k16v8-8b | cachegen-8b | offload-8b`) print
+their own JSON report line; they are not the headline.
 """
 import argparse
 import hashlib
@@ -617,6 +617,44 @@ FORMAT_NAMES = {0: "bf16", 1: "fp8-e4m3-scaled", 2: "fp8-e5m2-scaled", 3: "k16-v
 PART_BYTES = {0: (2, 2), 1: (1, 1), 2: (1, 1), 3: (2, 1)}
 
 
+CACHEGEN_KEY_BINS, CACHEGEN_VALUE_BINS = 32, 16    # bins used for every layer by the benchmark
+
+
+def bench_cachegen(args):
+    """CacheGen quantiser at the 8B shape (the fp8 workload's inputs): store =
+    gather + quantise, retrieve = dequantise + scatter of every chunk."""
+    import torch
+    import paged_kv_movement_amd as kvm
+    from paged_kv_movement_amd import workloads as wl
+
+    w = wl.fp8_8b()
+    pool, paged, batch, arena = setup(w, kvm.FMT_CACHEGEN)
+    stream = torch.cuda.Stream()
+    kb, vb = [CACHEGEN_KEY_BINS] * w.num_layers, [CACHEGEN_VALUE_BINS] * w.num_layers
+    tokens = sum(sq.tok_end - sq.tok_start for sq in w.seqs)
+    rtok = sum(hit_tokens(w))
+    # per element 2 bytes of bf16 and 1 symbol byte; per (layer, K/V, token) one float32 max1
+    st_bytes = tokens * w.num_layers * 2 * (3 * w.width + 4)
+    rt_bytes = rtok * w.num_layers * 2 * (3 * w.width + 4)
+    for _ in range(args.warmup):
+        kvm.store_cachegen(paged, batch, kb, vb, stream=stream)
+        kvm.retrieve_cachegen(paged, batch, kb, vb, stream=stream)
+    reps = max(3, args.steps)
+    st_ms = timed(stream, lambda: kvm.store_cachegen(paged, batch, kb, vb, stream=stream), reps)
+    rt_ms = timed(stream, lambda: kvm.retrieve_cachegen(paged, batch, kb, vb, stream=stream), reps)
+    assert kvm.take_faults() == 0
+    st, rt = st_bytes / (st_ms / 1e3) / 1e9, rt_bytes / (rt_ms / 1e3) / 1e9
+    return {
+        "metric": "store / retrieve algorithmic GB/s", "workload": "cachegen-8b",
+        "format": f"cachegen int8 symbols, key bins {CACHEGEN_KEY_BINS}, value bins {CACHEGEN_VALUE_BINS}",
+        "store_ms": round(st_ms, 4), "store_GBps": round(st, 2), "store_pct_hbm_peak": round(100 * st / HBM_PEAK_GBPS, 2),
+        "store_tokens_per_s": round(tokens / (st_ms / 1e3), 1),
+        "retrieve_ms": round(rt_ms, 4), "retrieve_GBps": round(rt, 2),
+        "retrieve_pct_hbm_peak": round(100 * rt / HBM_PEAK_GBPS, 2),
+        "retrieve_tokens_per_s": round(rtok / (rt_ms / 1e3), 1),
+    }
+
+
 def bench_simple(args, name, fmt):
     """Store + retrieve GB/s for the 70B-style workload and the quantised
     formats (the fp8 workload's inputs)."""
@@ -665,7 +703,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3.1-8b",
                     choices=["llama3.1-8b", "layerwise-8b", "layerwise-store-8b", "llama-70b-style", "fp8-8b",
-                             "e5m2-8b", "k16v8-8b",
+                             "e5m2-8b", "k16v8-8b", "cachegen-8b",
                              "offload-8b"])
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (used for profiler runs)")
@@ -695,6 +733,8 @@ def main():
         out = bench_simple(args, "fp8-8b", kvm.FMT_FP8_E5M2)
     elif args.workload == "k16v8-8b":
         out = bench_simple(args, "fp8-8b", kvm.FMT_K16_V8)
+    elif args.workload == "cachegen-8b":
+        out = bench_cachegen(args)
     else:
         out = bench_simple(args, "fp8-8b", kvm.FMT_FP8)
     print(json.dumps(out), flush=True)

@@ -31,6 +31,8 @@
  *   [blob]   "LMCache 中的 KV Cache 压缩：CacheGen 编解码原理..." (CacheGen
  *            page), section "2. 量化": a chunk's KV blob is shaped
  *            [num_layers, 2, num_tokens, num_heads, head_size].
+ *   [cachegen] the CacheGen page as [blob], section "2. 量化": per-layer bin
+ *            counts, per-token absolute maximum, symbols round(x*MAX/max1+MAX).
  *   [serde]  "LMCache 分布式 KV Cache 序列化框架 Serde..." (serde framework
  *            page), sections "4.2" (exact, layout-only size estimate) and
  *            "7.1 fp8 量化" (fp8 e4m3 cast, one byte per element, lossy).
@@ -115,7 +117,9 @@ typedef enum {
     KV_FMT_BF16 = 0,            /* bf16 copied bit for bit ("naive" serde) */
     KV_FMT_FP8_E4M3_SCALED = 1, /* e4m3 bytes + one float32 scale per (layer, K/V) */
     KV_FMT_FP8_E5M2_SCALED = 2, /* e5m2 bytes + one float32 scale per (layer, K/V) */
-    KV_FMT_K16_V8 = 3           /* K bf16, V e4m3 bytes + one float32 scale per layer */
+    KV_FMT_K16_V8 = 3,          /* K bf16, V e4m3 bytes + one float32 scale per layer */
+    KV_FMT_CACHEGEN_INT8 = 4    /* CacheGen symbols + one float32 max1 per (layer, K/V, token);
+                                   only through the *_cachegen entry points */
 } kv_fmt;
 
 /* The engine's paged pool.  All pointers are caller-owned. */
@@ -201,6 +205,26 @@ int kv_retrieve_layer(const kv_paged* paged, const kv_seq* seqs,
                       const uint8_t* const* hit_mask, int n_seqs, int fmt, int32_t layer,
                       int64_t* out_tokens, int32_t max_workgroups, hipStream_t copy_stream,
                       hipEvent_t layer_done);
+
+/* CacheGen quantiser ([cachegen] section "2. 量化"): store gathers and
+ * quantises every chunk, K and V of every layer, in format
+ * KV_FMT_CACHEGEN_INT8; retrieve dequantises the leading hit chunks and
+ * scatters them (hit rule, out_tokens and errors as kv_retrieve_chunks).
+ * key_bins / value_bins: HOST int32[num_layers], the bin count of each
+ * layer's K and V, each in [4, 129]; MAX = bins / 2 - 1.  For each token row
+ * of H*D elements, max1 = max |x| (float32; a NaN in the row makes it NaN);
+ * symbol q = round-half-even(x * (MAX / max1) + MAX) in float32, one rounding
+ * per operation, kept in [0, 2*MAX] (fits the page's int8), MAX for a zero
+ * row or a NaN; retrieve writes bf16((q - MAX) / MAX * max1).  Chunk of n
+ * tokens: symbols u8 [L][2][n][H*D], then float32 max1 [L][2][n]
+ * (kv_chunk_bytes with KV_FMT_CACHEGEN_INT8).  Limits: num_layers <= 128,
+ * H*D <= 4096.  Only the quantiser: the CDF and arithmetic coding that
+ * follow it on that page are not implemented. */
+int kv_store_chunks_cachegen(const kv_paged* paged, const kv_seq* seqs, int n_seqs, const int32_t* key_bins,
+                             const int32_t* value_bins, hipStream_t stream);
+int kv_retrieve_chunks_cachegen(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask,
+                                int n_seqs, const int32_t* key_bins, const int32_t* value_bins,
+                                int64_t* out_tokens, hipStream_t stream);
 
 /* Message for the last non-OK return on this thread ("" if none). */
 const char* kv_last_error(void);

@@ -23,13 +23,15 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["FMT_BF16", "FMT_FP8", "FMT_FP8_E5M2", "FMT_K16_V8", "KvError", "Paged", "Seq", "Batch", "store", "store_layer",
+__all__ = ["FMT_BF16", "FMT_FP8", "FMT_FP8_E5M2", "FMT_K16_V8", "FMT_CACHEGEN", "KvError", "Paged", "Seq", "Batch",
+           "store", "store_layer", "store_cachegen", "retrieve_cachegen",
            "retrieve", "retrieve_layer", "take_faults", "copy_bytes", "library_path", "load"]
 
 FMT_BF16 = 0          # K and V bf16, copied bit for bit
 FMT_FP8 = 1           # K and V e4m3 + one float32 scale per (layer, K/V)
 FMT_FP8_E5M2 = 2      # K and V e5m2 + one float32 scale per (layer, K/V)
 FMT_K16_V8 = 3        # K bf16, V e4m3 + one float32 scale per layer
+FMT_CACHEGEN = 4      # CacheGen symbols + one float32 max1 per (layer, K/V, token); store_cachegen / retrieve_cachegen
 
 KV_OK, KV_EINVAL, KV_ERANGE, KV_EHIP = 0, -1, -2, -3
 
@@ -91,6 +93,8 @@ def load():
         "kv_store_layer": (ctypes.c_int, [P, S, ctypes.c_int, ctypes.c_int, i32, i32, vp, vp]),
         "kv_retrieve_chunks": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, vp, vp]),
         "kv_retrieve_layer": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, i32, vp, i32, vp, vp]),
+        "kv_store_chunks_cachegen": (ctypes.c_int, [P, S, ctypes.c_int, vp, vp, vp]),
+        "kv_retrieve_chunks_cachegen": (ctypes.c_int, [P, S, vp, ctypes.c_int, vp, vp, vp, vp]),
         "kv_last_error": (ctypes.c_char_p, []),
         "kv_take_faults": (ctypes.c_int, []),
         "kv_copy_bytes": (ctypes.c_int, [vp, vp, ctypes.c_size_t, vp]),
@@ -255,6 +259,37 @@ def store_layer(paged: Paged, seqs, layer: int, fmt: int = FMT_BF16, stream=None
     b = _batch(paged, seqs)
     _check(load().kv_store_layer(ctypes.byref(paged.c), b.arr, b.n, fmt, layer, max_workgroups,
                                  _stream_handle(stream), _event_handle(event, stream)))
+
+
+def _bins(bins, n):
+    """One bin count per layer as a host int32 array."""
+    bins = [int(b) for b in bins]
+    if len(bins) != n:
+        raise KvError(KV_EINVAL, f"need {n} bin counts, got {len(bins)}")
+    return (ctypes.c_int32 * max(1, n))(*bins)
+
+
+def store_cachegen(paged: Paged, seqs, key_bins, value_bins, stream=None) -> None:
+    """CacheGen quantiser: gather + quantise every chunk (kv_store_chunks_cachegen).
+    key_bins / value_bins: one bin count per layer, each in [4, 129]."""
+    b = _batch(paged, seqs)
+    L = paged.c.num_layers
+    _check(load().kv_store_chunks_cachegen(ctypes.byref(paged.c), b.arr, b.n, _bins(key_bins, L),
+                                           _bins(value_bins, L), _stream_handle(stream)))
+
+
+def retrieve_cachegen(paged: Paged, seqs, key_bins, value_bins, masks=None, stream=None) -> list:
+    """Dequantise + scatter the leading hit chunks (kv_retrieve_chunks_cachegen).
+    Returns the tokens made available per sequence."""
+    b = _batch(paged, seqs)
+    if masks is not None:
+        b.set_masks(masks)
+    assert b._mask_ptrs is not None, "hit masks are required"
+    L = paged.c.num_layers
+    _check(load().kv_retrieve_chunks_cachegen(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n,
+                                              _bins(key_bins, L), _bins(value_bins, L), b.out,
+                                              _stream_handle(stream)))
+    return [int(b.out[i]) for i in range(b.n)]
 
 
 def retrieve(paged: Paged, seqs, masks=None, fmt: int = FMT_BF16, stream=None) -> list:

@@ -1,0 +1,184 @@
+// kv_cachegen.hpp -- the CacheGen quantiser fused into the movers: gather +
+// quantise pages into chunk symbols, and dequantise + scatter them back.
+//
+// The CacheGen page ("LMCache 中的 KV Cache 压缩：CacheGen 编解码原理...",
+// section "2. 量化") quantises K and V layer by layer, each layer with its own
+// bin count: MAX = bins / 2 - 1; for every token row, max1 = max |x| over its
+// channels; the symbol is round(x * (MAX / max1) + MAX) and max1 is kept for
+// the inverse (q - MAX) / MAX * max1.  Only the quantiser: the CDF and
+// arithmetic coding that follow it on that page are not part of this path.
+//
+// Chunk of n tokens: symbols u8 [L][2][n][H*D] (the section layout of the
+// 1-byte formats), then float32 max1 [L][2][n].
+//
+// Work unit = page unit as in the bf16 movers (sequence, chunk, layer, K/V,
+// page); one 256-thread workgroup per unit, wave w handling rows w, w+4, ...
+// of the page, a whole row per wave so its maximum is one wave reduction.
+#pragma once
+
+#include "kv_common.hpp"
+
+namespace kvmove {
+
+constexpr int kCgBlock = 256;
+constexpr int kCgWaves = kCgBlock / 64;
+constexpr int kCgMaxLayers = 128;
+constexpr int kCgMaxVpl = 8;            // 16-byte vectors per lane per row: rows up to 4096 elements
+
+struct CgArgs {
+    MoveArgs m;
+    uint8_t qmax[2][kCgMaxLayers];      // MAX = bins / 2 - 1 for K (0) and V (1) of each layer
+};
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t o = __shfl_xor(v, off, 64);
+        v = v > o ? v : o;
+    }
+    return v;
+}
+
+// Largest bf16 magnitude (as bits) of the eight elements of a vector.
+__device__ __forceinline__ uint32_t cg_max_magnitude(uint32_t m, const u32x4 x)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = x[j] & 0x7FFFu, hi = (x[j] >> 16) & 0x7FFFu;
+        m = m > lo ? m : lo;
+        m = m > hi ? m : hi;
+    }
+    return m;
+}
+
+// One symbol: x * factor and + MAX as two float32 operations, rounded half to
+// even, kept in [0, 2 * MAX]; a NaN gives MAX.
+__device__ __forceinline__ uint32_t cg_symbol(float x, float factor, float qmax)
+{
+    const float scaled = x * factor;
+    const float y = scaled + qmax;
+    if (y != y) return (uint32_t)qmax;
+    float r = __builtin_rintf(y);
+    r = r < 0.0f ? 0.0f : r;
+    r = r > 2.0f * qmax ? 2.0f * qmax : r;
+    return (uint32_t)r;
+}
+
+// Eight bf16 values (one 16-byte vector) -> eight symbol bytes.
+__device__ __forceinline__ u32x2 cg_quantise8(const u32x4 x, float factor, float qmax)
+{
+    u32x2 q;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t w0 = x[2 * j], w1 = x[2 * j + 1];
+        q[j] = cg_symbol(__uint_as_float(w0 << 16), factor, qmax) |
+               (cg_symbol(__uint_as_float(w0 & 0xFFFF0000u), factor, qmax) << 8) |
+               (cg_symbol(__uint_as_float(w1 << 16), factor, qmax) << 16) |
+               (cg_symbol(__uint_as_float(w1 & 0xFFFF0000u), factor, qmax) << 24);
+    }
+    return q;
+}
+
+// (q - MAX) / MAX without a division: c = q - MAX is exact; c * r with
+// r = 1/MAX plus one fused multiply-add for the residual and one to correct
+// (Markstein).  An exhaustive check over every MAX in [1, 63] and every
+// c in [-MAX, MAX] found the IEEE quotient in every case.
+__device__ __forceinline__ float cg_unit(uint32_t q, float qmax, float r)
+{
+    const float c = (float)q - qmax;
+    const float p = c * r;
+    const float e = __builtin_fmaf(-p, qmax, c);
+    return __builtin_fmaf(e, r, p);
+}
+
+// Byte offset of the max1 of row j0 + row of (l, kv) in a chunk of n_c tokens.
+__device__ __forceinline__ uint64_t cg_max_offset(const MoveArgs& a, uint32_t l, uint32_t kv, uint32_t n_c,
+                                                  uint32_t row)
+{
+    return (uint64_t)a.num_layers * 2 * n_c * a.width + ((uint64_t)(l * 2 + kv) * n_c + row) * 4;
+}
+
+template <int kVpl>
+__global__ __launch_bounds__(kCgBlock) void store_cachegen(CgArgs ca)
+{
+    const MoveArgs& a = ca.m;
+    const PageUnit u = locate_page_unit(a, a.item_base + xcd_contiguous(blockIdx.x, gridDim.x));
+    if (u.page < 0 || u.page >= a.num_pages) { raise_fault(kFaultPage); return; }
+    const uint64_t pool = wave_uniform(gptr<const gu64>(u.kv ? a.v_pages : a.k_pages)[u.l]);
+    const uint64_t chunk = wave_uniform(gptr<const gu64>(a.seq[u.s].chunks)[u.c]);
+    if (bad_addr(pool)) { raise_fault(kFaultPool); return; }
+    if (bad_addr(chunk)) { raise_fault(kFaultChunk); return; }
+    const float qmax = (float)ca.qmax[u.kv][u.l];
+    const uint32_t E = a.width, row_bytes = E * 2;
+    const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const uint64_t page_rows = pool + (uint64_t)u.page * a.page_size * row_bytes;
+    const uint64_t sym_rows = chunk + section_offset(a, u.l, u.kv, u.n_c) + (uint64_t)u.j0 * E;
+    for (uint32_t r = wave; r < u.rows; r += kCgWaves) {
+        // vectors past the row read as zero (range check), neutral for the maximum
+        const __amdgpu_buffer_rsrc_t rs = byte_range(page_rows + (uint64_t)r * row_bytes, row_bytes);
+        u32x4 v[kVpl];
+#pragma unroll
+        for (int k = 0; k < kVpl; ++k)
+            v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (k * 64 + lane) * 16, 0, kCpolNt);
+        uint32_t m = 0;
+#pragma unroll
+        for (int k = 0; k < kVpl; ++k) m = cg_max_magnitude(m, v[k]);
+        m = __builtin_amdgcn_readfirstlane(wave_max_u32(m));
+        // NaN magnitudes sort above infinity; any NaN makes max1 the quiet NaN
+        const float max1 = m > 0x7F80u ? __uint_as_float(0x7FC00000u) : __uint_as_float(m << 16);
+        const float factor = max1 == 0.0f ? 0.0f : qmax / max1;
+        const __amdgpu_buffer_rsrc_t rd = byte_range(sym_rows + (uint64_t)r * E, E);
+#pragma unroll
+        for (int k = 0; k < kVpl; ++k)
+            __builtin_amdgcn_raw_buffer_store_b64(cg_quantise8(v[k], factor, qmax), rd, (k * 64 + lane) * 8, 0,
+                                                  kCpolNt);
+        if (lane == 0) *gptr<gf32>(chunk + cg_max_offset(a, u.l, u.kv, u.n_c, u.j0 + r)) = max1;
+    }
+}
+
+template <int kVpl>
+__global__ __launch_bounds__(kCgBlock) void retrieve_cachegen(CgArgs ca)
+{
+    const MoveArgs& a = ca.m;
+    const PageUnit u = locate_page_unit(a, a.item_base + xcd_contiguous(blockIdx.x, gridDim.x));
+    if (u.page < 0 || u.page >= a.num_pages) { raise_fault(kFaultPage); return; }
+    const uint64_t pool = wave_uniform(gptr<const gu64>(u.kv ? a.v_pages : a.k_pages)[u.l]);
+    const uint64_t chunk = wave_uniform(gptr<const gu64>(a.seq[u.s].chunks)[u.c]);
+    if (bad_addr(pool)) { raise_fault(kFaultPool); return; }
+    if (bad_addr(chunk)) { raise_fault(kFaultChunk); return; }
+    const float qmax = (float)ca.qmax[u.kv][u.l];
+    const float rq = 1.0f / qmax;
+    const uint32_t E = a.width, row_bytes = E * 2;
+    const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const uint64_t page_rows = pool + (uint64_t)u.page * a.page_size * row_bytes;
+    const uint64_t sym_rows = chunk + section_offset(a, u.l, u.kv, u.n_c) + (uint64_t)u.j0 * E;
+    for (uint32_t r = wave; r < u.rows; r += kCgWaves) {
+        const float max1 = *gptr<const gf32>(chunk + cg_max_offset(a, u.l, u.kv, u.n_c, u.j0 + r));
+        const __amdgpu_buffer_rsrc_t rs = byte_range(sym_rows + (uint64_t)r * E, E);
+        const __amdgpu_buffer_rsrc_t rd = byte_range(page_rows + (uint64_t)r * row_bytes, row_bytes);
+        u32x2 q[kVpl];
+#pragma unroll
+        for (int k = 0; k < kVpl; ++k)
+            q[k] = __builtin_amdgcn_raw_buffer_load_b64(rs, (k * 64 + lane) * 8, 0, kCpolNt);
+#pragma unroll
+        for (int k = 0; k < kVpl; ++k) {
+            u32x4 o;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint32_t w = q[k][j];
+                const __bf16 h0 = (__bf16)(cg_unit(w & 0xFFu, qmax, rq) * max1);
+                const __bf16 h1 = (__bf16)(cg_unit((w >> 8) & 0xFFu, qmax, rq) * max1);
+                const __bf16 h2 = (__bf16)(cg_unit((w >> 16) & 0xFFu, qmax, rq) * max1);
+                const __bf16 h3 = (__bf16)(cg_unit(w >> 24, qmax, rq) * max1);
+                o[2 * j] = __builtin_bit_cast(unsigned short, h0) |
+                           ((uint32_t)__builtin_bit_cast(unsigned short, h1) << 16);
+                o[2 * j + 1] = __builtin_bit_cast(unsigned short, h2) |
+                               ((uint32_t)__builtin_bit_cast(unsigned short, h3) << 16);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * 64 + lane) * 16, 0, kCpolNt);
+        }
+    }
+}
+
+}  // namespace kvmove

@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <string>
 
+#include "kv_cachegen.hpp"
 #include "kv_fp8.hpp"
 #include "kv_move_bf16.hpp"
 
@@ -63,6 +64,8 @@ int check_paged(const kv_paged* p)
 
 int check_fmt(int fmt)
 {
+    if (fmt == KV_FMT_CACHEGEN_INT8)
+        return fail(KV_EINVAL, "format %d needs bin counts: use the *_cachegen entry points", fmt);
     if (fmt != KV_FMT_BF16 && fmt != KV_FMT_FP8_E4M3_SCALED && fmt != KV_FMT_FP8_E5M2_SCALED &&
         fmt != KV_FMT_K16_V8)
         return fail(KV_EINVAL, "unknown format %d", fmt);
@@ -150,7 +153,7 @@ struct Plan {
 // token count moved for sequence i (from its tok_start).
 int launch_units(const Launch& L, const Layout& lay, const kv_paged* p, const kv_seq* seqs,
                  const int64_t* n_tok, int n_seqs, int32_t layer0, int32_t n_layers, hipStream_t stream,
-                 int32_t max_workgroups = 0)
+                 int32_t max_workgroups = 0, const uint8_t (*cg_qmax)[kCgMaxLayers] = nullptr)
 {
     const KernelFn kernel = L.kernel;
     const int block = L.block, tile_bytes = L.tile_bytes;
@@ -185,8 +188,18 @@ int launch_units(const Launch& L, const Layout& lay, const kv_paged* p, const kv
         // only the tiled movers walk runs of tiles; group kernels need one
         // workgroup per group
         if (unit == Unit::Page && max_workgroups > 0 && grid > max_workgroups) grid = max_workgroups;
-        void* args[] = {&a};
-        hipError_t e = hipLaunchKernel(kernel, dim3(unsigned(grid)), dim3(block), args, 0, stream);
+        hipError_t e;
+        if (cg_qmax != nullptr) {            // CacheGen kernels take the bins beside the move arguments
+            CgArgs ca{};
+            ca.m = a;
+            for (int kv = 0; kv < 2; ++kv)
+                for (int l = 0; l < kCgMaxLayers; ++l) ca.qmax[kv][l] = cg_qmax[kv][l];
+            void* args[] = {&ca};
+            e = hipLaunchKernel(kernel, dim3(unsigned(grid)), dim3(block), args, 0, stream);
+        } else {
+            void* args[] = {&a};
+            e = hipLaunchKernel(kernel, dim3(unsigned(grid)), dim3(block), args, 0, stream);
+        }
         if (e != hipSuccess) return fail(KV_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
         return KV_OK;
     };
@@ -309,17 +322,57 @@ int retrieve(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hi
     return rc;
 }
 
+// CacheGen bins -> MAX table; rejects what the kernels cannot take.
+int cachegen_setup(const kv_paged* p, const int32_t* key_bins, const int32_t* value_bins,
+                   uint8_t (*qmax)[kCgMaxLayers], Launch* store, Launch* scatter)
+{
+    if (key_bins == nullptr || value_bins == nullptr) return fail(KV_EINVAL, "key_bins / value_bins is NULL");
+    if (p->num_layers > kCgMaxLayers)
+        return fail(KV_EINVAL, "the CacheGen format takes at most %d layers (got %d)", kCgMaxLayers, p->num_layers);
+    const int64_t width = int64_t(p->num_kv_heads) * p->head_dim;
+    if (width > int64_t(kCgMaxVpl) * 64 * 8)
+        return fail(KV_EINVAL, "the CacheGen format takes rows of at most %d elements (got %lld)",
+                    kCgMaxVpl * 64 * 8, (long long)width);
+    for (int l = 0; l < kCgMaxLayers; ++l) qmax[0][l] = qmax[1][l] = 1;
+    for (int l = 0; l < p->num_layers; ++l) {
+        const int32_t kb = key_bins[l], vb = value_bins[l];
+        if (kb < 4 || kb > 129 || vb < 4 || vb > 129)
+            return fail(KV_EINVAL, "layer %d: bin counts must lie in [4, 129] (got %d, %d)", l, kb, vb);
+        qmax[0][l] = uint8_t(kb / 2 - 1);
+        qmax[1][l] = uint8_t(vb / 2 - 1);
+    }
+    // rows of the page unit, a whole row per wave: kVpl 16-byte vectors per lane
+    const int64_t vpl = (width / 8 + 63) / 64;
+    KernelFn ks, kr;
+    if (vpl <= 1) { ks = reinterpret_cast<KernelFn>(&store_cachegen<1>); kr = reinterpret_cast<KernelFn>(&retrieve_cachegen<1>); }
+    else if (vpl <= 2) { ks = reinterpret_cast<KernelFn>(&store_cachegen<2>); kr = reinterpret_cast<KernelFn>(&retrieve_cachegen<2>); }
+    else if (vpl <= 4) { ks = reinterpret_cast<KernelFn>(&store_cachegen<4>); kr = reinterpret_cast<KernelFn>(&retrieve_cachegen<4>); }
+    else { ks = reinterpret_cast<KernelFn>(&store_cachegen<8>); kr = reinterpret_cast<KernelFn>(&retrieve_cachegen<8>); }
+    // one workgroup per page unit
+    const int page_bytes = int(int64_t(p->page_size) * width * 2);
+    *store = {ks, kCgBlock, page_bytes, Unit::Page, 0, 2};
+    *scatter = {kr, kCgBlock, page_bytes, Unit::Page, 0, 2};
+    return KV_OK;
+}
+
+constexpr Layout kCgLayout = {1, 1, 0};     // symbol sections addressed as 1-byte parts
+
 }  // namespace
 
 extern "C" {
 
 size_t kv_chunk_bytes(const kv_paged* paged, int64_t n_tokens, int fmt)
 {
-    if (check_paged(paged) != KV_OK || check_fmt(fmt) != KV_OK) return 0;
+    if (check_paged(paged) != KV_OK) return 0;
     if (n_tokens < 0) {
         fail(KV_EINVAL, "n_tokens < 0");
         return 0;
     }
+    if (fmt == KV_FMT_CACHEGEN_INT8) {       // symbols, then one float32 max1 per (layer, K/V, token)
+        const int64_t rows = int64_t(paged->num_layers) * 2 * n_tokens;
+        return size_t(rows) * paged->num_kv_heads * paged->head_dim + size_t(rows) * sizeof(float);
+    }
+    if (check_fmt(fmt) != KV_OK) return 0;
     const Layout lay = layout_of(fmt);
     const int64_t part = int64_t(paged->num_layers) * n_tokens * paged->num_kv_heads * paged->head_dim;
     return size_t(part) * (lay.elt_k + lay.elt_v) + size_t(paged->num_layers) * lay.n_scaled * sizeof(float);
@@ -433,6 +486,56 @@ int kv_copy_bytes(void* dst, const void* src, size_t bytes, hipStream_t stream)
                                    dim3((unsigned)grid), dim3(kCopyBlock), args, 0, stream);
     if (e != hipSuccess) return fail(KV_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+int kv_store_chunks_cachegen(const kv_paged* paged, const kv_seq* seqs, int n_seqs, const int32_t* key_bins,
+                             const int32_t* value_bins, hipStream_t stream)
+{
+    int rc = check_paged(paged);
+    if (rc == KV_OK) rc = check_seqs(paged, seqs, n_seqs);
+    if (rc != KV_OK) return rc;
+    uint8_t qmax[2][kCgMaxLayers];
+    Launch st, sc;
+    rc = cachegen_setup(paged, key_bins, value_bins, qmax, &st, &sc);
+    if (rc != KV_OK) return rc;
+    int64_t small[64];
+    int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
+    for (int i = 0; i < n_seqs; ++i) n_tok[i] = seqs[i].tok_end - seqs[i].tok_start;
+    rc = launch_units(st, kCgLayout, paged, seqs, n_tok, n_seqs, 0, paged->num_layers, stream, 0, qmax);
+    if (n_tok != small) delete[] n_tok;
+    return rc == KV_OK ? ok() : rc;
+}
+
+int kv_retrieve_chunks_cachegen(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask,
+                                int n_seqs, const int32_t* key_bins, const int32_t* value_bins,
+                                int64_t* out_tokens, hipStream_t stream)
+{
+    int rc = check_paged(paged);
+    if (rc == KV_OK) rc = check_seqs(paged, seqs, n_seqs);
+    if (rc != KV_OK) return rc;
+    uint8_t qmax[2][kCgMaxLayers];
+    Launch st, sc;
+    rc = cachegen_setup(paged, key_bins, value_bins, qmax, &st, &sc);
+    if (rc != KV_OK) return rc;
+    if (n_seqs > 0 && hit_mask == nullptr) return fail(KV_EINVAL, "hit_mask is NULL");
+    int64_t small[64];
+    int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
+    for (int i = 0; i < n_seqs; ++i) {
+        const kv_seq& q = seqs[i];
+        const int64_t n_chunks = ceil_div(q.tok_end - q.tok_start, paged->chunk_size);
+        if (n_chunks > 0 && hit_mask[i] == nullptr) {
+            if (n_tok != small) delete[] n_tok;
+            return fail(KV_EINVAL, "seq %d: hit_mask entry is NULL", i);
+        }
+        const int64_t n_hit = n_chunks > 0 ? hit_chunks(hit_mask[i], n_chunks) : 0;
+        const int64_t end = q.tok_start + n_hit * paged->chunk_size;
+        n_tok[i] = (end < q.tok_end ? end : q.tok_end) - q.tok_start;
+    }
+    rc = launch_units(sc, kCgLayout, paged, seqs, n_tok, n_seqs, 0, paged->num_layers, stream, 0, qmax);
+    if (rc == KV_OK && out_tokens != nullptr)
+        for (int i = 0; i < n_seqs; ++i) out_tokens[i] = n_tok[i];
+    if (n_tok != small) delete[] n_tok;
+    return rc == KV_OK ? ok() : rc;
 }
 
 }  // extern "C"

@@ -126,3 +126,36 @@ def check_retrieve(w, pool_before, got_pool, chunk_sets, fmt, masks, layer=-1, c
                                       layer))
     assert equal_blocked(got_pool, exp), (w.name, first_diff(got_pool, exp))
     return counts
+
+
+def cachegen_bins(L, seed):
+    """Seeded per-layer bin counts for K and V in [4, 129], both ends included."""
+    rng = np.random.default_rng(seed)
+    kb = rng.integers(4, 130, size=L).astype(np.int32)
+    vb = rng.integers(4, 130, size=L).astype(np.int32)
+    kb[0], vb[-1] = 4, 129
+    return kb, vb
+
+
+def check_store_cachegen(w, arr, chunk_sets, kb, vb):
+    """Oracle CacheGen store of every sequence vs the device chunks."""
+    opool = oracle_pool(w, arr)
+    for i, (sq, cs) in enumerate(zip(w.seqs, chunk_sets)):
+        got = host_chunks(cs)
+        exp = oracle.alloc_chunks(opool, sq.tok_start, sq.tok_end, oracle.FMT_CACHEGEN)
+        assert oracle.store_cachegen(opool, sq.block_table, sq.tok_start, sq.tok_end, exp, kb, vb) == 0
+        assert len(got) == len(exp)
+        for c, (g, e) in enumerate(zip(got, exp)):
+            assert g.size == e.size, (i, c)
+            assert np.array_equal(g, e), (w.name, "seq", i, "chunk", c, first_diff(g, e))
+
+
+def check_retrieve_cachegen(w, pool_before, got_pool, chunk_sets, masks, kb, vb):
+    """Oracle CacheGen retrieve (from the device's chunks) into a copy of the
+    pool as it was, vs the device pool; returns the oracle's token counts."""
+    exp = pool_before.copy()
+    opool = oracle_pool(w, exp)
+    counts = [oracle.retrieve_cachegen(opool, sq.block_table, sq.tok_start, sq.tok_end, m, host_chunks(cs), kb, vb)
+              for sq, cs, m in zip(w.seqs, chunk_sets, masks)]
+    assert equal_blocked(got_pool, exp), (w.name, first_diff(got_pool, exp))
+    return counts

@@ -69,7 +69,7 @@ def test_chunk_bytes_and_num_chunks():
     assert L.kv_chunk_bytes(ctypes.byref(p), 16, kvm.FMT_K16_V8) == 32 * 3 * 16 * 1024 + 32 * 4
     assert L.kv_chunk_bytes(ctypes.byref(p), 0, kvm.FMT_BF16) == 0
     assert L.kv_chunk_bytes(ctypes.byref(p), 256, 9) == 0
-    assert L.kv_chunk_bytes(ctypes.byref(p), 256, 4) == 0
+    assert L.kv_chunk_bytes(ctypes.byref(p), 256, 5) == 0
     assert L.kv_num_chunks(ctypes.byref(p), 0, 10000) == 40
     assert L.kv_num_chunks(ctypes.byref(p), 0, 10240) == 40
     assert L.kv_num_chunks(ctypes.byref(p), 512, 513) == 1
@@ -92,7 +92,7 @@ def test_store_rejections():
     assert _store(p, [_seq(16, 300, 40)]) == kvm.KV_EINVAL          # start not chunk-aligned
     assert "multiple of chunk_size" in L.kv_last_error().decode()
     assert _store(p, [_seq(0, 641, 40)]) == kvm.KV_ERANGE           # beyond 40 pages of 16
-    assert _store(p, [_seq(0, 100, 40)], fmt=4) == kvm.KV_EINVAL
+    assert _store(p, [_seq(0, 100, 40)], fmt=5) == kvm.KV_EINVAL
     assert _store(p, [_seq(0, 100, 40)], fmt=-1) == kvm.KV_EINVAL
     assert _store(p, [_seq(300, 200, 40)]) == kvm.KV_EINVAL
     assert _store(p, [_seq(0, 100, 40, bt=0)]) == kvm.KV_EINVAL
@@ -187,3 +187,36 @@ def test_binding_refuses_pageable_host_chunks():
     with pytest.raises(kvm.KvError, match="contiguous"):
         t = torch.empty(1 << 16, dtype=torch.uint8, device="meta")
         kvm.Seq(bt, 0, 64, [t[::2]])
+
+
+def test_cachegen_entry_points_reject_bad_calls():
+    L = _lib()
+    p = _paged(L=4)
+    ok = (kvm._KvSeq * 1)(_seq(0, 100, 40))
+    good = (ctypes.c_int32 * 4)(4, 32, 64, 129)
+    for bad_bins in ((3, 8, 8, 8), (8, 8, 8, 130), (0, 0, 0, 0)):
+        b = (ctypes.c_int32 * 4)(*bad_bins)
+        assert L.kv_store_chunks_cachegen(ctypes.byref(p), ok, 1, b, good, None) == kvm.KV_EINVAL
+        assert "bin counts" in L.kv_last_error().decode()
+        assert L.kv_store_chunks_cachegen(ctypes.byref(p), ok, 1, good, b, None) == kvm.KV_EINVAL
+    assert L.kv_store_chunks_cachegen(ctypes.byref(p), ok, 1, None, good, None) == kvm.KV_EINVAL
+    many = _paged(L=129)
+    bins129 = (ctypes.c_int32 * 129)(*([16] * 129))
+    assert L.kv_store_chunks_cachegen(ctypes.byref(many), ok, 1, bins129, bins129, None) == kvm.KV_EINVAL
+    wide = _paged(L=4, H=40, D=128)                         # 5120-element rows
+    assert L.kv_store_chunks_cachegen(ctypes.byref(wide), ok, 1, good, good, None) == kvm.KV_EINVAL
+    bad_seq = (kvm._KvSeq * 1)(_seq(16, 100, 40))
+    assert L.kv_store_chunks_cachegen(ctypes.byref(p), bad_seq, 1, good, good, None) == kvm.KV_EINVAL
+    # the generic entry points refuse the format: its bins would be missing
+    assert _store(p, [_seq(0, 100, 40)], fmt=kvm.FMT_CACHEGEN) == kvm.KV_EINVAL
+    assert "cachegen" in L.kv_last_error().decode()
+    # sizes: one byte per element, one float32 per (layer, K/V, token)
+    assert L.kv_chunk_bytes(ctypes.byref(p), 256, kvm.FMT_CACHEGEN) == 4 * 2 * 256 * 1024 + 4 * 2 * 256 * 4
+    # zero hits: nothing launched, out_tokens = 0 (no GPU here)
+    seqs = (kvm._KvSeq * 1)(_seq(0, 1000, 63))
+    m0 = (ctypes.c_uint8 * 4)(0, 1, 1, 1)
+    masks = (ctypes.c_void_p * 1)(ctypes.addressof(m0))
+    out = (ctypes.c_int64 * 1)(-7)
+    assert L.kv_retrieve_chunks_cachegen(ctypes.byref(p), seqs, masks, 1, good, good, out, None) == kvm.KV_OK
+    assert out[0] == 0
+    assert L.kv_retrieve_chunks_cachegen(ctypes.byref(p), seqs, None, 1, good, good, out, None) == kvm.KV_EINVAL

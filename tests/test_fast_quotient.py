@@ -27,3 +27,15 @@ def test_fast_quotient_matches_ieee_division(checker, fmt):
     assert r.returncode == 0, r.stdout + r.stderr
     checked, bad = [int(t) for t in r.stdout.split() if t.isdigit()]
     assert checked == 817512960 and bad == 0
+
+
+def test_cachegen_unit_matches_ieee_division(tmp_path):
+    # the CacheGen dequantiser's (q - MAX) / MAX: reciprocal product plus one
+    # Markstein correction equals the IEEE quotient for every MAX and symbol
+    exe = str(tmp_path / "cachegen_unit_check")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-o", exe,
+                    os.path.join(ROOT, "tests", "cachegen_unit_check.c"), "-lm"], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    checked, bad = [int(t) for t in r.stdout.split() if t.isdigit()]
+    assert checked == sum(2 * m + 1 for m in range(1, 64)) and bad == 0

@@ -591,3 +591,77 @@ def test_host_and_device_chunks_in_one_call():
     assert kvm.take_faults() == 0
     got = host_from_dev_pool(pool)
     check_retrieve(w, np.zeros(got.shape, np.uint16), got, cs, BF16, [s.hit_mask for s in w.seqs])
+
+
+# ------------------------------------------------------------ CacheGen quantiser
+
+from gpu_util import cachegen_bins, check_store_cachegen, check_retrieve_cachegen  # noqa: E402
+
+
+def _cachegen_roundtrip(w, kb, vb, fill=0x7E57, where="device", arr=None):
+    say("case cachegen", w.name, where)
+    arr = wl.host_pool(w) if arr is None else arr
+    pool, paged, batch, cs = setup_device(w, arr, fmt=kvm.FMT_CACHEGEN, fill=0xCD, where=where)
+    kvm.store_cachegen(paged, batch, kb, vb)
+    _sync()
+    assert kvm.take_faults() == 0
+    assert np.array_equal(host_from_dev_pool(pool), arr), "store wrote the pool"
+    check_store_cachegen(w, arr, cs, kb, vb)
+    masks = [sq.hit_mask for sq in w.seqs]
+    pool.view(torch.int16).fill_(int(np.uint16(fill).view(np.int16)))
+    n = kvm.retrieve_cachegen(paged, batch, kb, vb)
+    _sync()
+    assert kvm.take_faults() == 0
+    counts = check_retrieve_cachegen(w, np.full_like(arr, fill), host_from_dev_pool(pool), cs, masks, kb, vb)
+    assert n == counts
+    return n
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_cachegen_shapes_and_tails(shape):
+    name, seed, L, H, D, pages, ranges, kw = shape
+    w = wl.custom(name, seed, L, H, D, pages, ranges, outliers=2, **kw)
+    kb, vb = cachegen_bins(L, seed)
+    assert _cachegen_roundtrip(w, kb, vb) == [e - s for (s, e) in ranges]
+
+
+def test_cachegen_holes_and_host_chunks():
+    ranges = [(0, 1000), (0, 1000), (256, 1000), (0, 600)]
+    masks = [np.array(m, np.uint8) for m in ([1, 1, 0, 1], [0, 1, 1, 1], [1, 0, 1], [1, 1, 1])]
+    w = wl.custom("cg-holes", 321, 3, 2, 32, 400, ranges, masks=masks, outliers=2)
+    kb, vb = cachegen_bins(3, 321)
+    assert _cachegen_roundtrip(w, kb, vb, fill=0xA5A5) == [512, 0, 256, 600]
+    assert _cachegen_roundtrip(w, kb, vb, fill=0xA5A5, where="host") == [512, 0, 256, 600]
+
+
+def test_cachegen_special_rows():
+    # zero rows (with -0), a NaN, an infinity, rows of subnormals, rows whose
+    # maximum is negative; bins at both ends of the range
+    w = wl.custom("cg-special", 331, 2, 1, 64, 64, [(0, 40)], masks=[np.array([1], np.uint8)])
+    arr = wl.host_pool(w)
+    bt = w.seqs[0].block_table
+    arr[0, 0, bt[0], 0] = 0                      # layer 0 K, token 0: zero row
+    arr[0, 0, bt[0], 1, ::2] = 0x8000            # token 1: -0 in half the channels ...
+    arr[0, 0, bt[0], 1, 1::2] = 0                # ... +0 in the rest
+    arr[0, 1, bt[0], 2, 7] = 0x7FC1              # layer 0 V, token 2: one NaN
+    arr[1, 0, bt[1], 3, 5] = 0x7F80              # layer 1 K, token 19: +inf
+    arr[1, 1, bt[2], :, :] = 0x0003              # layer 1 V, tokens 32..39: subnormals
+    arr[1, 1, bt[0], 4, 9] = 0xC2F0              # layer 1 V, token 4: the maximum is negative (-120)
+    kb, vb = np.int32([4, 129]), np.int32([129, 4])
+    pool, paged, batch, cs = setup_device(w, arr, fmt=kvm.FMT_CACHEGEN, fill=0xCD)
+    kvm.store_cachegen(paged, batch, kb, vb)
+    _sync()
+    check_store_cachegen(w, arr, cs, kb, vb)
+    pool.zero_()
+    assert kvm.retrieve_cachegen(paged, batch, kb, vb) == [40]
+    _sync()
+    got = host_from_dev_pool(pool)
+    exp = np.zeros_like(arr)
+    op = oracle_pool(w, exp)
+    assert oracle.retrieve_cachegen(op, bt, 0, 40, [1], host_chunks(cs[0]), kb, vb) == 40
+    # NaN results (0 * inf, NaN * 0) may differ in sign between implementations:
+    # compare NaN-ness there, bits elsewhere
+    nan_g = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
+    nan_e = ((exp & 0x7F80) == 0x7F80) & ((exp & 0x7F) != 0)
+    assert np.array_equal(nan_g, nan_e) and nan_e.any()
+    assert np.array_equal(got[~nan_g], exp[~nan_e])

@@ -193,3 +193,66 @@ def test_full_layerwise_store_8b_behind_compute():
     check_store(w, arr, chunk_sets, BF16)
     del arr, pool, paged, batch, chunk_sets
     _free()
+
+
+def test_full_cachegen_8b_sampled_chunks_and_bound():
+    # the fp8 workload's inputs (N(0,1), 4 outlier channels x20) through the
+    # CacheGen quantiser, seeded per-layer bins
+    from gpu_util import cachegen_bins
+    w = wl.fp8_8b()
+    say("case", w.name, "cachegen")
+    kb, vb = cachegen_bins(w.num_layers, 4)
+    pool = wl.device_pool(w)
+    pool, paged, batch, chunk_sets = setup_device(w, pool=pool, fmt=kvm.FMT_CACHEGEN, fill=0xCD)
+    kvm.store_cachegen(paged, batch, kb, vb)
+    sync()
+    assert kvm.take_faults() == 0
+    arr = host_from_dev_pool(pool)
+    opool = oracle_pool(w, arr)
+    samples = [(0, 0), (0, 39), (4, 21), (7, 39)]            # (seq, chunk); 39 = 16-token tail
+    for si, c in samples:
+        sq = w.seqs[si]
+        s, e = c * w.chunk_size, min(sq.tok_end, (c + 1) * w.chunk_size)
+        exp = oracle.alloc_chunks(opool, s, e, kvm.FMT_CACHEGEN)
+        assert oracle.store_cachegen(opool, sq.block_table, s, e, exp, kb, vb) == 0
+        bufs, sizes = chunk_sets[si]
+        got = host_chunks(([bufs[c]], [sizes[c]]))[0]
+        assert np.array_equal(got, exp[0]), (si, c, first_diff(got, exp[0]))
+    say("  sampled cachegen chunks match")
+    del arr, opool
+    orig = pool.clone()
+    pool.zero_()
+    assert kvm.retrieve_cachegen(paged, batch, kb, vb, masks=[np.ones(40, np.uint8)] * 8) == [10000] * 8
+    sync()
+    # every element: |x' - x| <= max1 * (1/(2 MAX) + 2^-8 + 2^-20) (half a
+    # quantisation step, the float32 steps, the bf16 rounding)
+    L, E, P, C = w.num_layers, w.width, w.page_size, w.chunk_size
+    worst = 0.0
+    for sq, (bufs, sizes) in zip(w.seqs, chunk_sets):
+        bt = torch.from_numpy(sq.block_table.astype(np.int64)).cuda()
+        for c, (b, n_c) in enumerate(zip(bufs, chunk_tokens(w, sq))):
+            m1 = b[L * 2 * n_c * E: L * 2 * n_c * E + L * 2 * n_c * 4].view(torch.float32).view(L, 2, n_c)
+            t = sq.tok_start + c * C + torch.arange(n_c, device="cuda")
+            page, row = bt[t // P], t % P
+            for l in range(L):
+                for kv, bins in ((0, kb), (1, vb)):
+                    MAX = float(bins[l] // 2 - 1)
+                    x = orig[l, kv].view(-1, P, E)[page, row].double()
+                    y = pool[l, kv].view(-1, P, E)[page, row].double()
+                    lim = m1[l, kv].double()[:, None] * (0.5 / MAX + 2.0 ** -8 + 2.0 ** -20)
+                    over = ((y - x).abs() - lim).max()
+                    worst = max(worst, float(over))
+    say("  worst excess over the bound", worst)
+    assert worst <= 0.0
+    # 30-chunk mask: rows of later chunks keep the sentinel, hit rows equal the all-hit result
+    full = pool.clone()
+    pool.view(torch.int16).fill_(SENTINEL)
+    masks = [np.r_[np.ones(30, np.uint8), np.zeros(10, np.uint8)]] * 8
+    assert kvm.retrieve_cachegen(paged, batch, kb, vb, masks=masks) == [7680] * 8
+    sync()
+    for sq in w.seqs:
+        bt = torch.from_numpy(sq.block_table.astype(np.int64)).cuda()
+        assert torch.equal(pool[:, :, bt[:480]], full[:, :, bt[:480]])
+        assert (pool[:, :, bt[480:]].view(torch.int16) == SENTINEL).all()
+    del pool, orig, full, paged, batch, chunk_sets
+    _free()
