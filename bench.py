@@ -184,11 +184,15 @@ def bench_llama8b(args):
     store_bytes = 2 * store_tokens * bpt
     ret_bytes = 2 * ret_tokens * bpt
 
+    # the retrieve visits its pages in pool-address order (kv_retrieve_chunks_ws)
+    # unless --retrieve-order chunk asks for the chunk-major kv_retrieve_chunks
+    ws = paged.new_workspace() if args.retrieve_order == "address" else None
+
     def store():
         kvm.store(paged, batch, stream=stream)
 
     def retrieve():
-        kvm.retrieve(paged, batch, stream=stream)
+        kvm.retrieve(paged, batch, stream=stream, workspace=ws)
 
     for _ in range(args.warmup):
         store()
@@ -216,6 +220,11 @@ def bench_llama8b(args):
     value = (store_bytes + ret_bytes) / step_s / 1e9
     gather_gbps = store_bytes / (store_ms / 1e3) / 1e9
     scatter_gbps = ret_bytes / (ret_ms / 1e3) / 1e9
+
+    # the other visiting order, for context
+    other_ms = timed(stream, lambda: kvm.retrieve(paged, batch, stream=stream,
+                                                  workspace=None if ws is not None else paged.new_workspace()), 5)
+    assert kvm.take_faults() == 0
 
     # same-run calibration: a plain contiguous copy of the gather's payload
     src = pool.view(-1).view(torch.uint8)
@@ -262,6 +271,10 @@ def bench_llama8b(args):
         "detail": {
             "store_ms": round(store_ms, 4), "store_GBps": round(gather_gbps, 2),
             "retrieve_ms": round(ret_ms, 4), "retrieve_GBps": round(scatter_gbps, 2),
+            "retrieve_order": "pool-address (kv_retrieve_chunks_ws)" if ws is not None
+                              else "chunk-major (kv_retrieve_chunks)",
+            "retrieve_other_order_ms": round(other_ms, 4),
+            "retrieve_other_order_GBps": round(ret_bytes / (other_ms / 1e3) / 1e9, 2),
             "copy_ceiling_GBps": round(copy_gbps, 2),
             "kernel_source_sha256_16": kernel_source_hash(),
         },
@@ -705,6 +718,8 @@ def main():
                     choices=["llama3.1-8b", "layerwise-8b", "layerwise-store-8b", "llama-70b-style", "fp8-8b",
                              "e5m2-8b", "k16v8-8b", "cachegen-8b",
                              "offload-8b"])
+    ap.add_argument("--retrieve-order", choices=["address", "chunk"], default="address",
+                    help="headline retrieve: pool-address order with a workspace (default) or chunk-major")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (used for profiler runs)")
     args = ap.parse_args()

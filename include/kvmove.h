@@ -187,6 +187,23 @@ int kv_retrieve_chunks(const kv_paged* paged, const kv_seq* seqs,
                        const uint8_t* const* hit_mask, int n_seqs, int fmt,
                        int64_t* out_tokens, hipStream_t stream);
 
+/* Retrieve in pool-address order: the same operation and result as
+ * kv_retrieve_chunks, with the bf16 scatter visiting its page units by
+ * destination address (layer, K/V, page id) instead of chunk by chunk.
+ * Random destination pages cost DRAM more on writes than on reads; this
+ * order makes the writes near-sequential and measured about 6 % faster on
+ * the Llama-3.1-8B workload.  It needs the hit pages sorted by page id,
+ * which is done on the device in `workspace` (DEVICE memory the caller
+ * owns, at least kv_retrieve_workspace_bytes(paged) bytes, 256-byte
+ * aligned; its contents on entry do not matter and are overwritten).  Other
+ * formats ignore the workspace and run as kv_retrieve_chunks.  A sequence
+ * moving 2^26 pages or more is rejected (KV_EINVAL).  Calls that share a
+ * workspace must be ordered on one stream. */
+size_t kv_retrieve_workspace_bytes(const kv_paged* paged);   /* 0 on a malformed pool */
+int kv_retrieve_chunks_ws(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
+                          int fmt, int64_t* out_tokens, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
 /* Layerwise retrieve ([paper] layerwise pipeline; Table 2 start_load_kv /
  * wait_load_kv(layer)): as kv_retrieve_chunks but writes layer `layer` only,
  * on copy_stream, then records layer_done (if not NULL) on copy_stream -- also

@@ -94,6 +94,8 @@ def load():
         "kv_retrieve_chunks": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, vp, vp]),
         "kv_retrieve_layer": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, i32, vp, i32, vp, vp]),
         "kv_store_chunks_cachegen": (ctypes.c_int, [P, S, ctypes.c_int, vp, vp, vp]),
+        "kv_retrieve_workspace_bytes": (ctypes.c_size_t, [P]),
+        "kv_retrieve_chunks_ws": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]),
         "kv_retrieve_chunks_cachegen": (ctypes.c_int, [P, S, vp, ctypes.c_int, vp, vp, vp, vp]),
         "kv_last_error": (ctypes.c_char_p, []),
         "kv_take_faults": (ctypes.c_int, []),
@@ -166,6 +168,18 @@ class Paged:
         if n == 0 and n_tokens > 0:
             _check(KV_EINVAL)
         return int(n)
+
+    def retrieve_workspace_bytes(self) -> int:
+        """Device bytes retrieve(..., workspace=...) needs for this pool."""
+        n = load().kv_retrieve_workspace_bytes(ctypes.byref(self.c))
+        if n == 0:
+            _check(KV_EINVAL)
+        return int(n)
+
+    def new_workspace(self):
+        """A device tensor of retrieve_workspace_bytes() bytes (torch aligns it to 256)."""
+        import torch
+        return torch.empty(self.retrieve_workspace_bytes(), dtype=torch.uint8, device="cuda")
 
     def num_chunks(self, tok_start: int, tok_end: int) -> int:
         n = load().kv_num_chunks(ctypes.byref(self.c), tok_start, tok_end)
@@ -292,15 +306,25 @@ def retrieve_cachegen(paged: Paged, seqs, key_bins, value_bins, masks=None, stre
     return [int(b.out[i]) for i in range(b.n)]
 
 
-def retrieve(paged: Paged, seqs, masks=None, fmt: int = FMT_BF16, stream=None) -> list:
+def retrieve(paged: Paged, seqs, masks=None, fmt: int = FMT_BF16, stream=None, workspace=None) -> list:
     """Scatter the leading hit chunks back into pages (kv_retrieve_chunks).
-    Returns the tokens made available per sequence."""
+    With ``workspace`` (a device uint8 tensor of at least
+    paged.retrieve_workspace_bytes()) the bf16 scatter runs in pool-address
+    order (kv_retrieve_chunks_ws).  Returns the tokens made available per
+    sequence."""
     b = _batch(paged, seqs)
     if masks is not None:
         b.set_masks(masks)
     assert b._mask_ptrs is not None, "hit masks are required"
-    _check(load().kv_retrieve_chunks(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n, fmt, b.out,
-                                     _stream_handle(stream)))
+    if workspace is None:
+        _check(load().kv_retrieve_chunks(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n, fmt, b.out,
+                                         _stream_handle(stream)))
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise KvError(KV_EINVAL, "workspace must be a contiguous device tensor")
+        _check(load().kv_retrieve_chunks_ws(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n, fmt, b.out,
+                                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                            _stream_handle(stream)))
     return [int(b.out[i]) for i in range(b.n)]
 
 

@@ -18,14 +18,11 @@ constexpr int kScatterAuxStore = kCpolNt;
 constexpr int kCopyBlock = 256;
 constexpr int kCopyVpt = 1;
 
-// Gather (kToChunk) or scatter (!kToChunk) of one tile of one page unit,
+// Gather (kToChunk) or scatter (!kToChunk) of tile `tile` of page unit u,
 // bf16 copied bit for bit (the chunk part moved holds 2-byte elements).
 template <bool kToChunk, int kBlock, int kVpt, int kAuxLoad, int kAuxStore>
-__device__ __forceinline__ void move_tile(const MoveArgs& a, uint32_t b)
+__device__ __forceinline__ void move_unit_tile(const MoveArgs& a, const PageUnit& u, uint32_t tile)
 {
-    const uint32_t unit = b / a.tiles;
-    const uint32_t tile = b - unit * a.tiles;
-    const PageUnit u = locate_page_unit(a, a.item_base + unit);
     const uint32_t row_bytes = a.width * 2;
     const uint32_t nbytes = u.rows * row_bytes;
     const uint32_t lo = tile * (kBlock * kVpt * 16);
@@ -41,6 +38,15 @@ __device__ __forceinline__ void move_tile(const MoveArgs& a, uint32_t b)
     const uint64_t chunk_addr = chunk + section_offset(a, u.l, u.kv, u.n_c) + (uint64_t)u.j0 * row_bytes + lo;
     if (kToChunk) copy_tile<kBlock, kVpt, kAuxLoad, kAuxStore>(page_addr, chunk_addr, n);
     else copy_tile<kBlock, kVpt, kAuxLoad, kAuxStore>(chunk_addr, page_addr, n);
+}
+
+// Tile b of the launch: page units in chunk-major order, a.tiles tiles each.
+template <bool kToChunk, int kBlock, int kVpt, int kAuxLoad, int kAuxStore>
+__device__ __forceinline__ void move_tile(const MoveArgs& a, uint32_t b)
+{
+    const uint32_t unit = b / a.tiles;
+    const uint32_t tile = b - unit * a.tiles;
+    move_unit_tile<kToChunk, kBlock, kVpt, kAuxLoad, kAuxStore>(a, locate_page_unit(a, a.item_base + unit), tile);
 }
 
 // Grid = one workgroup per tile (units * a.tiles), or fewer workgroups that

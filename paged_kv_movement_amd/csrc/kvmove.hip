@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
@@ -16,6 +17,7 @@
 #include "kv_cachegen.hpp"
 #include "kv_fp8.hpp"
 #include "kv_move_bf16.hpp"
+#include "kv_order.hpp"
 
 namespace {
 
@@ -149,14 +151,14 @@ struct Plan {
 };
 
 // Packs up to kMaxSeqs non-empty sequences per launch, keeping every launch
-// under kMaxBlocks workgroups (the kernels index units in 32 bits).  n_tok[i] is the
-// token count moved for sequence i (from its tok_start).
-int launch_units(const Launch& L, const Layout& lay, const kv_paged* p, const kv_seq* seqs,
-                 const int64_t* n_tok, int n_seqs, int32_t layer0, int32_t n_layers, hipStream_t stream,
-                 int32_t max_workgroups = 0, const uint8_t (*cg_qmax)[kCgMaxLayers] = nullptr)
+// under kMaxBlocks workgroups (the kernels index units in 32 bits), and
+// calls flush(args, units) for each launch.  n_tok[i] is the token count
+// moved for sequence i (from its tok_start).
+template <class Flush>
+int pack_units(const Launch& L, const Layout& lay, const kv_paged* p, const kv_seq* seqs, const int64_t* n_tok,
+               int n_seqs, int32_t layer0, int32_t n_layers, Flush&& flush)
 {
-    const KernelFn kernel = L.kernel;
-    const int block = L.block, tile_bytes = L.tile_bytes;
+    const int tile_bytes = L.tile_bytes;
     const Unit unit = L.unit;
     MoveArgs a{};
     a.kv0 = L.kv0;
@@ -181,9 +183,49 @@ int launch_units(const Launch& L, const Layout& lay, const kv_paged* p, const kv
     if (int64_t(a.tiles) > kMaxBlocks) return fail(KV_EINVAL, "page too large for one launch");
     const int64_t max_units = kMaxBlocks / a.tiles;
 
-    auto flush = [&](int64_t total) -> int {
+    int64_t total = 0;
+    a.n_seqs = 0;
+    for (int i = 0; i < n_seqs; ++i) {
+        if (n_tok[i] <= 0) continue;
+        const int64_t units = unit == Unit::Page
+                                  ? ceil_div(n_tok[i], p->page_size) * n_layers * L.n_kv
+                                  : ceil_div(n_tok[i], p->chunk_size) * n_layers * L.n_kv;
+        if (units > max_units)
+            return fail(KV_EINVAL, "seq %d: %lld work units exceed one launch", i, (long long)units);
+        if (a.n_seqs == kMaxSeqs || total + units > max_units) {
+            a.item_base = 0;
+            a.total_tiles = uint32_t(total * a.tiles);
+            int rc = flush(a, total);
+            if (rc != KV_OK) return rc;
+            a.n_seqs = 0;
+            total = 0;
+        }
+        SeqArg& s = a.seq[a.n_seqs++];
+        s.bt = reinterpret_cast<uint64_t>(seqs[i].block_table);
+        s.chunks = reinterpret_cast<uint64_t>(seqs[i].chunks);
+        s.first_page = uint32_t(seqs[i].tok_start / p->page_size);
+        s.n_full = uint32_t(n_tok[i] / p->chunk_size);
+        s.tail_tokens = uint32_t(n_tok[i] % p->chunk_size);
+        s.item_begin = uint32_t(total);
+        total += units;
+    }
+    if (a.n_seqs > 0) {
         a.item_base = 0;
         a.total_tiles = uint32_t(total * a.tiles);
+        return flush(a, total);
+    }
+    return KV_OK;
+}
+
+int launch_units(const Launch& L, const Layout& lay, const kv_paged* p, const kv_seq* seqs,
+                 const int64_t* n_tok, int n_seqs, int32_t layer0, int32_t n_layers, hipStream_t stream,
+                 int32_t max_workgroups = 0, const uint8_t (*cg_qmax)[kCgMaxLayers] = nullptr)
+{
+    const KernelFn kernel = L.kernel;
+    const int block = L.block;
+    const Unit unit = L.unit;
+    auto flush = [&](MoveArgs& a, int64_t total) -> int {
+        (void)total;
         int64_t grid = a.total_tiles;
         // only the tiled movers walk runs of tiles; group kernels need one
         // workgroup per group
@@ -203,33 +245,7 @@ int launch_units(const Launch& L, const Layout& lay, const kv_paged* p, const kv
         if (e != hipSuccess) return fail(KV_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
         return KV_OK;
     };
-
-    int64_t total = 0;
-    a.n_seqs = 0;
-    for (int i = 0; i < n_seqs; ++i) {
-        if (n_tok[i] <= 0) continue;
-        const int64_t units = unit == Unit::Page
-                                  ? ceil_div(n_tok[i], p->page_size) * n_layers * L.n_kv
-                                  : ceil_div(n_tok[i], p->chunk_size) * n_layers * L.n_kv;
-        if (units > max_units)
-            return fail(KV_EINVAL, "seq %d: %lld work units exceed one launch", i, (long long)units);
-        if (a.n_seqs == kMaxSeqs || total + units > max_units) {
-            int rc = flush(total);
-            if (rc != KV_OK) return rc;
-            a.n_seqs = 0;
-            total = 0;
-        }
-        SeqArg& s = a.seq[a.n_seqs++];
-        s.bt = reinterpret_cast<uint64_t>(seqs[i].block_table);
-        s.chunks = reinterpret_cast<uint64_t>(seqs[i].chunks);
-        s.first_page = uint32_t(seqs[i].tok_start / p->page_size);
-        s.n_full = uint32_t(n_tok[i] / p->chunk_size);
-        s.tail_tokens = uint32_t(n_tok[i] % p->chunk_size);
-        s.item_begin = uint32_t(total);
-        total += units;
-    }
-    if (a.n_seqs > 0) return flush(total);
-    return KV_OK;
+    return pack_units(L, lay, p, seqs, n_tok, n_seqs, layer0, n_layers, flush);
 }
 
 Launch bf16_launch(bool to_chunk, uint32_t kv0, uint32_t n_kv)
@@ -295,26 +311,85 @@ int run_plan(const Plan& plan, int fmt, const kv_paged* p, const kv_seq* seqs, c
     return KV_OK;
 }
 
-// Shared body of the two retrieve entry points.
-int retrieve(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
-             int fmt, int32_t layer0, int32_t n_layers, int64_t* out_tokens, hipStream_t stream,
-             int32_t max_workgroups = 0)
+// Workspace of the pool-address-ordered scatter: the inverse page map, then
+// the sorted list, num_pages words each, 256-byte aligned.
+int64_t ordered_half_bytes(int64_t num_pages) { return ceil_div(num_pages * 4, 256) * 256; }
+
+// bf16 scatter of the tokens n_tok[i] in pool-address order (kv_order.hpp).
+int retrieve_ordered(const kv_paged* p, const kv_seq* seqs, const int64_t* n_tok, int n_seqs, int32_t layer0,
+                     int32_t n_layers, void* workspace, hipStream_t stream)
+{
+    const uint64_t inv = reinterpret_cast<uint64_t>(workspace);
+    const uint64_t list = inv + uint64_t(ordered_half_bytes(p->num_pages));
+    const uint32_t num_pages = uint32_t(p->num_pages);
+    const Launch L = bf16_launch(false, 0, 2);
+    auto flush = [&](MoveArgs& a, int64_t total) -> int {
+        const int64_t n_list = total / (int64_t(n_layers) * a.n_kv);      // pages moved by this launch
+        for (uint32_t s = 0; s < a.n_seqs; ++s)
+            if (a.seq[s].n_full * a.pages_per_chunk + ceil_div(a.seq[s].tail_tokens, a.page_size) > kPageIndexMask)
+                return fail(KV_EINVAL, "a sequence moves 2^26 pages or more: use kv_retrieve_chunks");
+        const unsigned fill_grid = unsigned(std::min<int64_t>(ceil_div(num_pages, 256), 4096));
+        const uint32_t none = kNoEntry;
+        uint32_t np = num_pages, nl = uint32_t(n_list);
+        uint64_t inv_a = inv, list_a = list;
+        void* fill_args[] = {&inv_a, &np, const_cast<uint32_t*>(&none)};
+        hipError_t e = hipLaunchKernel(reinterpret_cast<KernelFn>(&fill_u32), dim3(fill_grid), dim3(256), fill_args,
+                                       0, stream);
+        if (e == hipSuccess) {
+            void* inv_args[] = {&a, &inv_a, &nl};
+            e = hipLaunchKernel(reinterpret_cast<KernelFn>(&invert_pages), dim3(unsigned(ceil_div(n_list, 256))),
+                                dim3(256), inv_args, 0, stream);
+        }
+        if (e == hipSuccess) {
+            void* cmp_args[] = {&inv_a, &np, &list_a, &nl};
+            e = hipLaunchKernel(reinterpret_cast<KernelFn>(&compact_pages), dim3(1), dim3(kCompactBlock), cmp_args, 0,
+                                stream);
+        }
+        if (e == hipSuccess) {
+            void* sc_args[] = {&a, &list_a, &nl};
+            e = hipLaunchKernel(reinterpret_cast<KernelFn>(
+                                    &scatter_sorted<kMoveBlock, kMoveVpt, kScatterAuxLoad, kScatterAuxStore>),
+                                dim3(a.total_tiles), dim3(kMoveBlock), sc_args, 0, stream);
+        }
+        if (e != hipSuccess) return fail(KV_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+        return KV_OK;
+    };
+    return pack_units(L, layout_of(KV_FMT_BF16), p, seqs, n_tok, n_seqs, layer0, n_layers, flush);
+}
+
+// Tokens each sequence gets back: its leading hit chunks, from tok_start.
+int hit_tokens(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
+               int64_t* n_tok)
 {
     if (n_seqs > 0 && hit_mask == nullptr) return fail(KV_EINVAL, "hit_mask is NULL");
-    int64_t small[64];
-    int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
     for (int i = 0; i < n_seqs; ++i) {
         const kv_seq& s = seqs[i];
         const int64_t n_chunks = ceil_div(s.tok_end - s.tok_start, paged->chunk_size);
-        if (n_chunks > 0 && hit_mask[i] == nullptr) {
-            if (n_tok != small) delete[] n_tok;
-            return fail(KV_EINVAL, "seq %d: hit_mask entry is NULL", i);
-        }
+        if (n_chunks > 0 && hit_mask[i] == nullptr) return fail(KV_EINVAL, "seq %d: hit_mask entry is NULL", i);
         const int64_t n_hit = n_chunks > 0 ? hit_chunks(hit_mask[i], n_chunks) : 0;
         const int64_t end = s.tok_start + n_hit * paged->chunk_size;
         n_tok[i] = (end < s.tok_end ? end : s.tok_end) - s.tok_start;
     }
-    int rc = run_plan(scatter_plan(fmt), fmt, paged, seqs, n_tok, n_seqs, layer0, n_layers, stream,
+    return KV_OK;
+}
+
+// Shared body of the retrieve entry points; with a workspace the bf16
+// scatter runs in pool-address order.
+int retrieve(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
+             int fmt, int32_t layer0, int32_t n_layers, int64_t* out_tokens, hipStream_t stream,
+             int32_t max_workgroups = 0, void* workspace = nullptr)
+{
+    int64_t small[64];
+    int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
+    int rc = hit_tokens(paged, seqs, hit_mask, n_seqs, n_tok);
+    if (rc != KV_OK) {
+        if (n_tok != small) delete[] n_tok;
+        return rc;
+    }
+    if (workspace != nullptr && fmt == KV_FMT_BF16 && max_workgroups == 0)
+        rc = retrieve_ordered(paged, seqs, n_tok, n_seqs, layer0, n_layers, workspace, stream);
+    else
+        rc = run_plan(scatter_plan(fmt), fmt, paged, seqs, n_tok, n_seqs, layer0, n_layers, stream,
                       max_workgroups);
     if (rc == KV_OK && out_tokens != nullptr)
         for (int i = 0; i < n_seqs; ++i) out_tokens[i] = n_tok[i];
@@ -356,6 +431,7 @@ int cachegen_setup(const kv_paged* p, const int32_t* key_bins, const int32_t* va
 }
 
 constexpr Layout kCgLayout = {1, 1, 0};     // symbol sections addressed as 1-byte parts
+
 
 }  // namespace
 
@@ -433,6 +509,33 @@ int kv_retrieve_chunks(const kv_paged* paged, const kv_seq* seqs, const uint8_t*
     if (rc == KV_OK) rc = check_seqs(paged, seqs, n_seqs);
     if (rc != KV_OK) return rc;
     rc = retrieve(paged, seqs, hit_mask, n_seqs, fmt, 0, paged->num_layers, out_tokens, stream);
+    return rc == KV_OK ? ok() : rc;
+}
+
+size_t kv_retrieve_workspace_bytes(const kv_paged* paged)
+{
+    if (check_paged(paged) != KV_OK) return 0;
+    if (paged->num_pages > INT32_MAX) {
+        fail(KV_EINVAL, "num_pages above 2^31: the ordered scatter is not available");
+        return 0;
+    }
+    return size_t(2 * ordered_half_bytes(paged->num_pages));
+}
+
+int kv_retrieve_chunks_ws(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
+                          int fmt, int64_t* out_tokens, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream)
+{
+    int rc = check_paged(paged);
+    if (rc == KV_OK) rc = check_fmt(fmt);
+    if (rc == KV_OK) rc = check_seqs(paged, seqs, n_seqs);
+    if (rc != KV_OK) return rc;
+    const size_t need = kv_retrieve_workspace_bytes(paged);
+    if (need == 0) return KV_EINVAL;
+    if (workspace == nullptr || workspace_bytes < need)
+        return fail(KV_EINVAL, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes, workspace);
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(KV_EINVAL, "workspace must be 256-byte aligned");
+    rc = retrieve(paged, seqs, hit_mask, n_seqs, fmt, 0, paged->num_layers, out_tokens, stream, 0, workspace);
     return rc == KV_OK ? ok() : rc;
 }
 

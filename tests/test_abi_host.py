@@ -220,3 +220,27 @@ def test_cachegen_entry_points_reject_bad_calls():
     assert L.kv_retrieve_chunks_cachegen(ctypes.byref(p), seqs, masks, 1, good, good, out, None) == kvm.KV_OK
     assert out[0] == 0
     assert L.kv_retrieve_chunks_cachegen(ctypes.byref(p), seqs, None, 1, good, good, out, None) == kvm.KV_EINVAL
+
+
+def test_ordered_retrieve_workspace_size_and_rejections():
+    L = _lib()
+    p = _paged(n=8192)
+    assert L.kv_retrieve_workspace_bytes(ctypes.byref(p)) == 2 * 8192 * 4
+    assert L.kv_retrieve_workspace_bytes(ctypes.byref(_paged(n=1000))) == 2 * 4096    # 4000 B rounded to 256
+    assert L.kv_retrieve_workspace_bytes(None) == 0
+    seqs = (kvm._KvSeq * 1)(_seq(0, 1000, 63))
+    m = (ctypes.c_uint8 * 4)(1, 1, 1, 1)
+    masks = (ctypes.c_void_p * 1)(ctypes.addressof(m))
+    out = (ctypes.c_int64 * 1)()
+    need = 2 * 8192 * 4
+    args = (ctypes.byref(p), seqs, masks, 1, kvm.FMT_BF16, out)
+    assert L.kv_retrieve_chunks_ws(*args, None, need, None) == kvm.KV_EINVAL
+    assert L.kv_retrieve_chunks_ws(*args, 0x10000, need - 1, None) == kvm.KV_EINVAL
+    assert "workspace" in L.kv_last_error().decode()
+    assert L.kv_retrieve_chunks_ws(*args, 0x10080, need, None) == kvm.KV_EINVAL          # not 256-aligned
+    # zero hits: KV_OK, nothing launched (no GPU here)
+    m0 = (ctypes.c_uint8 * 4)(0, 1, 1, 1)
+    masks0 = (ctypes.c_void_p * 1)(ctypes.addressof(m0))
+    assert L.kv_retrieve_chunks_ws(ctypes.byref(p), seqs, masks0, 1, kvm.FMT_BF16, out, 0x10000, need,
+                                   None) == kvm.KV_OK
+    assert out[0] == 0

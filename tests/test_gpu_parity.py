@@ -665,3 +665,68 @@ def test_cachegen_special_rows():
     nan_e = ((exp & 0x7F80) == 0x7F80) & ((exp & 0x7F) != 0)
     assert np.array_equal(nan_g, nan_e) and nan_e.any()
     assert np.array_equal(got[~nan_g], exp[~nan_e])
+
+
+# ------------------------------------------------- retrieve in pool-address order
+
+def _ordered_roundtrip(w, fill=0x7E57, masks=None, ws=None):
+    say("case ordered retrieve", w.name)
+    arr = wl.host_pool(w)
+    pool, paged, batch, cs = setup_device(w, arr, fill=0xCD)
+    kvm.store(paged, batch)
+    masks = masks if masks is not None else [sq.hit_mask for sq in w.seqs]
+    ws = paged.new_workspace() if ws is None else ws
+    ws.fill_(0x5C)                                   # contents on entry must not matter
+    pool.view(torch.int16).fill_(int(np.uint16(fill).view(np.int16)))
+    n = kvm.retrieve(paged, batch, masks=masks, workspace=ws)
+    _sync()
+    assert kvm.take_faults() == 0
+    counts = check_retrieve(w, np.full_like(arr, fill), host_from_dev_pool(pool), cs, BF16, masks)
+    assert n == counts
+    return n
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_ordered_retrieve_shapes_and_tails(shape):
+    name, seed, L, H, D, pages, ranges, kw = shape
+    w = wl.custom(name, seed, L, H, D, pages, ranges, **kw)
+    assert _ordered_roundtrip(w) == [e - s for (s, e) in ranges]
+
+
+def test_ordered_retrieve_holes_many_sequences_and_reuse():
+    ranges = [(0, 1000), (0, 1000), (256, 1000), (0, 1000), (0, 600)]
+    masks = [np.array(m, np.uint8) for m in
+             ([1, 1, 0, 1], [0, 1, 1, 1], [1, 0, 1], [1, 1, 1, 1], [1, 1, 1])]
+    w = wl.custom("ord-holes", 351, 3, 2, 32, 400, ranges, masks=masks)
+    assert _ordered_roundtrip(w, fill=0xA5A5) == [512, 0, 256, 1000, 600]
+    # 70 sequences: several launches in one call, one workspace reused by each
+    many = wl.custom("ord-many", 352, 2, 2, 32, 6000, [(0, 1 + 37 * i) for i in range(70)])
+    _ordered_roundtrip(many, fill=0x1234)
+    # one workspace across calls on different pools of the same page count
+    w2 = wl.custom("ord-reuse", 353, 2, 2, 32, 400, [(0, 700), (256, 900)])
+    ws = kvm.Paged.from_pool(dev_pool_from_host(w2, wl.host_pool(w2)), chunk_size=256).new_workspace()
+    _ordered_roundtrip(w2, ws=ws)
+    _ordered_roundtrip(wl.custom("ord-reuse2", 354, 2, 2, 32, 400, [(0, 300)]), ws=ws)
+
+
+def test_ordered_retrieve_bad_page_is_skipped_and_reported():
+    w = wl.custom("ord-badpage", 355, 2, 2, 32, 64, [(0, 300)])
+    arr = wl.host_pool(w)
+    pool, paged, batch, cs = setup_device(w, arr)
+    kvm.store(paged, batch)
+    _sync()
+    bt = w.seqs[0].block_table.copy()
+    bt[3] = 64                                       # == num_pages: out of range
+    bad = kvm.Batch(paged, [kvm.Seq(torch.from_numpy(bt.astype(np.int32)).cuda(), 0, 300, cs[0][0])])
+    pool.view(torch.int16).fill_(0x7E57)
+    kvm.retrieve(paged, bad, masks=[np.ones(2, np.uint8)], workspace=paged.new_workspace())
+    _sync()
+    assert kvm.take_faults() & 1
+    # every other page was written as the oracle writes it; page 3 of the sequence was not
+    got = host_from_dev_pool(pool)
+    exp = np.full_like(arr, 0x7E57)
+    good = w.seqs[0].block_table
+    op = oracle_pool(w, exp)
+    assert oracle.retrieve(op, good, 0, 300, [1, 1], host_chunks(cs[0]), BF16) == 300
+    exp[:, :, good[3]] = 0x7E57                      # the skipped page keeps the sentinel
+    assert np.array_equal(got, exp)

@@ -256,3 +256,24 @@ def test_full_cachegen_8b_sampled_chunks_and_bound():
         assert (pool[:, :, bt[480:]].view(torch.int16) == SENTINEL).all()
     del pool, orig, full, paged, batch, chunk_sets
     _free()
+
+
+def test_full_llama8b_retrieve_in_pool_address_order():
+    # the headline retrieve (30 hit chunks of 8 x 10000 tokens) through the
+    # ordered scatter, compared in full
+    w = wl.llama8b()
+    say("case", w.name, "ordered retrieve")
+    pool = wl.device_pool(w)
+    pool, paged, batch, chunk_sets = setup_device(w, pool=pool, fill=0xCD)
+    kvm.store(paged, batch)
+    sync()
+    pool.view(torch.int16).fill_(SENTINEL)
+    n = kvm.retrieve(paged, batch, workspace=paged.new_workspace())
+    sync()
+    assert kvm.take_faults() == 0
+    assert n == [30 * 256] * 8
+    got = host_from_dev_pool(pool)
+    before = np.full(got.shape, SENTINEL, np.uint16)
+    assert check_retrieve(w, before, got, chunk_sets, BF16, [s.hit_mask for s in w.seqs], copy=False) == n
+    del got, before, pool, paged, batch, chunk_sets
+    _free()
