@@ -653,8 +653,10 @@ def bench_cachegen(args):
         kvm.store_cachegen(paged, batch, kb, vb, stream=stream)
         kvm.retrieve_cachegen(paged, batch, kb, vb, stream=stream)
     reps = max(3, args.steps)
+    ws = paged.new_workspace()
     st_ms = timed(stream, lambda: kvm.store_cachegen(paged, batch, kb, vb, stream=stream), reps)
-    rt_ms = timed(stream, lambda: kvm.retrieve_cachegen(paged, batch, kb, vb, stream=stream), reps)
+    rt_ms = timed(stream, lambda: kvm.retrieve_cachegen(paged, batch, kb, vb, stream=stream, workspace=ws), reps)
+    cm_ms = timed(stream, lambda: kvm.retrieve_cachegen(paged, batch, kb, vb, stream=stream), reps)
     assert kvm.take_faults() == 0
     st, rt = st_bytes / (st_ms / 1e3) / 1e9, rt_bytes / (rt_ms / 1e3) / 1e9
     return {
@@ -665,6 +667,9 @@ def bench_cachegen(args):
         "retrieve_ms": round(rt_ms, 4), "retrieve_GBps": round(rt, 2),
         "retrieve_pct_hbm_peak": round(100 * rt / HBM_PEAK_GBPS, 2),
         "retrieve_tokens_per_s": round(rtok / (rt_ms / 1e3), 1),
+        "retrieve_order": "pool-address (workspace)",
+        "retrieve_chunk_major_ms": round(cm_ms, 4),
+        "retrieve_chunk_major_GBps": round(rt_bytes / (cm_ms / 1e3) / 1e9, 2),
     }
 
 
@@ -694,8 +699,10 @@ def bench_simple(args, name, fmt):
         kvm.store(paged, batch, fmt, stream=stream)
         kvm.retrieve(paged, batch, fmt=fmt, stream=stream)
     reps = max(3, args.steps)
+    ws = paged.new_workspace()
     st_ms = timed(stream, lambda: kvm.store(paged, batch, fmt, stream=stream), reps)
-    rt_ms = timed(stream, lambda: kvm.retrieve(paged, batch, fmt=fmt, stream=stream), reps)
+    rt_ms = timed(stream, lambda: kvm.retrieve(paged, batch, fmt=fmt, stream=stream, workspace=ws), reps)
+    cm_ms = timed(stream, lambda: kvm.retrieve(paged, batch, fmt=fmt, stream=stream), reps)
     assert kvm.take_faults() == 0
     st, rt = st_bytes / (st_ms / 1e3) / 1e9, rt_bytes / (rt_ms / 1e3) / 1e9
     return {
@@ -706,6 +713,9 @@ def bench_simple(args, name, fmt):
         "retrieve_ms": round(rt_ms, 4), "retrieve_GBps": round(rt, 2),
         "retrieve_pct_hbm_peak": round(100 * rt / HBM_PEAK_GBPS, 2),
         "retrieve_tokens_per_s": round(rtok / (rt_ms / 1e3), 1),
+        "retrieve_order": "pool-address (workspace)",
+        "retrieve_chunk_major_ms": round(cm_ms, 4),
+        "retrieve_chunk_major_GBps": round(rt_bytes / (cm_ms / 1e3) / 1e9, 2),
     }
 
 

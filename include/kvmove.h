@@ -188,17 +188,17 @@ int kv_retrieve_chunks(const kv_paged* paged, const kv_seq* seqs,
                        int64_t* out_tokens, hipStream_t stream);
 
 /* Retrieve in pool-address order: the same operation and result as
- * kv_retrieve_chunks, with the bf16 scatter visiting its page units by
+ * kv_retrieve_chunks, with the scatter visiting its page units by
  * destination address (layer, K/V, page id) instead of chunk by chunk.
  * Random destination pages cost DRAM more on writes than on reads; this
  * order makes the writes near-sequential and measured about 6 % faster on
  * the Llama-3.1-8B workload.  It needs the hit pages sorted by page id,
  * which is done on the device in `workspace` (DEVICE memory the caller
  * owns, at least kv_retrieve_workspace_bytes(paged) bytes, 256-byte
- * aligned; its contents on entry do not matter and are overwritten).  Other
- * formats ignore the workspace and run as kv_retrieve_chunks.  A sequence
- * moving 2^26 pages or more is rejected (KV_EINVAL).  Calls that share a
- * workspace must be ordered on one stream. */
+ * aligned; its contents on entry do not matter and are overwritten).  Every
+ * format has an ordered scatter (for KV_FMT_K16_V8 each of its two launches
+ * builds the list).  A sequence moving 2^26 pages or more is rejected
+ * (KV_EINVAL).  Calls that share a workspace must be ordered on one stream. */
 size_t kv_retrieve_workspace_bytes(const kv_paged* paged);   /* 0 on a malformed pool */
 int kv_retrieve_chunks_ws(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
                           int fmt, int64_t* out_tokens, void* workspace, size_t workspace_bytes,
@@ -236,12 +236,15 @@ int kv_retrieve_layer(const kv_paged* paged, const kv_seq* seqs,
  * tokens: symbols u8 [L][2][n][H*D], then float32 max1 [L][2][n]
  * (kv_chunk_bytes with KV_FMT_CACHEGEN_INT8).  Limits: num_layers <= 128,
  * H*D <= 4096.  Only the quantiser: the CDF and arithmetic coding that
- * follow it on that page are not implemented. */
+ * follow it on that page are not implemented.  workspace / workspace_bytes
+ * as in kv_retrieve_chunks_ws: with one (DEVICE, caller-owned) the scatter
+ * runs in pool-address order; NULL runs it chunk by chunk. */
 int kv_store_chunks_cachegen(const kv_paged* paged, const kv_seq* seqs, int n_seqs, const int32_t* key_bins,
                              const int32_t* value_bins, hipStream_t stream);
 int kv_retrieve_chunks_cachegen(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask,
                                 int n_seqs, const int32_t* key_bins, const int32_t* value_bins,
-                                int64_t* out_tokens, hipStream_t stream);
+                                int64_t* out_tokens, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
 
 /* Message for the last non-OK return on this thread ("" if none). */
 const char* kv_last_error(void);

@@ -96,7 +96,7 @@ def load():
         "kv_store_chunks_cachegen": (ctypes.c_int, [P, S, ctypes.c_int, vp, vp, vp]),
         "kv_retrieve_workspace_bytes": (ctypes.c_size_t, [P]),
         "kv_retrieve_chunks_ws": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]),
-        "kv_retrieve_chunks_cachegen": (ctypes.c_int, [P, S, vp, ctypes.c_int, vp, vp, vp, vp]),
+        "kv_retrieve_chunks_cachegen": (ctypes.c_int, [P, S, vp, ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "kv_last_error": (ctypes.c_char_p, []),
         "kv_take_faults": (ctypes.c_int, []),
         "kv_copy_bytes": (ctypes.c_int, [vp, vp, ctypes.c_size_t, vp]),
@@ -275,6 +275,15 @@ def store_layer(paged: Paged, seqs, layer: int, fmt: int = FMT_BF16, stream=None
                                  _stream_handle(stream), _event_handle(event, stream)))
 
 
+def _workspace(workspace):
+    """(address, bytes) of a workspace tensor, or (None, 0)."""
+    if workspace is None:
+        return None, 0
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise KvError(KV_EINVAL, "workspace must be a contiguous device tensor")
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
 def _bins(bins, n):
     """One bin count per layer as a host int32 array."""
     bins = [int(b) for b in bins]
@@ -292,17 +301,19 @@ def store_cachegen(paged: Paged, seqs, key_bins, value_bins, stream=None) -> Non
                                            _bins(value_bins, L), _stream_handle(stream)))
 
 
-def retrieve_cachegen(paged: Paged, seqs, key_bins, value_bins, masks=None, stream=None) -> list:
-    """Dequantise + scatter the leading hit chunks (kv_retrieve_chunks_cachegen).
+def retrieve_cachegen(paged: Paged, seqs, key_bins, value_bins, masks=None, stream=None, workspace=None) -> list:
+    """Dequantise + scatter the leading hit chunks (kv_retrieve_chunks_cachegen);
+    in pool-address order when a ``workspace`` (as for retrieve) is given.
     Returns the tokens made available per sequence."""
     b = _batch(paged, seqs)
     if masks is not None:
         b.set_masks(masks)
     assert b._mask_ptrs is not None, "hit masks are required"
     L = paged.c.num_layers
+    ws_ptr, ws_bytes = _workspace(workspace)
     _check(load().kv_retrieve_chunks_cachegen(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n,
                                               _bins(key_bins, L), _bins(value_bins, L), b.out,
-                                              _stream_handle(stream)))
+                                              ws_ptr, ws_bytes, _stream_handle(stream)))
     return [int(b.out[i]) for i in range(b.n)]
 
 
@@ -320,11 +331,9 @@ def retrieve(paged: Paged, seqs, masks=None, fmt: int = FMT_BF16, stream=None, w
         _check(load().kv_retrieve_chunks(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n, fmt, b.out,
                                          _stream_handle(stream)))
     else:
-        if not workspace.is_cuda or not workspace.is_contiguous():
-            raise KvError(KV_EINVAL, "workspace must be a contiguous device tensor")
+        ws_ptr, ws_bytes = _workspace(workspace)
         _check(load().kv_retrieve_chunks_ws(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n, fmt, b.out,
-                                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                            _stream_handle(stream)))
+                                            ws_ptr, ws_bytes, _stream_handle(stream)))
     return [int(b.out[i]) for i in range(b.n)]
 
 

@@ -138,10 +138,9 @@ __global__ __launch_bounds__(kCgBlock) void store_cachegen(CgArgs ca)
 }
 
 template <int kVpl>
-__global__ __launch_bounds__(kCgBlock) void retrieve_cachegen(CgArgs ca)
+__device__ __forceinline__ void retrieve_cachegen_unit(const CgArgs& ca, const PageUnit& u)
 {
     const MoveArgs& a = ca.m;
-    const PageUnit u = locate_page_unit(a, a.item_base + xcd_contiguous(blockIdx.x, gridDim.x));
     if (u.page < 0 || u.page >= a.num_pages) { raise_fault(kFaultPage); return; }
     const uint64_t pool = wave_uniform(gptr<const gu64>(u.kv ? a.v_pages : a.k_pages)[u.l]);
     const uint64_t chunk = wave_uniform(gptr<const gu64>(a.seq[u.s].chunks)[u.c]);
@@ -179,6 +178,21 @@ __global__ __launch_bounds__(kCgBlock) void retrieve_cachegen(CgArgs ca)
             __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * 64 + lane) * 16, 0, kCpolNt);
         }
     }
+}
+
+template <int kVpl>
+__global__ __launch_bounds__(kCgBlock) void retrieve_cachegen(CgArgs ca)
+{
+    retrieve_cachegen_unit<kVpl>(ca, locate_page_unit(ca.m, ca.m.item_base + xcd_contiguous(blockIdx.x, gridDim.x)));
+}
+
+// The same in pool-address order (sorted page list, see sorted_unit).
+template <int kVpl>
+__global__ __launch_bounds__(kCgBlock) void retrieve_cachegen_sorted(CgArgs ca, uint64_t list, uint32_t n_list)
+{
+    PageUnit u;
+    if (!sorted_unit(ca.m, list, n_list, xcd_contiguous(blockIdx.x, gridDim.x), u)) return;
+    retrieve_cachegen_unit<kVpl>(ca, u);
 }
 
 }  // namespace kvmove

@@ -185,6 +185,36 @@ __device__ __forceinline__ PageUnit locate_page_unit(const MoveArgs& a, uint32_t
     return u;
 }
 
+// Entries of a launch's page list sorted by page id (kv_order.hpp builds it):
+// (sequence slot << 26) | page index in the sequence; kNoEntry pads it.
+constexpr uint32_t kNoEntry = 0xFFFFFFFFu;
+constexpr int kSeqShift = 26;
+constexpr uint32_t kPageIndexMask = (1u << kSeqShift) - 1;
+
+// The page unit of a pool-address-ordered launch: unit = slab * n_list + k,
+// slab = the (layer, K/V) pair, k = the k-th smallest page id; false for a
+// padding entry.
+__device__ __forceinline__ bool sorted_unit(const MoveArgs& a, uint64_t list, uint32_t n_list, uint32_t unit,
+                                            PageUnit& u)
+{
+    const uint32_t slab = unit / n_list, k = unit - slab * n_list;
+    const uint32_t e = __builtin_amdgcn_readfirstlane(gptr<const gi32>(list)[k]);
+    if (e == kNoEntry) return false;
+    u.s = e >> kSeqShift;
+    const uint32_t q = e & kPageIndexMask;
+    const SeqArg& sq = a.seq[u.s];
+    u.c = q / a.pages_per_chunk;
+    const uint32_t pi = q - u.c * a.pages_per_chunk;
+    u.n_c = u.c < sq.n_full ? a.chunk_size : sq.tail_tokens;
+    u.j0 = pi * a.page_size;
+    const uint32_t left = u.n_c - u.j0;
+    u.rows = left < a.page_size ? left : a.page_size;
+    u.l = a.layer0 + slab / a.n_kv;
+    u.kv = a.kv0 + slab % a.n_kv;
+    u.page = gptr<const gi32>(sq.bt)[sq.first_page + q];
+    return true;
+}
+
 // Streams nvec 16-byte vectors src -> dst: kVpt loads in flight per thread
 // before the matching stores; a strided remainder loop for partial pages.
 template <int kBlock, int kVpt, bool kNtLoad, bool kNtStore>

@@ -360,11 +360,8 @@ __global__ __launch_bounds__(kBlock) void store_fp8(MoveArgs a)
 // Tiles are kBlock*kVpt*16 bytes of bf16 output; grid = units * a.tiles, or
 // fewer workgroups each taking a contiguous run of tiles.
 template <int kBlock, int kVpt, bool kE5M2>
-__device__ __forceinline__ void retrieve_fp8_tile(const MoveArgs& a, uint32_t b)
+__device__ __forceinline__ void retrieve_fp8_unit_tile(const MoveArgs& a, const PageUnit& u, uint32_t tile)
 {
-    const uint32_t unit = b / a.tiles;
-    const uint32_t tile = b - unit * a.tiles;
-    const PageUnit u = locate_page_unit(a, a.item_base + unit);
     const uint32_t out_bytes = u.rows * a.width * 2;
     const uint32_t lo = tile * (kBlock * kVpt * 16);
     if (lo >= out_bytes) return;
@@ -402,6 +399,25 @@ __device__ __forceinline__ void retrieve_fp8_tile(const MoveArgs& a, uint32_t b)
         }
         __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * kBlock + threadIdx.x) * 16, 0, kCpolNt);
     }
+}
+
+template <int kBlock, int kVpt, bool kE5M2>
+__device__ __forceinline__ void retrieve_fp8_tile(const MoveArgs& a, uint32_t b)
+{
+    const uint32_t unit = b / a.tiles;
+    const uint32_t tile = b - unit * a.tiles;
+    retrieve_fp8_unit_tile<kBlock, kVpt, kE5M2>(a, locate_page_unit(a, a.item_base + unit), tile);
+}
+
+// The same in pool-address order (sorted page list, see sorted_unit).
+template <int kBlock, int kVpt, bool kE5M2>
+__global__ __launch_bounds__(kBlock) void retrieve_fp8_sorted(MoveArgs a, uint64_t list, uint32_t n_list)
+{
+    const uint32_t b = xcd_contiguous(blockIdx.x, gridDim.x);
+    const uint32_t unit = b / a.tiles, tile = b - unit * a.tiles;
+    PageUnit u;
+    if (!sorted_unit(a, list, n_list, unit, u)) return;
+    retrieve_fp8_unit_tile<kBlock, kVpt, kE5M2>(a, u, tile);
 }
 
 template <int kBlock, int kVpt, bool kE5M2>

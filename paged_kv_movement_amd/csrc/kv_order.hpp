@@ -13,7 +13,9 @@
 //   fill_u32       inv[0 .. num_pages) = kNoEntry
 //   invert_pages   inv[page] = (sequence slot << 26) | page index in the sequence
 //   compact_pages  list = the entries of inv in page order, padded with kNoEntry
-//   scatter_sorted one workgroup per tile of (layer, K/V, list entry)
+//   scatter_sorted one workgroup per tile of (layer, K/V, list entry); the
+//                  fp8 and CacheGen retrieves have ordered variants too
+//                  (retrieve_fp8_sorted, retrieve_cachegen_sorted)
 // inv and list live in a workspace the caller provides (2 * num_pages words).
 #pragma once
 
@@ -21,9 +23,6 @@
 
 namespace kvmove {
 
-constexpr uint32_t kNoEntry = 0xFFFFFFFFu;
-constexpr int kSeqShift = 26;                       // entry = slot << 26 | page index (< 2^26)
-constexpr uint32_t kPageIndexMask = (1u << kSeqShift) - 1;
 constexpr int kCompactBlock = 1024;
 constexpr int kCompactPerThread = 16;
 
@@ -102,30 +101,15 @@ __global__ __launch_bounds__(kCompactBlock) void compact_pages(uint64_t inv, uin
     for (uint32_t k = base + t; k < list_len; k += kCompactBlock) gptr<gu32>(list)[k] = kNoEntry;
 }
 
-// Scatter in destination order: unit = slab * n_list + k, slab = the (layer,
-// K/V) pair, k = the k-th smallest page id of the launch; a.tiles tiles per
-// unit, one workgroup per tile.
+// bf16 scatter in destination order: a.tiles tiles per sorted unit, one
+// workgroup per tile.
 template <int kBlock, int kVpt, int kAuxLoad, int kAuxStore>
 __global__ __launch_bounds__(kBlock) void scatter_sorted(MoveArgs a, uint64_t list, uint32_t n_list)
 {
     const uint32_t b = xcd_contiguous(blockIdx.x, gridDim.x);
     const uint32_t unit = b / a.tiles, tile = b - unit * a.tiles;
-    const uint32_t slab = unit / n_list, k = unit - slab * n_list;
-    const uint32_t e = __builtin_amdgcn_readfirstlane(gptr<const gu32>(list)[k]);
-    if (e == kNoEntry) return;
     PageUnit u;
-    u.s = e >> kSeqShift;
-    const uint32_t q = e & kPageIndexMask;
-    const SeqArg& sq = a.seq[u.s];
-    u.c = q / a.pages_per_chunk;
-    const uint32_t pi = q - u.c * a.pages_per_chunk;
-    u.n_c = u.c < sq.n_full ? a.chunk_size : sq.tail_tokens;
-    u.j0 = pi * a.page_size;
-    const uint32_t left = u.n_c - u.j0;
-    u.rows = left < a.page_size ? left : a.page_size;
-    u.l = a.layer0 + slab / a.n_kv;
-    u.kv = a.kv0 + slab % a.n_kv;
-    u.page = gptr<const gi32>(sq.bt)[sq.first_page + q];
+    if (!sorted_unit(a, list, n_list, unit, u)) return;
     move_unit_tile<false, kBlock, kVpt, kAuxLoad, kAuxStore>(a, u, tile);
 }
 

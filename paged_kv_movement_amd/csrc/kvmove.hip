@@ -141,6 +141,7 @@ struct Launch {
     int tile_bytes;   // bytes of page-side data per workgroup (0: one workgroup per unit)
     Unit unit;
     uint32_t kv0, n_kv;
+    KernelFn sorted;  // the scatter kernel in pool-address order (retrieves only; else nullptr)
 };
 
 // The launches of one store or retrieve: one, or one per part when K and V
@@ -254,7 +255,10 @@ Launch bf16_launch(bool to_chunk, uint32_t kv0, uint32_t n_kv)
         to_chunk ? reinterpret_cast<KernelFn>(&move_bf16<true, kMoveBlock, kMoveVpt, kGatherAuxLoad, kGatherAuxStore>)
                  : reinterpret_cast<KernelFn>(
                        &move_bf16<false, kMoveBlock, kMoveVpt, kScatterAuxLoad, kScatterAuxStore>);
-    return {k, kMoveBlock, kMoveBlock * kMoveVpt * 16, Unit::Page, kv0, n_kv};
+    const KernelFn sorted =
+        to_chunk ? nullptr
+                 : reinterpret_cast<KernelFn>(&scatter_sorted<kMoveBlock, kMoveVpt, kScatterAuxLoad, kScatterAuxStore>);
+    return {k, kMoveBlock, kMoveBlock * kMoveVpt * 16, Unit::Page, kv0, n_kv, sorted};
 }
 
 // Gather + quantise: a whole (chunk, layer, K/V) group on chip when it fits,
@@ -265,18 +269,21 @@ Launch quantise_launch(const kv_paged* p, bool e5m2, uint32_t kv0, uint32_t n_kv
     if (group_vectors <= int64_t(kOnchipMaxVectors) && p->chunk_size / p->page_size <= kOnchipMaxPages) {
         const KernelFn k = e5m2 ? reinterpret_cast<KernelFn>(&store_fp8_onchip<true>)
                                 : reinterpret_cast<KernelFn>(&store_fp8_onchip<false>);
-        return {k, kOnchipBlock, 0, Unit::Group, kv0, n_kv};
+        return {k, kOnchipBlock, 0, Unit::Group, kv0, n_kv, nullptr};
     }
     const KernelFn k = e5m2 ? reinterpret_cast<KernelFn>(&store_fp8<kFp8StoreBlock, kFp8StoreUnroll, true>)
                             : reinterpret_cast<KernelFn>(&store_fp8<kFp8StoreBlock, kFp8StoreUnroll, false>);
-    return {k, kFp8StoreBlock, 0, Unit::Group, kv0, n_kv};
+    return {k, kFp8StoreBlock, 0, Unit::Group, kv0, n_kv, nullptr};
 }
 
 Launch dequantise_launch(bool e5m2, uint32_t kv0, uint32_t n_kv)
 {
     const KernelFn k = e5m2 ? reinterpret_cast<KernelFn>(&retrieve_fp8<kFp8RetrieveBlock, kFp8RetrieveVpt, true>)
                             : reinterpret_cast<KernelFn>(&retrieve_fp8<kFp8RetrieveBlock, kFp8RetrieveVpt, false>);
-    return {k, kFp8RetrieveBlock, kFp8RetrieveBlock * kFp8RetrieveVpt * 16, Unit::Page, kv0, n_kv};
+    const KernelFn sorted =
+        e5m2 ? reinterpret_cast<KernelFn>(&retrieve_fp8_sorted<kFp8RetrieveBlock, kFp8RetrieveVpt, true>)
+             : reinterpret_cast<KernelFn>(&retrieve_fp8_sorted<kFp8RetrieveBlock, kFp8RetrieveVpt, false>);
+    return {k, kFp8RetrieveBlock, kFp8RetrieveBlock * kFp8RetrieveVpt * 16, Unit::Page, kv0, n_kv, sorted};
 }
 
 Plan gather_plan(const kv_paged* p, int fmt)
@@ -315,24 +322,25 @@ int run_plan(const Plan& plan, int fmt, const kv_paged* p, const kv_seq* seqs, c
 // the sorted list, num_pages words each, 256-byte aligned.
 int64_t ordered_half_bytes(int64_t num_pages) { return ceil_div(num_pages * 4, 256) * 256; }
 
-// bf16 scatter of the tokens n_tok[i] in pool-address order (kv_order.hpp).
-int retrieve_ordered(const kv_paged* p, const kv_seq* seqs, const int64_t* n_tok, int n_seqs, int32_t layer0,
-                     int32_t n_layers, void* workspace, hipStream_t stream)
+// Scatter launch L (its `sorted` kernel) of the tokens n_tok[i] in
+// pool-address order (kv_order.hpp): per packed launch, the page list is
+// built in the workspace, then the ordered kernel runs over it.
+int retrieve_ordered(const Launch& L, const Layout& lay, const kv_paged* p, const kv_seq* seqs,
+                     const int64_t* n_tok, int n_seqs, int32_t layer0, int32_t n_layers, void* workspace,
+                     hipStream_t stream, const uint8_t (*cg_qmax)[kCgMaxLayers] = nullptr)
 {
     const uint64_t inv = reinterpret_cast<uint64_t>(workspace);
     const uint64_t list = inv + uint64_t(ordered_half_bytes(p->num_pages));
     const uint32_t num_pages = uint32_t(p->num_pages);
-    const Launch L = bf16_launch(false, 0, 2);
     auto flush = [&](MoveArgs& a, int64_t total) -> int {
         const int64_t n_list = total / (int64_t(n_layers) * a.n_kv);      // pages moved by this launch
         for (uint32_t s = 0; s < a.n_seqs; ++s)
             if (a.seq[s].n_full * a.pages_per_chunk + ceil_div(a.seq[s].tail_tokens, a.page_size) > kPageIndexMask)
-                return fail(KV_EINVAL, "a sequence moves 2^26 pages or more: use kv_retrieve_chunks");
+                return fail(KV_EINVAL, "a sequence moves 2^26 pages or more: retrieve without a workspace");
         const unsigned fill_grid = unsigned(std::min<int64_t>(ceil_div(num_pages, 256), 4096));
-        const uint32_t none = kNoEntry;
-        uint32_t np = num_pages, nl = uint32_t(n_list);
+        uint32_t none = kNoEntry, np = num_pages, nl = uint32_t(n_list);
         uint64_t inv_a = inv, list_a = list;
-        void* fill_args[] = {&inv_a, &np, const_cast<uint32_t*>(&none)};
+        void* fill_args[] = {&inv_a, &np, &none};
         hipError_t e = hipLaunchKernel(reinterpret_cast<KernelFn>(&fill_u32), dim3(fill_grid), dim3(256), fill_args,
                                        0, stream);
         if (e == hipSuccess) {
@@ -346,15 +354,22 @@ int retrieve_ordered(const kv_paged* p, const kv_seq* seqs, const int64_t* n_tok
                                 stream);
         }
         if (e == hipSuccess) {
-            void* sc_args[] = {&a, &list_a, &nl};
-            e = hipLaunchKernel(reinterpret_cast<KernelFn>(
-                                    &scatter_sorted<kMoveBlock, kMoveVpt, kScatterAuxLoad, kScatterAuxStore>),
-                                dim3(a.total_tiles), dim3(kMoveBlock), sc_args, 0, stream);
+            if (cg_qmax != nullptr) {          // CacheGen kernels take the bins beside the move arguments
+                CgArgs ca{};
+                ca.m = a;
+                for (int kv = 0; kv < 2; ++kv)
+                    for (int l = 0; l < kCgMaxLayers; ++l) ca.qmax[kv][l] = cg_qmax[kv][l];
+                void* sc_args[] = {&ca, &list_a, &nl};
+                e = hipLaunchKernel(L.sorted, dim3(a.total_tiles), dim3(L.block), sc_args, 0, stream);
+            } else {
+                void* sc_args[] = {&a, &list_a, &nl};
+                e = hipLaunchKernel(L.sorted, dim3(a.total_tiles), dim3(L.block), sc_args, 0, stream);
+            }
         }
         if (e != hipSuccess) return fail(KV_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
         return KV_OK;
     };
-    return pack_units(L, layout_of(KV_FMT_BF16), p, seqs, n_tok, n_seqs, layer0, n_layers, flush);
+    return pack_units(L, lay, p, seqs, n_tok, n_seqs, layer0, n_layers, flush);
 }
 
 // Tokens each sequence gets back: its leading hit chunks, from tok_start.
@@ -386,9 +401,12 @@ int retrieve(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hi
         if (n_tok != small) delete[] n_tok;
         return rc;
     }
-    if (workspace != nullptr && fmt == KV_FMT_BF16 && max_workgroups == 0)
-        rc = retrieve_ordered(paged, seqs, n_tok, n_seqs, layer0, n_layers, workspace, stream);
-    else
+    if (workspace != nullptr && max_workgroups == 0) {
+        const Plan plan = scatter_plan(fmt);
+        for (int k = 0; k < plan.n && rc == KV_OK; ++k)
+            rc = retrieve_ordered(plan.part[k], layout_of(fmt), paged, seqs, n_tok, n_seqs, layer0, n_layers,
+                                  workspace, stream);
+    } else
         rc = run_plan(scatter_plan(fmt), fmt, paged, seqs, n_tok, n_seqs, layer0, n_layers, stream,
                       max_workgroups);
     if (rc == KV_OK && out_tokens != nullptr)
@@ -418,15 +436,28 @@ int cachegen_setup(const kv_paged* p, const int32_t* key_bins, const int32_t* va
     }
     // rows of the page unit, a whole row per wave: kVpl 16-byte vectors per lane
     const int64_t vpl = (width / 8 + 63) / 64;
-    KernelFn ks, kr;
-    if (vpl <= 1) { ks = reinterpret_cast<KernelFn>(&store_cachegen<1>); kr = reinterpret_cast<KernelFn>(&retrieve_cachegen<1>); }
-    else if (vpl <= 2) { ks = reinterpret_cast<KernelFn>(&store_cachegen<2>); kr = reinterpret_cast<KernelFn>(&retrieve_cachegen<2>); }
-    else if (vpl <= 4) { ks = reinterpret_cast<KernelFn>(&store_cachegen<4>); kr = reinterpret_cast<KernelFn>(&retrieve_cachegen<4>); }
-    else { ks = reinterpret_cast<KernelFn>(&store_cachegen<8>); kr = reinterpret_cast<KernelFn>(&retrieve_cachegen<8>); }
+    KernelFn ks, kr, ko;
+    if (vpl <= 1) {
+        ks = reinterpret_cast<KernelFn>(&store_cachegen<1>);
+        kr = reinterpret_cast<KernelFn>(&retrieve_cachegen<1>);
+        ko = reinterpret_cast<KernelFn>(&retrieve_cachegen_sorted<1>);
+    } else if (vpl <= 2) {
+        ks = reinterpret_cast<KernelFn>(&store_cachegen<2>);
+        kr = reinterpret_cast<KernelFn>(&retrieve_cachegen<2>);
+        ko = reinterpret_cast<KernelFn>(&retrieve_cachegen_sorted<2>);
+    } else if (vpl <= 4) {
+        ks = reinterpret_cast<KernelFn>(&store_cachegen<4>);
+        kr = reinterpret_cast<KernelFn>(&retrieve_cachegen<4>);
+        ko = reinterpret_cast<KernelFn>(&retrieve_cachegen_sorted<4>);
+    } else {
+        ks = reinterpret_cast<KernelFn>(&store_cachegen<8>);
+        kr = reinterpret_cast<KernelFn>(&retrieve_cachegen<8>);
+        ko = reinterpret_cast<KernelFn>(&retrieve_cachegen_sorted<8>);
+    }
     // one workgroup per page unit
     const int page_bytes = int(int64_t(p->page_size) * width * 2);
-    *store = {ks, kCgBlock, page_bytes, Unit::Page, 0, 2};
-    *scatter = {kr, kCgBlock, page_bytes, Unit::Page, 0, 2};
+    *store = {ks, kCgBlock, page_bytes, Unit::Page, 0, 2, nullptr};
+    *scatter = {kr, kCgBlock, page_bytes, Unit::Page, 0, 2, ko};
     return KV_OK;
 }
 
@@ -611,7 +642,7 @@ int kv_store_chunks_cachegen(const kv_paged* paged, const kv_seq* seqs, int n_se
 
 int kv_retrieve_chunks_cachegen(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask,
                                 int n_seqs, const int32_t* key_bins, const int32_t* value_bins,
-                                int64_t* out_tokens, hipStream_t stream)
+                                int64_t* out_tokens, void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
     int rc = check_paged(paged);
     if (rc == KV_OK) rc = check_seqs(paged, seqs, n_seqs);
@@ -634,7 +665,18 @@ int kv_retrieve_chunks_cachegen(const kv_paged* paged, const kv_seq* seqs, const
         const int64_t end = q.tok_start + n_hit * paged->chunk_size;
         n_tok[i] = (end < q.tok_end ? end : q.tok_end) - q.tok_start;
     }
-    rc = launch_units(sc, kCgLayout, paged, seqs, n_tok, n_seqs, 0, paged->num_layers, stream, 0, qmax);
+    if (workspace != nullptr) {
+        const size_t need = kv_retrieve_workspace_bytes(paged);
+        if (need == 0 || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0) {
+            if (n_tok != small) delete[] n_tok;
+            return fail(KV_EINVAL, "workspace of %zu bytes, 256-byte aligned, needed (got %zu at %p)", need,
+                        workspace_bytes, workspace);
+        }
+        rc = retrieve_ordered(sc, kCgLayout, paged, seqs, n_tok, n_seqs, 0, paged->num_layers, workspace, stream,
+                              qmax);
+    } else {
+        rc = launch_units(sc, kCgLayout, paged, seqs, n_tok, n_seqs, 0, paged->num_layers, stream, 0, qmax);
+    }
     if (rc == KV_OK && out_tokens != nullptr)
         for (int i = 0; i < n_seqs; ++i) out_tokens[i] = n_tok[i];
     if (n_tok != small) delete[] n_tok;

@@ -217,9 +217,18 @@ def test_cachegen_entry_points_reject_bad_calls():
     m0 = (ctypes.c_uint8 * 4)(0, 1, 1, 1)
     masks = (ctypes.c_void_p * 1)(ctypes.addressof(m0))
     out = (ctypes.c_int64 * 1)(-7)
-    assert L.kv_retrieve_chunks_cachegen(ctypes.byref(p), seqs, masks, 1, good, good, out, None) == kvm.KV_OK
+    assert L.kv_retrieve_chunks_cachegen(ctypes.byref(p), seqs, masks, 1, good, good, out, None, 0, None) == kvm.KV_OK
     assert out[0] == 0
-    assert L.kv_retrieve_chunks_cachegen(ctypes.byref(p), seqs, None, 1, good, good, out, None) == kvm.KV_EINVAL
+    assert L.kv_retrieve_chunks_cachegen(ctypes.byref(p), seqs, None, 1, good, good, out, None, 0,
+                                         None) == kvm.KV_EINVAL
+    # a workspace that is too small or misaligned is refused
+    m1 = (ctypes.c_uint8 * 4)(1, 1, 1, 1)
+    masks1 = (ctypes.c_void_p * 1)(ctypes.addressof(m1))
+    need = L.kv_retrieve_workspace_bytes(ctypes.byref(p))
+    assert L.kv_retrieve_chunks_cachegen(ctypes.byref(p), seqs, masks1, 1, good, good, out, 0x10000, need - 1,
+                                         None) == kvm.KV_EINVAL
+    assert L.kv_retrieve_chunks_cachegen(ctypes.byref(p), seqs, masks1, 1, good, good, out, 0x10040, need,
+                                         None) == kvm.KV_EINVAL
 
 
 def test_ordered_retrieve_workspace_size_and_rejections():

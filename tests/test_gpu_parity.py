@@ -669,21 +669,51 @@ def test_cachegen_special_rows():
 
 # ------------------------------------------------- retrieve in pool-address order
 
-def _ordered_roundtrip(w, fill=0x7E57, masks=None, ws=None):
-    say("case ordered retrieve", w.name)
+def _ordered_roundtrip(w, fill=0x7E57, masks=None, ws=None, fmt=BF16):
+    say("case ordered retrieve", w.name, fmt)
     arr = wl.host_pool(w)
-    pool, paged, batch, cs = setup_device(w, arr, fill=0xCD)
-    kvm.store(paged, batch)
+    pool, paged, batch, cs = setup_device(w, arr, fmt=fmt, fill=0xCD)
+    kvm.store(paged, batch, fmt)
     masks = masks if masks is not None else [sq.hit_mask for sq in w.seqs]
     ws = paged.new_workspace() if ws is None else ws
     ws.fill_(0x5C)                                   # contents on entry must not matter
     pool.view(torch.int16).fill_(int(np.uint16(fill).view(np.int16)))
-    n = kvm.retrieve(paged, batch, masks=masks, workspace=ws)
+    n = kvm.retrieve(paged, batch, masks=masks, fmt=fmt, workspace=ws)
     _sync()
     assert kvm.take_faults() == 0
-    counts = check_retrieve(w, np.full_like(arr, fill), host_from_dev_pool(pool), cs, BF16, masks)
+    counts = check_retrieve(w, np.full_like(arr, fill), host_from_dev_pool(pool), cs, fmt, masks)
     assert n == counts
     return n
+
+
+ORDERED_SHAPES = [s for s in SHAPES if s[0] in ("tails", "wide", "odd-width", "page32", "chunk128")]
+
+
+@pytest.mark.parametrize("shape", ORDERED_SHAPES, ids=[s[0] for s in ORDERED_SHAPES])
+@pytest.mark.parametrize("fmt", [FP8, E5M2, K16V8], ids=["fp8", "e5m2", "k16v8"])
+def test_ordered_retrieve_quantised_formats(shape, fmt):
+    name, seed, L, H, D, pages, ranges, kw = shape
+    w = wl.custom(name, seed, L, H, D, pages, ranges, outliers=2, **kw)
+    assert _ordered_roundtrip(w, fmt=fmt) == [e - s for (s, e) in ranges]
+
+
+@pytest.mark.parametrize("shape", ORDERED_SHAPES, ids=[s[0] for s in ORDERED_SHAPES])
+def test_ordered_retrieve_cachegen(shape):
+    name, seed, L, H, D, pages, ranges, kw = shape
+    w = wl.custom(name, seed, L, H, D, pages, ranges, outliers=2, **kw)
+    kb, vb = cachegen_bins(L, seed + 7)
+    arr = wl.host_pool(w)
+    pool, paged, batch, cs = setup_device(w, arr, fmt=kvm.FMT_CACHEGEN, fill=0xCD)
+    kvm.store_cachegen(paged, batch, kb, vb)
+    pool.view(torch.int16).fill_(0x7E57)
+    ws = paged.new_workspace()
+    ws.fill_(0xA3)
+    n = kvm.retrieve_cachegen(paged, batch, kb, vb, workspace=ws)
+    _sync()
+    assert kvm.take_faults() == 0
+    counts = check_retrieve_cachegen(w, np.full_like(arr, 0x7E57), host_from_dev_pool(pool), cs,
+                                     [sq.hit_mask for sq in w.seqs], kb, vb)
+    assert n == counts == [e - s for (s, e) in ranges]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])

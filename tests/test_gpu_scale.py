@@ -152,6 +152,14 @@ def test_full_fp8_8b_sampled_chunks_and_bounds(fmt):
     del got_pool
     from test_gpu_parity import _assert_fp8_bound
     _assert_fp8_bound(w, orig, pool, chunk_sets, fmt)
+    # the retrieve in pool-address order gives the same pool, bit for bit
+    ordered = pool.clone()
+    pool.zero_()
+    assert kvm.retrieve(paged, batch, fmt=fmt, workspace=paged.new_workspace()) == [10000] * 8
+    sync()
+    assert kvm.take_faults() == 0
+    assert torch.equal(pool.view(torch.int16), ordered.view(torch.int16))
+    del ordered
     # 30-chunk hit mask: rows of chunks >= 30 keep the sentinel, hit rows equal
     # the all-hit result
     full = pool.clone()
