@@ -25,6 +25,11 @@ constexpr int kCgWaves = kCgBlock / 64;
 constexpr int kCgMaxLayers = 128;
 constexpr int kCgMaxVpl = 8;            // 16-byte vectors per lane per row: rows up to 4096 elements
 
+// Rows a wave loads before it converts the first: as many as keep the data
+// within 8 vectors of 16 bytes per lane, at most 4 (a 16-row page over 4 waves).
+template <int kVpl>
+constexpr int kCgRows = kVpl <= 2 ? 4 : 8 / kVpl;
+
 struct CgArgs {
     MoveArgs m;
     uint8_t qmax[2][kCgMaxLayers];      // MAX = bins / 2 - 1 for K (0) and V (1) of each layer
@@ -114,26 +119,39 @@ __global__ __launch_bounds__(kCgBlock) void store_cachegen(CgArgs ca)
     const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const uint64_t page_rows = pool + (uint64_t)u.page * a.page_size * row_bytes;
     const uint64_t sym_rows = chunk + section_offset(a, u.l, u.kv, u.n_c) + (uint64_t)u.j0 * E;
-    for (uint32_t r = wave; r < u.rows; r += kCgWaves) {
-        // vectors past the row read as zero (range check), neutral for the maximum
-        const __amdgpu_buffer_rsrc_t rs = byte_range(page_rows + (uint64_t)r * row_bytes, row_bytes);
-        u32x4 v[kVpl];
+    // kCgRows<kVpl> rows per wave in flight: every load of the batch is
+    // issued before the first row is reduced.  A row past the unit's end
+    // gets an empty range (loads return zero, nothing is touched).
+    constexpr int kRows = kCgRows<kVpl>;
+    for (uint32_t r0 = wave; r0 < u.rows; r0 += kCgWaves * kRows) {
+        u32x4 v[kRows][kVpl];
 #pragma unroll
-        for (int k = 0; k < kVpl; ++k)
-            v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (k * 64 + lane) * 16, 0, kCpolNt);
-        uint32_t m = 0;
+        for (int i = 0; i < kRows; ++i) {
+            const uint32_t r = r0 + i * kCgWaves;
+            // vectors past the row read as zero (range check), neutral for the maximum
+            const __amdgpu_buffer_rsrc_t rs = byte_range(page_rows + (uint64_t)r * row_bytes, r < u.rows ? row_bytes : 0);
 #pragma unroll
-        for (int k = 0; k < kVpl; ++k) m = cg_max_magnitude(m, v[k]);
-        m = __builtin_amdgcn_readfirstlane(wave_max_u32(m));
-        // NaN magnitudes sort above infinity; any NaN makes max1 the quiet NaN
-        const float max1 = m > 0x7F80u ? __uint_as_float(0x7FC00000u) : __uint_as_float(m << 16);
-        const float factor = max1 == 0.0f ? 0.0f : qmax / max1;
-        const __amdgpu_buffer_rsrc_t rd = byte_range(sym_rows + (uint64_t)r * E, E);
+            for (int k = 0; k < kVpl; ++k)
+                v[i][k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (k * 64 + lane) * 16, 0, kCpolNt);
+        }
 #pragma unroll
-        for (int k = 0; k < kVpl; ++k)
-            __builtin_amdgcn_raw_buffer_store_b64(cg_quantise8(v[k], factor, qmax), rd, (k * 64 + lane) * 8, 0,
-                                                  kCpolNt);
-        if (lane == 0) *gptr<gf32>(chunk + cg_max_offset(a, u.l, u.kv, u.n_c, u.j0 + r)) = max1;
+        for (int i = 0; i < kRows; ++i) {
+            const uint32_t r = r0 + i * kCgWaves;
+            if (r >= u.rows) break;                       // the same for the whole wave
+            uint32_t m = 0;
+#pragma unroll
+            for (int k = 0; k < kVpl; ++k) m = cg_max_magnitude(m, v[i][k]);
+            m = __builtin_amdgcn_readfirstlane(wave_max_u32(m));
+            // NaN magnitudes sort above infinity; any NaN makes max1 the quiet NaN
+            const float max1 = m > 0x7F80u ? __uint_as_float(0x7FC00000u) : __uint_as_float(m << 16);
+            const float factor = max1 == 0.0f ? 0.0f : qmax / max1;
+            const __amdgpu_buffer_rsrc_t rd = byte_range(sym_rows + (uint64_t)r * E, E);
+#pragma unroll
+            for (int k = 0; k < kVpl; ++k)
+                __builtin_amdgcn_raw_buffer_store_b64(cg_quantise8(v[i][k], factor, qmax), rd, (k * 64 + lane) * 8, 0,
+                                                      kCpolNt);
+            if (lane == 0) *gptr<gf32>(chunk + cg_max_offset(a, u.l, u.kv, u.n_c, u.j0 + r)) = max1;
+        }
     }
 }
 
@@ -152,30 +170,43 @@ __device__ __forceinline__ void retrieve_cachegen_unit(const CgArgs& ca, const P
     const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const uint64_t page_rows = pool + (uint64_t)u.page * a.page_size * row_bytes;
     const uint64_t sym_rows = chunk + section_offset(a, u.l, u.kv, u.n_c) + (uint64_t)u.j0 * E;
-    for (uint32_t r = wave; r < u.rows; r += kCgWaves) {
-        const float max1 = *gptr<const gf32>(chunk + cg_max_offset(a, u.l, u.kv, u.n_c, u.j0 + r));
-        const __amdgpu_buffer_rsrc_t rs = byte_range(sym_rows + (uint64_t)r * E, E);
-        const __amdgpu_buffer_rsrc_t rd = byte_range(page_rows + (uint64_t)r * row_bytes, row_bytes);
-        u32x2 q[kVpl];
+    // kCgRows<kVpl> rows per wave in flight, as in the store; a row past the
+    // unit's end reads nothing (empty range, max1 not loaded).
+    constexpr int kRows = kCgRows<kVpl>;
+    for (uint32_t r0 = wave; r0 < u.rows; r0 += kCgWaves * kRows) {
+        u32x2 q[kRows][kVpl];
+        float max1[kRows];
 #pragma unroll
-        for (int k = 0; k < kVpl; ++k)
-            q[k] = __builtin_amdgcn_raw_buffer_load_b64(rs, (k * 64 + lane) * 8, 0, kCpolNt);
+        for (int i = 0; i < kRows; ++i) {
+            const uint32_t r = r0 + i * kCgWaves;
+            max1[i] = r < u.rows ? *gptr<const gf32>(chunk + cg_max_offset(a, u.l, u.kv, u.n_c, u.j0 + r)) : 0.0f;
+            const __amdgpu_buffer_rsrc_t rs = byte_range(sym_rows + (uint64_t)r * E, r < u.rows ? E : 0);
 #pragma unroll
-        for (int k = 0; k < kVpl; ++k) {
-            u32x4 o;
+            for (int k = 0; k < kVpl; ++k)
+                q[i][k] = __builtin_amdgcn_raw_buffer_load_b64(rs, (k * 64 + lane) * 8, 0, kCpolNt);
+        }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const uint32_t w = q[k][j];
-                const __bf16 h0 = (__bf16)(cg_unit(w & 0xFFu, qmax, rq) * max1);
-                const __bf16 h1 = (__bf16)(cg_unit((w >> 8) & 0xFFu, qmax, rq) * max1);
-                const __bf16 h2 = (__bf16)(cg_unit((w >> 16) & 0xFFu, qmax, rq) * max1);
-                const __bf16 h3 = (__bf16)(cg_unit(w >> 24, qmax, rq) * max1);
-                o[2 * j] = __builtin_bit_cast(unsigned short, h0) |
-                           ((uint32_t)__builtin_bit_cast(unsigned short, h1) << 16);
-                o[2 * j + 1] = __builtin_bit_cast(unsigned short, h2) |
-                               ((uint32_t)__builtin_bit_cast(unsigned short, h3) << 16);
+        for (int i = 0; i < kRows; ++i) {
+            const uint32_t r = r0 + i * kCgWaves;
+            if (r >= u.rows) break;                       // the same for the whole wave
+            const __amdgpu_buffer_rsrc_t rd = byte_range(page_rows + (uint64_t)r * row_bytes, row_bytes);
+#pragma unroll
+            for (int k = 0; k < kVpl; ++k) {
+                u32x4 o;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const uint32_t w = q[i][k][j];
+                    const __bf16 h0 = (__bf16)(cg_unit(w & 0xFFu, qmax, rq) * max1[i]);
+                    const __bf16 h1 = (__bf16)(cg_unit((w >> 8) & 0xFFu, qmax, rq) * max1[i]);
+                    const __bf16 h2 = (__bf16)(cg_unit((w >> 16) & 0xFFu, qmax, rq) * max1[i]);
+                    const __bf16 h3 = (__bf16)(cg_unit(w >> 24, qmax, rq) * max1[i]);
+                    o[2 * j] = __builtin_bit_cast(unsigned short, h0) |
+                               ((uint32_t)__builtin_bit_cast(unsigned short, h1) << 16);
+                    o[2 * j + 1] = __builtin_bit_cast(unsigned short, h2) |
+                                   ((uint32_t)__builtin_bit_cast(unsigned short, h3) << 16);
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * 64 + lane) * 16, 0, kCpolNt);
             }
-            __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * 64 + lane) * 16, 0, kCpolNt);
         }
     }
 }
