@@ -760,3 +760,14 @@ def test_ordered_retrieve_bad_page_is_skipped_and_reported():
     assert oracle.retrieve(op, good, 0, 300, [1, 1], host_chunks(cs[0]), BF16) == 300
     exp[:, :, good[3]] = 0x7E57                      # the skipped page keeps the sentinel
     assert np.array_equal(got, exp)
+
+
+def test_ordered_retrieve_large_pool_spans_several_compaction_blocks():
+    # the page-order compaction walks the inverse map 16384 pages at a time: a
+    # 40000-page pool (tiny rows) takes three blocks, with hit pages in each
+    w = wl.custom("ord-bigpool", 356, 2, 1, 8, 40000, [(0, 30000), (0, 20000), (256, 9000)],
+                  masks=[np.ones(118, np.uint8), np.r_[np.ones(50, np.uint8), np.zeros(29, np.uint8)],
+                         np.ones(35, np.uint8)])
+    pages_used = np.concatenate([sq.block_table for sq in w.seqs])
+    assert pages_used.max() > 32768 and pages_used.min() < 16384
+    assert _ordered_roundtrip(w) == [30000, 50 * 256, 9000 - 256]
