@@ -168,6 +168,54 @@ def cpu_baseline(w, pool, budget_s=20.0):
                       f"of the same workload ({moved / 1e9:.2f} GB moved in {secs:.1f} s, single thread)"}
 
 
+def oracle_beside(w, pool, fmt, n_chunks=4, bins=None, layer=-1, budget_s=4.0):
+    """The oracle timed beside a non-headline workload: store, then retrieve
+    (all hit), of the first n_chunks chunks of the first sequence, repeated
+    for about budget_s, single-threaded.  It runs on a host copy of only
+    those chunks' pages, renumbered from 0 (what moves does not depend on
+    page ids).  Bytes are counted as on the GPU side of the same workload."""
+    import numpy as np
+    import torch
+    import oracle
+    sq = w.seqs[0]
+    s = sq.tok_start
+    e = min(sq.tok_end, s + n_chunks * w.chunk_size)
+    first = s // w.page_size
+    pages = np.asarray(sq.block_table[first:(e + w.page_size - 1) // w.page_size], np.int64)
+    full = pool.view(torch.int16).view(w.num_layers, 2, w.num_pages, w.page_size, w.width)
+    part = full.index_select(2, torch.from_numpy(pages).to(pool.device)).cpu().numpy().view(np.uint16).copy()
+    opool = oracle.Pool.from_array(part, w.num_kv_heads, w.head_dim, w.chunk_size)
+    bt = np.concatenate([np.zeros(first, np.int32), np.arange(len(pages), dtype=np.int32)])
+    ch = oracle.alloc_chunks(opool, s, e, fmt)
+    mask = np.ones(len(ch), np.uint8)
+    layers = 1 if layer >= 0 else w.num_layers
+    elems = (e - s) * layers * w.width
+    if fmt == oracle.FMT_CACHEGEN:
+        nbytes = elems * 2 * 3 + (e - s) * layers * 2 * 4
+    else:
+        pb = PART_BYTES[fmt]
+        nbytes = elems * sum(2 + b for b in pb) + 4 * sum(b == 1 for b in pb) * layers * len(ch)
+    t_st = t_rt = 0.0
+    reps = 0
+    while reps == 0 or t_st + t_rt < budget_s:
+        t0 = time.perf_counter()
+        if fmt == oracle.FMT_CACHEGEN:
+            assert oracle.store_cachegen(opool, bt, s, e, ch, bins[0], bins[1]) == 0
+            t1 = time.perf_counter()
+            assert oracle.retrieve_cachegen(opool, bt, s, e, mask, ch, bins[0], bins[1]) == e - s
+        else:
+            assert oracle.store(opool, bt, s, e, ch, fmt, layer) == 0
+            t1 = time.perf_counter()
+            assert oracle.retrieve(opool, bt, s, e, mask, ch, fmt, layer) == e - s
+        t2 = time.perf_counter()
+        t_st, t_rt, reps = t_st + t1 - t0, t_rt + t2 - t1, reps + 1
+    return {"store_GBps": round(reps * nbytes / t_st / 1e9, 4), "retrieve_GBps": round(reps * nbytes / t_rt / 1e9, 4),
+            "store_tokens_per_s": round(reps * (e - s) / t_st, 1),
+            "retrieve_tokens_per_s": round(reps * (e - s) / t_rt, 1), "cores": 1, "kind": "oracle",
+            "sample": f"{reps} x (store + retrieve) of {len(ch)} chunks, {e - s} tokens"
+                      f"{', layer ' + str(layer) if layer >= 0 else ''}, of the same workload, single thread"}
+
+
 # ------------------------------------------------------------------ workloads
 
 def bench_llama8b(args):
@@ -374,6 +422,7 @@ def bench_layerwise(args):
         "workload": "layerwise-8b: 1 seq x 10240 tokens, 32 layers, GEMM 10240x4096x4096 bf16 per layer",
         "t_gemm_ms": round(t_gemm, 3), "t_dependency_only_ms": round(t_deps, 3),
         "best": best, "variants": variants,
+        "oracle_beside": oracle_beside(w, pool, kvm.FMT_BF16, n_chunks=40, layer=5),
     }
 
 
@@ -439,7 +488,8 @@ def bench_layerwise_store(args):
     return {"metric": "layerwise store: gather time hidden behind per-layer GEMMs",
             "workload": "layerwise-store-8b: 1 seq x 10240 tokens, 32 layers, GEMM 10240x4096x4096 bf16 per layer",
             "t_gemm_ms": round(t_gemm, 3), "best": min(variants, key=lambda v: v["t_both_ms"]),
-            "variants": variants}
+            "variants": variants,
+            "oracle_beside": oracle_beside(w, pool, kvm.FMT_BF16, n_chunks=40, layer=5)}
 
 
 def bench_offload(args):
@@ -549,6 +599,7 @@ def bench_offload(args):
     out["fp8_onload"] = {"ms": round(frt, 3), "GBps_link": gbps(fb_rt, frt), "tokens_per_s": round(rtok / (frt / 1e3), 1)}
     log(f"fp8 {out['fp8_offload']} {out['fp8_onload']}")
     assert kvm.take_faults() == 0
+    out["oracle_beside"] = oracle_beside(w, pool, kvm.FMT_BF16)
     del fb, farena, pool, paged
     torch.cuda.empty_cache()
     # the two streams already made: a third and fourth would share a
@@ -659,8 +710,10 @@ def bench_cachegen(args):
     cm_ms = timed(stream, lambda: kvm.retrieve_cachegen(paged, batch, kb, vb, stream=stream), reps)
     assert kvm.take_faults() == 0
     st, rt = st_bytes / (st_ms / 1e3) / 1e9, rt_bytes / (rt_ms / 1e3) / 1e9
+    beside = oracle_beside(w, pool, kvm.FMT_CACHEGEN, 4, bins=(kb, vb))
     return {
         "metric": "store / retrieve algorithmic GB/s", "workload": "cachegen-8b",
+        "oracle_beside": beside,
         "format": f"cachegen int8 symbols, key bins {CACHEGEN_KEY_BINS}, value bins {CACHEGEN_VALUE_BINS}",
         "store_ms": round(st_ms, 4), "store_GBps": round(st, 2), "store_pct_hbm_peak": round(100 * st / HBM_PEAK_GBPS, 2),
         "store_tokens_per_s": round(tokens / (st_ms / 1e3), 1),
@@ -705,9 +758,11 @@ def bench_simple(args, name, fmt):
     cm_ms = timed(stream, lambda: kvm.retrieve(paged, batch, fmt=fmt, stream=stream), reps)
     assert kvm.take_faults() == 0
     st, rt = st_bytes / (st_ms / 1e3) / 1e9, rt_bytes / (rt_ms / 1e3) / 1e9
+    beside = oracle_beside(w, pool, fmt, 4)
     return {
         "metric": "store / retrieve algorithmic GB/s", "workload": name,
         "format": FORMAT_NAMES[fmt],
+        "oracle_beside": beside,
         "store_ms": round(st_ms, 4), "store_GBps": round(st, 2), "store_pct_hbm_peak": round(100 * st / HBM_PEAK_GBPS, 2),
         "store_tokens_per_s": round(tokens / (st_ms / 1e3), 1),
         "retrieve_ms": round(rt_ms, 4), "retrieve_GBps": round(rt, 2),
