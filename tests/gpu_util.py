@@ -70,6 +70,7 @@ def setup_device(w, arr=None, pool=None, fmt=kvm.FMT_BF16, fill=0x00, where="dev
         seqs.append(kvm.Seq(bt, sq.tok_start, sq.tok_end, bufs))
         chunk_sets.append((bufs, sizes))
     batch = kvm.Batch(paged, seqs).set_masks([sq.hit_mask for sq in w.seqs])
+    torch.cuda.synchronize()      # fills done before any side-stream call touches the buffers
     return pool, paged, batch, chunk_sets
 
 

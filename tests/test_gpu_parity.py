@@ -560,6 +560,7 @@ def test_host_chunks_offload_and_onload(fmt):
     # layer by layer from host chunks, on a side stream with a capped grid
     pool.view(torch.int16).fill_(0x7E57)
     s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())       # the fill lands before the retrieve writes
     ev = torch.cuda.Event()
     for l in range(w.num_layers):
         kvm.retrieve_layer(paged, batch, l, fmt=fmt, stream=s, event=ev, max_workgroups=3)

@@ -71,6 +71,7 @@ def test_random_case(i):
     else:
         check_store(w, arr, cs, fmt)
     pool.view(torch.int16).fill_(0x7E57)
+    s.wait_stream(torch.cuda.current_stream())       # the fill lands before the retrieve writes
     ws = paged.new_workspace() if retrieve_form == "ordered" else None
     if fmt == kvm.FMT_CACHEGEN:
         n = kvm.retrieve_cachegen(paged, batch, kb, vb, stream=s, workspace=ws)
