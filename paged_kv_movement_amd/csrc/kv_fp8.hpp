@@ -114,31 +114,36 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* lds)
 }
 
 // Quotient x / s for the fp8 encoder without a division: q0 = x * r with
-// r = 1/s correctly rounded, one fused multiply-add for the exact residual,
-// one to correct q0 (Markstein's correction).  The result is the correctly
-// rounded quotient except for some |x| <= 2^-25; for groups whose amax is a
-// finite bf16 value >= 2^-4 an exhaustive check over every (amax, x) bf16
-// pair showed the e4m3 code, and the e5m2 code, always equal those of the
-// IEEE quotient.  The sign is taken from x, which also keeps -0.
+// r = 1/s correctly rounded, one fused multiply-add for the exact residual
+// (taken negated, q0*s - x), one to correct q0 (Markstein's correction).  The
+// result is the correctly rounded quotient except for some |x| <= 2^-25; for
+// groups whose amax is a finite bf16 value >= 2^-4 an exhaustive check over
+// every (amax, x) bf16 pair showed the e4m3 code, and the e5m2 code, always
+// equal those of the IEEE quotient, the sign of zero included (the negated
+// residual makes a zero quotient keep the sign of x).
 __device__ __forceinline__ float quotient_fast(float x, float s, float r)
 {
     const float q0 = x * r;
-    const float e = __builtin_fmaf(-q0, s, x);
-    const float q1 = __builtin_fmaf(e, r, q0);
-    return __uint_as_float((__float_as_uint(q1) & 0x7FFFFFFFu) | (__float_as_uint(x) & 0x80000000u));
+    const float e = __builtin_fmaf(q0, s, -x);
+    return __builtin_fmaf(-e, r, q0);
 }
 
-// Two floats -> two fp8 bytes (low 16 bits) with the hardware converter,
-// which rounds to nearest-even and matches the OCP encoding for |y| <= 464
-// (E4M3) and |y| < 59392 (E5M2; above, it overflows to infinity instead of
-// saturating) -- checked against the CPU oracle on every float32 in those
-// ranges.  The quotients fed to it stay within the scale's target maximum
-// (448, 57344) plus a few units in the last place.
+// Four floats -> four fp8 bytes (a, b, c, d from the low byte up) with the
+// hardware converter, which rounds to nearest-even and matches the OCP
+// encoding for |y| <= 464 (E4M3) and |y| < 59392 (E5M2; above, it overflows
+// to infinity instead of saturating) -- checked against the CPU oracle on
+// every float32 in those ranges.  The quotients fed to it stay within the
+// scale's target maximum (448, 57344) plus a few units in the last place.
+// The second conversion writes the upper half-word of the first's result.
 template <bool kE5M2>
-__device__ __forceinline__ uint32_t fp8x2(float a, float b)
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d)
 {
-    return (kE5M2 ? __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false)
-                  : __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
+    if (kE5M2) {
+        const int lo = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+        return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(c, d, lo, true);
+    }
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
 // amax bits (bf16 magnitude) for which the fast quotient is exact in e4m3
@@ -159,11 +164,8 @@ __device__ __forceinline__ u32x2 quantize8(const u32x4 x, float scale, float r, 
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const uint32_t w0 = x[2 * j], w1 = x[2 * j + 1];
-            const uint32_t p0 =
-                fp8x2<kE5M2>(quotient_fast(lo_bf16(w0), scale, r), quotient_fast(hi_bf16(w0), scale, r));
-            const uint32_t p1 =
-                fp8x2<kE5M2>(quotient_fast(lo_bf16(w1), scale, r), quotient_fast(hi_bf16(w1), scale, r));
-            q[j] = p0 | (p1 << 16);
+            q[j] = fp8x4<kE5M2>(quotient_fast(lo_bf16(w0), scale, r), quotient_fast(hi_bf16(w0), scale, r),
+                                quotient_fast(lo_bf16(w1), scale, r), quotient_fast(hi_bf16(w1), scale, r));
         }
     } else {   // tiny, infinite or NaN amax
 #pragma unroll
@@ -178,17 +180,27 @@ __device__ __forceinline__ u32x2 quantize8(const u32x4 x, float scale, float r, 
     return q;
 }
 
-__device__ __forceinline__ uint32_t max_magnitude(uint32_t m, const u32x4 x)
+// Running maximum of bf16 magnitude bits, two 16-bit lanes at once: m holds
+// the maximum of the low halves in bits [15:0] and of the high halves in
+// [31:16] (v_pk_max_u16, unsigned 16-bit lanes).  Integer order of the
+// magnitude bits is magnitude order for non-NaN values; NaN codes sort above
+// infinity.  pair_max folds the two halves at the end.
+__device__ __forceinline__ uint32_t max_magnitude2(uint32_t m, const u32x4 x)
 {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = x[j] & 0x7FFFu;
-        const uint32_t hi = (x[j] >> 16) & 0x7FFFu;
-        m = m > lo ? m : lo;
-        m = m > hi ? m : hi;
+        const uint32_t mag = x[j] & 0x7FFF7FFFu;
+        asm("v_pk_max_u16 %0, %1, %2" : "=v"(m) : "v"(m), "v"(mag));
     }
     return m;
 }
+
+__device__ __forceinline__ uint32_t pair_max(uint32_t m)
+{
+    const uint32_t lo = m & 0xFFFFu, hi = m >> 16;
+    return lo > hi ? lo : hi;
+}
+
 
 // Address of 16-byte vector v of a group (token-major) whose pool pages are
 // listed in `pages`, page_vecs vectors per page.  (A plain function: a
@@ -250,17 +262,17 @@ __global__ __launch_bounds__(kOnchipBlock) void store_fp8_onchip(MoveArgs a)
         reg[k] = u32x4{0u, 0u, 0u, 0u};                   // zero is neutral for the maximum
         if (v < total) reg[k] = __builtin_nontemporal_load(group_vector(pool, pages, page_vecs, page_bytes, v));
     }
-    uint32_t m1 = 0;
+    uint32_t m2 = 0;
 #pragma unroll
-    for (int k = 0; k < kOnchipRegSlots; ++k) m1 = max_magnitude(m1, reg[k]);
+    for (int k = 0; k < kOnchipRegSlots; ++k) m2 = max_magnitude2(m2, reg[k]);
     __builtin_amdgcn_s_waitcnt(0);                        // the LDS loads have landed
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < kOnchipLdsSlots; ++k) {
         const uint32_t v = (kOnchipRegSlots + k) * B + threadIdx.x;
-        if (v < total) m1 = max_magnitude(m1, lds[k * B + threadIdx.x]);
+        if (v < total) m2 = max_magnitude2(m2, lds[k * B + threadIdx.x]);
     }
-    const uint32_t amax_bits = block_max_u32<B>(m1, red);
+    const uint32_t amax_bits = block_max_u32<B>(pair_max(m2), red);
     const float amax = __uint_as_float(amax_bits << 16);
     const float scale = amax == 0.0f ? 1.0f : amax / fp8_max<kE5M2>();
     const bool fast = fast_quotient_ok(amax_bits);
@@ -304,12 +316,11 @@ __global__ __launch_bounds__(kBlock) void store_fp8(MoveArgs a)
     const uint32_t page_bytes = a.page_size * a.width * 2;
     constexpr uint32_t kStep = kBlock * kUnroll * 16;
 
-    // pass 1: absolute maximum as bf16 magnitude bits (integer order equals
-    // magnitude order for non-NaN; NaN codes sort above infinity).  Plain
-    // 32-bit operations: a packed-u16 form (bit_cast of a vector element into
-    // a u16x2 fed to __builtin_elementwise_max) was compiled by hipcc 7.2 into
-    // a load of only the first dword of each 16-byte vector.
-    uint32_t m1 = 0;
+    // pass 1: absolute maximum as bf16 magnitude bits.  (A packed-u16 form
+    // written with __builtin_elementwise_max on a bit_cast u16x2 was compiled
+    // by hipcc 7.2 into a load of only the first dword of each 16-byte
+    // vector; max_magnitude2 states the instruction directly.)
+    uint32_t m2 = 0;
     for (uint32_t pi = 0; pi < n_pages; ++pi) {
         const int64_t page = gptr<const gi32>(sq.bt)[first + pi];
         const uint32_t left = g.n_c - pi * a.page_size;
@@ -321,10 +332,10 @@ __global__ __launch_bounds__(kBlock) void store_fp8(MoveArgs a)
             for (int k = 0; k < kUnroll; ++k)
                 v[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, base + (k * kBlock + threadIdx.x) * 16, 0, 0);
 #pragma unroll
-            for (int k = 0; k < kUnroll; ++k) m1 = max_magnitude(m1, v[k]);
+            for (int k = 0; k < kUnroll; ++k) m2 = max_magnitude2(m2, v[k]);
         }
     }
-    const uint32_t amax_bits = block_max_u32<kBlock>(m1, red);
+    const uint32_t amax_bits = block_max_u32<kBlock>(pair_max(m2), red);
     const float amax = __uint_as_float(amax_bits << 16);
     const float scale = amax == 0.0f ? 1.0f : amax / fp8_max<kE5M2>();
     const bool fast = fast_quotient_ok(amax_bits);
