@@ -116,7 +116,9 @@ __global__ __launch_bounds__(kCgBlock) void store_cachegen(CgArgs ca)
     if (bad_addr(chunk)) { raise_fault(kFaultChunk); return; }
     const float qmax = (float)ca.qmax[u.kv][u.l];
     const uint32_t E = a.width, row_bytes = E * 2;
-    const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    // the wave index in a scalar register: row addresses, and the buffer
+    // descriptors built from them, are then known to be wave-uniform
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
     const uint64_t page_rows = pool + (uint64_t)u.page * a.page_size * row_bytes;
     const uint64_t sym_rows = chunk + section_offset(a, u.l, u.kv, u.n_c) + (uint64_t)u.j0 * E;
     // kCgRows<kVpl> rows per wave in flight: every load of the batch is
@@ -167,7 +169,9 @@ __device__ __forceinline__ void retrieve_cachegen_unit(const CgArgs& ca, const P
     const float qmax = (float)ca.qmax[u.kv][u.l];
     const float rq = 1.0f / qmax;
     const uint32_t E = a.width, row_bytes = E * 2;
-    const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    // the wave index in a scalar register: row addresses, and the buffer
+    // descriptors built from them, are then known to be wave-uniform
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
     const uint64_t page_rows = pool + (uint64_t)u.page * a.page_size * row_bytes;
     const uint64_t sym_rows = chunk + section_offset(a, u.l, u.kv, u.n_c) + (uint64_t)u.j0 * E;
     // kCgRows<kVpl> rows per wave in flight, as in the store; a row past the
@@ -196,14 +200,10 @@ __device__ __forceinline__ void retrieve_cachegen_unit(const CgArgs& ca, const P
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const uint32_t w = q[i][k][j];
-                    const __bf16 h0 = (__bf16)(cg_unit(w & 0xFFu, qmax, rq) * max1[i]);
-                    const __bf16 h1 = (__bf16)(cg_unit((w >> 8) & 0xFFu, qmax, rq) * max1[i]);
-                    const __bf16 h2 = (__bf16)(cg_unit((w >> 16) & 0xFFu, qmax, rq) * max1[i]);
-                    const __bf16 h3 = (__bf16)(cg_unit(w >> 24, qmax, rq) * max1[i]);
-                    o[2 * j] = __builtin_bit_cast(unsigned short, h0) |
-                               ((uint32_t)__builtin_bit_cast(unsigned short, h1) << 16);
-                    o[2 * j + 1] = __builtin_bit_cast(unsigned short, h2) |
-                                   ((uint32_t)__builtin_bit_cast(unsigned short, h3) << 16);
+                    o[2 * j] = bf16x2_rne(cg_unit(w & 0xFFu, qmax, rq) * max1[i],
+                                          cg_unit((w >> 8) & 0xFFu, qmax, rq) * max1[i]);
+                    o[2 * j + 1] = bf16x2_rne(cg_unit((w >> 16) & 0xFFu, qmax, rq) * max1[i],
+                                              cg_unit(w >> 24, qmax, rq) * max1[i]);
                 }
                 __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * 64 + lane) * 16, 0, kCpolNt);
             }

@@ -126,6 +126,15 @@ __device__ __forceinline__ uint32_t find_seq(const MoveArgs& a, uint32_t item)
     return s;
 }
 
+// Two float32 values -> two bf16 (round to nearest-even) packed in one word,
+// a in bits [15:0] and b in [31:16]: one v_cvt_pk_bf16_f32 for the pair.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 __device__ __forceinline__ bool bad_addr(uint64_t p) { return p == 0 || (p & 15u) != 0; }
 
 // A value every lane of the wave holds identically, moved into scalar

@@ -6,15 +6,20 @@
 
 namespace kvmove {
 
-// Launch shape, from sweeps on MI355X at the Llama-3.1-8B KV shape: tiles of
-// 8 KiB (256 threads x 2 vectors of 16 B), four per 32 KiB page; streaming
-// (nt) cache policy, with sc1 on the gather.
-constexpr int kMoveBlock = 256;
+// Launch shapes, from sweeps on MI355X at the Llama-3.1-8B KV shape.  A full
+// launch uses one-wave workgroups, each moving a 2 KiB tile (64 threads x 2
+// vectors of 16 B; sixteen tiles per 32 KiB page): more, smaller workgroups
+// kept HBM busier than 8 KiB tiles (gather +1 %, destination-ordered scatter
+// +2 %).  A launch with a workgroup cap keeps 256-thread workgroups and 8 KiB
+// tiles, so a cap means the same share of the GPU as before.  Streaming (nt)
+// cache policy with sc1, loads and stores alike.
+constexpr int kMoveBlock = 64;
+constexpr int kMoveBlockCapped = 256;
 constexpr int kMoveVpt = 2;
 constexpr int kGatherAuxLoad = kCpolNt | kCpolSc1;
 constexpr int kGatherAuxStore = kCpolNt | kCpolSc1;
-constexpr int kScatterAuxLoad = kCpolNt;
-constexpr int kScatterAuxStore = kCpolNt;
+constexpr int kScatterAuxLoad = kCpolNt | kCpolSc1;
+constexpr int kScatterAuxStore = kCpolNt | kCpolSc1;
 constexpr int kCopyBlock = 256;
 constexpr int kCopyVpt = 1;
 

@@ -24,7 +24,9 @@ namespace {
 using namespace kvmove;
 
 // Workgroups per launch: gridDim.x * blockDim.x must stay below 2^32.
-constexpr int64_t kMaxBlocks = (int64_t(1) << 24) - 1;
+// Most workgroups of `block` threads one launch takes (gridDim.x * blockDim.x
+// must stay below 2^32).
+int64_t max_blocks(int block) { return ((int64_t(1) << 32) - 1) / block; }
 
 thread_local std::string g_last_error;
 
@@ -152,7 +154,7 @@ struct Plan {
 };
 
 // Packs up to kMaxSeqs non-empty sequences per launch, keeping every launch
-// under kMaxBlocks workgroups (the kernels index units in 32 bits), and
+// within max_blocks workgroups (the kernels index units in 32 bits), and
 // calls flush(args, units) for each launch.  n_tok[i] is the token count
 // moved for sequence i (from its tok_start).
 template <class Flush>
@@ -181,8 +183,9 @@ int pack_units(const Launch& L, const Layout& lay, const kv_paged* p, const kv_s
     a.n_layers = uint32_t(n_layers);
     const int64_t page_bytes = int64_t(p->page_size) * a.width * 2;
     a.tiles = tile_bytes > 0 ? uint32_t(ceil_div(page_bytes, tile_bytes)) : 1u;
-    if (int64_t(a.tiles) > kMaxBlocks) return fail(KV_EINVAL, "page too large for one launch");
-    const int64_t max_units = kMaxBlocks / a.tiles;
+    const int64_t most = max_blocks(L.block);
+    if (int64_t(a.tiles) > most) return fail(KV_EINVAL, "page too large for one launch");
+    const int64_t max_units = most / a.tiles;
 
     int64_t total = 0;
     a.n_seqs = 0;
@@ -249,16 +252,25 @@ int launch_units(const Launch& L, const Layout& lay, const kv_paged* p, const kv
     return pack_units(L, lay, p, seqs, n_tok, n_seqs, layer0, n_layers, flush);
 }
 
-Launch bf16_launch(bool to_chunk, uint32_t kv0, uint32_t n_kv)
+// bf16 mover launch; `capped` (a workgroup cap is given) selects the
+// 256-thread shape, so a cap keeps its meaning in threads.
+Launch bf16_launch(bool to_chunk, uint32_t kv0, uint32_t n_kv, bool capped)
 {
+    if (capped) {
+        constexpr int B = kMoveBlockCapped;
+        const KernelFn k =
+            to_chunk ? reinterpret_cast<KernelFn>(&move_bf16<true, B, kMoveVpt, kGatherAuxLoad, kGatherAuxStore>)
+                     : reinterpret_cast<KernelFn>(&move_bf16<false, B, kMoveVpt, kScatterAuxLoad, kScatterAuxStore>);
+        return {k, B, B * kMoveVpt * 16, Unit::Page, kv0, n_kv, nullptr};
+    }
+    constexpr int B = kMoveBlock;
     const KernelFn k =
-        to_chunk ? reinterpret_cast<KernelFn>(&move_bf16<true, kMoveBlock, kMoveVpt, kGatherAuxLoad, kGatherAuxStore>)
-                 : reinterpret_cast<KernelFn>(
-                       &move_bf16<false, kMoveBlock, kMoveVpt, kScatterAuxLoad, kScatterAuxStore>);
+        to_chunk ? reinterpret_cast<KernelFn>(&move_bf16<true, B, kMoveVpt, kGatherAuxLoad, kGatherAuxStore>)
+                 : reinterpret_cast<KernelFn>(&move_bf16<false, B, kMoveVpt, kScatterAuxLoad, kScatterAuxStore>);
     const KernelFn sorted =
         to_chunk ? nullptr
-                 : reinterpret_cast<KernelFn>(&scatter_sorted<kMoveBlock, kMoveVpt, kScatterAuxLoad, kScatterAuxStore>);
-    return {k, kMoveBlock, kMoveBlock * kMoveVpt * 16, Unit::Page, kv0, n_kv, sorted};
+                 : reinterpret_cast<KernelFn>(&scatter_sorted<B, kMoveVpt, kScatterAuxLoad, kScatterAuxStore>);
+    return {k, B, B * kMoveVpt * 16, Unit::Page, kv0, n_kv, sorted};
 }
 
 // Gather + quantise: a whole (chunk, layer, K/V) group on chip when it fits,
@@ -276,33 +288,45 @@ Launch quantise_launch(const kv_paged* p, bool e5m2, uint32_t kv0, uint32_t n_kv
     return {k, kFp8StoreBlock, 0, Unit::Group, kv0, n_kv, nullptr};
 }
 
-Launch dequantise_launch(bool e5m2, uint32_t kv0, uint32_t n_kv)
+template <int B, int V>
+Launch dequantise_shape(bool e5m2, uint32_t kv0, uint32_t n_kv, bool sorted)
 {
-    const KernelFn k = e5m2 ? reinterpret_cast<KernelFn>(&retrieve_fp8<kFp8RetrieveBlock, kFp8RetrieveVpt, true>)
-                            : reinterpret_cast<KernelFn>(&retrieve_fp8<kFp8RetrieveBlock, kFp8RetrieveVpt, false>);
-    const KernelFn sorted =
-        e5m2 ? reinterpret_cast<KernelFn>(&retrieve_fp8_sorted<kFp8RetrieveBlock, kFp8RetrieveVpt, true>)
-             : reinterpret_cast<KernelFn>(&retrieve_fp8_sorted<kFp8RetrieveBlock, kFp8RetrieveVpt, false>);
-    return {k, kFp8RetrieveBlock, kFp8RetrieveBlock * kFp8RetrieveVpt * 16, Unit::Page, kv0, n_kv, sorted};
+    const KernelFn k = e5m2 ? reinterpret_cast<KernelFn>(&retrieve_fp8<B, V, true>)
+                            : reinterpret_cast<KernelFn>(&retrieve_fp8<B, V, false>);
+    const KernelFn ks = !sorted ? nullptr
+                        : e5m2  ? reinterpret_cast<KernelFn>(&retrieve_fp8_sorted<B, V, true>)
+                                : reinterpret_cast<KernelFn>(&retrieve_fp8_sorted<B, V, false>);
+    return {k, B, B * V * 16, Unit::Page, kv0, n_kv, ks};
 }
 
-Plan gather_plan(const kv_paged* p, int fmt)
+// Scatter + dequantise.  The chunk-major launch takes one-wave workgroups;
+// a capped launch, and the pool-address-ordered one (where they measured
+// slower), take 256 threads x 8 KiB.
+Launch dequantise_launch(bool e5m2, uint32_t kv0, uint32_t n_kv, bool capped, bool ordered)
+{
+    if (capped || ordered)
+        return dequantise_shape<kFp8RetrieveBlockCapped, kFp8RetrieveVptCapped>(e5m2, kv0, n_kv, !capped);
+    return dequantise_shape<kFp8RetrieveBlock, kFp8RetrieveVpt>(e5m2, kv0, n_kv, false);
+}
+
+Plan gather_plan(const kv_paged* p, int fmt, bool capped)
 {
     switch (fmt) {
-    case KV_FMT_BF16: return {{bf16_launch(true, 0, 2)}, 1};
+    case KV_FMT_BF16: return {{bf16_launch(true, 0, 2, capped)}, 1};
     case KV_FMT_FP8_E4M3_SCALED: return {{quantise_launch(p, false, 0, 2)}, 1};
     case KV_FMT_FP8_E5M2_SCALED: return {{quantise_launch(p, true, 0, 2)}, 1};
-    default: return {{bf16_launch(true, 0, 1), quantise_launch(p, false, 1, 1)}, 2};   // K16_V8
+    default: return {{bf16_launch(true, 0, 1, capped), quantise_launch(p, false, 1, 1)}, 2};   // K16_V8
     }
 }
 
-Plan scatter_plan(int fmt)
+Plan scatter_plan(int fmt, bool capped, bool ordered)
 {
     switch (fmt) {
-    case KV_FMT_BF16: return {{bf16_launch(false, 0, 2)}, 1};
-    case KV_FMT_FP8_E4M3_SCALED: return {{dequantise_launch(false, 0, 2)}, 1};
-    case KV_FMT_FP8_E5M2_SCALED: return {{dequantise_launch(true, 0, 2)}, 1};
-    default: return {{bf16_launch(false, 0, 1), dequantise_launch(false, 1, 1)}, 2};  // K16_V8
+    case KV_FMT_BF16: return {{bf16_launch(false, 0, 2, capped)}, 1};
+    case KV_FMT_FP8_E4M3_SCALED: return {{dequantise_launch(false, 0, 2, capped, ordered)}, 1};
+    case KV_FMT_FP8_E5M2_SCALED: return {{dequantise_launch(true, 0, 2, capped, ordered)}, 1};
+    default:                                                                                      // K16_V8
+        return {{bf16_launch(false, 0, 1, capped), dequantise_launch(false, 1, 1, capped, ordered)}, 2};
     }
 }
 
@@ -402,12 +426,12 @@ int retrieve(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hi
         return rc;
     }
     if (workspace != nullptr && max_workgroups == 0) {
-        const Plan plan = scatter_plan(fmt);
+        const Plan plan = scatter_plan(fmt, false, true);
         for (int k = 0; k < plan.n && rc == KV_OK; ++k)
             rc = retrieve_ordered(plan.part[k], layout_of(fmt), paged, seqs, n_tok, n_seqs, layer0, n_layers,
                                   workspace, stream);
     } else
-        rc = run_plan(scatter_plan(fmt), fmt, paged, seqs, n_tok, n_seqs, layer0, n_layers, stream,
+        rc = run_plan(scatter_plan(fmt, max_workgroups > 0, false), fmt, paged, seqs, n_tok, n_seqs, layer0, n_layers, stream,
                       max_workgroups);
     if (rc == KV_OK && out_tokens != nullptr)
         for (int i = 0; i < n_seqs; ++i) out_tokens[i] = n_tok[i];
@@ -504,7 +528,7 @@ int kv_store_chunks(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int f
     int64_t small[64];
     int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
     for (int i = 0; i < n_seqs; ++i) n_tok[i] = seqs[i].tok_end - seqs[i].tok_start;
-    rc = run_plan(gather_plan(paged, fmt), fmt, paged, seqs, n_tok, n_seqs, 0, paged->num_layers, stream, 0);
+    rc = run_plan(gather_plan(paged, fmt, false), fmt, paged, seqs, n_tok, n_seqs, 0, paged->num_layers, stream, 0);
     if (n_tok != small) delete[] n_tok;
     return rc == KV_OK ? ok() : rc;
 }
@@ -522,7 +546,8 @@ int kv_store_layer(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int fm
     int64_t small[64];
     int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
     for (int i = 0; i < n_seqs; ++i) n_tok[i] = seqs[i].tok_end - seqs[i].tok_start;
-    rc = run_plan(gather_plan(paged, fmt), fmt, paged, seqs, n_tok, n_seqs, layer, 1, stream, max_workgroups);
+    rc = run_plan(gather_plan(paged, fmt, max_workgroups > 0), fmt, paged, seqs, n_tok, n_seqs, layer, 1, stream,
+                  max_workgroups);
     if (n_tok != small) delete[] n_tok;
     if (rc != KV_OK) return rc;
     if (layer_done != nullptr) {
@@ -611,7 +636,7 @@ int kv_copy_bytes(void* dst, const void* src, size_t bytes, hipStream_t stream)
     if (bytes == 0) return ok();
     const int64_t tile = int64_t(kCopyBlock) * kCopyVpt * 16;
     const int64_t grid = ceil_div(int64_t(bytes), tile);
-    if (grid > kMaxBlocks) return fail(KV_EINVAL, "copy too large for one launch");
+    if (grid > max_blocks(kCopyBlock)) return fail(KV_EINVAL, "copy too large for one launch");
     uint64_t s = reinterpret_cast<uint64_t>(src);
     uint64_t d = reinterpret_cast<uint64_t>(dst);
     int64_t n = int64_t(bytes);
