@@ -209,11 +209,12 @@ int kv_retrieve_chunks_ws(const kv_paged* paged, const kv_seq* seqs, const uint8
  * on copy_stream, then records layer_done (if not NULL) on copy_stream -- also
  * when nothing hits, so a stream or host waiting on it never hangs.  Calling
  * it for layers 0 .. L-1 leaves the pool as one kv_retrieve_chunks call does.
- * max_workgroups = 0 launches one workgroup per 8 KiB tile (fastest when the
- * GPU is otherwise idle); a positive value caps the grid, each workgroup then
- * moving a contiguous run of tiles, so the scatter occupies few wave slots
- * while compute on another stream runs beside it (page-unit kernels: bf16
- * and the fp8 retrieve).  From host chunks the scatter is bound by PCIe, and
+ * max_workgroups = 0 launches one workgroup per tile (one-wave workgroups:
+ * 2 KiB tiles for bf16, 4 KiB of output for the fp8 retrieve; fastest when
+ * the GPU is otherwise idle); a positive value caps the grid at that many
+ * 256-thread workgroups, each moving a contiguous run of 8 KiB tiles, so the
+ * scatter occupies few wave slots while compute on another stream runs
+ * beside it (page-unit kernels: bf16 and the fp8 retrieve).  From host chunks the scatter is bound by PCIe, and
  * a cap of 32 workgroups already moves at the link's rate.  Overlap needs
  * copy_stream and the compute stream on different hardware queues: HIP
  * spreads a process's streams over a few queues (GPU_MAX_HW_QUEUES, 4 by
