@@ -43,12 +43,17 @@ def build() -> str:
 
 
 def lib():
-    """Load the oracle library, building it first only if it is not there."""
+    """Load the oracle library, building it first only if it is not there.
+    KVO_ORACLE_LIB names another build of kv_oracle.c to load instead (the
+    mutation tests point it at deliberately broken copies)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
-        _lib = _bind(ctypes.CDLL(_LIB))
+        path = os.environ.get("KVO_ORACLE_LIB")
+        if not path:
+            path = _LIB
+            if not os.path.exists(path):
+                build()
+        _lib = _bind(ctypes.CDLL(path))
     return _lib
 
 

@@ -429,6 +429,27 @@ def test_fp8_zero_group_and_signed_zero():
     assert (q[0, :, ::2] == 0x80).all() and (q[0, :, 1::2] == 0).all() and (q[1] == 0).all()
 
 
+def test_fp8_nan_group_follows_numpy_and_torch():
+    # a NaN anywhere in a group: numpy's maximum propagates it, so the scale
+    # and every quotient are NaN and the torch cast gives the NaN code; the
+    # other part of the chunk is unaffected
+    w = wl.custom("nan", 82, 1, 1, 16, 16, [(0, 16)])
+    rng = np.random.default_rng(82)
+    x = rng.standard_normal(w.pool_shape()).astype(np.float32)
+    arr = (x.view(np.uint32) >> 16).astype(np.uint16)
+    arr[0, 0, 3, 5, 7] = 0x7FC0                                        # one quiet NaN in K
+    _, pool = _pool(w, arr)
+    sq = w.seqs[0]
+    for fmt in (oracle.FMT_FP8, oracle.FMT_FP8_E5M2):
+        ch = oracle.alloc_chunks(pool, 0, 16, fmt)
+        assert oracle.store(pool, sq.block_table, 0, 16, ch, fmt) == 0
+        exp = _numpy_store_any(arr, sq.block_table, 0, 16, 16, fmt)[0]
+        assert np.array_equal(ch[0], exp)
+        n = 16 * 16
+        assert ((ch[0][:n] & 0x7F) == 0x7F).all()                      # NaN codes in both encodings
+        assert np.isnan(ch[0][2 * n:].view(np.float32)[0]) and np.isfinite(ch[0][2 * n:].view(np.float32)[1])
+
+
 # ------------------------------------------- e5m2 and asymmetric K16/V8 formats
 
 _PARTS = {oracle.FMT_BF16: ("bf16", "bf16"), oracle.FMT_FP8: ("e4m3", "e4m3"),
