@@ -35,32 +35,31 @@ struct CgArgs {
     uint8_t qmax[2][kCgMaxLayers];      // MAX = bins / 2 - 1 for K (0) and V (1) of each layer
 };
 
+// Maximum of v over the wave, returned in a scalar register.  DPP moves
+// (no LDS round trip): within each 16-lane row, shifts right by 1, 2, 4 and 8
+// leave the row's maximum in its lane 15 (lanes shifted in from outside the
+// row read 0, the identity of an unsigned maximum); row_bcast:15 and
+// row_bcast:31 then carry rows 0-1 into rows 1-3 and rows 0-1 into rows 2-3,
+// so lane 63 holds the maximum of all 64 lanes.
+__device__ __forceinline__ uint32_t umax_u32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const uint32_t o = __shfl_xor(v, off, 64);
-        v = v > o ? v : o;
-    }
-    return v;
-}
-
-// Largest bf16 magnitude (as bits) of the eight elements of a vector.
-__device__ __forceinline__ uint32_t cg_max_magnitude(uint32_t m, const u32x4 x)
-{
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = x[j] & 0x7FFFu, hi = (x[j] >> 16) & 0x7FFFu;
-        m = m > lo ? m : lo;
-        m = m > hi ? m : hi;
-    }
-    return m;
+    v = umax_u32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true));   // row_shr:1
+    v = umax_u32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true));   // row_shr:2
+    v = umax_u32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true));   // row_shr:4
+    v = umax_u32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true));   // row_shr:8
+    v = umax_u32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+    v = umax_u32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 // One symbol: x * factor and + MAX as two float32 operations, rounded half to
-// even, kept in [0, 2 * MAX]; a NaN gives MAX.
+// even, kept in [0, 2 * MAX]; a NaN gives MAX.  (The product and the sum must
+// stay two roundings: no contraction into a fused multiply-add.)
 __device__ __forceinline__ uint32_t cg_symbol(float x, float factor, float qmax)
 {
+#pragma clang fp contract(off)
     const float scaled = x * factor;
     const float y = scaled + qmax;
     if (y != y) return (uint32_t)qmax;
@@ -81,6 +80,44 @@ __device__ __forceinline__ u32x2 cg_quantise8(const u32x4 x, float factor, float
                (cg_symbol(__uint_as_float(w0 & 0xFFFF0000u), factor, qmax) << 8) |
                (cg_symbol(__uint_as_float(w1 << 16), factor, qmax) << 16) |
                (cg_symbol(__uint_as_float(w1 & 0xFFFF0000u), factor, qmax) << 24);
+    }
+    return q;
+}
+
+// The same symbol for a row whose max1 and factor are finite.  Then
+// |x| <= max1 gives |x * factor| <= MAX (1 + 2^-22) even with a subnormal
+// factor, so y = x * factor + MAX lies within 2^-17 of [0, 2 * MAX] and needs
+// no clamp and no NaN test (a CPU test checks the extremes x = +-max1 for every
+// MAX and every finite bf16 max1).  Adding 1.5 * 2^23 rounds y half to even
+// to an integer -- the sum's unit in the last place is 1 -- and leaves that
+// integer in the low bits of the sum; the symbol is its low byte.
+__device__ __forceinline__ uint32_t cg_symbol_bits(float x, float factor, float qmax)
+{
+#pragma clang fp contract(off)
+    const float scaled = x * factor;
+    const float y = scaled + qmax;
+    return __float_as_uint(y + 12582912.0f);
+}
+
+// Low bytes of a, b, c, d -> bytes 0, 1, 2, 3 of one word (v_perm_b32 picks
+// bytes of its two sources; selector 0x0c gives a zero byte).
+__device__ __forceinline__ uint32_t cg_pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    return __builtin_amdgcn_perm(b, a, 0x0c0c0400u) | __builtin_amdgcn_perm(d, c, 0x04000c0cu);
+}
+
+// Eight bf16 values -> eight symbol bytes on the fast path (finite max1 and
+// factor).
+__device__ __forceinline__ u32x2 cg_quantise8_fast(const u32x4 x, float factor, float qmax)
+{
+    u32x2 q;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t w0 = x[2 * j], w1 = x[2 * j + 1];
+        q[j] = cg_pack_low_bytes(cg_symbol_bits(__uint_as_float(w0 << 16), factor, qmax),
+                                 cg_symbol_bits(__uint_as_float(w0 & 0xFFFF0000u), factor, qmax),
+                                 cg_symbol_bits(__uint_as_float(w1 << 16), factor, qmax),
+                                 cg_symbol_bits(__uint_as_float(w1 & 0xFFFF0000u), factor, qmax));
     }
     return q;
 }
@@ -136,22 +173,37 @@ __global__ __launch_bounds__(kCgBlock) void store_cachegen(CgArgs ca)
             for (int k = 0; k < kVpl; ++k)
                 v[i][k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (k * 64 + lane) * 16, 0, kCpolNt);
         }
+        // the rows' maxima first, so that their cross-lane reductions overlap
+        // (a row past the unit's end read zeros and is not used)
+        uint32_t mrow[kRows];
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) {
+            uint32_t m2 = 0;
+#pragma unroll
+            for (int k = 0; k < kVpl; ++k) m2 = max_magnitude2(m2, v[i][k]);
+            mrow[i] = wave_max_u32(pair_max(m2));
+        }
 #pragma unroll
         for (int i = 0; i < kRows; ++i) {
             const uint32_t r = r0 + i * kCgWaves;
             if (r >= u.rows) break;                       // the same for the whole wave
-            uint32_t m = 0;
-#pragma unroll
-            for (int k = 0; k < kVpl; ++k) m = cg_max_magnitude(m, v[i][k]);
-            m = __builtin_amdgcn_readfirstlane(wave_max_u32(m));
+            const uint32_t m = mrow[i];
             // NaN magnitudes sort above infinity; any NaN makes max1 the quiet NaN
             const float max1 = m > 0x7F80u ? __uint_as_float(0x7FC00000u) : __uint_as_float(m << 16);
             const float factor = max1 == 0.0f ? 0.0f : qmax / max1;
+            const bool fast = m < 0x7F80u && (__float_as_uint(factor) & 0x7F800000u) != 0x7F800000u;
             const __amdgpu_buffer_rsrc_t rd = byte_range(sym_rows + (uint64_t)r * E, E);
+            if (fast) {                                   // the same for the whole wave
 #pragma unroll
-            for (int k = 0; k < kVpl; ++k)
-                __builtin_amdgcn_raw_buffer_store_b64(cg_quantise8(v[i][k], factor, qmax), rd, (k * 64 + lane) * 8, 0,
-                                                      kCpolNt);
+                for (int k = 0; k < kVpl; ++k)
+                    __builtin_amdgcn_raw_buffer_store_b64(cg_quantise8_fast(v[i][k], factor, qmax), rd,
+                                                          (k * 64 + lane) * 8, 0, kCpolNt);
+            } else {
+#pragma unroll
+                for (int k = 0; k < kVpl; ++k)
+                    __builtin_amdgcn_raw_buffer_store_b64(cg_quantise8(v[i][k], factor, qmax), rd,
+                                                          (k * 64 + lane) * 8, 0, kCpolNt);
+            }
             if (lane == 0) *gptr<gf32>(chunk + cg_max_offset(a, u.l, u.kv, u.n_c, u.j0 + r)) = max1;
         }
     }

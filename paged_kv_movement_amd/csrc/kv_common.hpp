@@ -135,6 +135,27 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
+// Running maximum of bf16 magnitude bits, two 16-bit lanes at once: m holds
+// the maximum of the low halves in bits [15:0] and of the high halves in
+// [31:16] (v_pk_max_u16, unsigned 16-bit lanes).  Integer order of the
+// magnitude bits is magnitude order for non-NaN values; NaN codes sort above
+// infinity.  pair_max folds the two halves at the end.
+__device__ __forceinline__ uint32_t max_magnitude2(uint32_t m, const u32x4 x)
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t mag = x[j] & 0x7FFF7FFFu;
+        asm("v_pk_max_u16 %0, %1, %2" : "=v"(m) : "v"(m), "v"(mag));
+    }
+    return m;
+}
+
+__device__ __forceinline__ uint32_t pair_max(uint32_t m)
+{
+    const uint32_t lo = m & 0xFFFFu, hi = m >> 16;
+    return lo > hi ? lo : hi;
+}
+
 __device__ __forceinline__ bool bad_addr(uint64_t p) { return p == 0 || (p & 15u) != 0; }
 
 // A value every lane of the wave holds identically, moved into scalar
