@@ -23,7 +23,6 @@ namespace {
 
 using namespace kvmove;
 
-// Workgroups per launch: gridDim.x * blockDim.x must stay below 2^32.
 // Most workgroups of `block` threads one launch takes (gridDim.x * blockDim.x
 // must stay below 2^32).
 int64_t max_blocks(int block) { return ((int64_t(1) << 32) - 1) / block; }
