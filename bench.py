@@ -323,6 +323,7 @@ def bench_llama8b(args):
     log(f"store {store_ms:.3f} ms ({gather_gbps:.0f} GB/s), retrieve {ret_ms:.3f} ms "
         f"({scatter_gbps:.0f} GB/s), step {step_s * 1e3:.3f} ms, copy ceiling {copy_gbps:.0f} GB/s")
 
+    traffic = read_traffic()
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -353,7 +354,7 @@ def bench_llama8b(args):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(gather_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": read_traffic(),
+            "traffic": traffic,
             "alg_bytes_per_launch": store_bytes,
             "avg_launch_ms": round(store_ms, 4),
         },
@@ -365,6 +366,8 @@ def bench_llama8b(args):
             "retrieve_other_order_ms": round(other_ms, 4),
             "retrieve_other_order_GBps": round(ret_bytes / (other_ms / 1e3) / 1e9, 2),
             "copy_ceiling_GBps": round(copy_gbps, 2),
+            # HBM bytes the counters measured for one gather launch, over this run's launch time
+            "gather_counter_GBps": (round(traffic / (store_ms / 1e3) / 1e9, 2) if traffic else None),
             "kernel_source_sha256_16": kernel_source_hash(),
         },
     }
