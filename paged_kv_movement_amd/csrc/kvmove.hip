@@ -440,7 +440,7 @@ int retrieve(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hi
 
 // CacheGen bins -> MAX table; rejects what the kernels cannot take.
 int cachegen_setup(const kv_paged* p, const int32_t* key_bins, const int32_t* value_bins,
-                   uint8_t (*qmax)[kCgMaxLayers], Launch* store, Launch* scatter)
+                   uint8_t (*qmax)[kCgMaxLayers], Launch* store, Launch* scatter, Launch* scatter_ordered)
 {
     if (key_bins == nullptr || value_bins == nullptr) return fail(KV_EINVAL, "key_bins / value_bins is NULL");
     if (p->num_layers > kCgMaxLayers)
@@ -477,10 +477,13 @@ int cachegen_setup(const kv_paged* p, const int32_t* key_bins, const int32_t* va
         kr = reinterpret_cast<KernelFn>(&retrieve_cachegen<8>);
         ko = reinterpret_cast<KernelFn>(&retrieve_cachegen_sorted<8>);
     }
-    // one workgroup per page unit
+    // the store and the chunk-major retrieve take one workgroup per page
+    // unit; the ordered retrieve one per kCgWaves rows of it (tile_bytes
+    // counts page-side bytes)
     const int page_bytes = int(int64_t(p->page_size) * width * 2);
     *store = {ks, kCgBlock, page_bytes, Unit::Page, 0, 2, nullptr};
-    *scatter = {kr, kCgBlock, page_bytes, Unit::Page, 0, 2, ko};
+    *scatter = {kr, kCgBlock, page_bytes, Unit::Page, 0, 2, nullptr};
+    *scatter_ordered = {kr, kCgBlock, int(kCgWaves * width * 2), Unit::Page, 0, 2, ko};
     return KV_OK;
 }
 
@@ -653,8 +656,8 @@ int kv_store_chunks_cachegen(const kv_paged* paged, const kv_seq* seqs, int n_se
     if (rc == KV_OK) rc = check_seqs(paged, seqs, n_seqs);
     if (rc != KV_OK) return rc;
     uint8_t qmax[2][kCgMaxLayers];
-    Launch st, sc;
-    rc = cachegen_setup(paged, key_bins, value_bins, qmax, &st, &sc);
+    Launch st, sc, so;
+    rc = cachegen_setup(paged, key_bins, value_bins, qmax, &st, &sc, &so);
     if (rc != KV_OK) return rc;
     int64_t small[64];
     int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
@@ -672,8 +675,8 @@ int kv_retrieve_chunks_cachegen(const kv_paged* paged, const kv_seq* seqs, const
     if (rc == KV_OK) rc = check_seqs(paged, seqs, n_seqs);
     if (rc != KV_OK) return rc;
     uint8_t qmax[2][kCgMaxLayers];
-    Launch st, sc;
-    rc = cachegen_setup(paged, key_bins, value_bins, qmax, &st, &sc);
+    Launch st, sc, so;
+    rc = cachegen_setup(paged, key_bins, value_bins, qmax, &st, &sc, &so);
     if (rc != KV_OK) return rc;
     if (n_seqs > 0 && hit_mask == nullptr) return fail(KV_EINVAL, "hit_mask is NULL");
     int64_t small[64];
@@ -696,7 +699,7 @@ int kv_retrieve_chunks_cachegen(const kv_paged* paged, const kv_seq* seqs, const
             return fail(KV_EINVAL, "workspace of %zu bytes, 256-byte aligned, needed (got %zu at %p)", need,
                         workspace_bytes, workspace);
         }
-        rc = retrieve_ordered(sc, kCgLayout, paged, seqs, n_tok, n_seqs, 0, paged->num_layers, workspace, stream,
+        rc = retrieve_ordered(so, kCgLayout, paged, seqs, n_tok, n_seqs, 0, paged->num_layers, workspace, stream,
                               qmax);
     } else {
         rc = launch_units(sc, kCgLayout, paged, seqs, n_tok, n_seqs, 0, paged->num_layers, stream, 0, qmax);
