@@ -772,3 +772,57 @@ def test_ordered_retrieve_large_pool_spans_several_compaction_blocks():
     pages_used = np.concatenate([sq.block_table for sq in w.seqs])
     assert pages_used.max() > 32768 and pages_used.min() < 16384
     assert _ordered_roundtrip(w) == [30000, 50 * 256, 9000 - 256]
+
+
+# ------------------------------------------------- page sizes that are not 16 or 32
+
+ODD_PAGES = [(1, 128), (3, 48), (8, 64), (12, 96), (24, 48)]
+ODD_FMTS = [BF16, FP8, E5M2, K16V8, kvm.FMT_CACHEGEN]
+
+
+@pytest.mark.parametrize("fmt", ODD_FMTS, ids=["bf16", "fp8", "e5m2", "k16v8", "cachegen"])
+@pytest.mark.parametrize("pc", ODD_PAGES, ids=[f"P{p}-C{c}" for p, c in ODD_PAGES])
+def test_odd_page_sizes(pc, fmt):
+    # one-row pages, page heights that are not a multiple of the four rows a
+    # CacheGen retrieve tile holds, more than 64 pages per chunk (the fp8
+    # store's two-pass path), tails, tok_start > 0, a one-token sequence and
+    # a hole; every retrieve form against the oracle
+    P, C = pc
+    ranges = [(0, 3 * C + 5), (C, 2 * C + P + 1), (0, 1)]
+    masks = [np.array([1, 1, 0, 1], np.uint8), np.array([1, 1], np.uint8), np.array([1], np.uint8)]
+    pages = sum(-(-e // P) for (_, e) in ranges) + 7
+    w = wl.custom(f"odd-P{P}", 400 + P, 2, 2, 24, pages, ranges, masks=masks, page_size=P, chunk_size=C,
+                  outliers=0 if fmt == BF16 else 2)
+    say("case odd page size", P, C, "fmt", fmt)
+    arr = wl.host_pool(w)
+    pool, paged, batch, cs = setup_device(w, arr, fmt=fmt, fill=0xCD)
+    cg = fmt == kvm.FMT_CACHEGEN
+    if cg:
+        kb, vb = cachegen_bins(w.num_layers, 400 + P)
+        kvm.store_cachegen(paged, batch, kb, vb)
+    else:
+        kvm.store(paged, batch, fmt)
+    _sync()
+    assert kvm.take_faults() == 0
+    check_store_cachegen(w, arr, cs, kb, vb) if cg else check_store(w, arr, cs, fmt)
+    expect = [2 * C, 2 * C + P + 1 - C, 1]
+    forms = ["chunk", "ordered"] if cg else ["chunk", "ordered", "layers"]
+    for form in forms:
+        pool.view(torch.int16).fill_(SENTINEL)
+        ws = paged.new_workspace() if form == "ordered" else None
+        if cg:
+            n = kvm.retrieve_cachegen(paged, batch, kb, vb, workspace=ws)
+        elif form == "layers":
+            for l in range(w.num_layers):
+                n = kvm.retrieve_layer(paged, batch, l, fmt=fmt)
+        else:
+            n = kvm.retrieve(paged, batch, fmt=fmt, workspace=ws)
+        _sync()
+        assert kvm.take_faults() == 0
+        before = np.full_like(arr, SENTINEL)
+        got = host_from_dev_pool(pool)
+        if cg:
+            counts = check_retrieve_cachegen(w, before, got, cs, masks, kb, vb)
+        else:
+            counts = check_retrieve(w, before, got, cs, fmt, masks)
+        assert n == counts == expect, (form, n, counts)
