@@ -826,3 +826,26 @@ def test_odd_page_sizes(pc, fmt):
         else:
             counts = check_retrieve(w, before, got, cs, fmt, masks)
         assert n == counts == expect, (form, n, counts)
+
+
+def test_cachegen_at_its_limits():
+    # the largest layer count the CacheGen entry points take (128, bins per
+    # layer all different) and the widest row (4096 elements), both orders
+    w = wl.custom("cg-128-layers", 451, 128, 1, 8, 40, [(0, 300)], masks=[np.array([1, 1], np.uint8)],
+                  page_size=16, chunk_size=256, outliers=1)
+    kb = np.arange(128, dtype=np.int32) % 126 + 4
+    vb = 129 - np.arange(128, dtype=np.int32) % 126
+    assert _cachegen_roundtrip(w, kb, vb) == [300]
+    w = wl.custom("cg-4096-wide", 452, 2, 32, 128, 40, [(0, 300)], masks=[np.array([1, 1], np.uint8)],
+                  page_size=16, chunk_size=256, outliers=2)
+    kb, vb = cachegen_bins(2, 452)
+    assert _cachegen_roundtrip(w, kb, vb) == [300]
+    arr = wl.host_pool(w)
+    pool, paged, batch, cs = setup_device(w, arr, fmt=kvm.FMT_CACHEGEN, fill=0xCD)
+    kvm.store_cachegen(paged, batch, kb, vb)
+    pool.view(torch.int16).fill_(SENTINEL)
+    assert kvm.retrieve_cachegen(paged, batch, kb, vb, workspace=paged.new_workspace()) == [300]
+    _sync()
+    assert kvm.take_faults() == 0
+    check_retrieve_cachegen(w, np.full_like(arr, SENTINEL), host_from_dev_pool(pool), cs,
+                            [sq.hit_mask for sq in w.seqs], kb, vb)
