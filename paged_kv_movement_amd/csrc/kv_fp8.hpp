@@ -375,7 +375,7 @@ __device__ __forceinline__ void retrieve_fp8_unit_tile(const MoveArgs& a, const 
     u32x2 q[kVpt];
 #pragma unroll
     for (int k = 0; k < kVpt; ++k)
-        q[k] = __builtin_amdgcn_raw_buffer_load_b64(rs, (k * kBlock + threadIdx.x) * 8, 0, kCpolNt);
+        q[k] = __builtin_amdgcn_raw_buffer_load_b64(rs, (k * kBlock + threadIdx.x) * 8, 0, kCpolNt | kCpolSc1);
 #pragma unroll
     for (int k = 0; k < kVpt; ++k) {
         u32x4 o;
@@ -388,7 +388,7 @@ __device__ __forceinline__ void retrieve_fp8_unit_tile(const MoveArgs& a, const 
             o[2 * j] = bf16x2_rne(d0[0] * scale, d0[1] * scale);
             o[2 * j + 1] = bf16x2_rne(d1[0] * scale, d1[1] * scale);
         }
-        __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * kBlock + threadIdx.x) * 16, 0, kCpolNt);
+        __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * kBlock + threadIdx.x) * 16, 0, kCpolNt | kCpolSc1);
     }
 }
 
