@@ -273,7 +273,8 @@ __device__ __forceinline__ void retrieve_cachegen_unit(const CgArgs& ca, const P
 // pool-address order these smaller workgroups measured 5.56 TB/s against 5.39
 // for one workgroup per page at the Llama-3.1-8B shape; in chunk-major order
 // they measured slower (5.08 against 5.33), so that order keeps
-// retrieve_cachegen_unit.
+// retrieve_cachegen_unit.  nt + sc1 on both sides (+0.8 % here; -0.4 % in
+// the chunk-major kernel, which keeps nt).
 template <int kVpl>
 __device__ __forceinline__ void retrieve_cachegen_tile(const CgArgs& ca, const PageUnit& u, uint32_t tile)
 {
@@ -299,7 +300,8 @@ __device__ __forceinline__ void retrieve_cachegen_tile(const CgArgs& ca, const P
         byte_range(pool + ((uint64_t)u.page * a.page_size + r) * row_bytes, row_bytes);
     u32x2 q[kVpl];
 #pragma unroll
-    for (int k = 0; k < kVpl; ++k) q[k] = __builtin_amdgcn_raw_buffer_load_b64(rs, (k * 64 + lane) * 8, 0, kCpolNt);
+    for (int k = 0; k < kVpl; ++k)
+        q[k] = __builtin_amdgcn_raw_buffer_load_b64(rs, (k * 64 + lane) * 8, 0, kCpolNt | kCpolSc1);
 #pragma unroll
     for (int k = 0; k < kVpl; ++k) {
         u32x4 o;
@@ -309,7 +311,7 @@ __device__ __forceinline__ void retrieve_cachegen_tile(const CgArgs& ca, const P
             o[2 * j] = bf16x2_rne(cg_unit(w & 0xFFu, qmax, rq) * max1, cg_unit((w >> 8) & 0xFFu, qmax, rq) * max1);
             o[2 * j + 1] = bf16x2_rne(cg_unit((w >> 16) & 0xFFu, qmax, rq) * max1, cg_unit(w >> 24, qmax, rq) * max1);
         }
-        __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * 64 + lane) * 16, 0, kCpolNt);
+        __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * 64 + lane) * 16, 0, kCpolNt | kCpolSc1);
     }
 }
 
