@@ -849,3 +849,66 @@ def test_cachegen_at_its_limits():
     assert kvm.take_faults() == 0
     check_retrieve_cachegen(w, np.full_like(arr, SENTINEL), host_from_dev_pool(pool), cs,
                             [sq.hit_mask for sq in w.seqs], kb, vb)
+
+
+# ------------------------------------------------------------ HIP graph capture
+
+@pytest.mark.parametrize("fmt", [BF16, FP8, kvm.FMT_CACHEGEN], ids=["bf16", "fp8", "cachegen"])
+def test_store_and_ordered_retrieve_replay_from_a_graph(fmt):
+    # The entry points enqueue kernels only (no allocation, no memset, no
+    # host synchronisation), so a caller can capture them into a HIP graph.
+    # One graph holds the store, another the ordered retrieve; each replay
+    # runs on fresh pool contents written eagerly in between, and every
+    # replay is checked against the oracle.
+    ranges = [(0, 700), (256, 1000)]
+    masks = [np.array([1, 1, 1], np.uint8), np.array([1, 0, 1], np.uint8)]
+    w = wl.custom("graph", 461, 3, 2, 32, 200, ranges, masks=masks, outliers=0 if fmt == BF16 else 2)
+    say("case graph replay", fmt)
+    arr0 = wl.host_pool(w)
+    pool, paged, batch, cs = setup_device(w, arr0, fmt=fmt, fill=0xCD)
+    cg = fmt == kvm.FMT_CACHEGEN
+    kb, vb = cachegen_bins(w.num_layers, 461) if cg else (None, None)
+    ws = paged.new_workspace()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                       # warm-up outside capture
+        if cg:
+            kvm.store_cachegen(paged, batch, kb, vb)
+            kvm.retrieve_cachegen(paged, batch, kb, vb, workspace=ws)
+        else:
+            kvm.store(paged, batch, fmt)
+            kvm.retrieve(paged, batch, fmt=fmt, workspace=ws)
+    torch.cuda.synchronize()
+    g_store, g_retrieve = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_store, stream=s):
+        kvm.store_cachegen(paged, batch, kb, vb) if cg else kvm.store(paged, batch, fmt)
+    with torch.cuda.graph(g_retrieve, stream=s):
+        if cg:
+            n = kvm.retrieve_cachegen(paged, batch, kb, vb, workspace=ws)
+        else:
+            n = kvm.retrieve(paged, batch, fmt=fmt, workspace=ws)
+    assert n == [700, 256]
+    rng = np.random.default_rng(461)
+    for rep in range(3):
+        say("replay", rep)
+        # new mantissa bits, same exponents: finite values stay finite
+        arr = arr0 ^ rng.integers(0, 1 << 7, size=arr0.shape, dtype=np.uint16) if rep else arr0
+        pool.copy_(dev_pool_from_host(w, arr))
+        torch.cuda.synchronize()
+        g_store.replay()
+        torch.cuda.synchronize()
+        assert kvm.take_faults() == 0
+        check_store_cachegen(w, arr, cs, kb, vb) if cg else check_store(w, arr, cs, fmt)
+        pool.view(torch.int16).fill_(SENTINEL + rep)
+        ws.fill_(0x5C + rep)                             # workspace contents on entry must not matter
+        torch.cuda.synchronize()
+        g_retrieve.replay()
+        torch.cuda.synchronize()
+        assert kvm.take_faults() == 0
+        before = np.full_like(arr, SENTINEL + rep)
+        got = host_from_dev_pool(pool)
+        if cg:
+            counts = check_retrieve_cachegen(w, before, got, cs, masks, kb, vb)
+        else:
+            counts = check_retrieve(w, before, got, cs, fmt, masks)
+        assert counts == [700, 256]
