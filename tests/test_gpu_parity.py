@@ -912,3 +912,39 @@ def test_store_and_ordered_retrieve_replay_from_a_graph(fmt):
         else:
             counts = check_retrieve(w, before, got, cs, fmt, masks)
         assert counts == [700, 256]
+
+
+def test_store_and_retrieve_on_two_streams_at_once():
+    # an offload of two sequences on one stream while two others onload on a
+    # second stream (disjoint pages, as the pool allocator guarantees): both
+    # results match the oracle
+    ranges = [(0, 900), (0, 650), (256, 1000), (0, 520)]
+    masks = [np.ones(4, np.uint8), np.ones(3, np.uint8), np.array([1, 1, 0], np.uint8), np.ones(3, np.uint8)]
+    w = wl.custom("two-streams", 471, 4, 2, 64, 300, ranges, masks=masks, outliers=2)
+    say("case two streams")
+    arr = wl.host_pool(w)
+    pool, paged, batch, cs = setup_device(w, arr, fmt=FP8, fill=0xCD)
+    a = kvm.Batch(paged, batch.seqs[:2]).set_masks(masks[:2])
+    b = kvm.Batch(paged, batch.seqs[2:]).set_masks(masks[2:])
+    kvm.store(paged, b, FP8)                          # b's chunks, to be onloaded
+    _sync()
+    # b's pages get a sentinel; a's pages keep their data for the store
+    dev = host_from_dev_pool(pool)
+    for sq in w.seqs[2:]:
+        for p in sq.block_table:
+            dev[:, :, p] = SENTINEL
+    pool.copy_(dev_pool_from_host(w, dev))
+    _sync()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    kvm.store(paged, a, FP8, stream=s1)
+    n = kvm.retrieve(paged, b, fmt=FP8, stream=s2, workspace=paged.new_workspace())
+    torch.cuda.synchronize()
+    assert kvm.take_faults() == 0
+    wa = wl.custom("two-streams", 471, 4, 2, 64, 300, ranges, masks=masks, outliers=2)
+    wa.seqs = w.seqs[:2]
+    check_store(wa, arr, cs[:2], FP8)
+    wb = wl.custom("two-streams", 471, 4, 2, 64, 300, ranges, masks=masks, outliers=2)
+    wb.seqs = w.seqs[2:]
+    assert n == check_retrieve(wb, dev, host_from_dev_pool(pool), cs[2:], FP8, masks[2:]) == [512, 520]
