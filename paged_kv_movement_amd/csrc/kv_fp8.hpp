@@ -140,7 +140,8 @@ __device__ __forceinline__ float quotient_fast(float x, float s, float r)
 // to infinity instead of saturating) -- checked against the CPU oracle on
 // every float32 in those ranges.  The quotients fed to it stay within the
 // scale's target maximum (448, 57344) plus a few units in the last place.
-// The second conversion writes the upper half-word of the first's result.
+// The second conversion writes the upper half-word of the first's result;
+// the pair was checked the same way, byte by byte, for both encodings.
 template <bool kE5M2>
 __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d)
 {
