@@ -821,7 +821,7 @@ def bench_simple(args, name, fmt):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3.1-8b",
                     choices=["llama3.1-8b", "layerwise-8b", "layerwise-store-8b", "llama-70b-style", "fp8-8b",
