@@ -198,7 +198,10 @@ int kv_retrieve_chunks(const kv_paged* paged, const kv_seq* seqs,
  * aligned; its contents on entry do not matter and are overwritten).  Every
  * format has an ordered scatter (for KV_FMT_K16_V8 each of its two launches
  * builds the list).  A sequence moving 2^26 pages or more is rejected
- * (KV_EINVAL).  Calls that share a workspace must be ordered on one stream. */
+ * (KV_EINVAL), and so, before anything is launched, is a call that moves
+ * more pages than the pool holds (its page ids cannot all be distinct, and
+ * its sorted list would not fit the workspace).  Calls that share a
+ * workspace must be ordered on one stream. */
 size_t kv_retrieve_workspace_bytes(const kv_paged* paged);   /* 0 on a malformed pool */
 int kv_retrieve_chunks_ws(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
                           int fmt, int64_t* out_tokens, void* workspace, size_t workspace_bytes,

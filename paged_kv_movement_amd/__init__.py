@@ -114,6 +114,12 @@ def _check(rc: int):
         raise KvError(rc, load().kv_last_error().decode())
 
 
+def _need(cond, msg: str):
+    """Argument check that stays on under ``python -O``."""
+    if not cond:
+        raise KvError(KV_EINVAL, msg)
+
+
 def _stream_handle(stream) -> int | None:
     if stream is None:
         import torch
@@ -142,9 +148,10 @@ class Paged:
     def from_pool(cls, pool, chunk_size: int = 256) -> "Paged":
         """From one bf16 tensor [L, 2, num_pages, page_size, H, D] (K at [:, 0], V at [:, 1])."""
         import torch
-        assert pool.dtype == torch.bfloat16 and pool.is_contiguous() and pool.dim() == 6
+        _need(pool.dtype == torch.bfloat16 and pool.is_contiguous() and pool.dim() == 6 and pool.is_cuda,
+              "pool must be a contiguous bf16 device tensor [L, 2, num_pages, page_size, H, D]")
         L, two, n, P, H, D = pool.shape
-        assert two == 2
+        _need(two == 2, "pool's second dimension must be 2 (K, V)")
         slab = n * P * H * D * pool.element_size()
         base = pool.data_ptr()
         k = torch.tensor([base + (2 * l) * slab for l in range(L)], dtype=torch.int64)
@@ -156,8 +163,10 @@ class Paged:
         """From per-layer bf16 tensors, each [num_pages, page_size, H, D]."""
         import torch
         n, P, H, D = k_layers[0].shape
+        _need(len(k_layers) == len(v_layers) > 0, "need one K and one V tensor per layer")
         for t in list(k_layers) + list(v_layers):
-            assert t.dtype == torch.bfloat16 and t.is_contiguous() and tuple(t.shape) == (n, P, H, D)
+            _need(t.dtype == torch.bfloat16 and t.is_contiguous() and t.is_cuda and tuple(t.shape) == (n, P, H, D),
+                  "per-layer pools must be contiguous bf16 device tensors of one shape [num_pages, page_size, H, D]")
         dev = k_layers[0].device
         k = torch.tensor([t.data_ptr() for t in k_layers], dtype=torch.int64).to(dev)
         v = torch.tensor([t.data_ptr() for t in v_layers], dtype=torch.int64).to(dev)
@@ -203,6 +212,8 @@ class Seq:
         self.block_table = block_table
         self.tok_start, self.tok_end = int(tok_start), int(tok_end)
         if isinstance(chunks, torch.Tensor) and chunks.dtype == torch.int64:
+            _need(chunks.is_cuda and chunks.is_contiguous() and chunks.dim() == 1,
+                  "chunk addresses must be a contiguous 1-D int64 device tensor")
             self.chunk_addrs, self._chunks = chunks, None
         else:
             self._chunks = list(chunks)
@@ -215,7 +226,10 @@ class Seq:
             addrs = torch.tensor([c.data_ptr() for c in self._chunks], dtype=torch.int64)
             dev = block_table.device if isinstance(block_table, torch.Tensor) else "cuda"
             self.chunk_addrs = addrs.to(dev)
-        assert block_table.dtype == torch.int32 and block_table.is_contiguous()
+        # the kernels read the block table from device memory
+        _need(isinstance(block_table, torch.Tensor) and block_table.dtype == torch.int32
+              and block_table.is_contiguous() and block_table.is_cuda,
+              "block_table must be a contiguous int32 device tensor")
 
     def c(self) -> _KvSeq:
         return _KvSeq(self.block_table.data_ptr(), self.block_table.numel(), self.tok_start,
@@ -236,7 +250,7 @@ class Batch:
 
     def set_masks(self, masks):
         """Host hit masks, one uint8 flag per chunk per sequence."""
-        assert len(masks) == self.n
+        _need(len(masks) == self.n, f"need {self.n} hit masks, got {len(masks)}")
         bufs = []
         for m in masks:
             b = bytes(int(x) & 0xFF for x in (m.tolist() if hasattr(m, "tolist") else m))
@@ -308,7 +322,7 @@ def retrieve_cachegen(paged: Paged, seqs, key_bins, value_bins, masks=None, stre
     b = _batch(paged, seqs)
     if masks is not None:
         b.set_masks(masks)
-    assert b._mask_ptrs is not None, "hit masks are required"
+    _need(b._mask_ptrs is not None, "hit masks are required")
     L = paged.c.num_layers
     ws_ptr, ws_bytes = _workspace(workspace)
     _check(load().kv_retrieve_chunks_cachegen(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n,
@@ -326,7 +340,7 @@ def retrieve(paged: Paged, seqs, masks=None, fmt: int = FMT_BF16, stream=None, w
     b = _batch(paged, seqs)
     if masks is not None:
         b.set_masks(masks)
-    assert b._mask_ptrs is not None, "hit masks are required"
+    _need(b._mask_ptrs is not None, "hit masks are required")
     if workspace is None:
         _check(load().kv_retrieve_chunks(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n, fmt, b.out,
                                          _stream_handle(stream)))
@@ -346,7 +360,7 @@ def retrieve_layer(paged: Paged, seqs, layer: int, masks=None, fmt: int = FMT_BF
     b = _batch(paged, seqs)
     if masks is not None:
         b.set_masks(masks)
-    assert b._mask_ptrs is not None, "hit masks are required"
+    _need(b._mask_ptrs is not None, "hit masks are required")
     _check(load().kv_retrieve_layer(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n, fmt, layer,
                                     b.out, max_workgroups, _stream_handle(stream),
                                     _event_handle(event, stream)))

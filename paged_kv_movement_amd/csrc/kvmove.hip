@@ -411,6 +411,20 @@ int hit_tokens(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* 
     return KV_OK;
 }
 
+// The ordered scatter's workspace holds one entry per pool page, and its
+// sorted list one per page moved; page ids are distinct within a call, so a
+// call that moves more pages than the pool holds breaks that rule and is
+// refused before anything runs (its list would not fit).
+int check_ordered_fits(const kv_paged* p, const int64_t* n_tok, int n_seqs)
+{
+    int64_t pages = 0;
+    for (int i = 0; i < n_seqs; ++i) pages += ceil_div(n_tok[i], p->page_size);
+    if (pages > p->num_pages)
+        return fail(KV_EINVAL, "the call moves %lld pages but the pool holds %lld: page ids repeat",
+                    (long long)pages, (long long)p->num_pages);
+    return KV_OK;
+}
+
 // Shared body of the retrieve entry points; with a workspace the bf16
 // scatter runs in pool-address order.
 int retrieve(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
@@ -426,6 +440,7 @@ int retrieve(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hi
     }
     if (workspace != nullptr && max_workgroups == 0) {
         const Plan plan = scatter_plan(fmt, false, true);
+        rc = check_ordered_fits(paged, n_tok, n_seqs);
         for (int k = 0; k < plan.n && rc == KV_OK; ++k)
             rc = retrieve_ordered(plan.part[k], layout_of(fmt), paged, seqs, n_tok, n_seqs, layer0, n_layers,
                                   workspace, stream);
@@ -678,30 +693,19 @@ int kv_retrieve_chunks_cachegen(const kv_paged* paged, const kv_seq* seqs, const
     Launch st, sc, so;
     rc = cachegen_setup(paged, key_bins, value_bins, qmax, &st, &sc, &so);
     if (rc != KV_OK) return rc;
-    if (n_seqs > 0 && hit_mask == nullptr) return fail(KV_EINVAL, "hit_mask is NULL");
     int64_t small[64];
     int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
-    for (int i = 0; i < n_seqs; ++i) {
-        const kv_seq& q = seqs[i];
-        const int64_t n_chunks = ceil_div(q.tok_end - q.tok_start, paged->chunk_size);
-        if (n_chunks > 0 && hit_mask[i] == nullptr) {
-            if (n_tok != small) delete[] n_tok;
-            return fail(KV_EINVAL, "seq %d: hit_mask entry is NULL", i);
-        }
-        const int64_t n_hit = n_chunks > 0 ? hit_chunks(hit_mask[i], n_chunks) : 0;
-        const int64_t end = q.tok_start + n_hit * paged->chunk_size;
-        n_tok[i] = (end < q.tok_end ? end : q.tok_end) - q.tok_start;
-    }
-    if (workspace != nullptr) {
+    rc = hit_tokens(paged, seqs, hit_mask, n_seqs, n_tok);
+    if (rc == KV_OK && workspace != nullptr) {
         const size_t need = kv_retrieve_workspace_bytes(paged);
-        if (need == 0 || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0) {
-            if (n_tok != small) delete[] n_tok;
-            return fail(KV_EINVAL, "workspace of %zu bytes, 256-byte aligned, needed (got %zu at %p)", need,
-                        workspace_bytes, workspace);
-        }
-        rc = retrieve_ordered(so, kCgLayout, paged, seqs, n_tok, n_seqs, 0, paged->num_layers, workspace, stream,
-                              qmax);
-    } else {
+        if (need == 0 || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+            rc = fail(KV_EINVAL, "workspace of %zu bytes, 256-byte aligned, needed (got %zu at %p)", need,
+                      workspace_bytes, workspace);
+        if (rc == KV_OK) rc = check_ordered_fits(paged, n_tok, n_seqs);
+        if (rc == KV_OK)
+            rc = retrieve_ordered(so, kCgLayout, paged, seqs, n_tok, n_seqs, 0, paged->num_layers, workspace,
+                                  stream, qmax);
+    } else if (rc == KV_OK) {
         rc = launch_units(sc, kCgLayout, paged, seqs, n_tok, n_seqs, 0, paged->num_layers, stream, 0, qmax);
     }
     if (rc == KV_OK && out_tokens != nullptr)

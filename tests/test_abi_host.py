@@ -189,6 +189,21 @@ def test_binding_refuses_pageable_host_chunks():
         kvm.Seq(bt, 0, 64, [t[::2]])
 
 
+def test_binding_refuses_host_block_tables_and_pools():
+    # the kernels read block tables, chunk-address arrays and pools from
+    # device memory: host tensors are refused before any call
+    import torch
+    with pytest.raises(kvm.KvError, match="block_table"):
+        kvm.Seq(torch.zeros(4, dtype=torch.int32), 0, 0, [])
+    with pytest.raises(kvm.KvError, match="chunk addresses"):
+        kvm.Seq(torch.zeros(4, dtype=torch.int32), 0, 64, torch.zeros(1, dtype=torch.int64))
+    with pytest.raises(kvm.KvError, match="pool"):
+        kvm.Paged.from_pool(torch.zeros(1, 2, 4, 16, 1, 8, dtype=torch.bfloat16))
+    with pytest.raises(kvm.KvError, match="per-layer"):
+        kvm.Paged.from_layers([torch.zeros(4, 16, 1, 8, dtype=torch.bfloat16)],
+                              [torch.zeros(4, 16, 1, 8, dtype=torch.bfloat16)])
+
+
 def test_cachegen_entry_points_reject_bad_calls():
     L = _lib()
     p = _paged(L=4)
@@ -253,3 +268,23 @@ def test_ordered_retrieve_workspace_size_and_rejections():
     assert L.kv_retrieve_chunks_ws(ctypes.byref(p), seqs, masks0, 1, kvm.FMT_BF16, out, 0x10000, need,
                                    None) == kvm.KV_OK
     assert out[0] == 0
+
+
+def test_ordered_retrieve_refuses_more_pages_than_the_pool():
+    # 1100 tokens = 69 pages of 16 on a 64-page pool: the page ids cannot be
+    # distinct and the sorted list would overrun the workspace, so the call
+    # is refused before any launch (no GPU here)
+    L = _lib()
+    p = _paged(n=64)
+    need = L.kv_retrieve_workspace_bytes(ctypes.byref(p))
+    seqs = (kvm._KvSeq * 1)(_seq(0, 1100, 69))
+    m = (ctypes.c_uint8 * 5)(1, 1, 1, 1, 1)
+    masks = (ctypes.c_void_p * 1)(ctypes.addressof(m))
+    out = (ctypes.c_int64 * 1)()
+    assert L.kv_retrieve_chunks_ws(ctypes.byref(p), seqs, masks, 1, kvm.FMT_BF16, out, 0x10000, need,
+                                   None) == kvm.KV_EINVAL
+    assert "pages" in L.kv_last_error().decode() and "repeat" in L.kv_last_error().decode()
+    kb = (ctypes.c_int32 * 32)(*([16] * 32))
+    assert L.kv_retrieve_chunks_cachegen(ctypes.byref(p), seqs, masks, 1, kb, kb, out, 0x10000, need,
+                                         None) == kvm.KV_EINVAL
+    assert "repeat" in L.kv_last_error().decode()

@@ -740,6 +740,15 @@ def test_ordered_retrieve_holes_many_sequences_and_reuse():
     _ordered_roundtrip(wl.custom("ord-reuse2", 354, 2, 2, 32, 400, [(0, 300)]), ws=ws)
 
 
+@pytest.mark.parametrize("fmt", [BF16, FP8], ids=["bf16", "fp8"])
+def test_ordered_retrieve_writes_every_page_of_the_pool(fmt):
+    # the call's pages are all 64 pages of the pool: the sorted list is as
+    # long as the workspace allows, with no padding entry
+    w = wl.custom("ord-fullpool", 357, 2, 2, 32, 64, [(0, 512), (0, 500)], outliers=2 if fmt == FP8 else 0)
+    assert sum(len(sq.block_table) for sq in w.seqs) == 64
+    assert _ordered_roundtrip(w, fmt=fmt) == [512, 500]
+
+
 def test_ordered_retrieve_bad_page_is_skipped_and_reported():
     w = wl.custom("ord-badpage", 355, 2, 2, 32, 64, [(0, 300)])
     arr = wl.host_pool(w)
