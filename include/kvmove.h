@@ -128,7 +128,8 @@ typedef struct {
     int32_t num_kv_heads;   /* H  > 0 */
     int32_t head_dim;       /* D  > 0; H*D must be a multiple of 8 (16-byte rows) */
     int32_t page_size;      /* P  > 0 tokens per page (16 in vLLM-style engines) */
-    int32_t chunk_size;     /* C  > 0 tokens per chunk, a multiple of P (256 by default) */
+    int32_t chunk_size;     /* C  > 0 tokens per chunk, a multiple of P (256 by default);
+                               C*H*D*2 <= 2^31 (one layer's K or V section of a chunk) */
     int64_t num_pages;      /* pages in each layer's K (and V) pool */
     const uint64_t* k_pages;/* DEVICE uint64[L]: address of layer l's K pool, 16-byte aligned */
     const uint64_t* v_pages;/* DEVICE uint64[L]: address of layer l's V pool, 16-byte aligned */

@@ -59,6 +59,11 @@ int check_paged(const kv_paged* p)
     if (p->page_size <= 0 || p->chunk_size <= 0 || p->chunk_size % p->page_size != 0)
         return fail(KV_EINVAL, "page_size (%d) and chunk_size (%d) must be > 0, chunk a multiple of page",
                     p->page_size, p->chunk_size);
+    // the kernels size a page, and a chunk's section of one layer's K or V,
+    // in 32-bit byte counts
+    if (int64_t(p->chunk_size) * width * 2 > (int64_t(1) << 31))
+        return fail(KV_EINVAL, "chunk_size * num_kv_heads * head_dim * 2 = %lld bytes: one layer's K or V section "
+                    "of a chunk must stay within 2^31 bytes", (long long)(int64_t(p->chunk_size) * width * 2));
     if (p->num_pages <= 0) return fail(KV_EINVAL, "num_pages must be > 0");
     if (p->k_pages == nullptr || p->v_pages == nullptr)
         return fail(KV_EINVAL, "k_pages / v_pages address arrays are NULL");

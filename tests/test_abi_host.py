@@ -74,6 +74,10 @@ def test_chunk_bytes_and_num_chunks():
     assert L.kv_num_chunks(ctypes.byref(p), 0, 10240) == 40
     assert L.kv_num_chunks(ctypes.byref(p), 512, 513) == 1
     assert L.kv_num_chunks(ctypes.byref(p), 5, 3) == -1
+    # one layer's K or V section of a chunk must fit 32-bit byte counts
+    assert L.kv_chunk_bytes(ctypes.byref(_paged(C=1 << 20)), 256, kvm.FMT_BF16) == 256 * 32 * 2 * 1024 * 2
+    assert L.kv_chunk_bytes(ctypes.byref(_paged(C=1 << 21)), 256, kvm.FMT_BF16) == 0
+    assert "2^31" in L.kv_last_error().decode()
 
 
 def _seq(s, e, n_bt, bt=0x3000, chunks=0x4000):
