@@ -223,7 +223,8 @@ constexpr uint32_t kPageIndexMask = (1u << kSeqShift) - 1;
 
 // The page unit of a pool-address-ordered launch: unit = slab * n_list + k,
 // slab = the (layer, K/V) pair, k = the k-th smallest page id; false for a
-// padding entry.
+// padding entry.  An entry naming no page of this launch (the list lives in
+// caller memory: two calls racing on one workspace) is skipped and reported.
 __device__ __forceinline__ bool sorted_unit(const MoveArgs& a, uint64_t list, uint32_t n_list, uint32_t unit,
                                             PageUnit& u)
 {
@@ -232,7 +233,12 @@ __device__ __forceinline__ bool sorted_unit(const MoveArgs& a, uint64_t list, ui
     if (e == kNoEntry) return false;
     u.s = e >> kSeqShift;
     const uint32_t q = e & kPageIndexMask;
+    if (u.s >= a.n_seqs) { raise_fault(kFaultPage); return false; }
     const SeqArg& sq = a.seq[u.s];
+    if (q >= sq.n_full * a.pages_per_chunk + (sq.tail_tokens + a.page_size - 1) / a.page_size) {
+        raise_fault(kFaultPage);
+        return false;
+    }
     u.c = q / a.pages_per_chunk;
     const uint32_t pi = q - u.c * a.pages_per_chunk;
     u.n_c = u.c < sq.n_full ? a.chunk_size : sq.tail_tokens;
