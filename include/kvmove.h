@@ -181,8 +181,9 @@ int kv_store_layer(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int fm
  * Page rows outside those chunks are not written.  out_tokens[i] (HOST,
  * may be NULL) = min(tok_end, tok_start + n_hit*C) - tok_start, which can
  * exceed what the engine lacked because whole chunks come back.  hit_mask is
- * a HOST array of n_seqs HOST pointers (an entry may be NULL when the range
- * is empty).  Nothing is launched when no chunk hits ([walk] "性能细节").
+ * a HOST array of n_seqs HOST pointers, entry i to at least
+ * n_chunks = ceil((tok_end - tok_start) / C) flags, all of which may be read
+ * (an entry may be NULL when the range is empty).  Nothing is launched when no chunk hits ([walk] "性能细节").
  * The page ids written by one call must be distinct. */
 int kv_retrieve_chunks(const kv_paged* paged, const kv_seq* seqs,
                        const uint8_t* const* hit_mask, int n_seqs, int fmt,

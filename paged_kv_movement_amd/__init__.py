@@ -241,6 +241,7 @@ class Batch:
 
     def __init__(self, paged: Paged, seqs):
         self.seqs = list(seqs)
+        self.chunk_size = paged.chunk_size
         n = len(self.seqs)
         self.arr = (_KvSeq * max(1, n))(*[s.c() for s in self.seqs])
         self.n = n
@@ -252,8 +253,11 @@ class Batch:
         """Host hit masks, one uint8 flag per chunk per sequence."""
         _need(len(masks) == self.n, f"need {self.n} hit masks, got {len(masks)}")
         bufs = []
-        for m in masks:
+        for i, (sq, m) in enumerate(zip(self.seqs, masks)):
             b = bytes(int(x) & 0xFF for x in (m.tolist() if hasattr(m, "tolist") else m))
+            # the library reads one flag for every chunk of the sequence
+            n_chunks = -(-(sq.tok_end - sq.tok_start) // self.chunk_size)
+            _need(len(b) >= n_chunks, f"sequence {i}: hit mask has {len(b)} flags for {n_chunks} chunks")
             bufs.append(ctypes.create_string_buffer(b, max(1, len(b))))
         self._mask_bufs = bufs
         self._mask_ptrs = (ctypes.c_void_p * max(1, self.n))(

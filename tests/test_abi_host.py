@@ -208,6 +208,26 @@ def test_binding_refuses_host_block_tables_and_pools():
                               [torch.zeros(4, 16, 1, 8, dtype=torch.bfloat16)])
 
 
+def test_binding_refuses_short_hit_masks():
+    # one flag per chunk is read: a shorter mask would be read past its end
+    import torch
+
+    class _P:
+        chunk_size = 256
+
+    seq = kvm.Seq.__new__(kvm.Seq)
+    seq.tok_start, seq.tok_end = 256, 1000                  # 3 chunks
+    seq.block_table = torch.zeros(1, dtype=torch.int32)
+    seq.chunk_addrs = torch.zeros(0, dtype=torch.int64)
+    b = kvm.Batch.__new__(kvm.Batch)
+    b.seqs, b.n, b.chunk_size = [seq], 1, _P.chunk_size
+    with pytest.raises(kvm.KvError, match="2 flags for 3 chunks"):
+        b.set_masks([[1, 1]])
+    assert b.set_masks([[1, 1, 0]]) is b
+    with pytest.raises(kvm.KvError, match="hit masks"):
+        b.set_masks([[1, 1, 0], [1]])
+
+
 def test_cachegen_entry_points_reject_bad_calls():
     L = _lib()
     p = _paged(L=4)
