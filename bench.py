@@ -126,9 +126,13 @@ def hit_tokens(w):
     return out
 
 
-def timed(stream, fn, reps):
-    """Mean ms of fn() over reps, HIP events on `stream`."""
+def timed(stream, fn, reps, warmup=3):
+    """Mean ms of fn() over reps, HIP events on `stream`, after `warmup`
+    untimed calls (short launches otherwise pay for the first calls' setup)."""
     import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in evs:
         a.record(stream)
