@@ -223,31 +223,35 @@ constexpr uint32_t kPageIndexMask = (1u << kSeqShift) - 1;
 
 // The page unit of a pool-address-ordered launch: unit = slab * n_list + k,
 // slab = the (layer, K/V) pair, k = the k-th smallest page id; false for a
-// padding entry.  An entry naming no page of this launch (the list lives in
-// caller memory: two calls racing on one workspace) is skipped and reported.
+// padding entry.  The list lives in caller memory (two calls racing on one
+// workspace could leave a stray entry), so the sequence slot is masked into
+// the launch's sequence array, and an entry naming no row its sequence moves
+// gets page id -1 (its block-table read is redirected to its own list slot),
+// which every tile function refuses with a fault bit before touching memory.
+// Both checks are selects, not branches: a branch here held back the unit's
+// remaining argument loads and cost the quantising ordered retrieves 8-14 %.
 __device__ __forceinline__ bool sorted_unit(const MoveArgs& a, uint64_t list, uint32_t n_list, uint32_t unit,
                                             PageUnit& u)
 {
+    static_assert((kMaxSeqs & (kMaxSeqs - 1)) == 0, "the sequence slot is masked");
     const uint32_t slab = unit / n_list, k = unit - slab * n_list;
     const uint32_t e = __builtin_amdgcn_readfirstlane(gptr<const gi32>(list)[k]);
     if (e == kNoEntry) return false;
-    u.s = e >> kSeqShift;
+    u.s = (e >> kSeqShift) & (kMaxSeqs - 1);
     const uint32_t q = e & kPageIndexMask;
-    if (u.s >= a.n_seqs) { raise_fault(kFaultPage); return false; }
     const SeqArg& sq = a.seq[u.s];
-    if (q >= sq.n_full * a.pages_per_chunk + (sq.tail_tokens + a.page_size - 1) / a.page_size) {
-        raise_fault(kFaultPage);
-        return false;
-    }
     u.c = q / a.pages_per_chunk;
     const uint32_t pi = q - u.c * a.pages_per_chunk;
     u.n_c = u.c < sq.n_full ? a.chunk_size : sq.tail_tokens;
     u.j0 = pi * a.page_size;
+    const bool stray = u.c > sq.n_full || u.j0 >= u.n_c;
     const uint32_t left = u.n_c - u.j0;
-    u.rows = left < a.page_size ? left : a.page_size;
+    u.rows = stray || left > a.page_size ? a.page_size : left;
     u.l = a.layer0 + slab / a.n_kv;
     u.kv = a.kv0 + slab % a.n_kv;
-    u.page = gptr<const gi32>(sq.bt)[sq.first_page + q];
+    const uint64_t at = stray ? list + 4ull * k : sq.bt + 4ull * (sq.first_page + q);
+    const int32_t page = *gptr<const gi32>(at);
+    u.page = stray ? -1 : page;
     return true;
 }
 
