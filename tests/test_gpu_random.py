@@ -14,7 +14,7 @@ from gpu_util import (say, setup_device, host_from_dev_pool, check_store, check_
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 160
+N_CASES = 600
 FORMATS = [kvm.FMT_BF16, kvm.FMT_FP8, kvm.FMT_FP8_E5M2, kvm.FMT_K16_V8, kvm.FMT_CACHEGEN]
 
 
