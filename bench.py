@@ -14,8 +14,9 @@ the stream it is launched on.  `cpu_baseline` times the CPU oracle on the
 same workload's data on this host's cores.
 
 Other workloads (`--workload layerwise-8b | layerwise-store-8b |
-llama-70b-style | fp8-8b | e5m2-8b | k16v8-8b | cachegen-8b | offload-8b`) print
-their own JSON report line; they are not the headline.
+llama-70b-style | llama3.1-8b-tp8-share | fp8-8b | e5m2-8b | k16v8-8b |
+cachegen-8b | offload-8b`) print their own JSON report line; they are not the
+headline.
 """
 import argparse
 import hashlib
@@ -840,7 +841,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3.1-8b",
-                    choices=["llama3.1-8b", "layerwise-8b", "layerwise-store-8b", "llama-70b-style", "fp8-8b",
+                    choices=["llama3.1-8b", "layerwise-8b", "layerwise-store-8b", "llama-70b-style",
+                             "llama3.1-8b-tp8-share", "fp8-8b",
                              "e5m2-8b", "k16v8-8b", "cachegen-8b",
                              "offload-8b"])
     ap.add_argument("--retrieve-order", choices=["address", "chunk"], default="address",
@@ -869,6 +871,8 @@ def main():
         out = bench_offload(args)
     elif args.workload == "llama-70b-style":
         out = bench_simple(args, "llama-70b-style", kvm.FMT_BF16)
+    elif args.workload == "llama3.1-8b-tp8-share":
+        out = bench_simple(args, "llama3.1-8b-tp8-share", kvm.FMT_BF16)
     elif args.workload == "e5m2-8b":
         out = bench_simple(args, "fp8-8b", kvm.FMT_FP8_E5M2)
     elif args.workload == "k16v8-8b":

@@ -13,6 +13,8 @@
 //   fill_u32       inv[0 .. num_pages) = kNoEntry
 //   invert_pages   inv[page] = (sequence slot << 26) | page index in the sequence
 //   compact_pages  list = the entries of inv in page order, padded with kNoEntry
+//   (order_pages_small does all three in one workgroup, inv in LDS, for pools
+//   of at most 32768 pages)
 //   scatter_sorted one workgroup per tile of (layer, K/V, list entry); the
 //                  fp8 and CacheGen retrieves have ordered variants too
 //                  (retrieve_fp8_sorted, retrieve_cachegen_sorted)
@@ -60,12 +62,14 @@ __global__ __launch_bounds__(256) void invert_pages(MoveArgs a, uint64_t inv, ui
     gptr<gu32>(inv)[page] = (s << kSeqShift) | q;
 }
 
-// One workgroup: the entries of inv[0 .. num_pages) in page order, written
-// to list[0 .. count), and kNoEntry in list[count .. list_len).
-__global__ __launch_bounds__(kCompactBlock) void compact_pages(uint64_t inv, uint32_t num_pages, uint64_t list,
-                                                               uint32_t list_len)
+// The entries of src[0 .. num_pages) in page order, written to
+// list[0 .. count), and kNoEntry in list[count .. list_len), by one
+// workgroup of kCompactBlock threads (src: the inverse map, in global memory
+// or LDS).
+template <class Src>
+__device__ __forceinline__ void compact_entries(Src src, uint32_t num_pages, uint64_t list, uint32_t list_len,
+                                                uint32_t* wave_sum)
 {
-    __shared__ uint32_t wave_sum[kCompactBlock / 64];
     const uint32_t t = threadIdx.x, lane = t % 64, wave = t / 64;
     uint32_t base = 0;
     for (uint32_t start = 0; start < num_pages; start += kCompactBlock * kCompactPerThread) {
@@ -74,7 +78,7 @@ __global__ __launch_bounds__(kCompactBlock) void compact_pages(uint64_t inv, uin
 #pragma unroll
         for (int j = 0; j < kCompactPerThread; ++j) {
             const uint32_t idx = start + t * kCompactPerThread + j;
-            v[j] = idx < num_pages ? gptr<const gu32>(inv)[idx] : kNoEntry;
+            v[j] = idx < num_pages ? src[idx] : kNoEntry;
             cnt += v[j] != kNoEntry;
         }
         // inclusive prefix of cnt over the wave, then over the waves
@@ -99,6 +103,72 @@ __global__ __launch_bounds__(kCompactBlock) void compact_pages(uint64_t inv, uin
         __syncthreads();                              // wave_sum is reused
     }
     for (uint32_t k = base + t; k < list_len; k += kCompactBlock) gptr<gu32>(list)[k] = kNoEntry;
+}
+
+__global__ __launch_bounds__(kCompactBlock) void compact_pages(uint64_t inv, uint32_t num_pages, uint64_t list,
+                                                               uint32_t list_len)
+{
+    __shared__ uint32_t wave_sum[kCompactBlock / 64];
+    compact_entries(gptr<const gu32>(inv), num_pages, list, list_len, wave_sum);
+}
+
+// Pools of at most kSmallPoolPages pages: the inverse map lives in LDS, and
+// one workgroup clears it, inverts the launch's pages and compacts them in
+// one launch, with no round trip through global memory (the three kernels
+// above take about 16 us plus two launch gaps at 8192 pages; this one
+// replaces them for every pool up to 32768 pages).
+constexpr uint32_t kSmallPoolPages = 32768;
+
+__global__ __launch_bounds__(kCompactBlock) void order_pages_small(MoveArgs a, uint64_t list, uint32_t n_list,
+                                                                   uint32_t num_pages)
+{
+    __shared__ uint32_t inv[kSmallPoolPages];
+    __shared__ uint32_t wave_sum[kCompactBlock / 64];
+    __shared__ uint32_t seq_end[kMaxSeqs];     // running page count after each sequence
+    __shared__ uint64_t seq_bt[kMaxSeqs];      // block-table address of each sequence's first moved page
+    const uint32_t t = threadIdx.x;
+    if (num_pages > kSmallPoolPages) num_pages = kSmallPoolPages;   // the host launches it for such pools only
+    if (t == 0) {
+        uint32_t acc = 0;
+        for (uint32_t s = 0; s < a.n_seqs; ++s) {
+            acc += seq_pages(a, a.seq[s]);
+            seq_end[s] = acc;
+            seq_bt[s] = a.seq[s].bt + 4ull * a.seq[s].first_page;
+        }
+    }
+    for (uint32_t i = t; i < num_pages; i += kCompactBlock) inv[i] = kNoEntry;
+    __syncthreads();
+    // invert: a thread's block-table loads are all issued before any is used,
+    // so the phase costs one memory latency rather than one per entry
+    constexpr int kBatch = 8;
+    for (uint32_t i0 = 0; i0 < n_list; i0 += kBatch * kCompactBlock) {
+        int32_t page[kBatch];
+        uint32_t entry[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const uint32_t i = i0 + k * kCompactBlock + t;
+            page[k] = -1;
+            entry[k] = kNoEntry;
+            if (i < n_list) {
+                uint32_t s = 0;
+                while (s + 1 < a.n_seqs && i >= seq_end[s]) ++s;
+                const uint32_t q = i - (s > 0 ? seq_end[s - 1] : 0u);
+                entry[k] = (s << kSeqShift) | q;
+                page[k] = gptr<const gi32>(seq_bt[s])[q];
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            if (entry[k] == kNoEntry) continue;
+            if (page[k] < 0 || page[k] >= a.num_pages || (uint32_t)page[k] >= num_pages) {
+                atomicOr(&g_kv_faults, kFaultPage);
+                continue;
+            }
+            inv[page[k]] = entry[k];
+        }
+    }
+    __syncthreads();
+    compact_entries(inv, num_pages, list, n_list, wave_sum);
 }
 
 // bf16 scatter in destination order: a.tiles tiles per sorted unit, one

@@ -365,21 +365,27 @@ int retrieve_ordered(const Launch& L, const Layout& lay, const kv_paged* p, cons
         for (uint32_t s = 0; s < a.n_seqs; ++s)
             if (a.seq[s].n_full * a.pages_per_chunk + ceil_div(a.seq[s].tail_tokens, a.page_size) > kPageIndexMask)
                 return fail(KV_EINVAL, "a sequence moves 2^26 pages or more: retrieve without a workspace");
-        const unsigned fill_grid = unsigned(std::min<int64_t>(ceil_div(num_pages, 256), 4096));
         uint32_t none = kNoEntry, np = num_pages, nl = uint32_t(n_list);
         uint64_t inv_a = inv, list_a = list;
-        void* fill_args[] = {&inv_a, &np, &none};
-        hipError_t e = hipLaunchKernel(reinterpret_cast<KernelFn>(&fill_u32), dim3(fill_grid), dim3(256), fill_args,
-                                       0, stream);
-        if (e == hipSuccess) {
-            void* inv_args[] = {&a, &inv_a, &nl};
-            e = hipLaunchKernel(reinterpret_cast<KernelFn>(&invert_pages), dim3(unsigned(ceil_div(n_list, 256))),
-                                dim3(256), inv_args, 0, stream);
-        }
-        if (e == hipSuccess) {
-            void* cmp_args[] = {&inv_a, &np, &list_a, &nl};
-            e = hipLaunchKernel(reinterpret_cast<KernelFn>(&compact_pages), dim3(1), dim3(kCompactBlock), cmp_args, 0,
+        hipError_t e = hipSuccess;
+        if (num_pages <= kSmallPoolPages) {     // one launch, the inverse map in LDS
+            void* args[] = {&a, &list_a, &nl, &np};
+            e = hipLaunchKernel(reinterpret_cast<KernelFn>(&order_pages_small), dim3(1), dim3(kCompactBlock), args, 0,
                                 stream);
+        } else {
+            const unsigned fill_grid = unsigned(std::min<int64_t>(ceil_div(num_pages, 256), 4096));
+            void* fill_args[] = {&inv_a, &np, &none};
+            e = hipLaunchKernel(reinterpret_cast<KernelFn>(&fill_u32), dim3(fill_grid), dim3(256), fill_args, 0, stream);
+            if (e == hipSuccess) {
+                void* inv_args[] = {&a, &inv_a, &nl};
+                e = hipLaunchKernel(reinterpret_cast<KernelFn>(&invert_pages), dim3(unsigned(ceil_div(n_list, 256))),
+                                    dim3(256), inv_args, 0, stream);
+            }
+            if (e == hipSuccess) {
+                void* cmp_args[] = {&inv_a, &np, &list_a, &nl};
+                e = hipLaunchKernel(reinterpret_cast<KernelFn>(&compact_pages), dim3(1), dim3(kCompactBlock), cmp_args,
+                                    0, stream);
+            }
         }
         if (e == hipSuccess) {
             if (cg_qmax != nullptr) {          // CacheGen kernels take the bins beside the move arguments

@@ -99,6 +99,21 @@ def llama8b(n_hit: int = 30) -> Workload:
     return w
 
 
+def llama8b_tp8_share(n_hit: int = 30) -> Workload:
+    """One rank's share of the 8B workload under 8-way tensor parallelism:
+    each rank caches its own KV head, so L=32, 1 KV head, head_dim 128
+    (256-byte token rows, 4 KiB pages); the same 8 sequences of 10000 tokens
+    on an 8192-page pool, retrieve mask n_hit ones then zeros."""
+    seed = 5
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(8192)
+    w = Workload("llama3.1-8b-tp8-share", seed, 32, 1, 128, 16, 256, 8192)
+    mask = np.zeros(40, np.uint8)
+    mask[:n_hit] = 1
+    w.seqs = [Sequence(bt, 0, 10000, mask.copy()) for bt in _slices(perm, [625] * 8)]
+    return w
+
+
 def layerwise8b() -> Workload:
     """One 10240-token sequence (40 full chunks, 640 pages) at the 8B shape on
     an 8192-page pool; all chunks hit."""
@@ -157,7 +172,7 @@ def custom(name, seed, num_layers, num_kv_heads, head_dim, num_pages, seq_ranges
 
 
 ALL = {"tiny": tiny, "llama3.1-8b": llama8b, "layerwise-8b": layerwise8b,
-       "llama-70b-style": llama70b, "fp8-8b": fp8_8b}
+       "llama-70b-style": llama70b, "fp8-8b": fp8_8b, "llama3.1-8b-tp8-share": llama8b_tp8_share}
 
 
 def host_pool(w: Workload) -> np.ndarray:

@@ -66,6 +66,11 @@ def test_full_llama8b_offload_to_host_and_onload():
     _full_bf16(wl.llama8b(), [30 * 256] * 8, where="host")
 
 
+def test_full_llama8b_tp8_share_store_and_30_chunk_retrieve():
+    # one rank's share under 8-way tensor parallelism: one KV head, 4 KiB pages
+    _full_bf16(wl.llama8b_tp8_share(), [30 * 256] * 8)
+
+
 def test_full_llama70b_store_and_retrieve():
     # 80 layers, one 32768-token sequence (128 chunks) on a 4096-page pool
     _full_bf16(wl.llama70b(), [32768])
