@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kBlock) void scatter_sorted(MoveArgs a, uint64_t li
     const uint32_t b = xcd_contiguous(blockIdx.x, gridDim.x);
     const uint32_t unit = b / a.tiles, tile = b - unit * a.tiles;
     PageUnit u;
-    if (!sorted_unit(a, list, n_list, unit, u)) return;
+    if (!sorted_unit<true>(a, list, n_list, unit, u)) return;
     move_unit_tile<false, kBlock, kVpt, kAuxLoad, kAuxStore>(a, u, tile);
 }
 
