@@ -126,6 +126,26 @@ __device__ __forceinline__ uint32_t find_seq(const MoveArgs& a, uint32_t item)
     return s;
 }
 
+// Arguments of the bf16 movers: the launch's arguments and a sequence lookup
+// table, lut[k] = the sequence holding unit k << lut_shift (the host picks
+// the shift so that 64 entries cover the launch).  A unit's sequence is then
+// found from its table entry in a step or two instead of by a walk from the
+// first sequence, one dependent argument load per step, ahead of every
+// workgroup's first data load.
+constexpr int kSeqLut = 64;
+struct MoveArgsLut {
+    MoveArgs m;
+    uint32_t lut_shift;
+    uint8_t lut[kSeqLut];
+};
+
+__device__ __forceinline__ uint32_t find_seq_lut(const MoveArgsLut& al, uint32_t item)
+{
+    uint32_t s = al.lut[item >> al.lut_shift];
+    while (s + 1 < al.m.n_seqs && item >= al.m.seq[s + 1].item_begin) ++s;
+    return s;
+}
+
 // Two float32 values -> two bf16 (round to nearest-even) packed in one word,
 // a in bits [15:0] and b in [31:16]: one v_cvt_pk_bf16_f32 for the pair.
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -184,10 +204,10 @@ struct PageUnit {
 // Units of a sequence run chunk-major: chunk, then layer, then K/V (the n_kv
 // parts from kv0), then page, so consecutive workgroups fill consecutive
 // bytes of a chunk.
-__device__ __forceinline__ PageUnit locate_page_unit(const MoveArgs& a, uint32_t item)
+__device__ __forceinline__ PageUnit locate_page_unit(const MoveArgs& a, uint32_t item, uint32_t seq)
 {
     PageUnit u;
-    u.s = find_seq(a, item);
+    u.s = seq;
     const SeqArg& sq = a.seq[u.s];
     uint32_t local = item - sq.item_begin;
     uint32_t pages_here;
@@ -213,6 +233,11 @@ __device__ __forceinline__ PageUnit locate_page_unit(const MoveArgs& a, uint32_t
     u.rows = left < a.page_size ? left : a.page_size;
     u.page = gptr<const gi32>(sq.bt)[sq.first_page + u.c * a.pages_per_chunk + pi];
     return u;
+}
+
+__device__ __forceinline__ PageUnit locate_page_unit(const MoveArgs& a, uint32_t item)
+{
+    return locate_page_unit(a, item, find_seq(a, item));
 }
 
 // Entries of a launch's page list sorted by page id (kv_order.hpp builds it):

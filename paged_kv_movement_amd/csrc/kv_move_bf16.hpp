@@ -47,25 +47,28 @@ __device__ __forceinline__ void move_unit_tile(const MoveArgs& a, const PageUnit
 
 // Tile b of the launch: page units in chunk-major order, a.tiles tiles each.
 template <bool kToChunk, int kBlock, int kVpt, int kAuxLoad, int kAuxStore>
-__device__ __forceinline__ void move_tile(const MoveArgs& a, uint32_t b)
+__device__ __forceinline__ void move_tile(const MoveArgsLut& al, uint32_t b)
 {
+    const MoveArgs& a = al.m;
     const uint32_t unit = b / a.tiles;
     const uint32_t tile = b - unit * a.tiles;
-    move_unit_tile<kToChunk, kBlock, kVpt, kAuxLoad, kAuxStore>(a, locate_page_unit(a, a.item_base + unit), tile);
+    const uint32_t item = a.item_base + unit;
+    move_unit_tile<kToChunk, kBlock, kVpt, kAuxLoad, kAuxStore>(a, locate_page_unit(a, item, find_seq_lut(al, item)),
+                                                                 tile);
 }
 
 // Grid = one workgroup per tile (units * a.tiles), or fewer workgroups that
 // each take a contiguous run of tiles.
 template <bool kToChunk, int kBlock, int kVpt, int kAuxLoad, int kAuxStore>
-__global__ __launch_bounds__(kBlock) void move_bf16(MoveArgs a)
+__global__ __launch_bounds__(kBlock) void move_bf16(MoveArgsLut al)
 {
-    if (gridDim.x >= a.total_tiles) {         // one workgroup per tile: straight-line code
-        move_tile<kToChunk, kBlock, kVpt, kAuxLoad, kAuxStore>(a, xcd_contiguous(blockIdx.x, gridDim.x));
+    if (gridDim.x >= al.m.total_tiles) {      // one workgroup per tile: straight-line code
+        move_tile<kToChunk, kBlock, kVpt, kAuxLoad, kAuxStore>(al, xcd_contiguous(blockIdx.x, gridDim.x));
         return;
     }
-    const TileRange r = my_tiles(a.total_tiles);
+    const TileRange r = my_tiles(al.m.total_tiles);
     for (uint32_t b = r.first; b < r.last; ++b)
-        move_tile<kToChunk, kBlock, kVpt, kAuxLoad, kAuxStore>(a, b);
+        move_tile<kToChunk, kBlock, kVpt, kAuxLoad, kAuxStore>(al, b);
 }
 
 // Plain contiguous copy (measurement aid): one tile of kBlock*kVpt vectors

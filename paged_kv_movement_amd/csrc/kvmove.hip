@@ -148,7 +148,26 @@ struct Launch {
     Unit unit;
     uint32_t kv0, n_kv;
     KernelFn sorted;  // the scatter kernel in pool-address order (retrieves only; else nullptr)
+    bool seq_lut;     // the kernel takes MoveArgsLut (the bf16 movers)
 };
+
+// The bf16 movers' arguments: a with its sequence lookup table over the
+// launch's `total` units (lut[k] = the sequence holding unit k << lut_shift).
+MoveArgsLut with_seq_lut(const MoveArgs& a, int64_t total)
+{
+    MoveArgsLut al{};
+    al.m = a;
+    uint32_t shift = 0;
+    while ((uint64_t(total - 1) >> shift) >= uint64_t(kSeqLut)) ++shift;
+    al.lut_shift = shift;
+    uint32_t s = 0;
+    for (int k = 0; k < kSeqLut; ++k) {
+        const uint64_t item = uint64_t(k) << shift;
+        while (s + 1 < a.n_seqs && item >= a.seq[s + 1].item_begin) ++s;
+        al.lut[k] = uint8_t(s);
+    }
+    return al;
+}
 
 // The launches of one store or retrieve: one, or one per part when K and V
 // are held differently.
@@ -233,7 +252,6 @@ int launch_units(const Launch& L, const Layout& lay, const kv_paged* p, const kv
     const int block = L.block;
     const Unit unit = L.unit;
     auto flush = [&](MoveArgs& a, int64_t total) -> int {
-        (void)total;
         int64_t grid = a.total_tiles;
         // only the tiled movers walk runs of tiles; group kernels need one
         // workgroup per group
@@ -245,6 +263,10 @@ int launch_units(const Launch& L, const Layout& lay, const kv_paged* p, const kv
             for (int kv = 0; kv < 2; ++kv)
                 for (int l = 0; l < kCgMaxLayers; ++l) ca.qmax[kv][l] = cg_qmax[kv][l];
             void* args[] = {&ca};
+            e = hipLaunchKernel(kernel, dim3(unsigned(grid)), dim3(block), args, 0, stream);
+        } else if (L.seq_lut) {
+            MoveArgsLut al = with_seq_lut(a, total);
+            void* args[] = {&al};
             e = hipLaunchKernel(kernel, dim3(unsigned(grid)), dim3(block), args, 0, stream);
         } else {
             void* args[] = {&a};
@@ -265,7 +287,7 @@ Launch bf16_launch(bool to_chunk, uint32_t kv0, uint32_t n_kv, bool capped)
         const KernelFn k =
             to_chunk ? reinterpret_cast<KernelFn>(&move_bf16<true, B, kMoveVpt, kGatherAuxLoad, kGatherAuxStore>)
                      : reinterpret_cast<KernelFn>(&move_bf16<false, B, kMoveVpt, kScatterAuxLoad, kScatterAuxStore>);
-        return {k, B, B * kMoveVpt * 16, Unit::Page, kv0, n_kv, nullptr};
+        return {k, B, B * kMoveVpt * 16, Unit::Page, kv0, n_kv, nullptr, true};
     }
     constexpr int B = kMoveBlock;
     const KernelFn k =
@@ -274,7 +296,7 @@ Launch bf16_launch(bool to_chunk, uint32_t kv0, uint32_t n_kv, bool capped)
     const KernelFn sorted =
         to_chunk ? nullptr
                  : reinterpret_cast<KernelFn>(&scatter_sorted<B, kMoveVpt, kScatterAuxLoad, kScatterAuxStore>);
-    return {k, B, B * kMoveVpt * 16, Unit::Page, kv0, n_kv, sorted};
+    return {k, B, B * kMoveVpt * 16, Unit::Page, kv0, n_kv, sorted, true};
 }
 
 // Gather + quantise: a whole (chunk, layer, K/V) group on chip when it fits,
