@@ -88,10 +88,10 @@ struct GroupUnit {
     uint32_t s;
 };
 
-__device__ __forceinline__ GroupUnit locate_group_unit(const MoveArgs& a, uint32_t item)
+__device__ __forceinline__ GroupUnit locate_group_unit(const MoveArgs& a, uint32_t item, uint32_t seq)
 {
     GroupUnit g;
-    g.s = find_seq(a, item);
+    g.s = seq;
     const SeqArg& sq = a.seq[g.s];
     const uint32_t local = item - sq.item_begin;
     g.c = local / a.units_per_chunk;                 // units_per_chunk = n_kv * n_layers
@@ -206,13 +206,15 @@ __device__ __forceinline__ const gvec4* group_vector(uint64_t pool, const int32_
 // One workgroup per group; vector v of the group (token-major, 8 elements)
 // is held by thread v % 1024 in slot v / 1024.
 template <bool kE5M2>
-__global__ __launch_bounds__(kOnchipBlock) void store_fp8_onchip(MoveArgs a)
+__global__ __launch_bounds__(kOnchipBlock) void store_fp8_onchip(MoveArgsLut al)
 {
+    const MoveArgs& a = al.m;
     constexpr int B = kOnchipBlock;
     __shared__ u32x4 lds[kOnchipLdsSlots * B];
     __shared__ uint32_t red[B / 64];
     __shared__ int32_t pages[kOnchipMaxPages];
-    const GroupUnit g = locate_group_unit(a, a.item_base + xcd_contiguous(blockIdx.x, gridDim.x));
+    const uint32_t item = a.item_base + xcd_contiguous(blockIdx.x, gridDim.x);
+    const GroupUnit g = locate_group_unit(a, item, find_seq_lut(al, item));
     const SeqArg& sq = a.seq[g.s];
     const uint64_t pool = wave_uniform(gptr<const gu64>(g.kv ? a.v_pages : a.k_pages)[g.l]);
     const uint64_t chunk = wave_uniform(gptr<const gu64>(sq.chunks)[g.c]);
@@ -283,10 +285,12 @@ __global__ __launch_bounds__(kOnchipBlock) void store_fp8_onchip(MoveArgs a)
 // max |x|; pass 2 re-reads them (streaming), quantises, and writes 8 bytes
 // per 16-byte input vector.  Used for groups too large for store_fp8_onchip.
 template <int kBlock, int kUnroll, bool kE5M2>
-__global__ __launch_bounds__(kBlock) void store_fp8(MoveArgs a)
+__global__ __launch_bounds__(kBlock) void store_fp8(MoveArgsLut al)
 {
+    const MoveArgs& a = al.m;
     __shared__ uint32_t red[kBlock / 64];
-    const GroupUnit g = locate_group_unit(a, a.item_base + xcd_contiguous(blockIdx.x, gridDim.x));
+    const uint32_t item = a.item_base + xcd_contiguous(blockIdx.x, gridDim.x);
+    const GroupUnit g = locate_group_unit(a, item, find_seq_lut(al, item));
     const SeqArg& sq = a.seq[g.s];
     const uint64_t pool = wave_uniform(gptr<const gu64>(g.kv ? a.v_pages : a.k_pages)[g.l]);
     const uint64_t chunk = wave_uniform(gptr<const gu64>(sq.chunks)[g.c]);
@@ -394,11 +398,13 @@ __device__ __forceinline__ void retrieve_fp8_unit_tile(const MoveArgs& a, const 
 }
 
 template <int kBlock, int kVpt, bool kE5M2>
-__device__ __forceinline__ void retrieve_fp8_tile(const MoveArgs& a, uint32_t b)
+__device__ __forceinline__ void retrieve_fp8_tile(const MoveArgsLut& al, uint32_t b)
 {
+    const MoveArgs& a = al.m;
     const uint32_t unit = b / a.tiles;
     const uint32_t tile = b - unit * a.tiles;
-    retrieve_fp8_unit_tile<kBlock, kVpt, kE5M2>(a, locate_page_unit(a, a.item_base + unit), tile);
+    const uint32_t item = a.item_base + unit;
+    retrieve_fp8_unit_tile<kBlock, kVpt, kE5M2>(a, locate_page_unit(a, item, find_seq_lut(al, item)), tile);
 }
 
 // The same in pool-address order (sorted page list, see sorted_unit).
@@ -413,14 +419,14 @@ __global__ __launch_bounds__(kBlock) void retrieve_fp8_sorted(MoveArgs a, uint64
 }
 
 template <int kBlock, int kVpt, bool kE5M2>
-__global__ __launch_bounds__(kBlock) void retrieve_fp8(MoveArgs a)
+__global__ __launch_bounds__(kBlock) void retrieve_fp8(MoveArgsLut al)
 {
-    if (gridDim.x >= a.total_tiles) {         // one workgroup per tile: straight-line code
-        retrieve_fp8_tile<kBlock, kVpt, kE5M2>(a, xcd_contiguous(blockIdx.x, gridDim.x));
+    if (gridDim.x >= al.m.total_tiles) {      // one workgroup per tile: straight-line code
+        retrieve_fp8_tile<kBlock, kVpt, kE5M2>(al, xcd_contiguous(blockIdx.x, gridDim.x));
         return;
     }
-    const TileRange r = my_tiles(a.total_tiles);
-    for (uint32_t b = r.first; b < r.last; ++b) retrieve_fp8_tile<kBlock, kVpt, kE5M2>(a, b);
+    const TileRange r = my_tiles(al.m.total_tiles);
+    for (uint32_t b = r.first; b < r.last; ++b) retrieve_fp8_tile<kBlock, kVpt, kE5M2>(al, b);
 }
 
 }  // namespace kvmove

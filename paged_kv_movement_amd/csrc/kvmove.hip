@@ -307,11 +307,11 @@ Launch quantise_launch(const kv_paged* p, bool e5m2, uint32_t kv0, uint32_t n_kv
     if (group_vectors <= int64_t(kOnchipMaxVectors) && p->chunk_size / p->page_size <= kOnchipMaxPages) {
         const KernelFn k = e5m2 ? reinterpret_cast<KernelFn>(&store_fp8_onchip<true>)
                                 : reinterpret_cast<KernelFn>(&store_fp8_onchip<false>);
-        return {k, kOnchipBlock, 0, Unit::Group, kv0, n_kv, nullptr};
+        return {k, kOnchipBlock, 0, Unit::Group, kv0, n_kv, nullptr, true};
     }
     const KernelFn k = e5m2 ? reinterpret_cast<KernelFn>(&store_fp8<kFp8StoreBlock, kFp8StoreUnroll, true>)
                             : reinterpret_cast<KernelFn>(&store_fp8<kFp8StoreBlock, kFp8StoreUnroll, false>);
-    return {k, kFp8StoreBlock, 0, Unit::Group, kv0, n_kv, nullptr};
+    return {k, kFp8StoreBlock, 0, Unit::Group, kv0, n_kv, nullptr, true};
 }
 
 template <int B, int V>
@@ -322,7 +322,7 @@ Launch dequantise_shape(bool e5m2, uint32_t kv0, uint32_t n_kv, bool sorted)
     const KernelFn ks = !sorted ? nullptr
                         : e5m2  ? reinterpret_cast<KernelFn>(&retrieve_fp8_sorted<B, V, true>)
                                 : reinterpret_cast<KernelFn>(&retrieve_fp8_sorted<B, V, false>);
-    return {k, B, B * V * 16, Unit::Page, kv0, n_kv, ks};
+    return {k, B, B * V * 16, Unit::Page, kv0, n_kv, ks, true};
 }
 
 // Scatter + dequantise.  The chunk-major launch takes one-wave workgroups;
