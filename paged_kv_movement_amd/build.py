@@ -42,6 +42,22 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_c_example(out: str | None = None) -> str:
+    """Compile tests/abi_c_example.c, a plain C program using the C ABI,
+    against libkvmove.so (found through the rpath, relative to the program
+    first, then by this tree's absolute path).  The HIP
+    headers need the platform macro that hipcc defines only for HIP sources."""
+    src = os.path.join(ROOT, "tests", "abi_c_example.c")
+    out = out or os.path.join(ROOT, "tests", "abi_c_example")
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+           "-I", "/opt/rocm/include", "-o", tmp, src, "-L", HERE, "-lkvmove", "-L", "/opt/rocm/lib", "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../paged_kv_movement_amd", "-Wl,-rpath," + HERE]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
     sys.exit(0)

@@ -312,3 +312,12 @@ def test_ordered_retrieve_refuses_more_pages_than_the_pool():
     assert L.kv_retrieve_chunks_cachegen(ctypes.byref(p), seqs, masks, 1, kb, kb, out, 0x10000, need,
                                          None) == kvm.KV_EINVAL
     assert "repeat" in L.kv_last_error().decode()
+
+
+def test_c_example_builds_against_the_header(tmp_path):
+    # a plain C program (tests/abi_c_example.c) compiles against
+    # include/kvmove.h and links libkvmove.so; a GPU test runs it
+    _lib()
+    from paged_kv_movement_amd import build
+    out = build.build_c_example(str(tmp_path / "abi_c_example"))
+    assert os.path.exists(out) and os.access(out, os.X_OK)
