@@ -244,6 +244,36 @@ uint8_t kvo_e5m2_encode(float y)
     return (uint8_t)(sign | (uint8_t)((E + 15) << 2) | (uint8_t)mant);
 }
 
+/* The default quiet NaN of binary32 (sign 0, quiet bit, zero payload).  The
+ * pages say nothing of NaN; the reading taken here gives every NaN the method
+ * produces a fixed pattern, so that two implementations agree bit for bit:
+ * the scale of a group holding a NaN, the max1 of a CacheGen row holding
+ * one, and (as bf16 0x7FC0, with the sign noted where it is kept) a NaN
+ * dequantised value. */
+static float default_nan(void)
+{
+    const uint32_t bits = 0x7FC00000u;
+    float f;
+    memcpy(&f, &bits, 4);
+    return f;
+}
+
+/* Code of an element whose quotient x / scale is NaN (the group holds a NaN,
+ * or x and the scale are both infinite): the NaN code of the encoding with
+ * the sign bit of the element itself, S.1111.111 (E4M3) or S.11111.11
+ * (E5M2) -- both are 0x7F | sign. */
+static uint8_t nan_code(uint16_t x_bits)
+{
+    return (uint8_t)(((x_bits >> 8) & 0x80u) | 0x7Fu);
+}
+
+/* bf16 result of a dequantised value that is NaN: the quiet NaN 0x7FC0, with
+ * the sign of the fp8 code it came from (sign_bit 0 or 1). */
+static uint16_t nan_bf16(int sign_bit)
+{
+    return (uint16_t)(0x7FC0u | (sign_bit ? 0x8000u : 0u));
+}
+
 /* One scale per (chunk, layer, K/V) group: the group's absolute maximum
  * mapped onto E4M3's largest finite value, so the group spans [-448, 448].
  * An all-zero group takes scale 1 (its elements encode as signed zeros). */
@@ -377,15 +407,19 @@ int kvo_store(const kvo_pool* p, const int32_t* bt, int64_t n_bt,
                             else if (fabsf(x) > amax) amax = fabsf(x);
                         }
                     }
-                    if (saw_nan) amax = NAN;
-                    float scale = kind == PART_E4M3 ? kvo_fp8_scale(amax) : kvo_e5m2_scale(amax);
+                    float scale;
+                    if (saw_nan) scale = default_nan();
+                    else scale = kind == PART_E4M3 ? kvo_fp8_scale(amax) : kvo_e5m2_scale(amax);
                     for (int64_t j = 0; j < n_c; j++) {
                         int64_t row = kvo_slot(bt, p->page_size, t0 + j);
                         for (int64_t i = 0; i < width; i++) {
-                            float x = kvo_float_from_bf16(*pool_elem(p, l, kv, row, i));
+                            uint16_t xb = *pool_elem(p, l, kv, row, i);
+                            float x = kvo_float_from_bf16(xb);
                             float y = x / scale;          /* binary32 division */
-                            sec[(j * width + i) * eb] =
-                                kind == PART_E4M3 ? kvo_e4m3_encode(y) : kvo_e5m2_encode(y);
+                            uint8_t code;
+                            if (isnan(y)) code = nan_code(xb);
+                            else code = kind == PART_E4M3 ? kvo_e4m3_encode(y) : kvo_e5m2_encode(y);
+                            sec[(j * width + i) * eb] = code;
                         }
                     }
                     memcpy(buf + scale_offset(p, fmt, l, kv, n_c), &scale, 4);
@@ -448,7 +482,8 @@ int64_t kvo_retrieve(const kvo_pool* p, const int32_t* bt, int64_t n_bt,
                         } else {
                             float d = kind == PART_E4M3 ? kvo_e4m3_decode(*src) : kvo_e5m2_decode(*src);
                             float prod = d * scale;       /* binary32 product */
-                            x = kvo_bf16_from_float(prod);
+                            if (isnan(prod)) x = nan_bf16(*src >> 7);
+                            else x = kvo_bf16_from_float(prod);
                         }
                         *pool_elem(p, l, kv, row, i) = x;
                     }
@@ -468,7 +503,9 @@ int64_t kvo_retrieve(const kvo_pool* p, const int32_t* bt, int64_t n_bt,
  * and max1 is kept for the inverse (q - MAX) / MAX * max1.  All arithmetic
  * in float32, one rounding per operation.  Readings: an all-zero row
  * (max1 == 0) gives every element the symbol MAX (the division by zero has
- * no value there); a NaN from the arithmetic also gives MAX. */
+ * no value there); a NaN from the arithmetic also gives MAX.  A row holding
+ * a NaN keeps max1 = the default quiet NaN, and a dequantised value that is
+ * NaN is written as the bf16 quiet NaN 0x7FC0. */
 static int cachegen_max(const int32_t* bins, int l)
 {
     return bins[l] / 2 - 1;
@@ -519,7 +556,7 @@ int kvo_store_cachegen(const kvo_pool* p, const int32_t* bt, int64_t n_bt,
                         if (isnan(x)) saw_nan = 1;
                         else if (fabsf(x) > max1) max1 = fabsf(x);
                     }
-                    if (saw_nan) max1 = NAN;
+                    if (saw_nan) max1 = default_nan();
                     float factor = max1 == 0.0f ? 0.0f : (float)MAX / max1;
                     uint8_t* out = buf + cg_row(p, l, kv, n_c, j) * width;
                     for (int64_t i = 0; i < width; i++) {
@@ -581,7 +618,8 @@ int64_t kvo_retrieve_cachegen(const kvo_pool* p, const int32_t* bt, int64_t n_bt
                         float centred = (float)in[i] - (float)MAX;   /* exact */
                         float unit = centred / (float)MAX;           /* binary32 quotient */
                         float x = unit * max1;                       /* binary32 product */
-                        *pool_elem(p, l, kv, row, i) = kvo_bf16_from_float(x);
+                        /* NaN (a NaN max1, or 0 times an infinite one): no sign to keep */
+                        *pool_elem(p, l, kv, row, i) = isnan(x) ? nan_bf16(0) : kvo_bf16_from_float(x);
                     }
                 }
             }

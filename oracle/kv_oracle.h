@@ -30,7 +30,10 @@
  *    双层接口设计与自定义扩展实战" (LMCache serde framework page), section
  *    "7.1 fp8 量化"), here with one fp32 absmax scale per (chunk, layer, K/V):
  *    scale = amax / fmax (448 for e4m3, 57344 for e5m2), q = fp8(x / scale)
- *    rounded to nearest-even and saturated.
+ *    rounded to nearest-even and saturated.  NaN (the pages are silent):
+ *    a group holding a NaN gets the default quiet NaN 0x7FC00000 as its
+ *    scale; a NaN quotient encodes as 0x7F | the element's sign bit; a
+ *    dequantised NaN is the bf16 quiet NaN 0x7FC0 with the code's sign.
  *  - The asymmetric K16/V8 serde named on the same page (section "7.3":
  *    K kept at 16 bits, V at 8): K copied as bf16, V quantised as scaled e4m3.
  *  - The CacheGen quantiser (CacheGen page, section "2. 量化"): per layer a
@@ -38,7 +41,8 @@
  *    absolute maximum max1 over its channels; symbol
  *    q = round(x * (MAX / max1) + MAX), kept with max1; dequantised as
  *    (q - MAX) / MAX * max1.  Only the quantiser, not the CDF and
- *    arithmetic coding that follow it on that page.
+ *    arithmetic coding that follow it on that page.  A row holding a NaN
+ *    keeps max1 = 0x7FC00000; a dequantised NaN is written as 0x7FC0.
  *
  * Parity pins (tests marked "not gpu") tie each function to something other
  * than itself: numpy page-gather + reshape formulations, store-then-retrieve

@@ -62,8 +62,20 @@ MUTANTS = [
      "return amax / 448.0f;",
      "return amax / 447.0f;"),
     ("fp8 group maximum ignores NaN",
-     "if (saw_nan) amax = NAN;",
-     "if (saw_nan) amax = amax;"),
+     "if (saw_nan) scale = default_nan();",
+     "if (0) scale = default_nan();"),
+    ("fp8 NaN quotient takes the sign the division gives",
+     "if (isnan(y)) code = nan_code(xb);",
+     "if (isnan(y)) code = kind == PART_E4M3 ? kvo_e4m3_encode(y) : kvo_e5m2_encode(y);"),
+    ("fp8 dequantised NaN left to the product",
+     "if (isnan(prod)) x = nan_bf16(*src >> 7);",
+     "if (0) x = nan_bf16(*src >> 7);"),
+    ("CacheGen: max1 of a NaN row left finite",
+     "if (saw_nan) max1 = default_nan();",
+     "if (0) max1 = default_nan();"),
+    ("CacheGen dequantised NaN left to the product",
+     "isnan(x) ? nan_bf16(0) : kvo_bf16_from_float(x)",
+     "kvo_bf16_from_float(x)"),
     ("fp8 quotient by reciprocal product",
      "float y = x / scale;          /* binary32 division */",
      "float y = x * (1.0f / scale);"),

@@ -431,23 +431,63 @@ def test_fp8_zero_group_and_signed_zero():
 
 def test_fp8_nan_group_follows_numpy_and_torch():
     # a NaN anywhere in a group: numpy's maximum propagates it, so the scale
-    # and every quotient are NaN and the torch cast gives the NaN code; the
-    # other part of the chunk is unaffected
+    # and every quotient are NaN; the NaN reading fixes their bits (scale
+    # 0x7FC00000, codes 0x7F | the element's sign); the other part of the
+    # chunk is unaffected.  Retrieve: every value of the NaN part is the bf16
+    # quiet NaN with its code's sign.
     w = wl.custom("nan", 82, 1, 1, 16, 16, [(0, 16)])
     rng = np.random.default_rng(82)
     x = rng.standard_normal(w.pool_shape()).astype(np.float32)
     arr = (x.view(np.uint32) >> 16).astype(np.uint16)
-    arr[0, 0, 3, 5, 7] = 0x7FC0                                        # one quiet NaN in K
+    arr[0, 0, 3, 5, 7] = 0xFFC1                                        # one negative NaN with a payload in K
     _, pool = _pool(w, arr)
     sq = w.seqs[0]
+    k_bits = arr[0, 0, sq.block_table[0]].ravel()                     # K rows of the one page, token-major
     for fmt in (oracle.FMT_FP8, oracle.FMT_FP8_E5M2):
         ch = oracle.alloc_chunks(pool, 0, 16, fmt)
         assert oracle.store(pool, sq.block_table, 0, 16, ch, fmt) == 0
         exp = _numpy_store_any(arr, sq.block_table, 0, 16, 16, fmt)[0]
         assert np.array_equal(ch[0], exp)
         n = 16 * 16
-        assert ((ch[0][:n] & 0x7F) == 0x7F).all()                      # NaN codes in both encodings
-        assert np.isnan(ch[0][2 * n:].view(np.float32)[0]) and np.isfinite(ch[0][2 * n:].view(np.float32)[1])
+        sign = ((k_bits >> 15) & 1).astype(np.uint8)
+        assert np.array_equal(ch[0][:n], (sign << 7) | 0x7F)            # 0x7F | sign, element by element
+        assert 0 < sign.sum() < n                                        # both signs occur
+        sc = ch[0][2 * n:].view(np.uint32)
+        assert sc[0] == 0x7FC00000 and np.isfinite(sc[1:].view(np.float32)).all()
+        back = np.zeros_like(arr)
+        bpool = oracle.Pool.from_array(back, w.num_kv_heads, w.head_dim, w.chunk_size)
+        assert oracle.retrieve(bpool, sq.block_table, 0, 16, [1], ch, fmt) == 16
+        k_back = back[0, 0, sq.block_table[0]].ravel()
+        assert np.array_equal(k_back, (sign.astype(np.uint16) << 15) | 0x7FC0)
+
+
+@pytest.mark.parametrize("fmt", [oracle.FMT_FP8, oracle.FMT_FP8_E5M2])
+def test_fp8_infinite_group_follows_ieee(fmt):
+    # a group whose maximum is infinite: scale = inf / fmax = inf; a finite
+    # element's quotient is a signed zero, an infinite one's inf / inf is NaN
+    # (0x7F | its sign).  Retrieve: +-0 * inf and NaN both give the bf16
+    # quiet NaN with the code's sign.
+    w = wl.custom("inf", 83, 1, 1, 16, 16, [(0, 16)])
+    rng = np.random.default_rng(83)
+    arr = (rng.standard_normal(w.pool_shape()).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    sq = w.seqs[0]
+    page = sq.block_table[0]
+    arr[0, 1, page, 2, 3] = 0xFF80                                     # -inf in V
+    arr[0, 1, page, 9, 1] = 0x7F80                                     # +inf in V
+    _, pool = _pool(w, arr)
+    ch = oracle.alloc_chunks(pool, 0, 16, fmt)
+    assert oracle.store(pool, sq.block_table, 0, 16, ch, fmt) == 0
+    n = 16 * 16
+    v_bits = arr[0, 1, page].ravel()
+    sign = ((v_bits >> 15) & 1).astype(np.uint8)
+    inf = (v_bits & 0x7FFF) == 0x7F80
+    expect = np.where(inf, (sign << 7) | 0x7F, sign << 7).astype(np.uint8)
+    assert np.array_equal(ch[0][n:2 * n], expect)
+    assert ch[0][2 * n:].view(np.float32)[1] == np.inf
+    back = np.zeros_like(arr)
+    bpool = oracle.Pool.from_array(back, w.num_kv_heads, w.head_dim, w.chunk_size)
+    assert oracle.retrieve(bpool, sq.block_table, 0, 16, [1], ch, fmt) == 16
+    assert np.array_equal(back[0, 1, page].ravel(), (sign.astype(np.uint16) << 15) | 0x7FC0)
 
 
 # ------------------------------------------- e5m2 and asymmetric K16/V8 formats
@@ -483,7 +523,12 @@ def _numpy_store_any(arr, bt, s, e, C, fmt):
                 x = (g[l, kv].astype(np.uint32) << 16).view(np.float32)
                 amax = np.abs(x).max()
                 scale = np.float32(1.0) if amax == 0 else np.float32(amax / _FMAX[kind])
-                parts.append(_CAST[kind]((x / scale).ravel()))
+                if np.isnan(amax):               # the NaN reading: the default quiet NaN
+                    scale = np.uint32(0x7FC00000).view(np.float32)
+                y = (x / scale).ravel()
+                # the NaN reading: a NaN quotient is 0x7F with the element's sign bit
+                sign = (g[l, kv].ravel() >> 8).astype(np.uint8) & np.uint8(0x80)
+                parts.append(np.where(np.isnan(y), sign | np.uint8(0x7F), _CAST[kind](y)).astype(np.uint8))
                 scales.append(scale)
         out.append(np.concatenate(parts + [np.array(scales, np.float32).view(np.uint8)]))
     return out
@@ -717,6 +762,38 @@ def test_cachegen_retrieve_matches_torch_and_error_bound():
                 assert (np.abs(xr - xo) <= bound).all(), (c, l, kv)
     # rows of the missed chunk keep the sentinel
     assert (got[:, :, slots[512:]] == 0xA5A5).all()
+
+
+def test_cachegen_nan_and_infinite_rows():
+    # the NaN reading: a row holding a NaN keeps max1 = 0x7FC00000 and every
+    # symbol MAX; a row whose maximum is infinite has factor MAX / inf = 0, so
+    # every symbol is MAX too (inf * 0 is NaN, which also gives MAX).  Back,
+    # (MAX - MAX) / MAX * max1 is 0 * NaN or 0 * inf: NaN, written 0x7FC0.
+    w = wl.custom("cgn", 305, 1, 1, 16, 32, [(0, 16)])
+    arr = wl.host_pool(w)
+    sq = w.seqs[0]
+    page = sq.block_table[0]
+    arr[0, 0, page, 2, 5] = 0xFFC1                         # K row 2: a negative NaN with a payload
+    arr[0, 1, page, 7, 0] = 0xFF80                         # V row 7: -inf
+    _, pool = _pool(w, arr)
+    kb, vb = [32], [16]
+    ch = oracle.alloc_chunks(pool, 0, 16, oracle.FMT_CACHEGEN)
+    assert oracle.store_cachegen(pool, sq.block_table, 0, 16, ch, kb, vb) == 0
+    E = w.width
+    sym = ch[0][:2 * 16 * E].reshape(2, 16, E)
+    mx = ch[0][2 * 16 * E:].view(np.uint32).reshape(2, 16)
+    assert mx[0, 2] == 0x7FC00000 and (sym[0, 2] == 15).all()
+    assert mx[1, 7] == np.float32(np.inf).view(np.uint32) and (sym[1, 7] == 7).all()
+    back = np.zeros_like(arr)
+    bpool = oracle.Pool.from_array(back, w.num_kv_heads, w.head_dim, w.chunk_size)
+    assert oracle.retrieve_cachegen(bpool, sq.block_table, 0, 16, [1], ch, kb, vb) == 16
+    assert (back[0, 0, page, 2] == 0x7FC0).all() and (back[0, 1, page, 7] == 0x7FC0).all()
+    # the other rows are finite and follow the torch formulation
+    exp = _torch_cachegen_store(arr, sq.block_table, 0, 16, 256, kb, vb)[0]
+    keep = np.ones((2, 16), bool)
+    keep[0, 2] = keep[1, 7] = False
+    assert np.array_equal(sym[keep], exp[:2 * 16 * E].reshape(2, 16, E)[keep])
+    assert np.isfinite((back[0][:, page][keep].astype(np.uint32) << 16).view(np.float32)).all()
 
 
 def test_cachegen_rejects_bins_out_of_range():
