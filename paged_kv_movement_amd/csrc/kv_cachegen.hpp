@@ -136,6 +136,46 @@ __device__ __forceinline__ float cg_unit(uint32_t q, float qmax, float r)
     return __builtin_fmaf(e, r, p);
 }
 
+// Two dequantised values -> two bf16 in one word.  In a row whose max1 is
+// NaN or infinite (`special`, the same for the whole wave) a value can be NaN
+// (NaN * x, 0 * inf); it is written as the quiet NaN 0x7FC0, whatever sign
+// and payload the product had.  A finite max1 gives finite values only.
+__device__ __forceinline__ uint32_t cg_pair(float a, float b, bool special)
+{
+    uint32_t o = bf16x2_rne(a, b);
+    if (special) {
+        if (a != a) o = (o & 0xFFFF0000u) | 0x7FC0u;
+        if (b != b) o = (o & 0x0000FFFFu) | 0x7FC00000u;
+    }
+    return o;
+}
+
+__device__ __forceinline__ bool cg_special(float max1) { return !(__builtin_fabsf(max1) < __builtin_inff()); }
+
+// Dequantise one row's kVpl vectors of 8 symbols and store them as bf16;
+// kSpecial as cg_pair's `special`.
+template <int kVpl, bool kSpecial>
+__device__ __forceinline__ void cg_dequantise_row(const u32x2 (&q)[kVpl], float qmax, float rq, float max1,
+                                                  __amdgpu_buffer_rsrc_t rd, uint32_t lane, int aux)
+{
+#pragma unroll
+    for (int k = 0; k < kVpl; ++k) {
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t w = q[k][j];
+            o[2 * j] = cg_pair(cg_unit(w & 0xFFu, qmax, rq) * max1, cg_unit((w >> 8) & 0xFFu, qmax, rq) * max1,
+                               kSpecial);
+            o[2 * j + 1] = cg_pair(cg_unit((w >> 16) & 0xFFu, qmax, rq) * max1, cg_unit(w >> 24, qmax, rq) * max1,
+                                   kSpecial);
+        }
+        if (aux == (kCpolNt | kCpolSc1))
+            __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * 64 + lane) * 16, 0, kCpolNt | kCpolSc1);
+        else
+            __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * 64 + lane) * 16, 0, kCpolNt);
+    }
+}
+
 // Byte offset of the max1 of row j0 + row of (l, kv) in a chunk of n_c tokens.
 __device__ __forceinline__ uint64_t cg_max_offset(const MoveArgs& a, uint32_t l, uint32_t kv, uint32_t n_c,
                                                   uint32_t row)
@@ -250,19 +290,10 @@ __device__ __forceinline__ void retrieve_cachegen_unit(const CgArgs& ca, const P
             const uint32_t r = r0 + i * kCgWaves;
             if (r >= u.rows) break;                       // the same for the whole wave
             const __amdgpu_buffer_rsrc_t rd = byte_range(page_rows + (uint64_t)r * row_bytes, row_bytes);
-#pragma unroll
-            for (int k = 0; k < kVpl; ++k) {
-                u32x4 o;
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const uint32_t w = q[i][k][j];
-                    o[2 * j] = bf16x2_rne(cg_unit(w & 0xFFu, qmax, rq) * max1[i],
-                                          cg_unit((w >> 8) & 0xFFu, qmax, rq) * max1[i]);
-                    o[2 * j + 1] = bf16x2_rne(cg_unit((w >> 16) & 0xFFu, qmax, rq) * max1[i],
-                                              cg_unit(w >> 24, qmax, rq) * max1[i]);
-                }
-                __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * 64 + lane) * 16, 0, kCpolNt);
-            }
+            if (cg_special(max1[i]))                      // the same for the whole wave
+                cg_dequantise_row<kVpl, true>(q[i], qmax, rq, max1[i], rd, lane, kCpolNt);
+            else
+                cg_dequantise_row<kVpl, false>(q[i], qmax, rq, max1[i], rd, lane, kCpolNt);
         }
     }
 }
@@ -302,17 +333,10 @@ __device__ __forceinline__ void retrieve_cachegen_tile(const CgArgs& ca, const P
 #pragma unroll
     for (int k = 0; k < kVpl; ++k)
         q[k] = __builtin_amdgcn_raw_buffer_load_b64(rs, (k * 64 + lane) * 8, 0, kCpolNt | kCpolSc1);
-#pragma unroll
-    for (int k = 0; k < kVpl; ++k) {
-        u32x4 o;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t w = q[k][j];
-            o[2 * j] = bf16x2_rne(cg_unit(w & 0xFFu, qmax, rq) * max1, cg_unit((w >> 8) & 0xFFu, qmax, rq) * max1);
-            o[2 * j + 1] = bf16x2_rne(cg_unit((w >> 16) & 0xFFu, qmax, rq) * max1, cg_unit(w >> 24, qmax, rq) * max1);
-        }
-        __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * 64 + lane) * 16, 0, kCpolNt | kCpolSc1);
-    }
+    if (cg_special(max1))                                 // the same for the whole wave
+        cg_dequantise_row<kVpl, true>(q, qmax, rq, max1, rd, lane, kCpolNt | kCpolSc1);
+    else
+        cg_dequantise_row<kVpl, false>(q, qmax, rq, max1, rd, lane, kCpolNt | kCpolSc1);
 }
 
 template <int kVpl>

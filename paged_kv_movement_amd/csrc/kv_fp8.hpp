@@ -159,6 +159,18 @@ __device__ __forceinline__ bool fast_quotient_ok(uint32_t amax_bits)
     return amax_bits >= 0x3D80u && amax_bits < 0x7F80u;     // [2^-4, largest finite]
 }
 
+// Code of one bf16 element (its 16 bits in h) on the slow path: IEEE
+// division and the integer encoder.  A NaN quotient -- the group holds a NaN,
+// or the element and the scale are both infinite -- encodes as 0x7F with the
+// element's own sign bit (the sign a division gives a NaN is not fixed by
+// IEEE 754; taking the element's makes the code deterministic).
+template <bool kE5M2>
+__device__ __forceinline__ uint32_t slow_code(uint32_t h, float scale)
+{
+    const float y = __uint_as_float(h << 16) / scale;
+    return y != y ? (((h >> 8) & 0x80u) | 0x7Fu) : fp8_from_float<kE5M2>(y);
+}
+
 // Eight bf16 values (one 16-byte vector) -> eight fp8 bytes.  `fast`
 // selects the division-free quotient (exact in both encodings for the
 // group's amax, see quotient_fast); otherwise IEEE division and the integer
@@ -177,14 +189,23 @@ __device__ __forceinline__ u32x2 quantize8(const u32x4 x, float scale, float r, 
     } else {   // tiny, infinite or NaN amax
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const uint32_t b0 = fp8_from_float<kE5M2>(lo_bf16(x[2 * j]) / scale);
-            const uint32_t b1 = fp8_from_float<kE5M2>(hi_bf16(x[2 * j]) / scale);
-            const uint32_t b2 = fp8_from_float<kE5M2>(lo_bf16(x[2 * j + 1]) / scale);
-            const uint32_t b3 = fp8_from_float<kE5M2>(hi_bf16(x[2 * j + 1]) / scale);
-            q[j] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+            const uint32_t w0 = x[2 * j], w1 = x[2 * j + 1];
+            q[j] = slow_code<kE5M2>(w0 & 0xFFFFu, scale) | (slow_code<kE5M2>(w0 >> 16, scale) << 8) |
+                   (slow_code<kE5M2>(w1 & 0xFFFFu, scale) << 16) | (slow_code<kE5M2>(w1 >> 16, scale) << 24);
         }
     }
     return q;
+}
+
+// The scale of a group from its maximum (bf16 magnitude bits): amax / fmax,
+// 1 for an all-zero group, and the default quiet NaN 0x7FC00000 when the
+// group holds a NaN (NaN magnitudes sort above infinity).
+template <bool kE5M2>
+__device__ __forceinline__ float group_scale(uint32_t amax_bits)
+{
+    const float amax = __uint_as_float(amax_bits << 16);
+    if (amax_bits > 0x7F80u) return __uint_as_float(0x7FC00000u);
+    return amax == 0.0f ? 1.0f : amax / fp8_max<kE5M2>();
 }
 
 // Address of 16-byte vector v of a group (token-major) whose pool pages are
@@ -260,8 +281,7 @@ __global__ __launch_bounds__(kOnchipBlock) void store_fp8_onchip(MoveArgsLut al)
         if (v < total) m2 = max_magnitude2(m2, lds[k * B + threadIdx.x]);
     }
     const uint32_t amax_bits = block_max_u32<B>(pair_max(m2), red);
-    const float amax = __uint_as_float(amax_bits << 16);
-    const float scale = amax == 0.0f ? 1.0f : amax / fp8_max<kE5M2>();
+    const float scale = group_scale<kE5M2>(amax_bits);
     const bool fast = fast_quotient_ok(amax_bits);
     const float r = 1.0f / scale;
 
@@ -325,8 +345,7 @@ __global__ __launch_bounds__(kBlock) void store_fp8(MoveArgsLut al)
         }
     }
     const uint32_t amax_bits = block_max_u32<kBlock>(pair_max(m2), red);
-    const float amax = __uint_as_float(amax_bits << 16);
-    const float scale = amax == 0.0f ? 1.0f : amax / fp8_max<kE5M2>();
+    const float scale = group_scale<kE5M2>(amax_bits);
     const bool fast = fast_quotient_ok(amax_bits);
     const float r = 1.0f / scale;
 
@@ -351,6 +370,42 @@ __global__ __launch_bounds__(kBlock) void store_fp8(MoveArgsLut al)
         }
     }
     if (threadIdx.x == 0) *gptr<gf32>(chunk + scale_offset(a, g.l, g.kv, g.n_c)) = scale;
+}
+
+// Two bf16 results packed in o (from the products p0, p1 of the fp8 codes
+// in bytes 0 and 1 of c): a NaN product becomes the quiet NaN 0x7FC0 with
+// its code's sign.
+__device__ __forceinline__ uint32_t nan_fix2(uint32_t o, float p0, float p1, uint32_t c)
+{
+    if (p0 != p0) o = (o & 0xFFFF0000u) | 0x7FC0u | ((c & 0x80u) << 8);
+    if (p1 != p1) o = (o & 0x0000FFFFu) | 0x7FC00000u | ((c & 0x8000u) << 16);
+    return o;
+}
+
+// Decode kVpt x 8 fp8 codes, scale them, round to bf16 and store them
+// (kBlock*kVpt 16-byte vectors per tile); kFixNan writes every NaN product as
+// the quiet NaN with its code's sign.
+template <int kBlock, int kVpt, bool kE5M2, bool kFixNan>
+__device__ __forceinline__ void dequantise_store(const u32x2 (&q)[kVpt], float scale, __amdgpu_buffer_rsrc_t rd)
+{
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k) {
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const auto d0 = kE5M2 ? __builtin_amdgcn_cvt_pk_f32_bf8(q[k][j], false)    // bytes 0, 1
+                                  : __builtin_amdgcn_cvt_pk_f32_fp8(q[k][j], false);
+            const auto d1 = kE5M2 ? __builtin_amdgcn_cvt_pk_f32_bf8(q[k][j], true)     // bytes 2, 3
+                                  : __builtin_amdgcn_cvt_pk_f32_fp8(q[k][j], true);
+            o[2 * j] = bf16x2_rne(d0[0] * scale, d0[1] * scale);
+            o[2 * j + 1] = bf16x2_rne(d1[0] * scale, d1[1] * scale);
+            if (kFixNan) {
+                o[2 * j] = nan_fix2(o[2 * j], d0[0] * scale, d0[1] * scale, q[k][j]);
+                o[2 * j + 1] = nan_fix2(o[2 * j + 1], d1[0] * scale, d1[1] * scale, q[k][j] >> 16);
+            }
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * kBlock + threadIdx.x) * 16, 0, kCpolNt | kCpolSc1);
+    }
 }
 
 // Scatter + dequantise one tile of one page unit: fp8 decoded by the
@@ -381,20 +436,16 @@ __device__ __forceinline__ void retrieve_fp8_unit_tile(const MoveArgs& a, const 
 #pragma unroll
     for (int k = 0; k < kVpt; ++k)
         q[k] = __builtin_amdgcn_raw_buffer_load_b64(rs, (k * kBlock + threadIdx.x) * 8, 0, kCpolNt | kCpolSc1);
-#pragma unroll
-    for (int k = 0; k < kVpt; ++k) {
-        u32x4 o;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const auto d0 = kE5M2 ? __builtin_amdgcn_cvt_pk_f32_bf8(q[k][j], false)    // bytes 0, 1
-                                  : __builtin_amdgcn_cvt_pk_f32_fp8(q[k][j], false);
-            const auto d1 = kE5M2 ? __builtin_amdgcn_cvt_pk_f32_bf8(q[k][j], true)     // bytes 2, 3
-                                  : __builtin_amdgcn_cvt_pk_f32_fp8(q[k][j], true);
-            o[2 * j] = bf16x2_rne(d0[0] * scale, d0[1] * scale);
-            o[2 * j + 1] = bf16x2_rne(d1[0] * scale, d1[1] * scale);
-        }
-        __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * kBlock + threadIdx.x) * 16, 0, kCpolNt | kCpolSc1);
-    }
+    // A scale that is NaN, infinite or zero can turn a product into NaN
+    // (NaN * x, +-0 * inf, inf * 0); such groups take the path that writes
+    // every NaN result as the quiet NaN 0x7FC0 with the code's sign.  The
+    // store writes NaN codes only under a NaN scale, so with any other scale
+    // the plain path is taken (a NaN code from elsewhere still comes out as
+    // a NaN: the hardware conversions keep its sign and quiet it).
+    if (!(__builtin_fabsf(scale) < __builtin_inff()) || scale == 0.0f)    // the same for the whole wave
+        dequantise_store<kBlock, kVpt, kE5M2, true>(q, scale, rd);
+    else
+        dequantise_store<kBlock, kVpt, kE5M2, false>(q, scale, rd);
 }
 
 template <int kBlock, int kVpt, bool kE5M2>
