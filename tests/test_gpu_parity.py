@@ -12,7 +12,7 @@ import oracle
 import paged_kv_movement_amd as kvm
 from paged_kv_movement_amd import workloads as wl
 from gpu_util import (say, dev_pool_from_host, host_from_dev_pool, oracle_pool, chunk_tokens,
-                      setup_device, host_chunks, check_store, check_retrieve, sync as _sync)
+                      setup_device, host_chunks, check_store, check_retrieve, first_diff, sync as _sync)
 
 pytestmark = pytest.mark.gpu
 
@@ -143,15 +143,31 @@ def test_layerwise_on_copy_stream_equals_full(fmt):
     _sync()
     prev = before
     for l in range(w.num_layers):
-        n = kvm.retrieve_layer(paged, batch, l, fmt=fmt, stream=copy, event=events[l])
-        assert n == [512, 274]
+        # the boundary's own form (no cap, no token counts) ...
+        assert kvm.retrieve_layer(paged, batch, l, fmt=fmt, stream=copy, event=events[l]) is None
         events[l].synchronize()
         now = host_from_dev_pool(pool)
         others = [x for x in range(w.num_layers) if x != l]
         assert np.array_equal(now[others], prev[others]), f"layer {l} call wrote another layer"
         prev = now
     masks = [sq.hit_mask for sq in w.seqs]
-    check_retrieve(w, before, prev, cs, fmt, masks)
+    assert check_retrieve(w, before, prev, cs, fmt, masks) == [512, 274]
+    # ... and every layer in one call, each layer's event recorded after it:
+    # a consumer stream that waits on event l copies layer l, which must
+    # already hold its final bytes
+    pool.view(torch.int16).fill_(0x0F0F)
+    _sync()
+    events = [torch.cuda.Event() for _ in range(w.num_layers)]
+    consumer = torch.cuda.Stream()
+    snaps = torch.empty_like(pool)
+    assert kvm.retrieve_layers(paged, batch, 0, w.num_layers, fmt=fmt, stream=copy, events=events) == [512, 274]
+    for l in range(w.num_layers):
+        consumer.wait_event(events[l])
+        with torch.cuda.stream(consumer):
+            snaps[l].copy_(pool[l])
+    _sync()
+    assert np.array_equal(host_from_dev_pool(pool), prev)
+    assert np.array_equal(host_from_dev_pool(snaps), prev)
     assert kvm.take_faults() == 0
 
 
@@ -172,7 +188,7 @@ def test_layer_event_recorded_without_hits():
         ev.record(s)
         for _ in range(8):
             c = torch.mm(a, b)
-    assert kvm.retrieve_layer(paged, batch, 1, stream=s, event=ev) == [0]
+    assert kvm.retrieve_layer_ex(paged, batch, 1, stream=s, event=ev) == [0]
     ev.synchronize()
     assert t0.elapsed_time(ev) > 0.2, "the layer event was not re-recorded after the queued work"
     del c
@@ -199,28 +215,63 @@ def test_fp8_zero_nan_and_extreme_groups(fmt):
     assert oracle.store(oracle_pool(w, arr), bt, 0, 40, exp, fmt) == 0
     exp = exp[0]
     n = 2 * 2 * 40 * w.width
-    # NaN results (x / NaN, inf / inf) may differ in sign or payload between
-    # implementations: there, both sides must give a NaN code / NaN scale
-    nan_e = (exp[:n] & 0x7F) == 0x7F
-    assert np.array_equal(got[:n][~nan_e], exp[:n][~nan_e])
-    assert ((got[:n][nan_e] & 0x7F) == 0x7F).all()
-    se, sg = exp[n:].view(np.float32), got[n:].view(np.float32)
-    assert np.array_equal(np.isnan(se), np.isnan(sg))
-    assert np.array_equal(se[~np.isnan(se)].view(np.uint32), sg[~np.isnan(sg)].view(np.uint32))
+    # NaN results (x / NaN, inf / inf) have fixed bits on both sides: codes
+    # 0x7F | the element's sign, the scale 0x7FC00000
+    assert np.array_equal(got, exp), first_diff(got, exp)
+    se = exp[n:].view(np.float32)
     assert list(np.isnan(se)) == [False, True, False, False]
-    assert se[0] == 1.0 and np.isinf(se[2])
-    pool.view(torch.int16).fill_(0)
-    kvm.retrieve(paged, batch, fmt=fmt)
+    assert se[0] == 1.0 and np.isinf(se[2]) and exp[n:].view(np.uint32)[1] == 0x7FC00000
+    for ws in (None, paged.new_workspace()):          # both retrieve orders
+        pool.view(torch.int16).fill_(0)
+        kvm.retrieve(paged, batch, fmt=fmt, workspace=ws)
+        _sync()
+        got = host_from_dev_pool(pool)
+        exp = np.zeros_like(arr)
+        op = oracle_pool(w, exp)
+        assert oracle.retrieve(op, bt, 0, 40, [1], host_chunks(cs[0]), fmt) == 40
+        # NaN values are the bf16 quiet NaN with their code's sign, on both sides
+        assert (((exp & 0x7F80) == 0x7F80) & ((exp & 0x7F) != 0)).any()
+        assert np.array_equal(got, exp), first_diff(got, exp)
+
+
+@pytest.mark.parametrize("fmt", **FP8_FMTS)
+def test_fp8_retrieve_of_nan_and_infinite_codes_under_finite_scales(fmt):
+    # chunk bytes the store never writes (NaN codes, and e5m2's infinity
+    # codes, under a finite scale), as a chunk from elsewhere could hold them:
+    # the retrieve gives the oracle's values bit for bit
+    w = wl.custom("fp8-codes", 182, 2, 1, 16, 64, [(0, 40)], masks=[np.array([1], np.uint8)])
+    arr = wl.host_pool(w)
+    bt = w.seqs[0].block_table
+    pool, paged, batch, cs = setup_device(w, arr, fmt=fmt, fill=0xCD)
+    kvm.store(paged, batch, fmt)
     _sync()
-    got = host_from_dev_pool(pool)
-    exp = np.zeros_like(arr)
-    op = oracle_pool(w, exp)
-    assert oracle.retrieve(op, bt, 0, 40, [1], host_chunks(cs[0]), fmt) == 40
-    # NaN codes may differ in payload between implementations: compare NaN-ness there
-    nan_g = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
-    nan_e = ((exp & 0x7F80) == 0x7F80) & ((exp & 0x7F) != 0)
-    assert np.array_equal(nan_g, nan_e)
-    assert np.array_equal(got[~nan_g], exp[~nan_e])
+    buf = cs[0][0][0]
+    size = cs[0][1][0]
+    host = buf[:size].cpu().numpy()
+    kinds = [(0, 1)] if fmt == K16V8 else [(0, 0), (0, 1), (1, 0), (1, 1)]
+    L, E = w.num_layers, w.width
+    rng = np.random.default_rng(182)
+    codes = [0x7F, 0xFF] + ([0x7C, 0xFC, 0x7D, 0xFE] if fmt == E5M2 else [])
+    planted = 0
+    for l, kv in kinds:
+        # byte offset of (l, kv)'s section: every quantised part is 1 byte per
+        # element here, except K16/V8's bf16 K sections before each V
+        off = (l * 3 * 40 * E + 2 * 40 * E) if fmt == K16V8 else (l * 2 + kv) * 40 * E
+        at = off + rng.choice(40 * E, size=12, replace=False)
+        host[at] = rng.choice(codes, size=12)
+        planted += 12
+    buf[:size].copy_(torch.from_numpy(host))
+    for ws in (None, paged.new_workspace()):
+        pool.view(torch.int16).fill_(0)
+        kvm.retrieve(paged, batch, fmt=fmt, workspace=ws)
+        _sync()
+        assert kvm.take_faults() == 0
+        got = host_from_dev_pool(pool)
+        exp = np.zeros_like(arr)
+        assert oracle.retrieve(oracle_pool(w, exp), bt, 0, 40, [1], [host], fmt) == 40
+        nan_e = ((exp & 0x7F80) == 0x7F80) & ((exp & 0x7F) != 0)
+        assert nan_e.sum() >= planted // 3
+        assert np.array_equal(got, exp), first_diff(got, exp)
 
 
 @pytest.mark.parametrize("fmt", [FP8, E5M2, K16V8], ids=["fp8", "e5m2", "k16v8"])
@@ -246,18 +297,22 @@ BOUND = {"e4m3": (1 + 2.0 ** -4) * (1 + 2.0 ** -24) * (1 + 2.0 ** -8) - 1,
 FLOOR = {"e4m3": 2.0 ** -6, "e5m2": 2.0 ** -14}
 
 
-def _assert_fp8_bound(w, orig, pool, chunk_sets, fmt=FP8):
+def _assert_fp8_bound(w, orig, pool, chunk_sets, fmt=FP8, ref_chunks=None):
     """max |x' - x| / max(|x|, floor * scale) over every stored element of a
     quantised part <= the part's closed-form bound (e4m3: 0.0667, e5m2:
-    0.1295); bf16 parts come back exactly."""
+    0.1295); bf16 parts come back exactly.  The scales come from ref_chunks
+    (the oracle's chunks, [sequence][chunk] host arrays) when given, else
+    from the device chunks."""
     L, E, P, C = w.num_layers, w.width, w.page_size, w.chunk_size
     kinds = PARTS[fmt]
     n_q = sum(k != "bf16" for k in kinds)
     worst = {k: 0.0 for k in kinds}
-    for sq, (bufs, sizes) in zip(w.seqs, chunk_sets):
+    for i, (sq, (bufs, sizes)) in enumerate(zip(w.seqs, chunk_sets)):
         bt = torch.from_numpy(sq.block_table.astype(np.int64)).cuda()
         for c, (b, n_c) in enumerate(zip(bufs, chunk_tokens(w, sq))):
             payload = L * n_c * E * sum(2 if k == "bf16" else 1 for k in kinds)
+            if ref_chunks is not None:
+                b = torch.from_numpy(ref_chunks[i][c]).cuda()
             scales = b[payload: payload + L * n_q * 4].view(torch.float32).view(L, n_q)
             t = sq.tok_start + c * C + torch.arange(n_c, device="cuda")
             page, row = bt[t // P], t % P
@@ -394,7 +449,7 @@ def test_layerwise_with_capped_grid(fmt, cap):
     _sync()
     s = torch.cuda.Stream()
     for l in range(w.num_layers):
-        assert kvm.retrieve_layer(paged, batch, l, fmt=fmt, stream=s, max_workgroups=cap) == [512, 275, 17]
+        assert kvm.retrieve_layer_ex(paged, batch, l, fmt=fmt, stream=s, max_workgroups=cap) == [512, 275, 17]
     torch.cuda.synchronize()
     assert kvm.take_faults() == 0
     before = np.full_like(arr, 0x2A2A)
@@ -494,7 +549,7 @@ def test_consumer_waiting_on_layer_event_sees_the_whole_layer(fmt):
     torch.cuda.synchronize()
     snaps = []
     for l in range(w.num_layers):
-        kvm.retrieve_layer(paged, batch, l, fmt=fmt, stream=copy, event=events[l], max_workgroups=1)
+        kvm.retrieve_layer_ex(paged, batch, l, fmt=fmt, stream=copy, event=events[l], max_workgroups=1)
         compute.wait_event(events[l])
         with torch.cuda.stream(compute):
             snaps.append(pool[l].clone())
@@ -507,14 +562,17 @@ def test_consumer_waiting_on_layer_event_sees_the_whole_layer(fmt):
                    [s.hit_mask for s in w.seqs], copy=False)
 
 
+@pytest.mark.parametrize("form", ["per-layer-calls", "one-call"])
 @pytest.mark.parametrize("fmt", [BF16, FP8, K16V8], ids=["bf16", "fp8", "k16v8"])
-def test_store_waiting_on_producer_event_sees_the_layer(fmt):
+def test_store_waiting_on_producer_event_sees_the_layer(fmt, form):
     # the producer (compute stream) writes layer l of the pool after a GEMM and
     # records its event; the layer store on the copy stream waits on it, so the
-    # chunks must hold the produced values, never the sentinel left before
+    # chunks must hold the produced values, never the sentinel left before.
+    # One store call per layer, or one call for every layer (kv_store_layers,
+    # its waits on the producer's events enqueued by the library)
     w = wl.custom("producer-order", 272, 4, 8, 128, 1024, [(0, 4096), (256, 1300)],
                   outliers=_outliers(fmt))
-    say("case", w.name, fmt)
+    say("case", w.name, fmt, form)
     arr = wl.host_pool(w)
     src = dev_pool_from_host(w, arr)
     pool, paged, batch, cs = setup_device(w, arr, fmt=fmt, fill=0xC3)
@@ -528,8 +586,11 @@ def test_store_waiting_on_producer_event_sees_the_layer(fmt):
             torch.mm(x, x)
             pool[l].copy_(src[l])
             done[l].record(compute)
-        copy.wait_event(done[l])
-        kvm.store_layer(paged, batch, l, fmt=fmt, stream=copy)
+        if form == "per-layer-calls":
+            copy.wait_event(done[l])
+            kvm.store_layer(paged, batch, l, fmt=fmt, stream=copy)
+    if form == "one-call":
+        kvm.store_layers(paged, batch, 0, w.num_layers, fmt=fmt, stream=copy, wait_events=done)
     torch.cuda.synchronize()
     assert kvm.take_faults() == 0
     check_store(w, arr, cs, fmt)
@@ -563,7 +624,7 @@ def test_host_chunks_offload_and_onload(fmt):
     s.wait_stream(torch.cuda.current_stream())       # the fill lands before the retrieve writes
     ev = torch.cuda.Event()
     for l in range(w.num_layers):
-        kvm.retrieve_layer(paged, batch, l, fmt=fmt, stream=s, event=ev, max_workgroups=3)
+        kvm.retrieve_layer_ex(paged, batch, l, fmt=fmt, stream=s, event=ev, max_workgroups=3)
     ev.synchronize()
     assert kvm.take_faults() == 0
     assert np.array_equal(host_from_dev_pool(pool), got)
@@ -660,12 +721,14 @@ def test_cachegen_special_rows():
     exp = np.zeros_like(arr)
     op = oracle_pool(w, exp)
     assert oracle.retrieve_cachegen(op, bt, 0, 40, [1], host_chunks(cs[0]), kb, vb) == 40
-    # NaN results (0 * inf, NaN * 0) may differ in sign between implementations:
-    # compare NaN-ness there, bits elsewhere
-    nan_g = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
-    nan_e = ((exp & 0x7F80) == 0x7F80) & ((exp & 0x7F) != 0)
-    assert np.array_equal(nan_g, nan_e) and nan_e.any()
-    assert np.array_equal(got[~nan_g], exp[~nan_e])
+    # NaN results (0 * inf, NaN * 0) are the bf16 quiet NaN 0x7FC0 on both sides
+    assert (exp == 0x7FC0).any()
+    assert np.array_equal(got, exp), first_diff(got, exp)
+    # the same in pool-address order
+    pool.zero_()
+    assert kvm.retrieve_cachegen(paged, batch, kb, vb, workspace=paged.new_workspace()) == [40]
+    _sync()
+    assert np.array_equal(host_from_dev_pool(pool), exp)
 
 
 # ------------------------------------------------- retrieve in pool-address order
@@ -823,7 +886,7 @@ def test_odd_page_sizes(pc, fmt):
             n = kvm.retrieve_cachegen(paged, batch, kb, vb, workspace=ws)
         elif form == "layers":
             for l in range(w.num_layers):
-                n = kvm.retrieve_layer(paged, batch, l, fmt=fmt)
+                n = kvm.retrieve_layer_ex(paged, batch, l, fmt=fmt)
         else:
             n = kvm.retrieve(paged, batch, fmt=fmt, workspace=ws)
         _sync()
