@@ -127,9 +127,10 @@ def hit_tokens(w):
     return out
 
 
-def timed(stream, fn, reps, warmup=3):
-    """Mean ms of fn() over reps, HIP events on `stream`, after `warmup`
-    untimed calls (short launches otherwise pay for the first calls' setup)."""
+def timed(stream, fn, reps, warmup=3, stat="mean"):
+    """ms of fn() over reps (mean, or median with stat="median"), HIP events
+    on `stream`, after `warmup` untimed calls (short launches otherwise pay
+    for the first calls' setup)."""
     import torch
     for _ in range(warmup):
         fn()
@@ -140,7 +141,14 @@ def timed(stream, fn, reps, warmup=3):
         fn()
         b.record(stream)
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / reps
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return median(ms) if stat == "median" else sum(ms) / reps
+
+
+def median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -321,8 +329,10 @@ def bench_llama8b(args):
     assert kvm.take_faults() == 0
 
     step_s = (t1 - t0) / K
-    store_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    ret_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+    store_each = [e[0].elapsed_time(e[1]) for e in ev]
+    ret_each = [e[2].elapsed_time(e[3]) for e in ev]
+    store_ms = sum(store_each) / K
+    ret_ms = sum(ret_each) / K
     value = (store_bytes + ret_bytes) / step_s / 1e9
     gather_gbps = store_bytes / (store_ms / 1e3) / 1e9
     scatter_gbps = ret_bytes / (ret_ms / 1e3) / 1e9
@@ -378,6 +388,11 @@ def bench_llama8b(args):
         "detail": {
             "store_ms": round(store_ms, 4), "store_GBps": round(gather_gbps, 2),
             "retrieve_ms": round(ret_ms, 4), "retrieve_GBps": round(scatter_gbps, 2),
+            # the median over the K timed steps (after the W warm-up steps)
+            "store_ms_median": round(median(store_each), 4),
+            "store_GBps_median": round(store_bytes / (median(store_each) / 1e3) / 1e9, 2),
+            "retrieve_ms_median": round(median(ret_each), 4),
+            "retrieve_GBps_median": round(ret_bytes / (median(ret_each) / 1e3) / 1e9, 2),
             "retrieve_order": "pool-address (kv_retrieve_chunks_ws)" if ws is not None
                               else "chunk-major (kv_retrieve_chunks)",
             "retrieve_other_order_ms": round(other_ms, 4),
@@ -398,8 +413,11 @@ def bench_llama8b(args):
 def bench_layerwise(args):
     """32 layer-by-layer scatters on a copy stream, each gating a bf16 GEMM
     (10240 x 4096 x 4096) on a compute stream; the copy of layer i+1 runs
-    while layer i computes.  Reported for several caps on the scatter's
-    workgroups (0 = one per tile)."""
+    while layer i computes.  Two ways to enqueue the scatters: one call per
+    layer (kv_retrieve_layer_ex, as an engine calling wait/load per layer
+    does) and one call for all layers (kv_retrieve_layers, the start of the
+    whole load at once), each for several caps on the scatter's workgroups
+    (0 = one per tile)."""
     import numpy as np
     import torch
     import paged_kv_movement_amd as kvm
@@ -431,57 +449,79 @@ def bench_layerwise(args):
         torch.cuda.synchronize()
         return (time.perf_counter() - t) / reps * 1e3
 
+    def consume():
+        for l in range(L):
+            compute.wait_event(events[l])
+            with torch.cuda.stream(compute):
+                torch.mm(x, wgt)
+
     reps = max(3, args.steps)
     t_gemm = wall(gemms, reps)
-    # the same pipeline with nothing hit: each call records its event and
-    # launches nothing, isolating the cost of the per-layer stream dependency
+    # the same pipelines with nothing hit: each layer's event is recorded and
+    # nothing is launched, isolating the cost of the per-layer stream dependency
     empty = kvm.Batch(paged, batch.seqs).set_masks([np.zeros_like(sq.hit_mask) for sq in w.seqs])
 
-    def deps_only():
+    def deps_per_call():
         for l in range(L):
             kvm.retrieve_layer(paged, empty, l, stream=copy, event=events[l])
             compute.wait_event(events[l])
             with torch.cuda.stream(compute):
                 torch.mm(x, wgt)
 
-    t_deps = wall(deps_only, reps)
+    def deps_one_call():
+        kvm.retrieve_layers(paged, empty, 0, L, stream=copy, events=events)
+        consume()
+
+    t_deps = {"per-layer-calls": wall(deps_per_call, reps), "one-call": wall(deps_one_call, reps)}
     variants = []
     # (cap for layer 0, cap for layers 1..L-1): layer 0 has nothing to overlap
     # with, the others run beside the previous layer's GEMM
     for first_cap, cap in ((0, 0), (0, 32), (0, 48), (0, 64), (0, 96), (0, 128), (0, 256), (128, 128)):
-        def caps(l):
-            return first_cap if l == 0 else cap
+        caps = [first_cap] + [cap] * (L - 1)
 
-        def copies():
+        def copies_per_call():
             for l in range(L):
-                kvm.retrieve_layer(paged, batch, l, stream=copy, event=events[l], max_workgroups=caps(l))
+                kvm.retrieve_layer_ex(paged, batch, l, stream=copy, event=events[l], max_workgroups=caps[l])
 
-        def both():
+        def both_per_call():
             for l in range(L):
-                kvm.retrieve_layer(paged, batch, l, stream=copy, event=events[l], max_workgroups=caps(l))
+                kvm.retrieve_layer_ex(paged, batch, l, stream=copy, event=events[l], max_workgroups=caps[l])
                 compute.wait_event(events[l])
                 with torch.cuda.stream(compute):
                     torch.mm(x, wgt)
 
-        t_copy, t_both = wall(copies, reps), wall(both, reps)
-        layer_ms = timed(copy, lambda: kvm.retrieve_layer(paged, batch, 5, stream=copy,
-                                                          max_workgroups=cap), 20)
-        variants.append({
-            "max_workgroups_layer0": first_cap, "max_workgroups": cap,
-            "t_copy_ms": round(t_copy, 3), "t_both_ms": round(t_both, 3),
-            "exposed_copy_ms": round(t_both - t_gemm, 3),
-            "exposed_vs_dependency_only_ms": round(t_both - t_deps, 3),
-            "overlap_efficiency": round((t_gemm + t_copy - t_both) / t_copy, 4),
-            "layer_scatter_ms": round(layer_ms, 4),
-            "layer_scatter_GBps": round(per_layer_bytes / (layer_ms / 1e3) / 1e9, 2),
-        })
-        log(f"layerwise caps {first_cap}/{cap}: {variants[-1]}")
+        def copies_one_call():
+            kvm.retrieve_layers(paged, batch, 0, L, stream=copy, events=events, max_workgroups=caps)
+
+        def both_one_call():
+            kvm.retrieve_layers(paged, batch, 0, L, stream=copy, events=events, max_workgroups=caps)
+            consume()
+
+        for form, copies, both in (("per-layer-calls", copies_per_call, both_per_call),
+                                   ("one-call", copies_one_call, both_one_call)):
+            t_copy, t_both = wall(copies, reps), wall(both, reps)
+            v = {"form": form, "max_workgroups_layer0": first_cap, "max_workgroups": cap,
+                 "t_copy_ms": round(t_copy, 3), "t_both_ms": round(t_both, 3),
+                 "exposed_copy_ms": round(t_both - t_gemm, 3),
+                 "exposed_vs_dependency_only_ms": round(t_both - t_deps[form], 3),
+                 "overlap_efficiency": round((t_gemm + t_copy - t_both) / t_copy, 4)}
+            if form == "one-call":
+                # the 32 scatters back to back on the copy stream, HIP events
+                # around the one call (the GPU, not the host, sets the pace):
+                # median of 20 after 3 warm-ups, per layer
+                lm = timed(copy, lambda: kvm.retrieve_layers(paged, batch, 0, L, stream=copy,
+                                                             max_workgroups=[cap] * L), 20, stat="median") / L
+                v["layer_scatter_ms"] = round(lm, 4)
+                v["layer_scatter_GBps"] = round(per_layer_bytes / (lm / 1e3) / 1e9, 2)
+            variants.append(v)
+            log(f"layerwise caps {first_cap}/{cap} {form}: {v}")
     assert kvm.take_faults() == 0
     best = min(variants, key=lambda v: v["t_both_ms"])
     return {
         "metric": "layerwise onload: copy time hidden behind per-layer GEMMs",
         "workload": "layerwise-8b: 1 seq x 10240 tokens, 32 layers, GEMM 10240x4096x4096 bf16 per layer",
-        "t_gemm_ms": round(t_gemm, 3), "t_dependency_only_ms": round(t_deps, 3),
+        "t_gemm_ms": round(t_gemm, 3),
+        "t_dependency_only_ms": {k: round(v, 3) for k, v in t_deps.items()},
         "best": best, "variants": variants,
         "oracle_beside": oracle_beside(w, pool, kvm.FMT_BF16, n_chunks=40, layer=5),
     }
@@ -490,9 +530,12 @@ def bench_layerwise(args):
 def bench_layerwise_store(args):
     """Prefill-style layerwise store: layer l's KV is gathered on a copy stream
     once layer l's GEMM (10240 x 4096 x 4096 bf16, the producer) has finished,
-    while layer l+1 computes.  Reports the exposed store time for several
-    workgroup caps (layer 0 always at full width; the last layer's store has
-    nothing left to hide behind)."""
+    while layer l+1 computes.  Two ways to enqueue the stores: one call per
+    layer after its GEMM (kv_store_layer), or one call for all layers after
+    the GEMMs are enqueued, the library enqueueing each layer's wait on its
+    GEMM's event (kv_store_layers).  Reports the exposed store time for
+    several workgroup caps (layer 0 always at full width; the last layer's
+    store has nothing left to hide behind)."""
     import torch
     import paged_kv_movement_amd as kvm
     from paged_kv_movement_amd import workloads as wl
@@ -525,26 +568,43 @@ def bench_layerwise_store(args):
     t_gemm = wall(gemms, reps)
     variants = []
     for cap in (0, 64, 128, 256):
-        def stores():
-            for l in range(L):
-                kvm.store_layer(paged, batch, l, stream=copy, max_workgroups=0 if l == 0 else cap)
+        caps = [0] + [cap] * (L - 1)
 
-        def both():
+        def stores_per_call():
+            for l in range(L):
+                kvm.store_layer(paged, batch, l, stream=copy, max_workgroups=caps[l])
+
+        def both_per_call():
             for l in range(L):
                 with torch.cuda.stream(compute):
                     torch.mm(x, wgt)
                     done[l].record(compute)
                 copy.wait_event(done[l])
-                kvm.store_layer(paged, batch, l, stream=copy, max_workgroups=0 if l == 0 else cap)
+                kvm.store_layer(paged, batch, l, stream=copy, max_workgroups=caps[l])
 
-        t_store, t_both = wall(stores, reps), wall(both, reps)
-        layer_ms = timed(copy, lambda: kvm.store_layer(paged, batch, 5, stream=copy, max_workgroups=cap), 20)
-        variants.append({"max_workgroups": cap, "t_store_ms": round(t_store, 3), "t_both_ms": round(t_both, 3),
-                         "exposed_store_ms": round(t_both - t_gemm, 3),
-                         "overlap_efficiency": round((t_gemm + t_store - t_both) / t_store, 4),
-                         "layer_store_ms": round(layer_ms, 4),
-                         "layer_store_GBps": round(per_layer_bytes / (layer_ms / 1e3) / 1e9, 2)})
-        log(f"layerwise store cap {cap}: {variants[-1]}")
+        def stores_one_call():
+            kvm.store_layers(paged, batch, 0, L, stream=copy, max_workgroups=caps)
+
+        def both_one_call():
+            for l in range(L):
+                with torch.cuda.stream(compute):
+                    torch.mm(x, wgt)
+                    done[l].record(compute)
+            kvm.store_layers(paged, batch, 0, L, stream=copy, wait_events=done, max_workgroups=caps)
+
+        for form, stores, both in (("per-layer-calls", stores_per_call, both_per_call),
+                                   ("one-call", stores_one_call, both_one_call)):
+            t_store, t_both = wall(stores, reps), wall(both, reps)
+            v = {"form": form, "max_workgroups": cap, "t_store_ms": round(t_store, 3), "t_both_ms": round(t_both, 3),
+                 "exposed_store_ms": round(t_both - t_gemm, 3),
+                 "overlap_efficiency": round((t_gemm + t_store - t_both) / t_store, 4)}
+            if form == "one-call":
+                lm = timed(copy, lambda: kvm.store_layers(paged, batch, 0, L, stream=copy,
+                                                          max_workgroups=[cap] * L), 20, stat="median") / L
+                v["layer_store_ms"] = round(lm, 4)
+                v["layer_store_GBps"] = round(per_layer_bytes / (lm / 1e3) / 1e9, 2)
+            variants.append(v)
+            log(f"layerwise store cap {cap} {form}: {v}")
     assert kvm.take_faults() == 0
     return {"metric": "layerwise store: gather time hidden behind per-layer GEMMs",
             "workload": "layerwise-store-8b: 1 seq x 10240 tokens, 32 layers, GEMM 10240x4096x4096 bf16 per layer",
@@ -716,11 +776,11 @@ def layerwise_from_host(args, copy, compute):
     for cap in (16, 32, 64, 0):
         def copies():
             for l in range(L):
-                kvm.retrieve_layer(paged, batch, l, stream=copy, max_workgroups=cap)
+                kvm.retrieve_layer_ex(paged, batch, l, stream=copy, max_workgroups=cap)
 
         def both():
             for l in range(L):
-                kvm.retrieve_layer(paged, batch, l, stream=copy, event=evs[l], max_workgroups=cap)
+                kvm.retrieve_layer_ex(paged, batch, l, stream=copy, event=evs[l], max_workgroups=cap)
                 compute.wait_event(evs[l])
                 with torch.cuda.stream(compute):
                     torch.mm(x, wgt)

@@ -148,11 +148,16 @@ typedef struct {
 
 /* Exact bytes of one chunk holding n_tokens tokens in format fmt ([serde]
  * "4.2": deterministic, from the layout alone); 0 on a malformed argument. */
-size_t kv_chunk_bytes(const kv_paged* paged, int64_t n_tokens, int fmt);
+size_t kv_chunk_bytes(const kv_paged* paged, int64_t n_tokens, kv_fmt fmt);
 
 /* Chunks covering [tok_start, tok_end): ceil((tok_end - tok_start) / C); the
  * last one holds the remainder ([walk] "store()").  -1 on a malformed argument. */
 int64_t kv_num_chunks(const kv_paged* paged, int64_t tok_start, int64_t tok_end);
+
+/* Tokens of chunk c of [tok_start, tok_end): C, or the remainder for the
+ * last chunk ([walk] "store()").  -1 on a malformed argument or a c outside
+ * [0, kv_num_chunks).  With kv_chunk_bytes it sizes each chunk buffer. */
+int64_t kv_chunk_tokens(const kv_paged* paged, int64_t tok_start, int64_t tok_end, int64_t c);
 
 /* Store: gather every chunk of every sequence, all layers, K and V, into the
  * sequences' chunk buffers, in one batched launch ([paper] configurable chunk
@@ -160,7 +165,7 @@ int64_t kv_num_chunks(const kv_paged* paged, int64_t tok_start, int64_t tok_end)
  * ([serde] "7.1").  The pool is only read.  Sequences with an empty range are
  * skipped.  To store a shorter prefix (e.g. after a failed allocation, [walk]
  * "store()"), pass a smaller tok_end. */
-int kv_store_chunks(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int fmt,
+int kv_store_chunks(const kv_paged* paged, const kv_seq* seqs, int n_seqs, kv_fmt fmt,
                     hipStream_t stream);
 
 /* Layerwise store ([paper] layerwise pipeline; Table 2 start_store_kv /
@@ -171,8 +176,22 @@ int kv_store_chunks(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int f
  * that are already stored are skipped by giving a later tok_start or an
  * earlier tok_end.  max_workgroups as for kv_retrieve_layer (bf16 only; the
  * fp8 store runs one workgroup per (chunk, K/V) group and ignores it). */
-int kv_store_layer(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int fmt, int32_t layer,
+int kv_store_layer(const kv_paged* paged, const kv_seq* seqs, int n_seqs, kv_fmt fmt, int32_t layer,
                    int32_t max_workgroups, hipStream_t stream, hipEvent_t layer_done);
+
+/* Several layers of a store in one call: for k = 0 .. layer_end-layer_begin-1
+ * and layer l = layer_begin + k, on stream: wait for wait_before[k] (if the
+ * array and the entry are not NULL; an event the caller recorded after its
+ * producer of layer l, e.g. that layer's compute), gather layer l as
+ * kv_store_layer does with max_workgroups[k] (NULL: 0 for every layer), then
+ * record layer_done[k] (if the array and the entry are not NULL).  The host
+ * arguments are checked and the launch plan made once for all layers, so a
+ * caller that has already enqueued its producers hands the whole pipeline
+ * over in one call.  HOST arrays of layer_end - layer_begin entries; layers
+ * [layer_begin, layer_end) must be a non-empty range inside [0, L). */
+int kv_store_layers(const kv_paged* paged, const kv_seq* seqs, int n_seqs, kv_fmt fmt, int32_t layer_begin,
+                    int32_t layer_end, const int32_t* max_workgroups, hipStream_t stream,
+                    const hipEvent_t* wait_before, const hipEvent_t* layer_done);
 
 /* Retrieve: for sequence i, n_hit = index of the first 0 in hit_mask[i][0 ..
  * n_chunks) (n_chunks if none); scatter chunks [0, n_hit) back into the
@@ -186,7 +205,7 @@ int kv_store_layer(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int fm
  * (an entry may be NULL when the range is empty).  Nothing is launched when no chunk hits ([walk] "性能细节").
  * The page ids written by one call must be distinct. */
 int kv_retrieve_chunks(const kv_paged* paged, const kv_seq* seqs,
-                       const uint8_t* const* hit_mask, int n_seqs, int fmt,
+                       const uint8_t* const* hit_mask, int n_seqs, kv_fmt fmt,
                        int64_t* out_tokens, hipStream_t stream);
 
 /* Retrieve in pool-address order: the same operation and result as
@@ -206,7 +225,7 @@ int kv_retrieve_chunks(const kv_paged* paged, const kv_seq* seqs,
  * workspace must be ordered on one stream. */
 size_t kv_retrieve_workspace_bytes(const kv_paged* paged);   /* 0 on a malformed pool */
 int kv_retrieve_chunks_ws(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
-                          int fmt, int64_t* out_tokens, void* workspace, size_t workspace_bytes,
+                          kv_fmt fmt, int64_t* out_tokens, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
 /* Layerwise retrieve ([paper] layerwise pipeline; Table 2 start_load_kv /
@@ -214,20 +233,41 @@ int kv_retrieve_chunks_ws(const kv_paged* paged, const kv_seq* seqs, const uint8
  * on copy_stream, then records layer_done (if not NULL) on copy_stream -- also
  * when nothing hits, so a stream or host waiting on it never hangs.  Calling
  * it for layers 0 .. L-1 leaves the pool as one kv_retrieve_chunks call does.
- * max_workgroups = 0 launches one workgroup per tile (one-wave workgroups:
- * 2 KiB tiles for bf16, 4 KiB of output for the fp8 retrieve; fastest when
- * the GPU is otherwise idle); a positive value caps the grid at that many
- * 256-thread workgroups, each moving a contiguous run of 8 KiB tiles, so the
- * scatter occupies few wave slots while compute on another stream runs
- * beside it (page-unit kernels: bf16 and the fp8 retrieve).  From host chunks the scatter is bound by PCIe, and
- * a cap of 32 workgroups already moves at the link's rate.  Overlap needs
- * copy_stream and the compute stream on different hardware queues: HIP
- * spreads a process's streams over a few queues (GPU_MAX_HW_QUEUES, 4 by
- * default), and two streams that share a queue run in order. */
-int kv_retrieve_layer(const kv_paged* paged, const kv_seq* seqs,
-                      const uint8_t* const* hit_mask, int n_seqs, int fmt, int32_t layer,
-                      int64_t* out_tokens, int32_t max_workgroups, hipStream_t copy_stream,
-                      hipEvent_t layer_done);
+ * The scatter takes one workgroup per tile (one-wave workgroups: 2 KiB tiles
+ * for bf16, 4 KiB of output for the fp8 retrieve).  Overlap needs copy_stream
+ * and the compute stream on different hardware queues: HIP spreads a
+ * process's streams over a few queues (GPU_MAX_HW_QUEUES, 4 by default), and
+ * two streams that share a queue run in order. */
+int kv_retrieve_layer(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
+                      kv_fmt fmt, int32_t layer, hipStream_t copy_stream, hipEvent_t layer_done);
+
+/* kv_retrieve_layer with two more arguments:
+ *   out_tokens      HOST int64[n_seqs] or NULL: as for kv_retrieve_chunks;
+ *   max_workgroups  0: one workgroup per tile (as kv_retrieve_layer, fastest
+ *                   when the GPU is otherwise idle); > 0 caps the grid at that
+ *                   many 256-thread workgroups, each moving a contiguous run of
+ *                   8 KiB tiles, so the scatter occupies few wave slots while
+ *                   compute on another stream runs beside it (page-unit
+ *                   kernels: bf16 and the fp8 retrieve).  From host chunks
+ *                   the scatter is bound by PCIe, and a cap of 32 workgroups
+ *                   already moves at the link's rate. */
+int kv_retrieve_layer_ex(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
+                         kv_fmt fmt, int32_t layer, int64_t* out_tokens, int32_t max_workgroups,
+                         hipStream_t copy_stream, hipEvent_t layer_done);
+
+/* Several layers of a retrieve in one call ([paper] Table 2: start_load_kv
+ * starts the load of every layer; wait_load_kv(layer) is the caller's wait on
+ * layer_done[k]): for k = 0 .. layer_end-layer_begin-1, the scatter of layer
+ * layer_begin + k as kv_retrieve_layer_ex does with max_workgroups[k] (HOST
+ * array, NULL: 0 for every layer), then a record of layer_done[k] (HOST array
+ * of events, NULL or NULL entries: none), all on copy_stream in layer order.
+ * The hit mask is read and the plan made once; out_tokens as for
+ * kv_retrieve_chunks.  Layers [layer_begin, layer_end) must be a non-empty
+ * range inside [0, L).  A compute stream that waits on layer_done[k] before
+ * layer k's work overlaps every later layer's load with that work. */
+int kv_retrieve_layers(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
+                       kv_fmt fmt, int32_t layer_begin, int32_t layer_end, const int32_t* max_workgroups,
+                       int64_t* out_tokens, hipStream_t copy_stream, const hipEvent_t* layer_done);
 
 /* CacheGen quantiser ([cachegen] section "2. 量化"): store gathers and
  * quantises every chunk, K and V of every layer, in format

@@ -24,8 +24,9 @@ import ctypes
 import os
 
 __all__ = ["FMT_BF16", "FMT_FP8", "FMT_FP8_E5M2", "FMT_K16_V8", "FMT_CACHEGEN", "KvError", "Paged", "Seq", "Batch",
-           "store", "store_layer", "store_cachegen", "retrieve_cachegen",
-           "retrieve", "retrieve_layer", "take_faults", "copy_bytes", "library_path", "load"]
+           "store", "store_layer", "store_layers", "store_cachegen", "retrieve_cachegen",
+           "retrieve", "retrieve_layer", "retrieve_layer_ex", "retrieve_layers", "take_faults", "copy_bytes",
+           "library_path", "load"]
 
 FMT_BF16 = 0          # K and V bf16, copied bit for bit
 FMT_FP8 = 1           # K and V e4m3 + one float32 scale per (layer, K/V)
@@ -89,10 +90,14 @@ def load():
     sig = {
         "kv_chunk_bytes": (ctypes.c_size_t, [P, i64, ctypes.c_int]),
         "kv_num_chunks": (i64, [P, i64, i64]),
+        "kv_chunk_tokens": (i64, [P, i64, i64, i64]),
         "kv_store_chunks": (ctypes.c_int, [P, S, ctypes.c_int, ctypes.c_int, vp]),
         "kv_store_layer": (ctypes.c_int, [P, S, ctypes.c_int, ctypes.c_int, i32, i32, vp, vp]),
+        "kv_store_layers": (ctypes.c_int, [P, S, ctypes.c_int, ctypes.c_int, i32, i32, vp, vp, vp, vp]),
         "kv_retrieve_chunks": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, vp, vp]),
-        "kv_retrieve_layer": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, i32, vp, i32, vp, vp]),
+        "kv_retrieve_layer": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, i32, vp, vp]),
+        "kv_retrieve_layer_ex": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, i32, vp, i32, vp, vp]),
+        "kv_retrieve_layers": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, i32, i32, vp, vp, vp, vp]),
         "kv_store_chunks_cachegen": (ctypes.c_int, [P, S, ctypes.c_int, vp, vp, vp]),
         "kv_retrieve_workspace_bytes": (ctypes.c_size_t, [P]),
         "kv_retrieve_chunks_ws": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]),
@@ -126,6 +131,29 @@ def _stream_handle(stream) -> int | None:
         stream = torch.cuda.current_stream()
     h = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
     return h or None
+
+
+def _used_on(stream, tensors, seen=None) -> None:
+    """Tell torch's caching allocator that kernels on ``stream`` read these
+    tensors (``record_stream``): the binding makes some device tensors itself
+    (address arrays) on the current stream, and a caller may pass a workspace
+    made inline; without this, freeing them while the side stream still runs
+    could hand their memory to new work too early.  With ``seen`` (a set kept
+    by the owner of the tensors, which keeps them alive) each (tensor, stream)
+    is recorded once.  Nothing is done for stream=None (the current stream)
+    or a raw stream handle (the caller then keeps the tensors alive)."""
+    if stream is None or not hasattr(stream, "cuda_stream"):
+        return
+    for t in tensors:
+        if t is None or not getattr(t, "is_cuda", False):
+            continue
+        if seen is None:
+            t.record_stream(stream)
+            continue
+        key = (id(t), stream.cuda_stream)
+        if key not in seen:
+            t.record_stream(stream)
+            seen.add(key)
 
 
 class Paged:
@@ -196,6 +224,13 @@ class Paged:
             _check(KV_EINVAL)
         return int(n)
 
+    def chunk_tokens(self, tok_start: int, tok_end: int, c: int) -> int:
+        """Tokens of chunk c of [tok_start, tok_end) (kv_chunk_tokens)."""
+        n = load().kv_chunk_tokens(ctypes.byref(self.c), tok_start, tok_end, c)
+        if n < 0:
+            _check(KV_EINVAL)
+        return int(n)
+
 
 class Seq:
     """One sequence's job: a device int32 block table, a token range and its
@@ -241,13 +276,17 @@ class Batch:
 
     def __init__(self, paged: Paged, seqs):
         self.seqs = list(seqs)
-        self.chunk_size = paged.chunk_size
+        self.paged = paged
         n = len(self.seqs)
         self.arr = (_KvSeq * max(1, n))(*[s.c() for s in self.seqs])
         self.n = n
         self._mask_bufs = None
         self._mask_ptrs = None
         self.out = (ctypes.c_int64 * max(1, n))()
+        self._checked_fmts = set()      # formats whose chunk tensors were sized against the library
+        self._on_streams = set()        # (tensor, stream) pairs already given to record_stream
+        # device tensors the kernels read besides the caller's own
+        self._dev_tensors = [paged.k_addrs, paged.v_addrs] + [s.chunk_addrs for s in self.seqs]
 
     def set_masks(self, masks):
         """Host hit masks, one uint8 flag per chunk per sequence."""
@@ -256,7 +295,7 @@ class Batch:
         for i, (sq, m) in enumerate(zip(self.seqs, masks)):
             b = bytes(int(x) & 0xFF for x in (m.tolist() if hasattr(m, "tolist") else m))
             # the library reads one flag for every chunk of the sequence
-            n_chunks = -(-(sq.tok_end - sq.tok_start) // self.chunk_size)
+            n_chunks = self.paged.num_chunks(sq.tok_start, sq.tok_end)
             _need(len(b) >= n_chunks, f"sequence {i}: hit mask has {len(b)} flags for {n_chunks} chunks")
             bufs.append(ctypes.create_string_buffer(b, max(1, len(b))))
         self._mask_bufs = bufs
@@ -264,14 +303,48 @@ class Batch:
             *[ctypes.cast(b, ctypes.c_void_p).value for b in bufs])
         return self
 
+    def check_chunks(self, fmt: int) -> "Batch":
+        """For sequences whose chunks were given as tensors: one tensor per
+        chunk of the range, each at least kv_chunk_bytes(tokens of the chunk,
+        fmt) bytes, sizes from the library (kv_num_chunks, kv_chunk_tokens,
+        kv_chunk_bytes).  The kernels write every chunk buffer up to that size
+        and cannot see a buffer's end, so a short list or a small tensor is
+        refused here, before anything runs.  Chunks given as an address
+        tensor cannot be checked.  Done once per format."""
+        if fmt in self._checked_fmts:
+            return self
+        p = self.paged
+        for i, sq in enumerate(self.seqs):
+            if sq._chunks is None:
+                continue
+            n = p.num_chunks(sq.tok_start, sq.tok_end)
+            _need(len(sq._chunks) >= n, f"sequence {i}: {len(sq._chunks)} chunk tensors for {n} chunks")
+            for c in range(n):
+                need = p.chunk_bytes(p.chunk_tokens(sq.tok_start, sq.tok_end, c), fmt)
+                have = sq._chunks[c].numel() * sq._chunks[c].element_size()
+                _need(have >= need, f"sequence {i}, chunk {c}: {have} bytes, format {fmt} needs {need}")
+        self._checked_fmts.add(fmt)
+        return self
 
-def _batch(paged, seqs) -> Batch:
-    return seqs if isinstance(seqs, Batch) else Batch(paged, seqs)
+    def used_on(self, stream, *extra) -> None:
+        """record_stream for the Batch's own device tensors (once per stream)
+        and for ``extra`` tensors of this call (every time)."""
+        _used_on(stream, self._dev_tensors, self._on_streams)
+        _used_on(stream, extra)
+
+
+def _batch(paged, seqs, fmt, stream, *extra) -> Batch:
+    """The Batch for a call: chunk tensors sized for fmt, and the device
+    tensors the call reads marked as used on stream."""
+    b = seqs if isinstance(seqs, Batch) else Batch(paged, seqs)
+    b.check_chunks(fmt)
+    b.used_on(stream, *extra)
+    return b
 
 
 def store(paged: Paged, seqs, fmt: int = FMT_BF16, stream=None) -> None:
     """Gather every chunk of every sequence (kv_store_chunks)."""
-    b = _batch(paged, seqs)
+    b = _batch(paged, seqs, fmt, stream)
     _check(load().kv_store_chunks(ctypes.byref(paged.c), b.arr, b.n, fmt, _stream_handle(stream)))
 
 
@@ -288,9 +361,41 @@ def store_layer(paged: Paged, seqs, layer: int, fmt: int = FMT_BF16, stream=None
                 max_workgroups: int = 0) -> None:
     """Gather one layer of every chunk on ``stream``, then record ``event``
     (a torch.cuda.Event) on it (kv_store_layer)."""
-    b = _batch(paged, seqs)
+    b = _batch(paged, seqs, fmt, stream)
     _check(load().kv_store_layer(ctypes.byref(paged.c), b.arr, b.n, fmt, layer, max_workgroups,
                                  _stream_handle(stream), _event_handle(event, stream)))
+
+
+def _layer_arrays(n, max_workgroups, events, stream):
+    """Host arrays of a layer-range call: caps (or None) and event handles (or None)."""
+    caps = None
+    if max_workgroups is not None:
+        caps = [int(m) for m in max_workgroups]
+        _need(len(caps) == n, f"need {n} workgroup caps, got {len(caps)}")
+        caps = (ctypes.c_int32 * n)(*caps)
+    evs = None
+    if events is not None:
+        _need(len(events) == n, f"need {n} events, got {len(events)}")
+        evs = (ctypes.c_void_p * n)(*[_event_handle(e, stream) for e in events])
+    return caps, evs
+
+
+def store_layers(paged: Paged, seqs, layer_begin: int, layer_end: int, fmt: int = FMT_BF16, stream=None,
+                 wait_events=None, events=None, max_workgroups=None) -> None:
+    """Gather layers [layer_begin, layer_end) on ``stream`` in one call
+    (kv_store_layers): before layer l, wait for ``wait_events[l - layer_begin]``
+    (torch.cuda.Event, already recorded by the producer); after it, record
+    ``events[l - layer_begin]``.  ``max_workgroups``: one cap per layer."""
+    b = _batch(paged, seqs, fmt, stream)
+    n = layer_end - layer_begin
+    caps, evs = _layer_arrays(n, max_workgroups, events, stream)
+    waits = None
+    if wait_events is not None:
+        _need(len(wait_events) == n, f"need {n} wait events, got {len(wait_events)}")
+        _need(all(e.cuda_event for e in wait_events), "wait events must have been recorded")
+        waits = (ctypes.c_void_p * n)(*[e.cuda_event for e in wait_events])
+    _check(load().kv_store_layers(ctypes.byref(paged.c), b.arr, b.n, fmt, layer_begin, layer_end, caps,
+                                  _stream_handle(stream), waits, evs))
 
 
 def _workspace(workspace):
@@ -313,7 +418,7 @@ def _bins(bins, n):
 def store_cachegen(paged: Paged, seqs, key_bins, value_bins, stream=None) -> None:
     """CacheGen quantiser: gather + quantise every chunk (kv_store_chunks_cachegen).
     key_bins / value_bins: one bin count per layer, each in [4, 129]."""
-    b = _batch(paged, seqs)
+    b = _batch(paged, seqs, FMT_CACHEGEN, stream)
     L = paged.c.num_layers
     _check(load().kv_store_chunks_cachegen(ctypes.byref(paged.c), b.arr, b.n, _bins(key_bins, L),
                                            _bins(value_bins, L), _stream_handle(stream)))
@@ -323,7 +428,7 @@ def retrieve_cachegen(paged: Paged, seqs, key_bins, value_bins, masks=None, stre
     """Dequantise + scatter the leading hit chunks (kv_retrieve_chunks_cachegen);
     in pool-address order when a ``workspace`` (as for retrieve) is given.
     Returns the tokens made available per sequence."""
-    b = _batch(paged, seqs)
+    b = _batch(paged, seqs, FMT_CACHEGEN, stream, workspace)
     if masks is not None:
         b.set_masks(masks)
     _need(b._mask_ptrs is not None, "hit masks are required")
@@ -341,7 +446,7 @@ def retrieve(paged: Paged, seqs, masks=None, fmt: int = FMT_BF16, stream=None, w
     paged.retrieve_workspace_bytes()) the bf16 scatter runs in pool-address
     order (kv_retrieve_chunks_ws).  Returns the tokens made available per
     sequence."""
-    b = _batch(paged, seqs)
+    b = _batch(paged, seqs, fmt, stream, workspace)
     if masks is not None:
         b.set_masks(masks)
     _need(b._mask_ptrs is not None, "hit masks are required")
@@ -355,19 +460,45 @@ def retrieve(paged: Paged, seqs, masks=None, fmt: int = FMT_BF16, stream=None, w
     return [int(b.out[i]) for i in range(b.n)]
 
 
-def retrieve_layer(paged: Paged, seqs, layer: int, masks=None, fmt: int = FMT_BF16,
-                   stream=None, event=None, max_workgroups: int = 0) -> list:
-    """Scatter one layer of the leading hit chunks on ``stream``, then record
-    ``event`` (a torch.cuda.Event) on it (kv_retrieve_layer).  A positive
-    ``max_workgroups`` caps the grid so compute on another stream keeps most
-    of the GPU."""
-    b = _batch(paged, seqs)
+def _masked(paged, seqs, masks, fmt, stream) -> Batch:
+    b = _batch(paged, seqs, fmt, stream)
     if masks is not None:
         b.set_masks(masks)
     _need(b._mask_ptrs is not None, "hit masks are required")
+    return b
+
+
+def retrieve_layer(paged: Paged, seqs, layer: int, masks=None, fmt: int = FMT_BF16, stream=None,
+                   event=None) -> None:
+    """Scatter one layer of the leading hit chunks on ``stream``, then record
+    ``event`` (a torch.cuda.Event) on it (kv_retrieve_layer)."""
+    b = _masked(paged, seqs, masks, fmt, stream)
     _check(load().kv_retrieve_layer(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n, fmt, layer,
-                                    b.out, max_workgroups, _stream_handle(stream),
-                                    _event_handle(event, stream)))
+                                    _stream_handle(stream), _event_handle(event, stream)))
+
+
+def retrieve_layer_ex(paged: Paged, seqs, layer: int, masks=None, fmt: int = FMT_BF16, stream=None,
+                      event=None, max_workgroups: int = 0) -> list:
+    """retrieve_layer with a workgroup cap (kv_retrieve_layer_ex): a positive
+    ``max_workgroups`` caps the grid so compute on another stream keeps most
+    of the GPU.  Returns the tokens made available per sequence."""
+    b = _masked(paged, seqs, masks, fmt, stream)
+    _check(load().kv_retrieve_layer_ex(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n, fmt, layer,
+                                       b.out, max_workgroups, _stream_handle(stream),
+                                       _event_handle(event, stream)))
+    return [int(b.out[i]) for i in range(b.n)]
+
+
+def retrieve_layers(paged: Paged, seqs, layer_begin: int, layer_end: int, masks=None, fmt: int = FMT_BF16,
+                    stream=None, events=None, max_workgroups=None) -> list:
+    """Scatter layers [layer_begin, layer_end) of the leading hit chunks on
+    ``stream`` in one call, recording ``events[l - layer_begin]`` after layer
+    l (kv_retrieve_layers).  ``max_workgroups``: one cap per layer, or None.
+    Returns the tokens made available per sequence."""
+    b = _masked(paged, seqs, masks, fmt, stream)
+    caps, evs = _layer_arrays(layer_end - layer_begin, max_workgroups, events, stream)
+    _check(load().kv_retrieve_layers(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n, fmt, layer_begin,
+                                     layer_end, caps, b.out, _stream_handle(stream), evs))
     return [int(b.out[i]) for i in range(b.n)]
 
 

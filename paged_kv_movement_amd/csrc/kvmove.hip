@@ -537,12 +537,89 @@ int cachegen_setup(const kv_paged* p, const int32_t* key_bins, const int32_t* va
 
 constexpr Layout kCgLayout = {1, 1, 0};     // symbol sections addressed as 1-byte parts
 
+int check_layers(const kv_paged* p, int32_t layer_begin, int32_t layer_end, const int32_t* max_workgroups)
+{
+    if (layer_begin < 0 || layer_end > p->num_layers || layer_begin >= layer_end)
+        return fail(KV_EINVAL, "layers [%d, %d) not a non-empty range inside [0, %d)", layer_begin, layer_end,
+                    p->num_layers);
+    if (max_workgroups != nullptr)
+        for (int32_t k = 0; k < layer_end - layer_begin; ++k)
+            if (max_workgroups[k] < 0) return fail(KV_EINVAL, "max_workgroups[%d] < 0", k);
+    return KV_OK;
+}
+
+int record(hipEvent_t ev, hipStream_t stream)
+{
+    if (ev == nullptr) return KV_OK;
+    const hipError_t e = hipEventRecord(ev, stream);
+    if (e != hipSuccess) return fail(KV_EHIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+    return KV_OK;
+}
+
+// Layers [layer_begin, layer_end) of a retrieve, one scatter launch each on
+// copy_stream (max_workgroups[k] caps layer_begin + k's grid; NULL: no cap),
+// each followed by a record of layer_done[k] -- also when nothing hits.  The
+// hit plan is made once for all of them.  Host arguments are checked before
+// anything is enqueued.
+int retrieve_layers(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs, int fmt,
+                    int32_t layer_begin, int32_t layer_end, const int32_t* max_workgroups, int64_t* out_tokens,
+                    hipStream_t copy_stream, const hipEvent_t* layer_done)
+{
+    int rc = check_paged(paged);
+    if (rc == KV_OK) rc = check_fmt(fmt);
+    if (rc == KV_OK) rc = check_seqs(paged, seqs, n_seqs);
+    if (rc == KV_OK) rc = check_layers(paged, layer_begin, layer_end, max_workgroups);
+    if (rc != KV_OK) return rc;
+    int64_t small[64];
+    int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
+    rc = hit_tokens(paged, seqs, hit_mask, n_seqs, n_tok);
+    const Plan full = scatter_plan(fmt, false, false), capped = scatter_plan(fmt, true, false);
+    for (int32_t l = layer_begin; l < layer_end && rc == KV_OK; ++l) {
+        const int32_t cap = max_workgroups != nullptr ? max_workgroups[l - layer_begin] : 0;
+        rc = run_plan(cap > 0 ? capped : full, fmt, paged, seqs, n_tok, n_seqs, l, 1, copy_stream, cap);
+        if (rc == KV_OK && layer_done != nullptr) rc = record(layer_done[l - layer_begin], copy_stream);
+    }
+    if (rc == KV_OK && out_tokens != nullptr)
+        for (int i = 0; i < n_seqs; ++i) out_tokens[i] = n_tok[i];
+    if (n_tok != small) delete[] n_tok;
+    return rc == KV_OK ? ok() : rc;
+}
+
+// Layers [layer_begin, layer_end) of a store, one gather launch each on
+// stream: first a wait on wait_before[k] (if given), then the launch, then a
+// record of layer_done[k] (if given).
+int store_layers(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int fmt, int32_t layer_begin,
+                 int32_t layer_end, const int32_t* max_workgroups, hipStream_t stream, const hipEvent_t* wait_before,
+                 const hipEvent_t* layer_done)
+{
+    int rc = check_paged(paged);
+    if (rc == KV_OK) rc = check_fmt(fmt);
+    if (rc == KV_OK) rc = check_seqs(paged, seqs, n_seqs);
+    if (rc == KV_OK) rc = check_layers(paged, layer_begin, layer_end, max_workgroups);
+    if (rc != KV_OK) return rc;
+    int64_t small[64];
+    int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
+    for (int i = 0; i < n_seqs; ++i) n_tok[i] = seqs[i].tok_end - seqs[i].tok_start;
+    const Plan full = gather_plan(paged, fmt, false), capped = gather_plan(paged, fmt, true);
+    for (int32_t l = layer_begin; l < layer_end && rc == KV_OK; ++l) {
+        const int32_t cap = max_workgroups != nullptr ? max_workgroups[l - layer_begin] : 0;
+        if (wait_before != nullptr && wait_before[l - layer_begin] != nullptr) {
+            const hipError_t e = hipStreamWaitEvent(stream, wait_before[l - layer_begin], 0);
+            if (e != hipSuccess) rc = fail(KV_EHIP, "hipStreamWaitEvent failed: %s", hipGetErrorString(e));
+        }
+        if (rc == KV_OK) rc = run_plan(cap > 0 ? capped : full, fmt, paged, seqs, n_tok, n_seqs, l, 1, stream, cap);
+        if (rc == KV_OK && layer_done != nullptr) rc = record(layer_done[l - layer_begin], stream);
+    }
+    if (n_tok != small) delete[] n_tok;
+    return rc == KV_OK ? ok() : rc;
+}
+
 
 }  // namespace
 
 extern "C" {
 
-size_t kv_chunk_bytes(const kv_paged* paged, int64_t n_tokens, int fmt)
+size_t kv_chunk_bytes(const kv_paged* paged, int64_t n_tokens, kv_fmt fmt)
 {
     if (check_paged(paged) != KV_OK) return 0;
     if (n_tokens < 0) {
@@ -569,7 +646,7 @@ int64_t kv_num_chunks(const kv_paged* paged, int64_t tok_start, int64_t tok_end)
     return ceil_div(tok_end - tok_start, paged->chunk_size);
 }
 
-int kv_store_chunks(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int fmt, hipStream_t stream)
+int kv_store_chunks(const kv_paged* paged, const kv_seq* seqs, int n_seqs, kv_fmt fmt, hipStream_t stream)
 {
     int rc = check_paged(paged);
     if (rc == KV_OK) rc = check_fmt(fmt);
@@ -583,32 +660,14 @@ int kv_store_chunks(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int f
     return rc == KV_OK ? ok() : rc;
 }
 
-int kv_store_layer(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int fmt, int32_t layer,
+int kv_store_layer(const kv_paged* paged, const kv_seq* seqs, int n_seqs, kv_fmt fmt, int32_t layer,
                    int32_t max_workgroups, hipStream_t stream, hipEvent_t layer_done)
 {
-    int rc = check_paged(paged);
-    if (rc == KV_OK) rc = check_fmt(fmt);
-    if (rc == KV_OK) rc = check_seqs(paged, seqs, n_seqs);
-    if (rc != KV_OK) return rc;
-    if (layer < 0 || layer >= paged->num_layers)
-        return fail(KV_EINVAL, "layer %d outside [0, %d)", layer, paged->num_layers);
-    if (max_workgroups < 0) return fail(KV_EINVAL, "max_workgroups < 0");
-    int64_t small[64];
-    int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
-    for (int i = 0; i < n_seqs; ++i) n_tok[i] = seqs[i].tok_end - seqs[i].tok_start;
-    rc = run_plan(gather_plan(paged, fmt, max_workgroups > 0), fmt, paged, seqs, n_tok, n_seqs, layer, 1, stream,
-                  max_workgroups);
-    if (n_tok != small) delete[] n_tok;
-    if (rc != KV_OK) return rc;
-    if (layer_done != nullptr) {
-        hipError_t e = hipEventRecord(layer_done, stream);
-        if (e != hipSuccess) return fail(KV_EHIP, "hipEventRecord failed: %s", hipGetErrorString(e));
-    }
-    return ok();
+    return store_layers(paged, seqs, n_seqs, fmt, layer, layer + 1, &max_workgroups, stream, nullptr, &layer_done);
 }
 
 int kv_retrieve_chunks(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask,
-                       int n_seqs, int fmt, int64_t* out_tokens, hipStream_t stream)
+                       int n_seqs, kv_fmt fmt, int64_t* out_tokens, hipStream_t stream)
 {
     int rc = check_paged(paged);
     if (rc == KV_OK) rc = check_fmt(fmt);
@@ -629,7 +688,7 @@ size_t kv_retrieve_workspace_bytes(const kv_paged* paged)
 }
 
 int kv_retrieve_chunks_ws(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
-                          int fmt, int64_t* out_tokens, void* workspace, size_t workspace_bytes,
+                          kv_fmt fmt, int64_t* out_tokens, void* workspace, size_t workspace_bytes,
                           hipStream_t stream)
 {
     int rc = check_paged(paged);
@@ -645,24 +704,48 @@ int kv_retrieve_chunks_ws(const kv_paged* paged, const kv_seq* seqs, const uint8
     return rc == KV_OK ? ok() : rc;
 }
 
-int kv_retrieve_layer(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask,
-                      int n_seqs, int fmt, int32_t layer, int64_t* out_tokens, int32_t max_workgroups,
-                      hipStream_t copy_stream, hipEvent_t layer_done)
+int kv_retrieve_layer_ex(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask,
+                         int n_seqs, kv_fmt fmt, int32_t layer, int64_t* out_tokens, int32_t max_workgroups,
+                         hipStream_t copy_stream, hipEvent_t layer_done)
 {
-    int rc = check_paged(paged);
-    if (rc == KV_OK) rc = check_fmt(fmt);
-    if (rc == KV_OK) rc = check_seqs(paged, seqs, n_seqs);
-    if (rc != KV_OK) return rc;
-    if (layer < 0 || layer >= paged->num_layers)
-        return fail(KV_EINVAL, "layer %d outside [0, %d)", layer, paged->num_layers);
-    if (max_workgroups < 0) return fail(KV_EINVAL, "max_workgroups < 0");
-    rc = retrieve(paged, seqs, hit_mask, n_seqs, fmt, layer, 1, out_tokens, copy_stream, max_workgroups);
-    if (rc != KV_OK) return rc;
-    if (layer_done != nullptr) {
-        hipError_t e = hipEventRecord(layer_done, copy_stream);
-        if (e != hipSuccess) return fail(KV_EHIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+    return retrieve_layers(paged, seqs, hit_mask, n_seqs, fmt, layer, layer + 1, &max_workgroups, out_tokens,
+                           copy_stream, &layer_done);
+}
+
+int kv_retrieve_layer(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
+                      kv_fmt fmt, int32_t layer, hipStream_t copy_stream, hipEvent_t layer_done)
+{
+    return retrieve_layers(paged, seqs, hit_mask, n_seqs, fmt, layer, layer + 1, nullptr, nullptr, copy_stream,
+                           &layer_done);
+}
+
+int kv_retrieve_layers(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
+                       kv_fmt fmt, int32_t layer_begin, int32_t layer_end, const int32_t* max_workgroups,
+                       int64_t* out_tokens, hipStream_t copy_stream, const hipEvent_t* layer_done)
+{
+    return retrieve_layers(paged, seqs, hit_mask, n_seqs, fmt, layer_begin, layer_end, max_workgroups, out_tokens,
+                           copy_stream, layer_done);
+}
+
+int kv_store_layers(const kv_paged* paged, const kv_seq* seqs, int n_seqs, kv_fmt fmt, int32_t layer_begin,
+                    int32_t layer_end, const int32_t* max_workgroups, hipStream_t stream,
+                    const hipEvent_t* wait_before, const hipEvent_t* layer_done)
+{
+    return store_layers(paged, seqs, n_seqs, fmt, layer_begin, layer_end, max_workgroups, stream, wait_before,
+                        layer_done);
+}
+
+int64_t kv_chunk_tokens(const kv_paged* paged, int64_t tok_start, int64_t tok_end, int64_t c)
+{
+    const int64_t n = kv_num_chunks(paged, tok_start, tok_end);
+    if (n < 0) return -1;
+    if (c < 0 || c >= n) {
+        fail(KV_EINVAL, "chunk %lld outside [0, %lld)", (long long)c, (long long)n);
+        return -1;
     }
-    return ok();
+    const int64_t first = tok_start + c * paged->chunk_size;
+    const int64_t last = first + paged->chunk_size < tok_end ? first + paged->chunk_size : tok_end;
+    return last - first;
 }
 
 const char* kv_last_error(void) { return g_last_error.c_str(); }

@@ -2,7 +2,8 @@
  * abi_c_example.c -- the C ABI of libkvmove.so used from plain C (no Python):
  * a two-layer paged pool with a known pattern, one 300-token sequence
  * (a full 256-token chunk and a 44-token tail) on scattered pages, stored
- * into chunks, the pool cleared, the chunks retrieved.  Checks that every
+ * into chunks, the pool cleared, the chunks retrieved (in one call, then
+ * again layer by layer, one event per layer).  Checks that every
  * row the sequence owns comes back bit for bit, that the other pages stay
  * clear, that the retrieve reports 300 tokens and that no fault bit is set.
  * Exit status 0 on success.  Built by the package's build step; run by a
@@ -36,6 +37,40 @@
     } while (0)
 
 enum { L = 2, H = 2, D = 64, P = 16, C = 256, NUM_PAGES = 64, TOKENS = 300 };
+
+/* Copies the device pool back and checks it: every row the sequence owns
+ * holds the original pattern, every other row is still zero. */
+static int check_pool(const uint16_t* pool, uint16_t* back, const uint16_t* host_pool, const int32_t* bt, int n_bt,
+                      size_t pool_elems, size_t layer_elems, size_t row)
+{
+    CHECK_HIP(hipMemcpy(back, pool, pool_elems * 2, hipMemcpyDeviceToHost));
+    size_t restored = 0;
+    for (int l = 0; l < L; ++l) {
+        for (int kv = 0; kv < 2; ++kv) {
+            const size_t base = (size_t)(2 * l + kv) * layer_elems;
+            for (int page = 0; page < NUM_PAGES; ++page) {
+                for (int r = 0; r < P; ++r) {
+                    /* token of this row, if the sequence owns it */
+                    int token = -1;
+                    for (int i = 0; i < n_bt; ++i)
+                        if (bt[i] == page && i * P + r < TOKENS) token = i * P + r;
+                    const size_t at = base + ((size_t)page * P + r) * row;
+                    for (size_t e = 0; e < row; ++e) {
+                        const uint16_t want = token >= 0 ? host_pool[at + e] : 0;
+                        if (back[at + e] != want) {
+                            fprintf(stderr, "layer %d kv %d page %d row %d elem %zu: %u, want %u\n", l, kv, page, r,
+                                    e, back[at + e], want);
+                            return 7;
+                        }
+                    }
+                    restored += token >= 0;
+                }
+            }
+        }
+    }
+    if (restored != (size_t)L * 2 * TOKENS) { fprintf(stderr, "%zu rows restored\n", restored); return 7; }
+    return 0;
+}
 
 int main(void)
 {
@@ -108,32 +143,23 @@ int main(void)
     const int faults = kv_take_faults();
     if (faults != 0) { fprintf(stderr, "fault bits %d\n", faults); return 6; }
 
-    CHECK_HIP(hipMemcpy(back, pool, pool_elems * 2, hipMemcpyDeviceToHost));
-    size_t restored = 0;
-    for (int l = 0; l < L; ++l) {
-        for (int kv = 0; kv < 2; ++kv) {
-            const size_t base = (size_t)(2 * l + kv) * layer_elems;
-            for (int page = 0; page < NUM_PAGES; ++page) {
-                for (int r = 0; r < P; ++r) {
-                    /* token of this row, if the sequence owns it */
-                    int token = -1;
-                    for (int i = 0; i < n_bt; ++i)
-                        if (bt[i] == page && i * P + r < TOKENS) token = i * P + r;
-                    const size_t at = base + ((size_t)page * P + r) * row;
-                    for (size_t e = 0; e < row; ++e) {
-                        const uint16_t want = token >= 0 ? host_pool[at + e] : 0;
-                        if (back[at + e] != want) {
-                            fprintf(stderr, "layer %d kv %d page %d row %d elem %zu: %u, want %u\n", l, kv, page, r,
-                                    e, back[at + e], want);
-                            return 7;
-                        }
-                    }
-                    restored += token >= 0;
-                }
-            }
-        }
-    }
-    if (restored != (size_t)L * 2 * TOKENS) { fprintf(stderr, "%zu rows restored\n", restored); return 7; }
-    printf("C ABI round trip: %d tokens x %d layers x K,V restored bit for bit; other rows untouched\n", TOKENS, L);
+    int rc = check_pool(pool, back, host_pool, bt, n_bt, pool_elems, layer_elems, row);
+    if (rc != 0) return rc;
+
+    /* the same retrieve layer by layer (the boundary's kv_retrieve_layer),
+     * each layer's event recorded on the stream after its scatter; the host
+     * waits on the last one */
+    CHECK_HIP(hipMemset(pool, 0, pool_elems * 2));
+    CHECK_HIP(hipDeviceSynchronize());
+    hipEvent_t done[L];
+    for (int l = 0; l < L; ++l) CHECK_HIP(hipEventCreateWithFlags(&done[l], hipEventDisableTiming));
+    for (int l = 0; l < L; ++l) CHECK_KV(kv_retrieve_layer(&paged, &seq, masks, 1, KV_FMT_BF16, l, stream, done[l]));
+    CHECK_HIP(hipEventSynchronize(done[L - 1]));
+    rc = check_pool(pool, back, host_pool, bt, n_bt, pool_elems, layer_elems, row);
+    if (rc != 0) return rc;
+    if (kv_take_faults() != 0) { fprintf(stderr, "fault bits after the layer calls\n"); return 6; }
+    for (int l = 0; l < L; ++l) CHECK_HIP(hipEventDestroy(done[l]));
+    printf("C ABI round trip: %d tokens x %d layers x K,V restored bit for bit, in one call and layer by layer; "
+           "other rows untouched\n", TOKENS, L);
     return 0;
 }

@@ -29,8 +29,9 @@ def _declared_functions():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ["kv_store_chunks", "kv_store_layer", "kv_retrieve_chunks", "kv_retrieve_layer", "kv_chunk_bytes",
-              "kv_num_chunks", "kv_last_error", "kv_take_faults", "kv_copy_bytes"]:
+    for n in ["kv_store_chunks", "kv_store_layer", "kv_store_layers", "kv_retrieve_chunks", "kv_retrieve_layer",
+              "kv_retrieve_layer_ex", "kv_retrieve_layers", "kv_chunk_bytes", "kv_num_chunks", "kv_chunk_tokens",
+              "kv_last_error", "kv_take_faults", "kv_copy_bytes"]:
         assert n in names
 
 
@@ -142,9 +143,15 @@ def test_retrieve_with_no_hits_launches_nothing():
     assert list(out) == [0, 0]
     for layer in (0, 31):
         out[0] = out[1] = -7
-        assert L.kv_retrieve_layer(ctypes.byref(p), seqs, masks, 2, kvm.FMT_FP8, layer, out, 0, None,
-                                   None) == kvm.KV_OK
+        assert L.kv_retrieve_layer_ex(ctypes.byref(p), seqs, masks, 2, kvm.FMT_FP8, layer, out, 0, None,
+                                      None) == kvm.KV_OK
         assert list(out) == [0, 0]
+        assert L.kv_retrieve_layer(ctypes.byref(p), seqs, masks, 2, kvm.FMT_FP8, layer, None, None) == kvm.KV_OK
+    # every layer in one call, no events: nothing is enqueued either
+    out[0] = out[1] = -7
+    assert L.kv_retrieve_layers(ctypes.byref(p), seqs, masks, 2, kvm.FMT_BF16, 0, 32, None, out, None,
+                                None) == kvm.KV_OK
+    assert list(out) == [0, 0]
 
 
 def test_retrieve_rejections():
@@ -158,10 +165,21 @@ def test_retrieve_rejections():
     nullm = (ctypes.c_void_p * 1)(None)
     assert L.kv_retrieve_chunks(ctypes.byref(p), seqs, nullm, 1, 0, out, None) == kvm.KV_EINVAL
     for bad_layer in (-1, 32):
-        assert L.kv_retrieve_layer(ctypes.byref(p), seqs, masks, 1, 0, bad_layer, out, 0, None,
-                                   None) == kvm.KV_EINVAL
-    assert L.kv_retrieve_layer(ctypes.byref(p), seqs, masks, 1, 0, 0, out, -5, None,
-                               None) == kvm.KV_EINVAL
+        assert L.kv_retrieve_layer(ctypes.byref(p), seqs, masks, 1, 0, bad_layer, None, None) == kvm.KV_EINVAL
+        assert L.kv_retrieve_layer_ex(ctypes.byref(p), seqs, masks, 1, 0, bad_layer, out, 0, None,
+                                      None) == kvm.KV_EINVAL
+    assert L.kv_retrieve_layer_ex(ctypes.byref(p), seqs, masks, 1, 0, 0, out, -5, None,
+                                  None) == kvm.KV_EINVAL
+    assert L.kv_retrieve_layer(ctypes.byref(p), seqs, None, 1, 0, 0, None, None) == kvm.KV_EINVAL
+    # layer ranges: empty, reversed or outside [0, L), and negative caps
+    for lo, hi in ((3, 3), (5, 4), (-1, 2), (30, 33)):
+        assert L.kv_retrieve_layers(ctypes.byref(p), seqs, masks, 1, 0, lo, hi, None, out, None,
+                                    None) == kvm.KV_EINVAL
+        assert L.kv_store_layers(ctypes.byref(p), seqs, 1, 0, lo, hi, None, None, None, None) == kvm.KV_EINVAL
+    caps = (ctypes.c_int32 * 4)(0, 8, -1, 8)
+    assert L.kv_retrieve_layers(ctypes.byref(p), seqs, masks, 1, 0, 4, 8, caps, out, None, None) == kvm.KV_EINVAL
+    assert "max_workgroups[2]" in L.kv_last_error().decode()
+    assert L.kv_store_layers(ctypes.byref(p), seqs, 1, 0, 4, 8, caps, None, None, None) == kvm.KV_EINVAL
     bad = (kvm._KvSeq * 1)(_seq(100, 1000, 63))
     assert L.kv_retrieve_chunks(ctypes.byref(p), bad, masks, 1, 0, out, None) == kvm.KV_EINVAL
 
@@ -208,24 +226,102 @@ def test_binding_refuses_host_block_tables_and_pools():
                               [torch.zeros(4, 16, 1, 8, dtype=torch.bfloat16)])
 
 
-def test_binding_refuses_short_hit_masks():
-    # one flag per chunk is read: a shorter mask would be read past its end
+def _host_paged(L=2, H=2, D=64, P=16, C=256, n=64):
+    """A Paged whose address arrays are host tensors: enough for the host-side
+    checks (nothing here reaches a kernel)."""
     import torch
+    z = torch.zeros(L, dtype=torch.int64)
+    return kvm.Paged(z, z.clone(), L, H, D, P, C, n)
 
-    class _P:
-        chunk_size = 256
 
+def _host_seq(s, e, chunks=None):
+    """A Seq built past the device checks of its constructor (host tensors,
+    for host-side checks only)."""
+    import torch
     seq = kvm.Seq.__new__(kvm.Seq)
-    seq.tok_start, seq.tok_end = 256, 1000                  # 3 chunks
-    seq.block_table = torch.zeros(1, dtype=torch.int32)
-    seq.chunk_addrs = torch.zeros(0, dtype=torch.int64)
-    b = kvm.Batch.__new__(kvm.Batch)
-    b.seqs, b.n, b.chunk_size = [seq], 1, _P.chunk_size
+    seq.tok_start, seq.tok_end = s, e
+    seq.block_table = torch.zeros(64, dtype=torch.int32)
+    seq._chunks = chunks
+    seq.chunk_addrs = torch.zeros(len(chunks) if chunks else 1, dtype=torch.int64)
+    return seq
+
+
+def test_binding_refuses_short_hit_masks():
+    # one flag per chunk is read: a shorter mask would be read past its end;
+    # the chunk count comes from the library (kv_num_chunks)
+    _lib()
+    b = kvm.Batch(_host_paged(), [_host_seq(256, 1000)])     # 3 chunks
     with pytest.raises(kvm.KvError, match="2 flags for 3 chunks"):
         b.set_masks([[1, 1]])
     assert b.set_masks([[1, 1, 0]]) is b
     with pytest.raises(kvm.KvError, match="hit masks"):
         b.set_masks([[1, 1, 0], [1]])
+
+
+def test_binding_refuses_short_chunk_lists_and_small_chunks():
+    # the kernels write each chunk buffer up to kv_chunk_bytes for its token
+    # count and cannot see its end: too few chunk tensors, or one too small
+    # for the format, is refused with KV_EINVAL before any library call that
+    # would launch (here, with no GPU, a launch would fail with KV_EHIP)
+    import torch
+    _lib()
+    paged = _host_paged()
+    sizes = [paged.chunk_bytes(paged.chunk_tokens(0, 600, c), kvm.FMT_BF16) for c in range(3)]
+    assert [paged.chunk_tokens(0, 600, c) for c in range(3)] == [256, 256, 88]
+    ok = [torch.empty(n, dtype=torch.uint8) for n in sizes]
+    short_list = kvm.Batch(paged, [_host_seq(0, 600, ok[:2])]).set_masks([[1, 1, 1]])
+    with pytest.raises(kvm.KvError, match="2 chunk tensors for 3 chunks") as e:
+        kvm.store(paged, short_list)
+    assert e.value.code == kvm.KV_EINVAL
+    with pytest.raises(kvm.KvError, match="2 chunk tensors for 3 chunks"):
+        kvm.retrieve(paged, short_list)
+    small = ok[:2] + [torch.empty(sizes[2] - 16, dtype=torch.uint8)]
+    b = kvm.Batch(paged, [_host_seq(0, 600, small)]).set_masks([[1, 1, 1]])
+    with pytest.raises(kvm.KvError, match="chunk 2") as e:
+        kvm.retrieve_layer(paged, b, 0)
+    assert e.value.code == kvm.KV_EINVAL
+    # sized for fp8 (1 byte per element) but used as bf16 (2 bytes)
+    fp8 = [torch.empty(paged.chunk_bytes(paged.chunk_tokens(0, 600, c), kvm.FMT_FP8), dtype=torch.uint8)
+           for c in range(3)]
+    b = kvm.Batch(paged, [_host_seq(0, 600, fp8)]).set_masks([[1, 1, 1]])
+    b.check_chunks(kvm.FMT_FP8)
+    with pytest.raises(kvm.KvError, match="format 0 needs"):
+        kvm.store_layers(paged, b, 0, 2)
+    # enough tensors of the right size pass the check (the call then goes on
+    # to the library, which cannot launch without a GPU)
+    good = kvm.Batch(paged, [_host_seq(0, 600, ok)]).set_masks([[1, 1, 1]])
+    assert good.check_chunks(kvm.FMT_BF16) is good
+    assert paged.chunk_tokens(0, 600, 2) == 88
+    with pytest.raises(kvm.KvError, match="outside"):
+        paged.chunk_tokens(0, 600, 3)
+
+
+def test_boundary_signatures_match_the_contract():
+    # the boundary's own calls keep their argument lists: pool, sequences,
+    # (hit masks,) count, format, ..., stream, (event); the format typed
+    # kv_fmt.  Parsed from include/kvmove.h.
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+
+    def params(name):
+        m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+        assert m, name
+        return [re.sub(r"\s+", " ", a.strip()) for a in m.group(1).split(",")]
+
+    assert params("kv_store_chunks") == ["const kv_paged* paged", "const kv_seq* seqs", "int n_seqs", "kv_fmt fmt",
+                                         "hipStream_t stream"]
+    assert params("kv_retrieve_chunks") == ["const kv_paged* paged", "const kv_seq* seqs",
+                                            "const uint8_t* const* hit_mask", "int n_seqs", "kv_fmt fmt",
+                                            "int64_t* out_tokens", "hipStream_t stream"]
+    assert params("kv_retrieve_layer") == ["const kv_paged* paged", "const kv_seq* seqs",
+                                           "const uint8_t* const* hit_mask", "int n_seqs", "kv_fmt fmt",
+                                           "int32_t layer", "hipStream_t copy_stream", "hipEvent_t layer_done"]
+    assert params("kv_chunk_bytes") == ["const kv_paged* paged", "int64_t n_tokens", "kv_fmt fmt"]
+    assert params("kv_last_error") == ["void"]
+    # every format argument of every entry point is a kv_fmt
+    for m in re.finditer(r"\b(kv_[a-z_]+)\s*\(([^)]*)\)\s*;", text):
+        for a in m.group(2).split(","):
+            if re.search(r"\bfmt\b", a):
+                assert a.split()[0] == "kv_fmt", (m.group(1), a)
 
 
 def test_cachegen_entry_points_reject_bad_calls():

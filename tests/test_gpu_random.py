@@ -37,8 +37,8 @@ def _case(i):
     pages_needed = sum(-(-e // P) for (_, e) in ranges)
     num_pages = pages_needed + int(rng.integers(1, 64))
     fmt = FORMATS[int(rng.integers(0, len(FORMATS)))]
-    store_form = rng.choice(["full", "layers"]) if fmt != kvm.FMT_CACHEGEN else "full"
-    retrieve_form = rng.choice(["chunk", "ordered", "layers"]) if fmt != kvm.FMT_CACHEGEN else \
+    store_form = rng.choice(["full", "layers", "layer-range"]) if fmt != kvm.FMT_CACHEGEN else "full"
+    retrieve_form = rng.choice(["chunk", "ordered", "layers", "layer-range"]) if fmt != kvm.FMT_CACHEGEN else \
         rng.choice(["chunk", "ordered"])
     where = rng.choice(["device", "device", "host"])
     cap = int(rng.choice([0, 0, 1, 3, 17]))
@@ -61,6 +61,10 @@ def test_random_case(i):
         kvm.store_cachegen(paged, batch, kb, vb, stream=s)
     elif store_form == "full":
         kvm.store(paged, batch, fmt, stream=s)
+    elif store_form == "layer-range":
+        # every layer in one call, the first at full width and the rest capped
+        kvm.store_layers(paged, batch, 0, w.num_layers, fmt=fmt, stream=s,
+                         max_workgroups=[0] + [cap] * (w.num_layers - 1))
     else:
         for l in range(w.num_layers):
             kvm.store_layer(paged, batch, l, fmt=fmt, stream=s, max_workgroups=cap)
@@ -77,7 +81,10 @@ def test_random_case(i):
         n = kvm.retrieve_cachegen(paged, batch, kb, vb, stream=s, workspace=ws)
     elif retrieve_form == "layers":
         for l in range(w.num_layers):
-            n = kvm.retrieve_layer(paged, batch, l, fmt=fmt, stream=s, max_workgroups=cap)
+            n = kvm.retrieve_layer_ex(paged, batch, l, fmt=fmt, stream=s, max_workgroups=cap)
+    elif retrieve_form == "layer-range":
+        n = kvm.retrieve_layers(paged, batch, 0, w.num_layers, fmt=fmt, stream=s,
+                                max_workgroups=[0] + [cap] * (w.num_layers - 1))
     else:
         n = kvm.retrieve(paged, batch, fmt=fmt, stream=s, workspace=ws)
     s.synchronize()
