@@ -2,7 +2,9 @@
 numpy arrays (what the oracle reads) and device tensors (what the HIP path
 reads), and allocating guarded chunk buffers.  No movement arithmetic here
 beyond sizes taken from the library and from the oracle."""
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -159,4 +161,73 @@ def check_retrieve_cachegen(w, pool_before, got_pool, chunk_sets, masks, kb, vb)
     counts = [oracle.retrieve_cachegen(opool, sq.block_table, sq.tok_start, sq.tok_end, m, host_chunks(cs), kb, vb)
               for sq, cs, m in zip(w.seqs, chunk_sets, masks)]
     assert equal_blocked(got_pool, exp), (w.name, first_diff(got_pool, exp))
+    return counts
+
+
+ORACLE_THREADS = 16      # the GPU machine's CPU share
+
+
+def _oracle_pool_map(fn, tasks):
+    """fn over tasks on up to ORACLE_THREADS threads (each oracle call goes
+    through ctypes, which releases the interpreter lock)."""
+    with ThreadPoolExecutor(max(1, min(ORACLE_THREADS, os.cpu_count() or 1))) as ex:
+        return list(ex.map(fn, tasks))
+
+
+def _chunk_range(w, sq, c):
+    """Token range of chunk c of a sequence (its length from the oracle)."""
+    s = sq.tok_start + c * w.chunk_size
+    return s, s + oracle.chunk_tokens(sq.tok_start, sq.tok_end, w.chunk_size, c)
+
+
+def oracle_store_all(w, opool, fmt, bins=None):
+    """The oracle's store of every chunk of every sequence, one task per
+    (sequence, chunk) over the thread pool; returns [sequence][chunk] arrays.
+    bins = (key_bins, value_bins) for the CacheGen format."""
+    tasks = [(i, c) for i, sq in enumerate(w.seqs)
+             for c in range(oracle.num_chunks(sq.tok_start, sq.tok_end, w.chunk_size))]
+
+    def one(task):
+        i, c = task
+        sq = w.seqs[i]
+        s, e = _chunk_range(w, sq, c)
+        exp = oracle.alloc_chunks(opool, s, e, fmt)
+        if fmt == oracle.FMT_CACHEGEN:
+            rc = oracle.store_cachegen(opool, sq.block_table, s, e, exp, bins[0], bins[1])
+        else:
+            rc = oracle.store(opool, sq.block_table, s, e, exp, fmt)
+        assert rc == 0, task
+        return exp[0]
+
+    flat = _oracle_pool_map(one, tasks)
+    out = [[] for _ in w.seqs]
+    for (i, _), a in zip(tasks, flat):
+        out[i].append(a)
+    return out
+
+
+def oracle_retrieve_all(w, opool, chunks, fmt, masks, bins=None):
+    """The oracle's retrieve of each sequence's leading hit chunks into
+    opool (in place), one task per (sequence, hit chunk) over the thread pool:
+    hit chunks of one call write distinct pages, so the tasks touch disjoint
+    rows.  chunks: [sequence][chunk] host arrays.  Returns the tokens made
+    available per sequence."""
+    tasks, counts = [], []
+    for i, (sq, m) in enumerate(zip(w.seqs, masks)):
+        n = oracle.num_chunks(sq.tok_start, sq.tok_end, w.chunk_size)
+        n_hit = oracle.hit_chunks(np.asarray(m, np.uint8)[:n]) if n else 0
+        tasks += [(i, c) for c in range(n_hit)]
+        counts.append(sum(oracle.chunk_tokens(sq.tok_start, sq.tok_end, w.chunk_size, c) for c in range(n_hit)))
+
+    def one(task):
+        i, c = task
+        sq = w.seqs[i]
+        s, e = _chunk_range(w, sq, c)
+        if fmt == oracle.FMT_CACHEGEN:
+            got = oracle.retrieve_cachegen(opool, sq.block_table, s, e, [1], [chunks[i][c]], bins[0], bins[1])
+        else:
+            got = oracle.retrieve(opool, sq.block_table, s, e, [1], [chunks[i][c]], fmt)
+        assert got == e - s, task
+
+    _oracle_pool_map(one, tasks)
     return counts

@@ -1,10 +1,11 @@
 """Parity at the workloads' full sizes, in the launch configuration the
 benchmark times (one store call and one retrieve call over all sequences).
 
-bf16 workloads are compared in full against the oracle; the fp8 workload is
-compared on sampled chunks (the oracle's per-element e4m3 path is slow) plus
-properties that hold at any size: the round-trip error bound over every
-element, and rows outside the hit chunks keeping a sentinel.
+Every workload is compared in full against the oracle: every chunk's bytes
+after the store, and the whole pool after the retrieve.  For the quantised
+formats the oracle (one element at a time, slow) runs one task per
+(sequence, chunk) on the host's threads; the round-trip error bound is then
+checked over every element as well.
 """
 import numpy as np
 import pytest
@@ -14,7 +15,8 @@ import oracle
 import paged_kv_movement_amd as kvm
 from paged_kv_movement_amd import workloads as wl
 from gpu_util import (say, host_from_dev_pool, oracle_pool, chunk_tokens, setup_device, host_chunks,
-                      check_store, check_retrieve, equal_blocked, first_diff, sync)
+                      check_store, check_retrieve, equal_blocked, first_diff, sync, oracle_store_all,
+                      oracle_retrieve_all)
 
 pytestmark = pytest.mark.gpu
 
@@ -76,11 +78,13 @@ def test_full_llama70b_store_and_retrieve():
     _full_bf16(wl.llama70b(), [32768])
 
 
-def test_full_layerwise_8b_with_compute_stream():
+@pytest.mark.parametrize("form", ["per-layer-calls", "one-call"])
+def test_full_layerwise_8b_with_compute_stream(form):
     # one 10240-token sequence retrieved layer by layer on a copy stream, each
-    # layer's event gating a bf16 GEMM (tokens x 4096 x 4096) on the compute stream
+    # layer's event gating a bf16 GEMM (tokens x 4096 x 4096) on the compute
+    # stream; the layers enqueued one call each, or all by one call
     w = wl.layerwise8b()
-    say("case", w.name)
+    say("case", w.name, form)
     pool = wl.device_pool(w)
     pool, paged, batch, chunk_sets = setup_device(w, pool=pool, fill=0xCD)
     kvm.store(paged, batch)
@@ -92,11 +96,16 @@ def test_full_layerwise_8b_with_compute_stream():
     x = torch.randn(10240, 4096, device="cuda", dtype=torch.bfloat16)
     wgt = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16) * 0.01
     outs = []
+    # layer 0 at full width, the rest on a capped grid (as the benchmark's
+    # overlap variants do)
+    caps = [0] + [128] * (w.num_layers - 1)
+    if form == "one-call":
+        assert kvm.retrieve_layers(paged, batch, 0, w.num_layers, stream=copy, events=events,
+                                   max_workgroups=caps) == [10240]
     for l in range(w.num_layers):
-        # layer 0 at full width, the rest on a capped grid (as the benchmark's
-        # overlap variants do)
-        cap = 0 if l == 0 else 128
-        assert kvm.retrieve_layer(paged, batch, l, stream=copy, event=events[l], max_workgroups=cap) == [10240]
+        if form == "per-layer-calls":
+            assert kvm.retrieve_layer_ex(paged, batch, l, stream=copy, event=events[l],
+                                         max_workgroups=caps[l]) == [10240]
         compute.wait_event(events[l])
         with torch.cuda.stream(compute):
             outs.append(torch.mm(x, wgt))
@@ -110,82 +119,96 @@ def test_full_layerwise_8b_with_compute_stream():
     _free()
 
 
-@pytest.mark.parametrize("fmt", [FP8, E5M2, K16V8], ids=["fp8", "e5m2", "k16v8"])
-def test_full_fp8_8b_sampled_chunks_and_bounds(fmt):
-    w = wl.fp8_8b()
-    say("case", w.name, fmt)
+def _full_quantised(w, fmt, bins=None):
+    """Store every chunk of the 8B-shape workload in a quantised format and
+    compare every chunk's bytes (codes and scales, or symbols and max1) with
+    the oracle's; retrieve every chunk into a zeroed pool and compare the
+    whole pool with the oracle's retrieve; the same retrieve in pool-address
+    order must give the same pool; a 30-chunk hit mask into a sentinel pool is
+    compared with the oracle as a whole as well.  The oracle runs one task per
+    (sequence, chunk) on the host's threads.  Returns the original and
+    retrieved device pools, the chunk buffers and the oracle's chunks for
+    the bound checks."""
     pool = wl.device_pool(w)
     pool, paged, batch, chunk_sets = setup_device(w, pool=pool, fmt=fmt, fill=0xCD)
-    kvm.store(paged, batch, fmt)
+    if fmt == kvm.FMT_CACHEGEN:
+        kvm.store_cachegen(paged, batch, *bins)
+    else:
+        kvm.store(paged, batch, fmt)
     sync()
     assert kvm.take_faults() == 0
     arr = host_from_dev_pool(pool)
-    opool = oracle_pool(w, arr)
-    samples = [(0, 0), (0, 17), (0, 39), (3, 38), (7, 5), (7, 39)]   # (seq, chunk); 39 = tail
-    for si, c in samples:
-        sq = w.seqs[si]
-        s = c * w.chunk_size
-        e = min(sq.tok_end, s + w.chunk_size)
-        exp = oracle.alloc_chunks(opool, s, e, fmt)
-        assert oracle.store(opool, sq.block_table, s, e, exp, fmt) == 0
-        bufs, sizes = chunk_sets[si]
-        got = host_chunks(([bufs[c]], [sizes[c]]))[0]
-        assert np.array_equal(got, exp[0]), (si, c, first_diff(got, exp[0]))
-    say("  sampled fp8 chunks match")
-    # full retrieve (all hit) into a zeroed pool: sampled chunks vs the oracle
-    # and the error bound over every element
+    exp = oracle_store_all(w, oracle_pool(w, arr), fmt, bins)
+    del arr
+    got = [host_chunks(cs) for cs in chunk_sets]
+    n_chunks = 0
+    for i, (g_seq, e_seq) in enumerate(zip(got, exp)):
+        assert len(g_seq) == len(e_seq)
+        for c, (g, e) in enumerate(zip(g_seq, e_seq)):
+            assert g.size == e.size and np.array_equal(g, e), (w.name, fmt, "seq", i, "chunk", c, first_diff(g, e))
+            n_chunks += 1
+    say("  store: all", n_chunks, "chunks equal the oracle's, bit for bit")
+    del exp
+
+    def retrieve(masks=None, ws=None):
+        if fmt == kvm.FMT_CACHEGEN:
+            return kvm.retrieve_cachegen(paged, batch, *bins, masks=masks, workspace=ws)
+        return kvm.retrieve(paged, batch, masks=masks, fmt=fmt, workspace=ws)
+
     orig = pool.clone()
     pool.zero_()
-    assert kvm.retrieve(paged, batch, fmt=fmt) == [10000] * 8
-    sync()
-    got_pool = host_from_dev_pool(pool)
-    for si, c in samples:
-        sq = w.seqs[si]
-        s = c * w.chunk_size
-        e = min(sq.tok_end, s + w.chunk_size)
-        bufs, sizes = chunk_sets[si]
-        ch = host_chunks(([bufs[c]], [sizes[c]]))
-        pages = sq.block_table[s // 16: (e + 15) // 16]
-        # the oracle retrieves this one chunk into a small zeroed pool holding
-        # just its pages, renumbered 0..k-1 (rows do not depend on the page
-        # numbering); the device pool is read back at the real page ids
-        part = np.zeros((w.num_layers, 2, len(pages), 16, w.width), np.uint16)
-        ptmp = oracle.Pool.from_array(part, w.num_kv_heads, w.head_dim, w.chunk_size)
-        padded_bt = np.concatenate([np.zeros(s // 16, np.int32), np.arange(len(pages), dtype=np.int32)])
-        assert oracle.retrieve(ptmp, padded_bt, s, e, [1], ch, fmt) == e - s
-        assert np.array_equal(got_pool[:, :, pages], part), (si, c)
-    del got_pool
-    from test_gpu_parity import _assert_fp8_bound
-    _assert_fp8_bound(w, orig, pool, chunk_sets, fmt)
-    # the retrieve in pool-address order gives the same pool, bit for bit
-    ordered = pool.clone()
-    pool.zero_()
-    assert kvm.retrieve(paged, batch, fmt=fmt, workspace=paged.new_workspace()) == [10000] * 8
+    all_hit = [np.ones(40, np.uint8)] * len(w.seqs)
+    assert retrieve(all_hit) == [10000] * 8
     sync()
     assert kvm.take_faults() == 0
-    assert torch.equal(pool.view(torch.int16), ordered.view(torch.int16))
-    del ordered
-    # 30-chunk hit mask: rows of chunks >= 30 keep the sentinel, hit rows equal
-    # the all-hit result
-    full = pool.clone()
+    got_pool = host_from_dev_pool(pool)
+    exp_pool = np.zeros_like(got_pool)
+    assert oracle_retrieve_all(w, oracle_pool(w, exp_pool), got, fmt, all_hit, bins) == [10000] * 8
+    assert equal_blocked(got_pool, exp_pool), (w.name, fmt, first_diff(got_pool, exp_pool))
+    say("  retrieve (all hit): the whole pool equals the oracle's")
+    del got_pool
+    # the retrieve in pool-address order gives the same pool, bit for bit
+    retrieved = pool.clone()
+    pool.zero_()
+    assert retrieve(all_hit, paged.new_workspace()) == [10000] * 8
+    sync()
+    assert kvm.take_faults() == 0
+    assert torch.equal(pool.view(torch.int16), retrieved.view(torch.int16))
+    # 30-chunk hit mask into a sentinel pool: the whole pool vs the oracle's
     pool.view(torch.int16).fill_(SENTINEL)
     masks = [np.r_[np.ones(30, np.uint8), np.zeros(10, np.uint8)]] * 8
-    assert kvm.retrieve(paged, batch, masks=masks, fmt=fmt) == [7680] * 8
+    assert retrieve(masks) == [7680] * 8
     sync()
-    for sq in w.seqs:
-        bt = torch.from_numpy(sq.block_table.astype(np.int64)).cuda()
-        hit, miss = bt[:480], bt[480:]
-        assert torch.equal(pool[:, :, hit], full[:, :, hit])
-        assert (pool[:, :, miss].view(torch.int16) == SENTINEL).all()
-    del pool, orig, full, paged, batch, chunk_sets
+    assert kvm.take_faults() == 0
+    got_pool = host_from_dev_pool(pool)
+    exp_pool[...] = SENTINEL
+    assert oracle_retrieve_all(w, oracle_pool(w, exp_pool), got, fmt, masks, bins) == [7680] * 8
+    assert equal_blocked(got_pool, exp_pool), (w.name, fmt, "mask", first_diff(got_pool, exp_pool))
+    say("  retrieve (30 of 40 chunks): the whole pool equals the oracle's")
+    del got_pool, exp_pool
+    return pool, paged, batch, chunk_sets, orig, retrieved, got
+
+
+@pytest.mark.parametrize("fmt", [FP8, E5M2, K16V8], ids=["fp8", "e5m2", "k16v8"])
+def test_full_fp8_8b_every_chunk_and_whole_pool(fmt):
+    w = wl.fp8_8b()
+    say("case", w.name, fmt)
+    pool, paged, batch, chunk_sets, orig, retrieved, ref = _full_quantised(w, fmt)
+    # the round-trip error bound over every element, each group's floor
+    # taken from the oracle's scale
+    from test_gpu_parity import _assert_fp8_bound
+    _assert_fp8_bound(w, orig, retrieved, chunk_sets, fmt, ref_chunks=ref)
+    del pool, paged, batch, chunk_sets, orig, retrieved, ref
     _free()
 
 
-def test_full_layerwise_store_8b_behind_compute():
+@pytest.mark.parametrize("form", ["per-layer-calls", "one-call"])
+def test_full_layerwise_store_8b_behind_compute(form):
     # prefill-style: layer l's KV is stored on a copy stream once layer l's
-    # GEMM (the producer) is done, while layer l+1 computes
+    # GEMM (the producer) is done, while layer l+1 computes; one store call
+    # per layer, or one call for all layers after the GEMMs are enqueued
     w = wl.layerwise8b()
-    say("case", w.name, "layerwise store")
+    say("case", w.name, "layerwise store", form)
     pool = wl.device_pool(w)
     pool, paged, batch, chunk_sets = setup_device(w, pool=pool, fill=0xCD)
     copy, compute = torch.cuda.Stream(), torch.cuda.Stream()
@@ -194,12 +217,17 @@ def test_full_layerwise_store_8b_behind_compute():
     x = torch.randn(10240, 4096, device="cuda", dtype=torch.bfloat16)
     wgt = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16) * 0.01
     sync()
+    caps = [0] + [128] * (w.num_layers - 1)
     for l in range(w.num_layers):
         with torch.cuda.stream(compute):
             torch.mm(x, wgt)
             done[l].record(compute)
-        copy.wait_event(done[l])
-        kvm.store_layer(paged, batch, l, stream=copy, event=stored[l], max_workgroups=0 if l == 0 else 128)
+        if form == "per-layer-calls":
+            copy.wait_event(done[l])
+            kvm.store_layer(paged, batch, l, stream=copy, event=stored[l], max_workgroups=caps[l])
+    if form == "one-call":
+        kvm.store_layers(paged, batch, 0, w.num_layers, stream=copy, wait_events=done, events=stored,
+                         max_workgroups=caps)
     sync()
     assert kvm.take_faults() == 0
     arr = host_from_dev_pool(pool)
@@ -208,66 +236,36 @@ def test_full_layerwise_store_8b_behind_compute():
     _free()
 
 
-def test_full_cachegen_8b_sampled_chunks_and_bound():
+def test_full_cachegen_8b_every_chunk_and_whole_pool():
     # the fp8 workload's inputs (N(0,1), 4 outlier channels x20) through the
     # CacheGen quantiser, seeded per-layer bins
     from gpu_util import cachegen_bins
     w = wl.fp8_8b()
     say("case", w.name, "cachegen")
     kb, vb = cachegen_bins(w.num_layers, 4)
-    pool = wl.device_pool(w)
-    pool, paged, batch, chunk_sets = setup_device(w, pool=pool, fmt=kvm.FMT_CACHEGEN, fill=0xCD)
-    kvm.store_cachegen(paged, batch, kb, vb)
-    sync()
-    assert kvm.take_faults() == 0
-    arr = host_from_dev_pool(pool)
-    opool = oracle_pool(w, arr)
-    samples = [(0, 0), (0, 39), (4, 21), (7, 39)]            # (seq, chunk); 39 = 16-token tail
-    for si, c in samples:
-        sq = w.seqs[si]
-        s, e = c * w.chunk_size, min(sq.tok_end, (c + 1) * w.chunk_size)
-        exp = oracle.alloc_chunks(opool, s, e, kvm.FMT_CACHEGEN)
-        assert oracle.store_cachegen(opool, sq.block_table, s, e, exp, kb, vb) == 0
-        bufs, sizes = chunk_sets[si]
-        got = host_chunks(([bufs[c]], [sizes[c]]))[0]
-        assert np.array_equal(got, exp[0]), (si, c, first_diff(got, exp[0]))
-    say("  sampled cachegen chunks match")
-    del arr, opool
-    orig = pool.clone()
-    pool.zero_()
-    assert kvm.retrieve_cachegen(paged, batch, kb, vb, masks=[np.ones(40, np.uint8)] * 8) == [10000] * 8
-    sync()
+    pool, paged, batch, chunk_sets, orig, retrieved, ref = _full_quantised(w, kvm.FMT_CACHEGEN, (kb, vb))
     # every element: |x' - x| <= max1 * (1/(2 MAX) + 2^-8 + 2^-20) (half a
-    # quantisation step, the float32 steps, the bf16 rounding)
+    # quantisation step, the float32 steps, the bf16 rounding), max1 from the
+    # oracle's chunks
     L, E, P, C = w.num_layers, w.width, w.page_size, w.chunk_size
     worst = 0.0
-    for sq, (bufs, sizes) in zip(w.seqs, chunk_sets):
+    for sq, ref_seq in zip(w.seqs, ref):
         bt = torch.from_numpy(sq.block_table.astype(np.int64)).cuda()
-        for c, (b, n_c) in enumerate(zip(bufs, chunk_tokens(w, sq))):
-            m1 = b[L * 2 * n_c * E: L * 2 * n_c * E + L * 2 * n_c * 4].view(torch.float32).view(L, 2, n_c)
+        for c, (b, n_c) in enumerate(zip(ref_seq, chunk_tokens(w, sq))):
+            m1 = torch.from_numpy(b[L * 2 * n_c * E:].view(np.float32).reshape(L, 2, n_c).copy()).cuda()
             t = sq.tok_start + c * C + torch.arange(n_c, device="cuda")
             page, row = bt[t // P], t % P
             for l in range(L):
                 for kv, bins in ((0, kb), (1, vb)):
                     MAX = float(bins[l] // 2 - 1)
                     x = orig[l, kv].view(-1, P, E)[page, row].double()
-                    y = pool[l, kv].view(-1, P, E)[page, row].double()
+                    y = retrieved[l, kv].view(-1, P, E)[page, row].double()
                     lim = m1[l, kv].double()[:, None] * (0.5 / MAX + 2.0 ** -8 + 2.0 ** -20)
                     over = ((y - x).abs() - lim).max()
                     worst = max(worst, float(over))
     say("  worst excess over the bound", worst)
     assert worst <= 0.0
-    # 30-chunk mask: rows of later chunks keep the sentinel, hit rows equal the all-hit result
-    full = pool.clone()
-    pool.view(torch.int16).fill_(SENTINEL)
-    masks = [np.r_[np.ones(30, np.uint8), np.zeros(10, np.uint8)]] * 8
-    assert kvm.retrieve_cachegen(paged, batch, kb, vb, masks=masks) == [7680] * 8
-    sync()
-    for sq in w.seqs:
-        bt = torch.from_numpy(sq.block_table.astype(np.int64)).cuda()
-        assert torch.equal(pool[:, :, bt[:480]], full[:, :, bt[:480]])
-        assert (pool[:, :, bt[480:]].view(torch.int16) == SENTINEL).all()
-    del pool, orig, full, paged, batch, chunk_sets
+    del pool, paged, batch, chunk_sets, orig, retrieved, ref
     _free()
 
 
