@@ -382,10 +382,38 @@ __device__ __forceinline__ uint32_t nan_fix2(uint32_t o, float p0, float p1, uin
     return o;
 }
 
+// Bit 7 of each byte of the result is set where that byte of w is an fp8
+// NaN code: S.1111.111 (E4M3), S.11111.01 / .10 / .11 (E5M2) -- the low seven
+// bits at or above 0x7F / 0x7D; adding 1 / 3 to them carries into bit 7
+// there and nowhere else.
+template <bool kE5M2>
+__device__ __forceinline__ uint32_t nan_code_bits(uint32_t w)
+{
+    return ((w & 0x7F7F7F7Fu) + (kE5M2 ? 0x03030303u : 0x01010101u)) & 0x80808080u;
+}
+
+// The bf16 results of the four codes in c (bytes 0, 1 in lo; 2, 3 in hi) where
+// a code is NaN: the quiet NaN 0x7FC0 with the code's sign.
+template <bool kE5M2>
+__device__ __forceinline__ void fix_nan_codes(uint32_t& lo, uint32_t& hi, uint32_t c)
+{
+    const uint32_t m = nan_code_bits<kE5M2>(c);
+    if (m & 0x80u) lo = (lo & 0xFFFF0000u) | 0x7FC0u | ((c & 0x80u) << 8);
+    if (m & 0x8000u) lo = (lo & 0x0000FFFFu) | 0x7FC00000u | ((c & 0x8000u) << 16);
+    if (m & 0x800000u) hi = (hi & 0xFFFF0000u) | 0x7FC0u | ((c >> 8) & 0x8000u);
+    if (m & 0x80000000u) hi = (hi & 0x0000FFFFu) | 0x7FC00000u | (c & 0x80000000u);
+}
+
+// How dequantise_store treats NaN results: kNanPlain leaves them to the
+// hardware (for finite, nonzero scales and no NaN code, none arise);
+// kNanByProduct writes every NaN product as the quiet NaN with its code's
+// sign (any scale); kNanByCode does that for the NaN codes (finite, nonzero
+// scales, where only a NaN code gives a NaN product).
+enum NanMode { kNanPlain, kNanByProduct, kNanByCode };
+
 // Decode kVpt x 8 fp8 codes, scale them, round to bf16 and store them
-// (kBlock*kVpt 16-byte vectors per tile); kFixNan writes every NaN product as
-// the quiet NaN with its code's sign.
-template <int kBlock, int kVpt, bool kE5M2, bool kFixNan>
+// (kBlock*kVpt 16-byte vectors per tile).
+template <int kBlock, int kVpt, bool kE5M2, NanMode kNan>
 __device__ __forceinline__ void dequantise_store(const u32x2 (&q)[kVpt], float scale, __amdgpu_buffer_rsrc_t rd)
 {
 #pragma unroll
@@ -399,9 +427,15 @@ __device__ __forceinline__ void dequantise_store(const u32x2 (&q)[kVpt], float s
                                   : __builtin_amdgcn_cvt_pk_f32_fp8(q[k][j], true);
             o[2 * j] = bf16x2_rne(d0[0] * scale, d0[1] * scale);
             o[2 * j + 1] = bf16x2_rne(d1[0] * scale, d1[1] * scale);
-            if (kFixNan) {
+            if (kNan == kNanByProduct) {
                 o[2 * j] = nan_fix2(o[2 * j], d0[0] * scale, d0[1] * scale, q[k][j]);
                 o[2 * j + 1] = nan_fix2(o[2 * j + 1], d1[0] * scale, d1[1] * scale, q[k][j] >> 16);
+            }
+            if (kNan == kNanByCode) {
+                uint32_t lo = o[2 * j], hi = o[2 * j + 1];
+                fix_nan_codes<kE5M2>(lo, hi, q[k][j]);
+                o[2 * j] = lo;
+                o[2 * j + 1] = hi;
             }
         }
         __builtin_amdgcn_raw_buffer_store_b128(o, rd, (k * kBlock + threadIdx.x) * 16, 0, kCpolNt | kCpolSc1);
@@ -436,16 +470,24 @@ __device__ __forceinline__ void retrieve_fp8_unit_tile(const MoveArgs& a, const 
 #pragma unroll
     for (int k = 0; k < kVpt; ++k)
         q[k] = __builtin_amdgcn_raw_buffer_load_b64(rs, (k * kBlock + threadIdx.x) * 8, 0, kCpolNt | kCpolSc1);
-    // A scale that is NaN, infinite or zero can turn a product into NaN
-    // (NaN * x, +-0 * inf, inf * 0); such groups take the path that writes
-    // every NaN result as the quiet NaN 0x7FC0 with the code's sign.  The
-    // store writes NaN codes only under a NaN scale, so with any other scale
-    // the plain path is taken (a NaN code from elsewhere still comes out as
-    // a NaN: the hardware conversions keep its sign and quiet it).
-    if (!(__builtin_fabsf(scale) < __builtin_inff()) || scale == 0.0f)    // the same for the whole wave
-        dequantise_store<kBlock, kVpt, kE5M2, true>(q, scale, rd);
+    // Every NaN result is written as the quiet NaN 0x7FC0 with its code's
+    // sign (the hardware's conversions do not keep that sign).  A scale that
+    // is NaN, infinite or zero can turn any product into NaN (NaN * x,
+    // +-0 * inf, inf * 0): such groups take the path that checks every
+    // product.  Under any other scale only a NaN code gives a NaN, and the
+    // store writes none there; a lane whose codes hold one (a chunk from
+    // elsewhere) takes the path that checks the codes.
+    if (!(__builtin_fabsf(scale) < __builtin_inff()) || scale == 0.0f) {   // the same for the whole wave
+        dequantise_store<kBlock, kVpt, kE5M2, kNanByProduct>(q, scale, rd);
+        return;
+    }
+    uint32_t nan_any = 0;
+#pragma unroll
+    for (int k = 0; k < kVpt; ++k) nan_any |= nan_code_bits<kE5M2>(q[k][0]) | nan_code_bits<kE5M2>(q[k][1]);
+    if (nan_any != 0)
+        dequantise_store<kBlock, kVpt, kE5M2, kNanByCode>(q, scale, rd);
     else
-        dequantise_store<kBlock, kVpt, kE5M2, false>(q, scale, rd);
+        dequantise_store<kBlock, kVpt, kE5M2, kNanPlain>(q, scale, rd);
 }
 
 template <int kBlock, int kVpt, bool kE5M2>
