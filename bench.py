@@ -410,6 +410,37 @@ def bench_llama8b(args):
     return out
 
 
+def bench_layers_only(args, store):
+    """The 32 layer-by-layer scatters (store=False) or gathers (store=True) of
+    the layerwise workload alone, no compute beside them: one call for all
+    layers (kv_retrieve_layers / kv_store_layers) with every layer's grid
+    capped at --layers-only workgroups (0: one per tile), repeated --steps
+    times.  For kernel traces of one launch shape at a time."""
+    import torch
+    import paged_kv_movement_amd as kvm
+    from paged_kv_movement_amd import workloads as wl
+
+    w = wl.layerwise8b()
+    pool, paged, batch, arena = setup(w, kvm.FMT_BF16)
+    kvm.store(paged, batch)
+    torch.cuda.synchronize()
+    copy = torch.cuda.Stream()
+    L, cap = w.num_layers, args.layers_only
+    per_layer_bytes = 2 * 10240 * 2 * w.width * 2
+    if store:
+        def run():
+            kvm.store_layers(paged, batch, 0, L, stream=copy, max_workgroups=[cap] * L)
+    else:
+        def run():
+            kvm.retrieve_layers(paged, batch, 0, L, stream=copy, max_workgroups=[cap] * L)
+    ms = timed(copy, run, max(3, args.steps), warmup=args.warmup, stat="median")
+    assert kvm.take_faults() == 0
+    return {"metric": f"layer {'gather' if store else 'scatter'} alone, 32 layers per call",
+            "workload": "layerwise-8b: 1 seq x 10240 tokens, 32 layers", "max_workgroups": cap,
+            "calls": max(3, args.steps), "ms_per_32_layers_median": round(ms, 4),
+            "layer_ms": round(ms / L, 4), "layer_GBps": round(per_layer_bytes / (ms / L / 1e3) / 1e9, 2)}
+
+
 def bench_layerwise(args):
     """32 layer-by-layer scatters on a copy stream, each gating a bf16 GEMM
     (10240 x 4096 x 4096) on a compute stream; the copy of layer i+1 runs
@@ -909,6 +940,9 @@ def main():
                     help="headline retrieve: pool-address order with a workspace (default) or chunk-major")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (used for profiler runs)")
+    ap.add_argument("--layers-only", type=int, default=None, metavar="CAP",
+                    help="layerwise workloads: time only the 32 layer calls, one call for all layers, every "
+                         "layer's grid capped at CAP workgroups (0: none); for kernel traces")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -923,6 +957,8 @@ def main():
     log(f"device: {torch.cuda.get_device_name(0)}")
     if args.workload == "llama3.1-8b":
         out = bench_llama8b(args)
+    elif args.workload in ("layerwise-8b", "layerwise-store-8b") and args.layers_only is not None:
+        out = bench_layers_only(args, store=args.workload == "layerwise-store-8b")
     elif args.workload == "layerwise-8b":
         out = bench_layerwise(args)
     elif args.workload == "layerwise-store-8b":

@@ -20,6 +20,11 @@ constexpr int kGatherAuxLoad = kCpolNt | kCpolSc1;
 constexpr int kGatherAuxStore = kCpolNt | kCpolSc1;
 constexpr int kScatterAuxLoad = kCpolNt | kCpolSc1;
 constexpr int kScatterAuxStore = kCpolNt | kCpolSc1;
+// The plain copy (measurement aid): the fastest contiguous-copy shape of a
+// sweep over tile size (1-16 KiB), workgroup size (64-1024 threads), vectors
+// per lane (1-8), cache policy and workgroup order on the 8B workload's
+// 10.49 GB: 256 threads x 1 vector, nt + sc1 both ways, XCD-contiguous
+// order, 6.78 TB/s (512 x 1: 6.79; 64 x 1: 6.75; the movers' 64 x 2: 6.31).
 constexpr int kCopyBlock = 256;
 constexpr int kCopyVpt = 1;
 
@@ -72,14 +77,16 @@ __global__ __launch_bounds__(kBlock) void move_bf16(MoveArgsLut al)
 }
 
 // Plain contiguous copy (measurement aid): one tile of kBlock*kVpt vectors
-// per workgroup, the same instruction form as the movers.
+// per workgroup, the movers' instruction form (buffer loads and stores, nt +
+// sc1, XCD-contiguous workgroup order) without their page lookups.
 template <int kBlock, int kVpt>
 __global__ __launch_bounds__(kBlock) void copy_contiguous(uint64_t src, uint64_t dst, int64_t nbytes)
 {
     const int64_t tile = (int64_t)kBlock * kVpt * 16;
-    const int64_t lo = (int64_t)blockIdx.x * tile;
+    const int64_t lo = (int64_t)xcd_contiguous(blockIdx.x, gridDim.x) * tile;
     const int64_t left = nbytes - lo;
-    copy_tile<kBlock, kVpt, kCpolNt, kCpolNt>(src + lo, dst + lo, (uint32_t)(left < tile ? left : tile));
+    copy_tile<kBlock, kVpt, kCpolNt | kCpolSc1, kCpolNt | kCpolSc1>(src + lo, dst + lo,
+                                                                   (uint32_t)(left < tile ? left : tile));
 }
 
 }  // namespace kvmove
