@@ -78,8 +78,10 @@
  * library's addition.
  *
  * Ownership: every buffer is allocated and freed by the caller.  The library
- * allocates nothing and keeps no state between calls except a per-device
- * fault word (kv_take_faults).  Host arrays are read only during the call.
+ * allocates nothing and keeps no state between calls except, on each device,
+ * a fault word (kv_take_faults) and the 8 MiB scratch array of
+ * kv_retrieve_chunks_noalloc, both part of its code object.  Host arrays are
+ * read only during the call.
  *
  * Ordering: every call enqueues work on the given HIP stream (0 = the null
  * stream) and returns without waiting for it.  Results computed from host
@@ -227,6 +229,20 @@ size_t kv_retrieve_workspace_bytes(const kv_paged* paged);   /* 0 on a malformed
 int kv_retrieve_chunks_ws(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
                           kv_fmt fmt, int64_t* out_tokens, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * kv_retrieve_chunks_ws with the workspace taken from a scratch array that
+ * the library holds on each GPU (8 MiB, allocated when the library's code is
+ * loaded onto the device and held until the process ends).  Same arguments,
+ * result and errors as kv_retrieve_chunks, plus: a pool of more than 2^20
+ * pages is refused (KV_EINVAL; use kv_retrieve_chunks_ws), and so is a
+ * stream that belongs to another device than the current one.  It calls no
+ * allocator.  Every call on a GPU shares that GPU's scratch: calls that
+ * overlap in time on one GPU (on streams not ordered with each other) race
+ * and must not be made; calls ordered on one stream are safe. */
+int kv_retrieve_chunks_noalloc(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask,
+                               int n_seqs, kv_fmt fmt, int64_t* out_tokens, hipStream_t stream);
 
 /* Layerwise retrieve ([paper] layerwise pipeline; Table 2 start_load_kv /
  * wait_load_kv(layer)): as kv_retrieve_chunks but writes layer `layer` only,

@@ -25,7 +25,8 @@ import os
 
 __all__ = ["FMT_BF16", "FMT_FP8", "FMT_FP8_E5M2", "FMT_K16_V8", "FMT_CACHEGEN", "KvError", "Paged", "Seq", "Batch",
            "store", "store_layer", "store_layers", "store_cachegen", "retrieve_cachegen",
-           "retrieve", "retrieve_layer", "retrieve_layer_ex", "retrieve_layers", "take_faults", "copy_bytes",
+           "retrieve", "retrieve_noalloc", "retrieve_layer", "retrieve_layer_ex", "retrieve_layers", "take_faults",
+           "copy_bytes",
            "library_path", "load"]
 
 FMT_BF16 = 0          # K and V bf16, copied bit for bit
@@ -101,6 +102,7 @@ def load():
         "kv_store_chunks_cachegen": (ctypes.c_int, [P, S, ctypes.c_int, vp, vp, vp]),
         "kv_retrieve_workspace_bytes": (ctypes.c_size_t, [P]),
         "kv_retrieve_chunks_ws": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]),
+        "kv_retrieve_chunks_noalloc": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, vp, vp]),
         "kv_retrieve_chunks_cachegen": (ctypes.c_int, [P, S, vp, ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "kv_last_error": (ctypes.c_char_p, []),
         "kv_take_faults": (ctypes.c_int, []),
@@ -457,6 +459,17 @@ def retrieve(paged: Paged, seqs, masks=None, fmt: int = FMT_BF16, stream=None, w
         ws_ptr, ws_bytes = _workspace(workspace)
         _check(load().kv_retrieve_chunks_ws(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n, fmt, b.out,
                                             ws_ptr, ws_bytes, _stream_handle(stream)))
+    return [int(b.out[i]) for i in range(b.n)]
+
+
+def retrieve_noalloc(paged: Paged, seqs, masks=None, fmt: int = FMT_BF16, stream=None) -> list:
+    """retrieve in pool-address order with the library's own scratch array
+    instead of a caller's workspace (kv_retrieve_chunks_noalloc): no device
+    allocation anywhere in the call.  Calls that overlap on one GPU race.
+    Returns the tokens made available per sequence."""
+    b = _masked(paged, seqs, masks, fmt, stream)
+    _check(load().kv_retrieve_chunks_noalloc(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n, fmt, b.out,
+                                             _stream_handle(stream)))
     return [int(b.out[i]) for i in range(b.n)]
 
 

@@ -12,6 +12,7 @@
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "kv_cachegen.hpp"
@@ -537,6 +538,44 @@ int cachegen_setup(const kv_paged* p, const int32_t* key_bins, const int32_t* va
 
 constexpr Layout kCgLayout = {1, 1, 0};     // symbol sections addressed as 1-byte parts
 
+// Scratch of the ordered retrieve for callers that cannot allocate
+// (kv_retrieve_chunks_noalloc): the workspace kv_retrieve_chunks_ws takes
+// from its caller -- the inverse page map, then the sorted page list, one
+// 32-bit word per pool page each -- as one device array per GPU, sized for
+// pools of up to kScratchMaxPages pages (8 MiB).  Host code never names the
+// array in a kernel argument or a copy: in host code `scratch` is a host-side
+// stand-in, and the device address comes from hipGetSymbolAddress, once per
+// device (scratch_address).  Every kernel that uses it rewrites what it
+// reads (the inverse map is cleared by a kernel before it is filled; the
+// list is written whole), so a call does not depend on what the last call
+// left there.  Calls that use it concurrently on one GPU race.
+constexpr int64_t kScratchMaxPages = int64_t(1) << 20;
+__device__ __align__(256) uint32_t scratch[2 * kScratchMaxPages];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];     // device address of `scratch` on each device, once looked up
+
+// Device address of `scratch` on the current device (looked up on the
+// device's first call, with that device current).
+int scratch_address(void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KV_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(KV_EINVAL, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(KV_EHIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KV_OK;
+}
+
 int check_layers(const kv_paged* p, int32_t layer_begin, int32_t layer_end, const int32_t* max_workgroups)
 {
     if (layer_begin < 0 || layer_end > p->num_layers || layer_begin >= layer_end)
@@ -701,6 +740,38 @@ int kv_retrieve_chunks_ws(const kv_paged* paged, const kv_seq* seqs, const uint8
         return fail(KV_EINVAL, "workspace of %zu bytes needed (got %zu at %p)", need, workspace_bytes, workspace);
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return fail(KV_EINVAL, "workspace must be 256-byte aligned");
     rc = retrieve(paged, seqs, hit_mask, n_seqs, fmt, 0, paged->num_layers, out_tokens, stream, 0, workspace);
+    return rc == KV_OK ? ok() : rc;
+}
+
+int kv_retrieve_chunks_noalloc(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask,
+                               int n_seqs, kv_fmt fmt, int64_t* out_tokens, hipStream_t stream)
+{
+    int rc = check_paged(paged);
+    if (rc == KV_OK) rc = check_fmt(fmt);
+    if (rc == KV_OK) rc = check_seqs(paged, seqs, n_seqs);
+    if (rc != KV_OK) return rc;
+    if (paged->num_pages > kScratchMaxPages)
+        return fail(KV_EINVAL, "pool of %lld pages: the no-allocation retrieve's scratch holds pools of at most "
+                    "%lld pages (use kv_retrieve_chunks_ws with a workspace)", (long long)paged->num_pages,
+                    (long long)kScratchMaxPages);
+    {   // the host-side checks of the retrieve itself, before any HIP call
+        int64_t small[64];
+        int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
+        rc = hit_tokens(paged, seqs, hit_mask, n_seqs, n_tok);
+        if (rc == KV_OK) rc = check_ordered_fits(paged, n_tok, n_seqs);
+        if (n_tok != small) delete[] n_tok;
+        if (rc != KV_OK) return rc;
+    }
+    int dev = -1, sdev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess && stream != nullptr) e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return fail(KV_EHIP, "reading the device failed: %s", hipGetErrorString(e));
+    if (stream != nullptr && sdev != dev)
+        return fail(KV_EINVAL, "the stream belongs to device %d, the current device is %d", sdev, dev);
+    void* ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc != KV_OK) return rc;
+    rc = retrieve(paged, seqs, hit_mask, n_seqs, fmt, 0, paged->num_layers, out_tokens, stream, 0, ws);
     return rc == KV_OK ? ok() : rc;
 }
 

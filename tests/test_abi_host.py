@@ -417,3 +417,22 @@ def test_c_example_builds_against_the_header(tmp_path):
     from paged_kv_movement_amd import build
     out = build.build_c_example(str(tmp_path / "abi_c_example"))
     assert os.path.exists(out) and os.access(out, os.X_OK)
+
+
+def test_noalloc_retrieve_refuses_pools_beyond_its_scratch():
+    # the no-allocation retrieve keeps its page list in a fixed 8 MiB scratch
+    # array per GPU: pools of more than 2^20 pages are refused before any HIP
+    # call (no GPU here), and so are the usual malformed calls
+    L = _lib()
+    seqs = (kvm._KvSeq * 1)(_seq(0, 1000, 63))
+    m = (ctypes.c_uint8 * 4)(1, 1, 1, 1)
+    masks = (ctypes.c_void_p * 1)(ctypes.addressof(m))
+    out = (ctypes.c_int64 * 1)()
+    big = _paged(n=(1 << 20) + 1)
+    assert L.kv_retrieve_chunks_noalloc(ctypes.byref(big), seqs, masks, 1, kvm.FMT_BF16, out, None) == kvm.KV_EINVAL
+    assert "at most 1048576 pages" in L.kv_last_error().decode()
+    p = _paged(n=8192)
+    assert L.kv_retrieve_chunks_noalloc(ctypes.byref(p), seqs, masks, 1, kvm.FMT_CACHEGEN, out, None) == kvm.KV_EINVAL
+    assert L.kv_retrieve_chunks_noalloc(ctypes.byref(p), seqs, None, 1, kvm.FMT_BF16, out, None) == kvm.KV_EINVAL
+    bad = (kvm._KvSeq * 1)(_seq(100, 1000, 63))
+    assert L.kv_retrieve_chunks_noalloc(ctypes.byref(p), bad, masks, 1, kvm.FMT_BF16, out, None) == kvm.KV_EINVAL
