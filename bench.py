@@ -425,18 +425,20 @@ def bench_layers_only(args, store):
     kvm.store(paged, batch)
     torch.cuda.synchronize()
     copy = torch.cuda.Stream()
+    alt = torch.cuda.Stream() if args.alt_stream else None
     L, cap = w.num_layers, args.layers_only
     per_layer_bytes = 2 * 10240 * 2 * w.width * 2
     if store:
         def run():
-            kvm.store_layers(paged, batch, 0, L, stream=copy, max_workgroups=[cap] * L)
+            kvm.store_layers(paged, batch, 0, L, stream=copy, max_workgroups=[cap] * L, alt_stream=alt)
     else:
         def run():
-            kvm.retrieve_layers(paged, batch, 0, L, stream=copy, max_workgroups=[cap] * L)
+            kvm.retrieve_layers(paged, batch, 0, L, stream=copy, max_workgroups=[cap] * L, alt_stream=alt)
     ms = timed(copy, run, max(3, args.steps), warmup=args.warmup, stat="median")
     assert kvm.take_faults() == 0
     return {"metric": f"layer {'gather' if store else 'scatter'} alone, 32 layers per call",
             "workload": "layerwise-8b: 1 seq x 10240 tokens, 32 layers", "max_workgroups": cap,
+            "streams": 2 if alt is not None else 1,
             "calls": max(3, args.steps), "ms_per_32_layers_median": round(ms, 4),
             "layer_ms": round(ms / L, 4), "layer_GBps": round(per_layer_bytes / (ms / L / 1e3) / 1e9, 2)}
 
@@ -503,7 +505,14 @@ def bench_layerwise(args):
         kvm.retrieve_layers(paged, empty, 0, L, stream=copy, events=events)
         consume()
 
-    t_deps = {"per-layer-calls": wall(deps_per_call, reps), "one-call": wall(deps_one_call, reps)}
+    alt = torch.cuda.Stream()
+
+    def deps_two_streams():
+        kvm.retrieve_layers(paged, empty, 0, L, stream=copy, events=events, alt_stream=alt)
+        consume()
+
+    t_deps = {"per-layer-calls": wall(deps_per_call, reps), "one-call": wall(deps_one_call, reps),
+              "one-call-two-streams": wall(deps_two_streams, reps)}
     variants = []
     # (cap for layer 0, cap for layers 1..L-1): layer 0 has nothing to overlap
     # with, the others run beside the previous layer's GEMM
@@ -521,27 +530,32 @@ def bench_layerwise(args):
                 with torch.cuda.stream(compute):
                     torch.mm(x, wgt)
 
-        def copies_one_call():
-            kvm.retrieve_layers(paged, batch, 0, L, stream=copy, events=events, max_workgroups=caps)
+        def copies_one_call(a=None):
+            kvm.retrieve_layers(paged, batch, 0, L, stream=copy, events=events, max_workgroups=caps, alt_stream=a)
 
-        def both_one_call():
-            kvm.retrieve_layers(paged, batch, 0, L, stream=copy, events=events, max_workgroups=caps)
+        def both_one_call(a=None):
+            kvm.retrieve_layers(paged, batch, 0, L, stream=copy, events=events, max_workgroups=caps, alt_stream=a)
             consume()
 
         for form, copies, both in (("per-layer-calls", copies_per_call, both_per_call),
-                                   ("one-call", copies_one_call, both_one_call)):
+                                   ("one-call", copies_one_call, both_one_call),
+                                   ("one-call-two-streams", lambda: copies_one_call(alt),
+                                    lambda: both_one_call(alt))):
             t_copy, t_both = wall(copies, reps), wall(both, reps)
             v = {"form": form, "max_workgroups_layer0": first_cap, "max_workgroups": cap,
                  "t_copy_ms": round(t_copy, 3), "t_both_ms": round(t_both, 3),
                  "exposed_copy_ms": round(t_both - t_gemm, 3),
                  "exposed_vs_dependency_only_ms": round(t_both - t_deps[form], 3),
                  "overlap_efficiency": round((t_gemm + t_copy - t_both) / t_copy, 4)}
-            if form == "one-call":
-                # the 32 scatters back to back on the copy stream, HIP events
-                # around the one call (the GPU, not the host, sets the pace):
+            if form.startswith("one-call"):
+                # the 32 scatters back to back on the copy stream (every other
+                # one on the second stream), HIP events around the one call
+                # on the copy stream (the GPU, not the host, sets the pace):
                 # median of 20 after 3 warm-ups, per layer
+                a = alt if form.endswith("two-streams") else None
                 lm = timed(copy, lambda: kvm.retrieve_layers(paged, batch, 0, L, stream=copy,
-                                                             max_workgroups=[cap] * L), 20, stat="median") / L
+                                                             max_workgroups=[cap] * L, alt_stream=a),
+                           20, stat="median") / L
                 v["layer_scatter_ms"] = round(lm, 4)
                 v["layer_scatter_GBps"] = round(per_layer_bytes / (lm / 1e3) / 1e9, 2)
             variants.append(v)
@@ -573,7 +587,7 @@ def bench_layerwise_store(args):
 
     w = wl.layerwise8b()
     pool, paged, batch, arena = setup(w, kvm.FMT_BF16)
-    copy, compute = torch.cuda.Stream(), torch.cuda.Stream()
+    copy, compute, alt = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
     x = torch.randn(10240, 4096, device="cuda", dtype=torch.bfloat16)
     wgt = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16) * 0.01
     L = w.num_layers
@@ -613,25 +627,28 @@ def bench_layerwise_store(args):
                 copy.wait_event(done[l])
                 kvm.store_layer(paged, batch, l, stream=copy, max_workgroups=caps[l])
 
-        def stores_one_call():
-            kvm.store_layers(paged, batch, 0, L, stream=copy, max_workgroups=caps)
+        def stores_one_call(a=None):
+            kvm.store_layers(paged, batch, 0, L, stream=copy, max_workgroups=caps, alt_stream=a)
 
-        def both_one_call():
+        def both_one_call(a=None):
             for l in range(L):
                 with torch.cuda.stream(compute):
                     torch.mm(x, wgt)
                     done[l].record(compute)
-            kvm.store_layers(paged, batch, 0, L, stream=copy, wait_events=done, max_workgroups=caps)
+            kvm.store_layers(paged, batch, 0, L, stream=copy, wait_events=done, max_workgroups=caps, alt_stream=a)
 
         for form, stores, both in (("per-layer-calls", stores_per_call, both_per_call),
-                                   ("one-call", stores_one_call, both_one_call)):
+                                   ("one-call", stores_one_call, both_one_call),
+                                   ("one-call-two-streams", lambda: stores_one_call(alt),
+                                    lambda: both_one_call(alt))):
             t_store, t_both = wall(stores, reps), wall(both, reps)
             v = {"form": form, "max_workgroups": cap, "t_store_ms": round(t_store, 3), "t_both_ms": round(t_both, 3),
                  "exposed_store_ms": round(t_both - t_gemm, 3),
                  "overlap_efficiency": round((t_gemm + t_store - t_both) / t_store, 4)}
-            if form == "one-call":
-                lm = timed(copy, lambda: kvm.store_layers(paged, batch, 0, L, stream=copy,
-                                                          max_workgroups=[cap] * L), 20, stat="median") / L
+            if form.startswith("one-call"):
+                a = alt if form.endswith("two-streams") else None
+                lm = timed(copy, lambda: kvm.store_layers(paged, batch, 0, L, stream=copy, max_workgroups=[cap] * L,
+                                                          alt_stream=a), 20, stat="median") / L
                 v["layer_store_ms"] = round(lm, 4)
                 v["layer_store_GBps"] = round(per_layer_bytes / (lm / 1e3) / 1e9, 2)
             variants.append(v)
@@ -943,6 +960,8 @@ def main():
     ap.add_argument("--layers-only", type=int, default=None, metavar="CAP",
                     help="layerwise workloads: time only the 32 layer calls, one call for all layers, every "
                          "layer's grid capped at CAP workgroups (0: none); for kernel traces")
+    ap.add_argument("--alt-stream", action="store_true",
+                    help="with --layers-only: every other layer on a second stream (the calls' alt_stream)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -94,11 +94,12 @@ def load():
         "kv_chunk_tokens": (i64, [P, i64, i64, i64]),
         "kv_store_chunks": (ctypes.c_int, [P, S, ctypes.c_int, ctypes.c_int, vp]),
         "kv_store_layer": (ctypes.c_int, [P, S, ctypes.c_int, ctypes.c_int, i32, i32, vp, vp]),
-        "kv_store_layers": (ctypes.c_int, [P, S, ctypes.c_int, ctypes.c_int, i32, i32, vp, vp, vp, vp]),
+        "kv_store_layers": (ctypes.c_int, [P, S, ctypes.c_int, ctypes.c_int, i32, i32, vp, vp, vp, vp, vp]),
         "kv_retrieve_chunks": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, vp, vp]),
         "kv_retrieve_layer": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, i32, vp, vp]),
         "kv_retrieve_layer_ex": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, i32, vp, i32, vp, vp]),
-        "kv_retrieve_layers": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, i32, i32, vp, vp, vp, vp]),
+        "kv_retrieve_layers": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, i32, i32, vp, vp, vp, vp,
+                                              vp]),
         "kv_store_chunks_cachegen": (ctypes.c_int, [P, S, ctypes.c_int, vp, vp, vp]),
         "kv_retrieve_workspace_bytes": (ctypes.c_size_t, [P]),
         "kv_retrieve_chunks_ws": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]),
@@ -368,6 +369,15 @@ def store_layer(paged: Paged, seqs, layer: int, fmt: int = FMT_BF16, stream=None
                                  _stream_handle(stream), _event_handle(event, stream)))
 
 
+def _alt_handle(alt_stream) -> int | None:
+    """Handle of a layer-range call's second stream (None: none)."""
+    if alt_stream is None:
+        return None
+    h = alt_stream.cuda_stream if hasattr(alt_stream, "cuda_stream") else int(alt_stream)
+    _need(h != 0, "alt_stream must be a stream of its own, not the null stream")
+    return h
+
+
 def _layer_arrays(n, max_workgroups, events, stream):
     """Host arrays of a layer-range call: caps (or None) and event handles (or None)."""
     caps = None
@@ -383,12 +393,15 @@ def _layer_arrays(n, max_workgroups, events, stream):
 
 
 def store_layers(paged: Paged, seqs, layer_begin: int, layer_end: int, fmt: int = FMT_BF16, stream=None,
-                 wait_events=None, events=None, max_workgroups=None) -> None:
+                 wait_events=None, events=None, max_workgroups=None, alt_stream=None) -> None:
     """Gather layers [layer_begin, layer_end) on ``stream`` in one call
     (kv_store_layers): before layer l, wait for ``wait_events[l - layer_begin]``
     (torch.cuda.Event, already recorded by the producer); after it, record
-    ``events[l - layer_begin]``.  ``max_workgroups``: one cap per layer."""
+    ``events[l - layer_begin]``.  ``max_workgroups``: one cap per layer.
+    ``alt_stream``: a second torch stream that takes every other layer, so
+    consecutive layers' kernels may overlap."""
     b = _batch(paged, seqs, fmt, stream)
+    b.used_on(alt_stream)
     n = layer_end - layer_begin
     caps, evs = _layer_arrays(n, max_workgroups, events, stream)
     waits = None
@@ -397,7 +410,7 @@ def store_layers(paged: Paged, seqs, layer_begin: int, layer_end: int, fmt: int 
         _need(all(e.cuda_event for e in wait_events), "wait events must have been recorded")
         waits = (ctypes.c_void_p * n)(*[e.cuda_event for e in wait_events])
     _check(load().kv_store_layers(ctypes.byref(paged.c), b.arr, b.n, fmt, layer_begin, layer_end, caps,
-                                  _stream_handle(stream), waits, evs))
+                                  _stream_handle(stream), _alt_handle(alt_stream), waits, evs))
 
 
 def _workspace(workspace):
@@ -503,15 +516,18 @@ def retrieve_layer_ex(paged: Paged, seqs, layer: int, masks=None, fmt: int = FMT
 
 
 def retrieve_layers(paged: Paged, seqs, layer_begin: int, layer_end: int, masks=None, fmt: int = FMT_BF16,
-                    stream=None, events=None, max_workgroups=None) -> list:
+                    stream=None, events=None, max_workgroups=None, alt_stream=None) -> list:
     """Scatter layers [layer_begin, layer_end) of the leading hit chunks on
     ``stream`` in one call, recording ``events[l - layer_begin]`` after layer
     l (kv_retrieve_layers).  ``max_workgroups``: one cap per layer, or None.
-    Returns the tokens made available per sequence."""
+    ``alt_stream``: a second torch stream that takes every other layer, so
+    consecutive layers' kernels may overlap.  Returns the tokens made
+    available per sequence."""
     b = _masked(paged, seqs, masks, fmt, stream)
+    b.used_on(alt_stream)
     caps, evs = _layer_arrays(layer_end - layer_begin, max_workgroups, events, stream)
     _check(load().kv_retrieve_layers(ctypes.byref(paged.c), b.arr, b._mask_ptrs, b.n, fmt, layer_begin,
-                                     layer_end, caps, b.out, _stream_handle(stream), evs))
+                                     layer_end, caps, b.out, _stream_handle(stream), _alt_handle(alt_stream), evs))
     return [int(b.out[i]) for i in range(b.n)]
 
 

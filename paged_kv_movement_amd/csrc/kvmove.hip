@@ -595,14 +595,74 @@ int record(hipEvent_t ev, hipStream_t stream)
     return KV_OK;
 }
 
-// Layers [layer_begin, layer_end) of a retrieve, one scatter launch each on
-// copy_stream (max_workgroups[k] caps layer_begin + k's grid; NULL: no cap),
-// each followed by a record of layer_done[k] -- also when nothing hits.  The
-// hit plan is made once for all of them.  Host arguments are checked before
-// anything is enqueued.
+// The streams of a layer-range call: layer k of the range runs on
+// lane[k % n].  With an alternate stream (n = 2) the alternate first waits
+// for what the caller enqueued on the main stream before the call (fork),
+// and the main stream ends waiting for the alternate's last layer (join), so
+// work the caller enqueues on the main stream after the call still follows
+// every layer, while consecutive layers' kernels, on two streams, may
+// overlap: one layer's workgroups start while the last ones of the layer
+// before are still finishing.  The fork and join events are the call's own.
+struct LayerLanes {
+    hipStream_t lane[2];
+    int n;
+    hipEvent_t join;
+};
+
+// Both streams must belong to the current device (the events are made there).
+int open_lanes(LayerLanes& ll, hipStream_t main, hipStream_t alt)
+{
+    ll.lane[0] = ll.lane[1] = main;
+    ll.n = 1;
+    ll.join = nullptr;
+    if (alt == nullptr) return KV_OK;
+    if (alt == main) return fail(KV_EINVAL, "alt_stream is the main stream");
+    int dev = -1, d_main = -1, d_alt = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipStreamGetDevice(alt, &d_alt);
+    if (e == hipSuccess && main != nullptr) e = hipStreamGetDevice(main, &d_main);
+    if (e != hipSuccess) return fail(KV_EHIP, "reading the device failed: %s", hipGetErrorString(e));
+    if (d_alt != dev || (main != nullptr && d_main != dev))
+        return fail(KV_EINVAL, "the streams belong to devices %d and %d, the current device is %d",
+                    main != nullptr ? d_main : dev, d_alt, dev);
+    hipEvent_t fork = nullptr;
+    e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ll.join, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(fork, main);
+    if (e == hipSuccess) e = hipStreamWaitEvent(alt, fork, 0);
+    if (fork != nullptr) (void)hipEventDestroy(fork);       // released once its wait is done
+    if (e != hipSuccess) {
+        if (ll.join != nullptr) (void)hipEventDestroy(ll.join);
+        ll.join = nullptr;
+        return fail(KV_EHIP, "forking onto alt_stream failed: %s", hipGetErrorString(e));
+    }
+    ll.lane[1] = alt;
+    ll.n = 2;
+    return KV_OK;
+}
+
+// Joins the alternate stream back into the main one (also after a failed
+// launch, so the main stream's order holds); returns rc, or the join's error.
+int close_lanes(LayerLanes& ll, int rc)
+{
+    if (ll.n == 1) return rc;
+    hipError_t e = hipEventRecord(ll.join, ll.lane[1]);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ll.lane[0], ll.join, 0);
+    (void)hipEventDestroy(ll.join);
+    ll.join = nullptr;
+    if (e != hipSuccess && rc == KV_OK) return fail(KV_EHIP, "joining alt_stream failed: %s", hipGetErrorString(e));
+    return rc;
+}
+
+// Layers [layer_begin, layer_end) of a retrieve, one scatter launch each
+// (max_workgroups[k] caps layer_begin + k's grid; NULL: no cap), each
+// followed by a record of layer_done[k] -- also when nothing hits -- on
+// copy_stream, or alternately on copy_stream and alt_stream (LayerLanes).
+// The hit plan is made once for all of them.  Host arguments are checked
+// before anything is enqueued.
 int retrieve_layers(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs, int fmt,
                     int32_t layer_begin, int32_t layer_end, const int32_t* max_workgroups, int64_t* out_tokens,
-                    hipStream_t copy_stream, const hipEvent_t* layer_done)
+                    hipStream_t copy_stream, hipStream_t alt_stream, const hipEvent_t* layer_done)
 {
     int rc = check_paged(paged);
     if (rc == KV_OK) rc = check_fmt(fmt);
@@ -612,11 +672,17 @@ int retrieve_layers(const kv_paged* paged, const kv_seq* seqs, const uint8_t* co
     int64_t small[64];
     int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
     rc = hit_tokens(paged, seqs, hit_mask, n_seqs, n_tok);
-    const Plan full = scatter_plan(fmt, false, false), capped = scatter_plan(fmt, true, false);
-    for (int32_t l = layer_begin; l < layer_end && rc == KV_OK; ++l) {
-        const int32_t cap = max_workgroups != nullptr ? max_workgroups[l - layer_begin] : 0;
-        rc = run_plan(cap > 0 ? capped : full, fmt, paged, seqs, n_tok, n_seqs, l, 1, copy_stream, cap);
-        if (rc == KV_OK && layer_done != nullptr) rc = record(layer_done[l - layer_begin], copy_stream);
+    LayerLanes ll;
+    if (rc == KV_OK) rc = open_lanes(ll, copy_stream, alt_stream);
+    if (rc == KV_OK) {
+        const Plan full = scatter_plan(fmt, false, false), capped = scatter_plan(fmt, true, false);
+        for (int32_t l = layer_begin; l < layer_end && rc == KV_OK; ++l) {
+            const int32_t k = l - layer_begin, cap = max_workgroups != nullptr ? max_workgroups[k] : 0;
+            hipStream_t st = ll.lane[k % ll.n];
+            rc = run_plan(cap > 0 ? capped : full, fmt, paged, seqs, n_tok, n_seqs, l, 1, st, cap);
+            if (rc == KV_OK && layer_done != nullptr) rc = record(layer_done[k], st);
+        }
+        rc = close_lanes(ll, rc);
     }
     if (rc == KV_OK && out_tokens != nullptr)
         for (int i = 0; i < n_seqs; ++i) out_tokens[i] = n_tok[i];
@@ -625,11 +691,12 @@ int retrieve_layers(const kv_paged* paged, const kv_seq* seqs, const uint8_t* co
 }
 
 // Layers [layer_begin, layer_end) of a store, one gather launch each on
-// stream: first a wait on wait_before[k] (if given), then the launch, then a
-// record of layer_done[k] (if given).
+// stream, or alternately on stream and alt_stream (LayerLanes): first a wait
+// on wait_before[k] (if given), then the launch, then a record of
+// layer_done[k] (if given).
 int store_layers(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int fmt, int32_t layer_begin,
-                 int32_t layer_end, const int32_t* max_workgroups, hipStream_t stream, const hipEvent_t* wait_before,
-                 const hipEvent_t* layer_done)
+                 int32_t layer_end, const int32_t* max_workgroups, hipStream_t stream, hipStream_t alt_stream,
+                 const hipEvent_t* wait_before, const hipEvent_t* layer_done)
 {
     int rc = check_paged(paged);
     if (rc == KV_OK) rc = check_fmt(fmt);
@@ -639,15 +706,21 @@ int store_layers(const kv_paged* paged, const kv_seq* seqs, int n_seqs, int fmt,
     int64_t small[64];
     int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
     for (int i = 0; i < n_seqs; ++i) n_tok[i] = seqs[i].tok_end - seqs[i].tok_start;
-    const Plan full = gather_plan(paged, fmt, false), capped = gather_plan(paged, fmt, true);
-    for (int32_t l = layer_begin; l < layer_end && rc == KV_OK; ++l) {
-        const int32_t cap = max_workgroups != nullptr ? max_workgroups[l - layer_begin] : 0;
-        if (wait_before != nullptr && wait_before[l - layer_begin] != nullptr) {
-            const hipError_t e = hipStreamWaitEvent(stream, wait_before[l - layer_begin], 0);
-            if (e != hipSuccess) rc = fail(KV_EHIP, "hipStreamWaitEvent failed: %s", hipGetErrorString(e));
+    LayerLanes ll;
+    rc = open_lanes(ll, stream, alt_stream);
+    if (rc == KV_OK) {
+        const Plan full = gather_plan(paged, fmt, false), capped = gather_plan(paged, fmt, true);
+        for (int32_t l = layer_begin; l < layer_end && rc == KV_OK; ++l) {
+            const int32_t k = l - layer_begin, cap = max_workgroups != nullptr ? max_workgroups[k] : 0;
+            hipStream_t st = ll.lane[k % ll.n];
+            if (wait_before != nullptr && wait_before[k] != nullptr) {
+                const hipError_t e = hipStreamWaitEvent(st, wait_before[k], 0);
+                if (e != hipSuccess) rc = fail(KV_EHIP, "hipStreamWaitEvent failed: %s", hipGetErrorString(e));
+            }
+            if (rc == KV_OK) rc = run_plan(cap > 0 ? capped : full, fmt, paged, seqs, n_tok, n_seqs, l, 1, st, cap);
+            if (rc == KV_OK && layer_done != nullptr) rc = record(layer_done[k], st);
         }
-        if (rc == KV_OK) rc = run_plan(cap > 0 ? capped : full, fmt, paged, seqs, n_tok, n_seqs, l, 1, stream, cap);
-        if (rc == KV_OK && layer_done != nullptr) rc = record(layer_done[l - layer_begin], stream);
+        rc = close_lanes(ll, rc);
     }
     if (n_tok != small) delete[] n_tok;
     return rc == KV_OK ? ok() : rc;
@@ -702,7 +775,8 @@ int kv_store_chunks(const kv_paged* paged, const kv_seq* seqs, int n_seqs, kv_fm
 int kv_store_layer(const kv_paged* paged, const kv_seq* seqs, int n_seqs, kv_fmt fmt, int32_t layer,
                    int32_t max_workgroups, hipStream_t stream, hipEvent_t layer_done)
 {
-    return store_layers(paged, seqs, n_seqs, fmt, layer, layer + 1, &max_workgroups, stream, nullptr, &layer_done);
+    return store_layers(paged, seqs, n_seqs, fmt, layer, layer + 1, &max_workgroups, stream, nullptr, nullptr,
+                        &layer_done);
 }
 
 int kv_retrieve_chunks(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask,
@@ -780,30 +854,31 @@ int kv_retrieve_layer_ex(const kv_paged* paged, const kv_seq* seqs, const uint8_
                          hipStream_t copy_stream, hipEvent_t layer_done)
 {
     return retrieve_layers(paged, seqs, hit_mask, n_seqs, fmt, layer, layer + 1, &max_workgroups, out_tokens,
-                           copy_stream, &layer_done);
+                           copy_stream, nullptr, &layer_done);
 }
 
 int kv_retrieve_layer(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
                       kv_fmt fmt, int32_t layer, hipStream_t copy_stream, hipEvent_t layer_done)
 {
     return retrieve_layers(paged, seqs, hit_mask, n_seqs, fmt, layer, layer + 1, nullptr, nullptr, copy_stream,
-                           &layer_done);
+                           nullptr, &layer_done);
 }
 
 int kv_retrieve_layers(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
                        kv_fmt fmt, int32_t layer_begin, int32_t layer_end, const int32_t* max_workgroups,
-                       int64_t* out_tokens, hipStream_t copy_stream, const hipEvent_t* layer_done)
+                       int64_t* out_tokens, hipStream_t copy_stream, hipStream_t alt_stream,
+                       const hipEvent_t* layer_done)
 {
     return retrieve_layers(paged, seqs, hit_mask, n_seqs, fmt, layer_begin, layer_end, max_workgroups, out_tokens,
-                           copy_stream, layer_done);
+                           copy_stream, alt_stream, layer_done);
 }
 
 int kv_store_layers(const kv_paged* paged, const kv_seq* seqs, int n_seqs, kv_fmt fmt, int32_t layer_begin,
-                    int32_t layer_end, const int32_t* max_workgroups, hipStream_t stream,
+                    int32_t layer_end, const int32_t* max_workgroups, hipStream_t stream, hipStream_t alt_stream,
                     const hipEvent_t* wait_before, const hipEvent_t* layer_done)
 {
-    return store_layers(paged, seqs, n_seqs, fmt, layer_begin, layer_end, max_workgroups, stream, wait_before,
-                        layer_done);
+    return store_layers(paged, seqs, n_seqs, fmt, layer_begin, layer_end, max_workgroups, stream, alt_stream,
+                        wait_before, layer_done);
 }
 
 int64_t kv_chunk_tokens(const kv_paged* paged, int64_t tok_start, int64_t tok_end, int64_t c)

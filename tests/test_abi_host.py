@@ -149,7 +149,7 @@ def test_retrieve_with_no_hits_launches_nothing():
         assert L.kv_retrieve_layer(ctypes.byref(p), seqs, masks, 2, kvm.FMT_FP8, layer, None, None) == kvm.KV_OK
     # every layer in one call, no events: nothing is enqueued either
     out[0] = out[1] = -7
-    assert L.kv_retrieve_layers(ctypes.byref(p), seqs, masks, 2, kvm.FMT_BF16, 0, 32, None, out, None,
+    assert L.kv_retrieve_layers(ctypes.byref(p), seqs, masks, 2, kvm.FMT_BF16, 0, 32, None, out, None, None,
                                 None) == kvm.KV_OK
     assert list(out) == [0, 0]
 
@@ -173,13 +173,22 @@ def test_retrieve_rejections():
     assert L.kv_retrieve_layer(ctypes.byref(p), seqs, None, 1, 0, 0, None, None) == kvm.KV_EINVAL
     # layer ranges: empty, reversed or outside [0, L), and negative caps
     for lo, hi in ((3, 3), (5, 4), (-1, 2), (30, 33)):
-        assert L.kv_retrieve_layers(ctypes.byref(p), seqs, masks, 1, 0, lo, hi, None, out, None,
+        assert L.kv_retrieve_layers(ctypes.byref(p), seqs, masks, 1, 0, lo, hi, None, out, None, None,
                                     None) == kvm.KV_EINVAL
-        assert L.kv_store_layers(ctypes.byref(p), seqs, 1, 0, lo, hi, None, None, None, None) == kvm.KV_EINVAL
+        assert L.kv_store_layers(ctypes.byref(p), seqs, 1, 0, lo, hi, None, None, None, None,
+                                 None) == kvm.KV_EINVAL
     caps = (ctypes.c_int32 * 4)(0, 8, -1, 8)
-    assert L.kv_retrieve_layers(ctypes.byref(p), seqs, masks, 1, 0, 4, 8, caps, out, None, None) == kvm.KV_EINVAL
+    assert L.kv_retrieve_layers(ctypes.byref(p), seqs, masks, 1, 0, 4, 8, caps, out, None, None,
+                                None) == kvm.KV_EINVAL
     assert "max_workgroups[2]" in L.kv_last_error().decode()
-    assert L.kv_store_layers(ctypes.byref(p), seqs, 1, 0, 4, 8, caps, None, None, None) == kvm.KV_EINVAL
+    assert L.kv_store_layers(ctypes.byref(p), seqs, 1, 0, 4, 8, caps, None, None, None, None) == kvm.KV_EINVAL
+    # a second stream that is the first one is refused before any HIP call
+    same = ctypes.c_void_p(0x1000)
+    assert L.kv_retrieve_layers(ctypes.byref(p), seqs, masks, 1, 0, 0, 4, None, out, same, same,
+                                None) == kvm.KV_EINVAL
+    assert "alt_stream" in L.kv_last_error().decode()
+    assert L.kv_store_layers(ctypes.byref(p), seqs, 1, 0, 0, 4, None, same, same, None, None) == kvm.KV_EINVAL
+    assert "alt_stream" in L.kv_last_error().decode()
     bad = (kvm._KvSeq * 1)(_seq(100, 1000, 63))
     assert L.kv_retrieve_chunks(ctypes.byref(p), bad, masks, 1, 0, out, None) == kvm.KV_EINVAL
 

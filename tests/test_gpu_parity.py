@@ -168,6 +168,32 @@ def test_layerwise_on_copy_stream_equals_full(fmt):
     _sync()
     assert np.array_equal(host_from_dev_pool(pool), prev)
     assert np.array_equal(host_from_dev_pool(snaps), prev)
+    # ... and with a second stream taking every other layer: the sentinel
+    # fill enqueued on the copy stream just before the call (behind a GEMM,
+    # not waited for) must land before every layer, the per-layer snapshots
+    # must see each layer final, and a copy enqueued on the copy stream after
+    # the call must see every layer
+    alt = torch.cuda.Stream()
+    events = [torch.cuda.Event() for _ in range(w.num_layers)]
+    snaps.zero_()
+    whole = torch.empty_like(pool)
+    x = torch.randn(4096, 4096, device="cuda", dtype=torch.bfloat16)
+    _sync()
+    with torch.cuda.stream(copy):
+        torch.mm(x, x)
+        pool.view(torch.int16).fill_(0x0F0F)
+    assert kvm.retrieve_layers(paged, batch, 0, w.num_layers, fmt=fmt, stream=copy, events=events,
+                               alt_stream=alt) == [512, 274]
+    with torch.cuda.stream(copy):
+        whole.copy_(pool)
+    for l in range(w.num_layers):
+        consumer.wait_event(events[l])
+        with torch.cuda.stream(consumer):
+            snaps[l].copy_(pool[l])
+    _sync()
+    assert np.array_equal(host_from_dev_pool(pool), prev)
+    assert np.array_equal(host_from_dev_pool(snaps), prev)
+    assert np.array_equal(host_from_dev_pool(whole), prev)
     assert kvm.take_faults() == 0
 
 
@@ -562,7 +588,7 @@ def test_consumer_waiting_on_layer_event_sees_the_whole_layer(fmt):
                    [s.hit_mask for s in w.seqs], copy=False)
 
 
-@pytest.mark.parametrize("form", ["per-layer-calls", "one-call"])
+@pytest.mark.parametrize("form", ["per-layer-calls", "one-call", "one-call-two-streams"])
 @pytest.mark.parametrize("fmt", [BF16, FP8, K16V8], ids=["bf16", "fp8", "k16v8"])
 def test_store_waiting_on_producer_event_sees_the_layer(fmt, form):
     # the producer (compute stream) writes layer l of the pool after a GEMM and
@@ -591,6 +617,9 @@ def test_store_waiting_on_producer_event_sees_the_layer(fmt, form):
             kvm.store_layer(paged, batch, l, fmt=fmt, stream=copy)
     if form == "one-call":
         kvm.store_layers(paged, batch, 0, w.num_layers, fmt=fmt, stream=copy, wait_events=done)
+    if form == "one-call-two-streams":
+        kvm.store_layers(paged, batch, 0, w.num_layers, fmt=fmt, stream=copy, wait_events=done,
+                         alt_stream=torch.cuda.Stream())
     torch.cuda.synchronize()
     assert kvm.take_faults() == 0
     check_store(w, arr, cs, fmt)

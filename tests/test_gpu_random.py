@@ -37,9 +37,10 @@ def _case(i):
     pages_needed = sum(-(-e // P) for (_, e) in ranges)
     num_pages = pages_needed + int(rng.integers(1, 64))
     fmt = FORMATS[int(rng.integers(0, len(FORMATS)))]
-    store_form = rng.choice(["full", "layers", "layer-range"]) if fmt != kvm.FMT_CACHEGEN else "full"
-    retrieve_form = rng.choice(["chunk", "ordered", "layers", "layer-range"]) if fmt != kvm.FMT_CACHEGEN else \
-        rng.choice(["chunk", "ordered"])
+    store_form = rng.choice(["full", "layers", "layer-range", "layer-range-2s"]) if fmt != kvm.FMT_CACHEGEN \
+        else "full"
+    retrieve_form = rng.choice(["chunk", "ordered", "layers", "layer-range", "layer-range-2s"]) \
+        if fmt != kvm.FMT_CACHEGEN else rng.choice(["chunk", "ordered"])
     where = rng.choice(["device", "device", "host"])
     cap = int(rng.choice([0, 0, 1, 3, 17]))
     w = wl.custom(f"rand{i}", 9000 + i, L, H, D, num_pages, ranges, masks=masks, page_size=P, chunk_size=C,
@@ -61,10 +62,12 @@ def test_random_case(i):
         kvm.store_cachegen(paged, batch, kb, vb, stream=s)
     elif store_form == "full":
         kvm.store(paged, batch, fmt, stream=s)
-    elif store_form == "layer-range":
-        # every layer in one call, the first at full width and the rest capped
+    elif store_form.startswith("layer-range"):
+        # every layer in one call, the first at full width and the rest
+        # capped; with "-2s" every other layer on a second stream
         kvm.store_layers(paged, batch, 0, w.num_layers, fmt=fmt, stream=s,
-                         max_workgroups=[0] + [cap] * (w.num_layers - 1))
+                         max_workgroups=[0] + [cap] * (w.num_layers - 1),
+                         alt_stream=torch.cuda.Stream() if store_form.endswith("-2s") else None)
     else:
         for l in range(w.num_layers):
             kvm.store_layer(paged, batch, l, fmt=fmt, stream=s, max_workgroups=cap)
@@ -82,9 +85,10 @@ def test_random_case(i):
     elif retrieve_form == "layers":
         for l in range(w.num_layers):
             n = kvm.retrieve_layer_ex(paged, batch, l, fmt=fmt, stream=s, max_workgroups=cap)
-    elif retrieve_form == "layer-range":
+    elif retrieve_form.startswith("layer-range"):
         n = kvm.retrieve_layers(paged, batch, 0, w.num_layers, fmt=fmt, stream=s,
-                                max_workgroups=[0] + [cap] * (w.num_layers - 1))
+                                max_workgroups=[0] + [cap] * (w.num_layers - 1),
+                                alt_stream=torch.cuda.Stream() if retrieve_form.endswith("-2s") else None)
     else:
         n = kvm.retrieve(paged, batch, fmt=fmt, stream=s, workspace=ws)
     s.synchronize()

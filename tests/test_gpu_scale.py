@@ -78,11 +78,12 @@ def test_full_llama70b_store_and_retrieve():
     _full_bf16(wl.llama70b(), [32768])
 
 
-@pytest.mark.parametrize("form", ["per-layer-calls", "one-call"])
+@pytest.mark.parametrize("form", ["per-layer-calls", "one-call", "one-call-two-streams"])
 def test_full_layerwise_8b_with_compute_stream(form):
     # one 10240-token sequence retrieved layer by layer on a copy stream, each
     # layer's event gating a bf16 GEMM (tokens x 4096 x 4096) on the compute
-    # stream; the layers enqueued one call each, or all by one call
+    # stream; the layers enqueued one call each, or all by one call (with
+    # every other layer on a second stream)
     w = wl.layerwise8b()
     say("case", w.name, form)
     pool = wl.device_pool(w)
@@ -99,9 +100,10 @@ def test_full_layerwise_8b_with_compute_stream(form):
     # layer 0 at full width, the rest on a capped grid (as the benchmark's
     # overlap variants do)
     caps = [0] + [128] * (w.num_layers - 1)
-    if form == "one-call":
+    if form.startswith("one-call"):
+        alt = torch.cuda.Stream() if form.endswith("two-streams") else None
         assert kvm.retrieve_layers(paged, batch, 0, w.num_layers, stream=copy, events=events,
-                                   max_workgroups=caps) == [10240]
+                                   max_workgroups=caps, alt_stream=alt) == [10240]
     for l in range(w.num_layers):
         if form == "per-layer-calls":
             assert kvm.retrieve_layer_ex(paged, batch, l, stream=copy, event=events[l],
@@ -202,7 +204,7 @@ def test_full_fp8_8b_every_chunk_and_whole_pool(fmt):
     _free()
 
 
-@pytest.mark.parametrize("form", ["per-layer-calls", "one-call"])
+@pytest.mark.parametrize("form", ["per-layer-calls", "one-call", "one-call-two-streams"])
 def test_full_layerwise_store_8b_behind_compute(form):
     # prefill-style: layer l's KV is stored on a copy stream once layer l's
     # GEMM (the producer) is done, while layer l+1 computes; one store call
@@ -225,9 +227,10 @@ def test_full_layerwise_store_8b_behind_compute(form):
         if form == "per-layer-calls":
             copy.wait_event(done[l])
             kvm.store_layer(paged, batch, l, stream=copy, event=stored[l], max_workgroups=caps[l])
-    if form == "one-call":
+    if form.startswith("one-call"):
+        alt = torch.cuda.Stream() if form.endswith("two-streams") else None
         kvm.store_layers(paged, batch, 0, w.num_layers, stream=copy, wait_events=done, events=stored,
-                         max_workgroups=caps)
+                         max_workgroups=caps, alt_stream=alt)
     sync()
     assert kvm.take_faults() == 0
     arr = host_from_dev_pool(pool)
