@@ -445,12 +445,14 @@ def bench_layers_only(args, store):
 
 def bench_layerwise(args):
     """32 layer-by-layer scatters on a copy stream, each gating a bf16 GEMM
-    (10240 x 4096 x 4096) on a compute stream; the copy of layer i+1 runs
-    while layer i computes.  Two ways to enqueue the scatters: one call per
-    layer (kv_retrieve_layer_ex, as an engine calling wait/load per layer
-    does) and one call for all layers (kv_retrieve_layers, the start of the
-    whole load at once), each for several caps on the scatter's workgroups
-    (0 = one per tile)."""
+    (10240 x 4096 x 4096) on a compute stream.  Ways to enqueue the
+    scatters: one call per layer (kv_retrieve_layer_ex, as an engine calling
+    wait/load per layer does), either all at once or paced so that layer
+    i+1's scatter starts with layer i's GEMM (the copy stream waits on an
+    event the compute stream records before each GEMM); one call for all
+    layers (kv_retrieve_layers, the start of the whole load at once), on one
+    stream or two.  Each for several caps on the scatter's workgroups (0 =
+    one per tile)."""
     import numpy as np
     import torch
     import paged_kv_movement_amd as kvm
@@ -501,6 +503,23 @@ def bench_layerwise(args):
             with torch.cuda.stream(compute):
                 torch.mm(x, wgt)
 
+    # the pages' pipeline, layer l+1 loading while layer l computes: the copy
+    # stream waits for the start of GEMM l-1 before layer l's scatter, so
+    # each scatter runs beside one GEMM instead of all of them at once
+    started = [torch.cuda.Event() for _ in range(L)]
+
+    def paced(b, cap_of):
+        def run():
+            for l in range(L):
+                if l > 0:
+                    copy.wait_event(started[l - 1])
+                kvm.retrieve_layer_ex(paged, b, l, stream=copy, event=events[l], max_workgroups=cap_of(l))
+                compute.wait_event(events[l])
+                started[l].record(compute)
+                with torch.cuda.stream(compute):
+                    torch.mm(x, wgt)
+        return run
+
     def deps_one_call():
         kvm.retrieve_layers(paged, empty, 0, L, stream=copy, events=events)
         consume()
@@ -512,7 +531,8 @@ def bench_layerwise(args):
         consume()
 
     t_deps = {"per-layer-calls": wall(deps_per_call, reps), "one-call": wall(deps_one_call, reps),
-              "one-call-two-streams": wall(deps_two_streams, reps)}
+              "one-call-two-streams": wall(deps_two_streams, reps),
+              "per-layer-calls-paced": wall(paced(empty, lambda l: 0), reps)}
     variants = []
     # (cap for layer 0, cap for layers 1..L-1): layer 0 has nothing to overlap
     # with, the others run beside the previous layer's GEMM
@@ -538,6 +558,7 @@ def bench_layerwise(args):
             consume()
 
         for form, copies, both in (("per-layer-calls", copies_per_call, both_per_call),
+                                   ("per-layer-calls-paced", copies_per_call, paced(batch, lambda l: caps[l])),
                                    ("one-call", copies_one_call, both_one_call),
                                    ("one-call-two-streams", lambda: copies_one_call(alt),
                                     lambda: both_one_call(alt))):

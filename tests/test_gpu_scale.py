@@ -78,12 +78,13 @@ def test_full_llama70b_store_and_retrieve():
     _full_bf16(wl.llama70b(), [32768])
 
 
-@pytest.mark.parametrize("form", ["per-layer-calls", "one-call", "one-call-two-streams"])
+@pytest.mark.parametrize("form", ["per-layer-calls", "per-layer-calls-paced", "one-call", "one-call-two-streams"])
 def test_full_layerwise_8b_with_compute_stream(form):
     # one 10240-token sequence retrieved layer by layer on a copy stream, each
     # layer's event gating a bf16 GEMM (tokens x 4096 x 4096) on the compute
-    # stream; the layers enqueued one call each, or all by one call (with
-    # every other layer on a second stream)
+    # stream; the layers enqueued one call each (paced: layer l's scatter
+    # waits for the start of GEMM l-1), or all by one call (with every other
+    # layer on a second stream)
     w = wl.layerwise8b()
     say("case", w.name, form)
     pool = wl.device_pool(w)
@@ -104,11 +105,15 @@ def test_full_layerwise_8b_with_compute_stream(form):
         alt = torch.cuda.Stream() if form.endswith("two-streams") else None
         assert kvm.retrieve_layers(paged, batch, 0, w.num_layers, stream=copy, events=events,
                                    max_workgroups=caps, alt_stream=alt) == [10240]
+    started = [torch.cuda.Event() for _ in range(w.num_layers)]
     for l in range(w.num_layers):
-        if form == "per-layer-calls":
+        if form == "per-layer-calls-paced" and l > 0:
+            copy.wait_event(started[l - 1])
+        if form.startswith("per-layer-calls"):
             assert kvm.retrieve_layer_ex(paged, batch, l, stream=copy, event=events[l],
                                          max_workgroups=caps[l]) == [10240]
         compute.wait_event(events[l])
+        started[l].record(compute)
         with torch.cuda.stream(compute):
             outs.append(torch.mm(x, wgt))
     sync()
