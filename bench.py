@@ -299,11 +299,14 @@ def bench_llama8b(args):
     ret_bytes = 2 * ret_tokens * bpt
 
     # the retrieve visits its pages in pool-address order (kv_retrieve_chunks_ws)
-    # unless --retrieve-order chunk asks for the chunk-major kv_retrieve_chunks
+    # unless --retrieve-order chunk asks for the chunk-major kv_retrieve_chunks;
+    # the store gathers through its address plan (kv_store_chunks_ws) unless
+    # --store-plan off asks for kv_store_chunks
     ws = paged.new_workspace() if args.retrieve_order == "address" else None
+    sws = batch.new_store_workspace() if args.store_plan == "on" else None
 
     def store():
-        kvm.store(paged, batch, stream=stream)
+        kvm.store(paged, batch, stream=stream, workspace=sws)
 
     def retrieve():
         kvm.retrieve(paged, batch, stream=stream, workspace=ws)
@@ -337,9 +340,12 @@ def bench_llama8b(args):
     gather_gbps = store_bytes / (store_ms / 1e3) / 1e9
     scatter_gbps = ret_bytes / (ret_ms / 1e3) / 1e9
 
-    # the other visiting order, for context
+    # the other visiting order and the other store form, for context
     other_ms = timed(stream, lambda: kvm.retrieve(paged, batch, stream=stream,
                                                   workspace=None if ws is not None else paged.new_workspace()), 5)
+    other_store_ms = timed(stream, lambda: kvm.store(paged, batch, stream=stream,
+                                                     workspace=None if sws is not None else
+                                                     batch.new_store_workspace()), 5)
     assert kvm.take_faults() == 0
 
     # same-run calibration: a plain contiguous copy of the gather's payload
@@ -376,7 +382,8 @@ def bench_llama8b(args):
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "kvmove::move_bf16<true,...> (gather)",
+            "kernel": ("kvmove::gather_planned (gather; the store call, its plan kernel included)"
+                       if sws is not None else "kvmove::move_bf16<true,...> (gather)"),
             "achieved": round(gather_gbps, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -397,6 +404,9 @@ def bench_llama8b(args):
                               else "chunk-major (kv_retrieve_chunks)",
             "retrieve_other_order_ms": round(other_ms, 4),
             "retrieve_other_order_GBps": round(ret_bytes / (other_ms / 1e3) / 1e9, 2),
+            "store_form": "address plan (kv_store_chunks_ws)" if sws is not None else "kv_store_chunks",
+            "store_other_form_ms": round(other_store_ms, 4),
+            "store_other_form_GBps": round(store_bytes / (other_store_ms / 1e3) / 1e9, 2),
             "copy_ceiling_GBps": round(copy_gbps, 2),
             # HBM bytes the counters measured for one gather launch, over this run's launch time
             "gather_counter_GBps": (round(traffic / (store_ms / 1e3) / 1e9, 2) if traffic else None),
@@ -938,12 +948,14 @@ def bench_simple(args, name, fmt):
     per_elem = sum(2 + b for b in PART_BYTES[fmt])
     st_bytes = per_elem * part_elems_st + 4 * n_q * w.num_layers * chunks_st
     rt_bytes = per_elem * part_elems_rt + 4 * n_q * w.num_layers * chunks_rt
+    sws = batch.new_store_workspace(fmt)             # None for the fp8 formats (no bf16 part)
     for _ in range(args.warmup):
-        kvm.store(paged, batch, fmt, stream=stream)
+        kvm.store(paged, batch, fmt, stream=stream, workspace=sws)
         kvm.retrieve(paged, batch, fmt=fmt, stream=stream)
     reps = max(3, args.steps)
     ws = paged.new_workspace()
-    st_ms = timed(stream, lambda: kvm.store(paged, batch, fmt, stream=stream), reps)
+    st_ms = timed(stream, lambda: kvm.store(paged, batch, fmt, stream=stream, workspace=sws), reps)
+    plain_ms = timed(stream, lambda: kvm.store(paged, batch, fmt, stream=stream), reps) if sws is not None else None
     rt_ms = timed(stream, lambda: kvm.retrieve(paged, batch, fmt=fmt, stream=stream, workspace=ws), reps)
     cm_ms = timed(stream, lambda: kvm.retrieve(paged, batch, fmt=fmt, stream=stream), reps)
     assert kvm.take_faults() == 0
@@ -961,6 +973,9 @@ def bench_simple(args, name, fmt):
         "retrieve_order": "pool-address (workspace)",
         "retrieve_chunk_major_ms": round(cm_ms, 4),
         "retrieve_chunk_major_GBps": round(rt_bytes / (cm_ms / 1e3) / 1e9, 2),
+        "store_form": "address plan (kv_store_chunks_ws)" if sws is not None else "kv_store_chunks (no bf16 part)",
+        "store_plain_ms": round(plain_ms, 4) if plain_ms else None,
+        "store_plain_GBps": round(st_bytes / (plain_ms / 1e3) / 1e9, 2) if plain_ms else None,
     }
 
 
@@ -976,6 +991,8 @@ def main():
                              "offload-8b"])
     ap.add_argument("--retrieve-order", choices=["address", "chunk"], default="address",
                     help="headline retrieve: pool-address order with a workspace (default) or chunk-major")
+    ap.add_argument("--store-plan", choices=["on", "off"], default="on",
+                    help="headline store: through its address plan with a workspace (default) or kv_store_chunks")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg (used for profiler runs)")
     ap.add_argument("--layers-only", type=int, default=None, metavar="CAP",

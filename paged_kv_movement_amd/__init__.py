@@ -102,6 +102,8 @@ def load():
                                               vp]),
         "kv_store_chunks_cachegen": (ctypes.c_int, [P, S, ctypes.c_int, vp, vp, vp]),
         "kv_retrieve_workspace_bytes": (ctypes.c_size_t, [P]),
+        "kv_store_workspace_bytes": (ctypes.c_size_t, [P, S, ctypes.c_int, ctypes.c_int]),
+        "kv_store_chunks_ws": (ctypes.c_int, [P, S, ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t, vp]),
         "kv_retrieve_chunks_ws": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_size_t, vp]),
         "kv_retrieve_chunks_noalloc": (ctypes.c_int, [P, S, vp, ctypes.c_int, ctypes.c_int, vp, vp]),
         "kv_retrieve_chunks_cachegen": (ctypes.c_int, [P, S, vp, ctypes.c_int, vp, vp, vp, vp, ctypes.c_size_t, vp]),
@@ -329,6 +331,21 @@ class Batch:
         self._checked_fmts.add(fmt)
         return self
 
+    def store_workspace_bytes(self, fmt: int = FMT_BF16) -> int:
+        """Device bytes store(..., workspace=...) needs for these sequences
+        in this format (kv_store_workspace_bytes; 0 for the fp8 formats)."""
+        n = load().kv_store_workspace_bytes(ctypes.byref(self.paged.c), self.arr, self.n, fmt)
+        if n == 0:
+            _check(KV_OK if load().kv_last_error() == b"" else KV_EINVAL)
+        return int(n)
+
+    def new_store_workspace(self, fmt: int = FMT_BF16):
+        """A device tensor of store_workspace_bytes(fmt) bytes (torch aligns it
+        to 256), or None when the format needs none."""
+        import torch
+        n = self.store_workspace_bytes(fmt)
+        return torch.empty(n, dtype=torch.uint8, device="cuda") if n > 0 else None
+
     def used_on(self, stream, *extra) -> None:
         """record_stream for the Batch's own device tensors (once per stream)
         and for ``extra`` tensors of this call (every time)."""
@@ -345,10 +362,18 @@ def _batch(paged, seqs, fmt, stream, *extra) -> Batch:
     return b
 
 
-def store(paged: Paged, seqs, fmt: int = FMT_BF16, stream=None) -> None:
-    """Gather every chunk of every sequence (kv_store_chunks)."""
-    b = _batch(paged, seqs, fmt, stream)
-    _check(load().kv_store_chunks(ctypes.byref(paged.c), b.arr, b.n, fmt, _stream_handle(stream)))
+def store(paged: Paged, seqs, fmt: int = FMT_BF16, stream=None, workspace=None) -> None:
+    """Gather every chunk of every sequence (kv_store_chunks).  With
+    ``workspace`` (a device uint8 tensor of at least
+    batch.store_workspace_bytes(fmt)) the bf16 gather runs through an address
+    plan (kv_store_chunks_ws)."""
+    b = _batch(paged, seqs, fmt, stream, workspace)
+    if workspace is None:
+        _check(load().kv_store_chunks(ctypes.byref(paged.c), b.arr, b.n, fmt, _stream_handle(stream)))
+    else:
+        ws_ptr, ws_bytes = _workspace(workspace)
+        _check(load().kv_store_chunks_ws(ctypes.byref(paged.c), b.arr, b.n, fmt, ws_ptr, ws_bytes,
+                                         _stream_handle(stream)))
 
 
 def _event_handle(event, stream):

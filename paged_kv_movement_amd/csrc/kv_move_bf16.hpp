@@ -76,6 +76,68 @@ __global__ __launch_bounds__(kBlock) void move_bf16(MoveArgsLut al)
         move_tile<kToChunk, kBlock, kVpt, kAuxLoad, kAuxStore>(al, b);
 }
 
+// Address plan of a gather (kv_store_chunks_ws): one kPlanEntryBytes entry
+// per page unit of a launch, in the launch's unit order -- the unit's
+// page-side address, its chunk-side address and its byte count (0: the unit
+// is skipped and its fault bit set) -- written by build_gather_plan, read by
+// gather_planned.  With the addresses ready, a workgroup's first data load
+// waits on one uniform load of its entry instead of the movers' chain of
+// argument, block-table and address reads, and 4 KiB tiles of 256 threads
+// (the fastest plain-copy shape) keep HBM busy: the 8B gather measured 2 %
+// faster, plan included.
+constexpr int kPlanEntryBytes = 32;
+constexpr int kPlanBuildBlock = 256;
+constexpr int kPlanBlock = 256;
+constexpr int kPlanVpt = 1;
+
+// One thread per page unit of the launch (units [0, n_units) from
+// a.item_base): the unit's addresses, with the movers' checks.
+__global__ __launch_bounds__(kPlanBuildBlock) void build_gather_plan(MoveArgsLut al, uint64_t plan, uint32_t n_units)
+{
+    const MoveArgs& a = al.m;
+    const uint32_t i = blockIdx.x * kPlanBuildBlock + threadIdx.x;
+    if (i >= n_units) return;
+    const uint32_t item = a.item_base + i;
+    uint32_t s = al.lut[item >> al.lut_shift];
+    while (s + 1 < a.n_seqs && item >= a.seq[s + 1].item_begin) ++s;
+    const PageUnit u = locate_page_unit(a, item, s);
+    const uint64_t pool = gptr<const gu64>(u.kv ? a.v_pages : a.k_pages)[u.l];
+    const uint64_t chunk = gptr<const gu64>(a.seq[u.s].chunks)[u.c];
+    const uint32_t row_bytes = a.width * 2;
+    uint64_t page_addr = 0, chunk_addr = 0;
+    uint32_t bytes = 0;
+    if (u.page < 0 || u.page >= a.num_pages) atomicOr(&g_kv_faults, kFaultPage);
+    else if (bad_addr(pool)) atomicOr(&g_kv_faults, kFaultPool);
+    else if (bad_addr(chunk)) atomicOr(&g_kv_faults, kFaultChunk);
+    else {
+        page_addr = pool + (uint64_t)u.page * a.page_size * row_bytes;
+        chunk_addr = chunk + section_offset(a, u.l, u.kv, u.n_c) + (uint64_t)u.j0 * row_bytes;
+        bytes = u.rows * row_bytes;
+    }
+    gu64* e = gptr<gu64>(plan + (uint64_t)i * kPlanEntryBytes);
+    e[0] = page_addr;
+    e[1] = chunk_addr;
+    e[2] = bytes;
+    e[3] = 0;
+}
+
+// The gather over a plan: tiles tiles of kBlock * kVpt vectors per unit, one
+// workgroup per tile, XCD-contiguous.
+template <int kBlock, int kVpt, int kAuxLoad, int kAuxStore>
+__global__ __launch_bounds__(kBlock) void gather_planned(const uint64_t* __restrict__ plan, uint32_t tiles)
+{
+    const uint32_t b = xcd_contiguous(blockIdx.x, gridDim.x);
+    const uint32_t unit = b / tiles, t = b - unit * tiles;
+    const uint64_t* e = plan + (uint64_t)unit * (kPlanEntryBytes / 8);      // uniform: scalar loads
+    const uint64_t page_addr = e[0], chunk_addr = e[1];
+    const uint32_t bytes = (uint32_t)e[2];
+    constexpr uint32_t tile = kBlock * kVpt * 16;
+    const uint32_t lo = t * tile;
+    if (lo >= bytes) return;                          // tile past a short page, or a skipped unit
+    const uint32_t n = bytes - lo < tile ? bytes - lo : tile;
+    copy_tile<kBlock, kVpt, kAuxLoad, kAuxStore>(page_addr + lo, chunk_addr + lo, n);
+}
+
 // Plain contiguous copy (measurement aid): one tile of kBlock*kVpt vectors
 // per workgroup, the movers' instruction form (buffer loads and stores, nt +
 // sc1, XCD-contiguous workgroup order) without their page lookups.

@@ -357,6 +357,49 @@ Plan scatter_plan(int fmt, bool capped, bool ordered)
     }
 }
 
+// The bf16 gather (launch L of a store plan, uncapped) through an address
+// plan in `plan` (device memory of at least kPlanEntryBytes per page unit of
+// the largest packed launch): per launch, build_gather_plan writes the plan,
+// then gather_planned moves 4 KiB tiles over it.
+int gather_through_plan(const Launch& L, const Layout& lay, const kv_paged* p, const kv_seq* seqs,
+                        const int64_t* n_tok, int n_seqs, uint64_t plan, hipStream_t stream)
+{
+    Launch P = L;
+    P.block = kPlanBlock;
+    P.tile_bytes = kPlanBlock * kPlanVpt * 16;
+    auto flush = [&](MoveArgs& a, int64_t total) -> int {
+        MoveArgsLut al = with_seq_lut(a, total);
+        uint64_t plan_a = plan;
+        uint32_t n = uint32_t(total);
+        void* build_args[] = {&al, &plan_a, &n};
+        hipError_t e = hipLaunchKernel(reinterpret_cast<KernelFn>(&build_gather_plan),
+                                       dim3(unsigned(ceil_div(total, kPlanBuildBlock))), dim3(kPlanBuildBlock),
+                                       build_args, 0, stream);
+        if (e == hipSuccess) {
+            const uint64_t* plan_p = reinterpret_cast<const uint64_t*>(plan);
+            uint32_t tiles = a.tiles;
+            void* move_args[] = {&plan_p, &tiles};
+            e = hipLaunchKernel(
+                reinterpret_cast<KernelFn>(&gather_planned<kPlanBlock, kPlanVpt, kGatherAuxLoad, kGatherAuxStore>),
+                dim3(a.total_tiles), dim3(kPlanBlock), move_args, 0, stream);
+        }
+        if (e != hipSuccess) return fail(KV_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+        return KV_OK;
+    };
+    return pack_units(P, lay, p, seqs, n_tok, n_seqs, 0, p->num_layers, flush);
+}
+
+// The page units a store's bf16 parts move (the plan's entries): per
+// sequence ceil(tokens / P) pages of each layer's K and V (K only for
+// KV_FMT_K16_V8; none for the fp8 formats).
+int64_t store_plan_units(const kv_paged* p, const int64_t* n_tok, int n_seqs, int fmt)
+{
+    const int64_t parts = fmt == KV_FMT_BF16 ? 2 : fmt == KV_FMT_K16_V8 ? 1 : 0;
+    int64_t pages = 0;
+    for (int i = 0; i < n_seqs; ++i) pages += ceil_div(n_tok[i], p->page_size);
+    return pages * p->num_layers * parts;
+}
+
 int run_plan(const Plan& plan, int fmt, const kv_paged* p, const kv_seq* seqs, const int64_t* n_tok,
              int n_seqs, int32_t layer0, int32_t n_layers, hipStream_t stream, int32_t max_workgroups)
 {
@@ -768,6 +811,49 @@ int kv_store_chunks(const kv_paged* paged, const kv_seq* seqs, int n_seqs, kv_fm
     int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
     for (int i = 0; i < n_seqs; ++i) n_tok[i] = seqs[i].tok_end - seqs[i].tok_start;
     rc = run_plan(gather_plan(paged, fmt, false), fmt, paged, seqs, n_tok, n_seqs, 0, paged->num_layers, stream, 0);
+    if (n_tok != small) delete[] n_tok;
+    return rc == KV_OK ? ok() : rc;
+}
+
+size_t kv_store_workspace_bytes(const kv_paged* paged, const kv_seq* seqs, int n_seqs, kv_fmt fmt)
+{
+    int rc = check_paged(paged);
+    if (rc == KV_OK) rc = check_fmt(fmt);
+    if (rc == KV_OK) rc = check_seqs(paged, seqs, n_seqs);
+    if (rc != KV_OK) return 0;
+    int64_t units = 0;
+    for (int i = 0; i < n_seqs; ++i) {
+        const int64_t n = seqs[i].tok_end - seqs[i].tok_start;
+        units += store_plan_units(paged, &n, 1, fmt);
+    }
+    ok();
+    return size_t(ceil_div(units * kPlanEntryBytes, 256) * 256);
+}
+
+int kv_store_chunks_ws(const kv_paged* paged, const kv_seq* seqs, int n_seqs, kv_fmt fmt, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream)
+{
+    int rc = check_paged(paged);
+    if (rc == KV_OK) rc = check_fmt(fmt);
+    if (rc == KV_OK) rc = check_seqs(paged, seqs, n_seqs);
+    if (rc != KV_OK) return rc;
+    int64_t small[64];
+    int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
+    for (int i = 0; i < n_seqs; ++i) n_tok[i] = seqs[i].tok_end - seqs[i].tok_start;
+    const int64_t need = ceil_div(store_plan_units(paged, n_tok, n_seqs, fmt) * kPlanEntryBytes, 256) * 256;
+    if (need > 0 && (workspace == nullptr || int64_t(workspace_bytes) < need ||
+                     reinterpret_cast<uintptr_t>(workspace) % 256 != 0))
+        rc = fail(KV_EINVAL, "workspace of %lld bytes, 256-byte aligned, needed (got %zu at %p)", (long long)need,
+                  workspace_bytes, workspace);
+    const Plan plan = gather_plan(paged, fmt, false);
+    const Layout lay = layout_of(fmt);
+    for (int k = 0; k < plan.n && rc == KV_OK; ++k) {
+        const bool bf16 = plan.part[k].kernel ==
+                          reinterpret_cast<KernelFn>(&move_bf16<true, kMoveBlock, kMoveVpt, kGatherAuxLoad, kGatherAuxStore>);
+        rc = bf16 ? gather_through_plan(plan.part[k], lay, paged, seqs, n_tok, n_seqs,
+                                        reinterpret_cast<uint64_t>(workspace), stream)
+                  : launch_units(plan.part[k], lay, paged, seqs, n_tok, n_seqs, 0, paged->num_layers, stream);
+    }
     if (n_tok != small) delete[] n_tok;
     return rc == KV_OK ? ok() : rc;
 }

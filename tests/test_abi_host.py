@@ -399,6 +399,37 @@ def test_ordered_retrieve_workspace_size_and_rejections():
     assert out[0] == 0
 
 
+def test_store_workspace_size_and_rejections():
+    # 32 bytes per page unit of the bf16 parts, rounded up to 256; refusals
+    # before any HIP call
+    L = _lib()
+    p = _paged()
+    seqs = (kvm._KvSeq * 2)(_seq(0, 1000, 63), _seq(256, 530, 34))
+    units = (63 + 18) * 32 * 2                       # ceil(1000/16) + ceil(274/16) pages, 32 layers, K and V
+    assert L.kv_store_workspace_bytes(ctypes.byref(p), seqs, 2, kvm.FMT_BF16) == units * 32
+    assert L.kv_store_workspace_bytes(ctypes.byref(p), seqs, 2, kvm.FMT_K16_V8) == units * 16
+    assert L.kv_store_workspace_bytes(ctypes.byref(p), seqs, 2, kvm.FMT_FP8) == 0
+    assert L.kv_last_error().decode() == ""
+    one = (kvm._KvSeq * 1)(_seq(0, 17, 2))
+    assert L.kv_store_workspace_bytes(ctypes.byref(p), one, 1, kvm.FMT_BF16) == 2 * 64 * 32
+    assert L.kv_store_workspace_bytes(ctypes.byref(_paged(L=1)), one, 1, kvm.FMT_BF16) == 256   # 128 B rounded up
+    assert L.kv_store_workspace_bytes(ctypes.byref(p), seqs, 2, 9) == 0
+    assert L.kv_last_error().decode() != ""
+    assert L.kv_store_workspace_bytes(None, seqs, 2, kvm.FMT_BF16) == 0
+    need = units * 32
+    args = (ctypes.byref(p), seqs, 2, kvm.FMT_BF16)
+    assert L.kv_store_chunks_ws(*args, None, need, None) == kvm.KV_EINVAL
+    assert "workspace" in L.kv_last_error().decode()
+    assert L.kv_store_chunks_ws(*args, 0x10000, need - 1, None) == kvm.KV_EINVAL
+    assert L.kv_store_chunks_ws(*args, 0x10080, need, None) == kvm.KV_EINVAL          # not 256-aligned
+    bad = (kvm._KvSeq * 1)(_seq(100, 1000, 63))
+    assert L.kv_store_chunks_ws(ctypes.byref(p), bad, 1, kvm.FMT_BF16, 0x10000, need, None) == kvm.KV_EINVAL
+    # nothing to move: no workspace needed, nothing launched (no GPU here)
+    empty = (kvm._KvSeq * 1)(_seq(256, 256, 63))
+    assert L.kv_store_workspace_bytes(ctypes.byref(p), empty, 1, kvm.FMT_BF16) == 0
+    assert L.kv_store_chunks_ws(ctypes.byref(p), empty, 1, kvm.FMT_BF16, None, 0, None) == kvm.KV_OK
+
+
 def test_ordered_retrieve_refuses_more_pages_than_the_pool():
     # 1100 tokens = 69 pages of 16 on a 64-page pool: the page ids cannot be
     # distinct and the sorted list would overrun the workspace, so the call

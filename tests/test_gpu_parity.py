@@ -124,6 +124,73 @@ def test_store_is_deterministic_and_leaves_pool():
         assert all(torch.equal(a, b) for a, b in zip(first, cs[0][0]))
 
 
+# ------------------------------------------------------- store through an address plan
+
+def _planned_store(w, fmt, ws=None):
+    arr = wl.host_pool(w)
+    pool, paged, batch, cs = setup_device(w, arr, fmt=fmt, fill=0xCD)
+    if ws is None:
+        ws = batch.new_store_workspace(fmt)
+    if fmt in (FP8, E5M2):
+        assert ws is None                            # no bf16 part: nothing to plan
+    kvm.store(paged, batch, fmt, workspace=ws)
+    _sync()
+    assert kvm.take_faults() == 0
+    assert np.array_equal(host_from_dev_pool(pool), arr), "store wrote the pool"
+    check_store(w, arr, cs, fmt)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+@pytest.mark.parametrize("fmt", **ALL_FMTS)
+def test_planned_store_shapes_and_tails(shape, fmt):
+    name, seed, L, H, D, pages, ranges, kw = shape
+    say("case planned store", name, fmt)
+    _planned_store(wl.custom(name, seed, L, H, D, pages, ranges, outliers=_outliers(fmt), **kw), fmt)
+
+
+def test_planned_store_many_sequences_and_reused_workspace():
+    # 70 sequences: several launches, each writing its plan over the last one's
+    ranges = [(0, 1 + 37 * i) for i in range(70)]
+    for fmt in (BF16, K16V8):
+        _planned_store(wl.custom("plan-many", 113, 2, 2, 32, 6000, ranges, outliers=_outliers(fmt)), fmt)
+    # one workspace, larger than needed, over two different calls
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    _planned_store(wl.custom("plan-reuse", 114, 3, 2, 64, 300, [(0, 1000), (256, 700)]), BF16, ws=ws)
+    _planned_store(wl.custom("plan-reuse2", 115, 2, 4, 32, 200, [(0, 300)]), BF16, ws=ws)
+
+
+def test_planned_store_bad_page_and_bad_chunk_are_skipped_and_reported():
+    w = wl.custom("plan-bad", 202, 2, 2, 32, 64, [(0, 300)])
+    arr = wl.host_pool(w)
+    good_bt = w.seqs[0].block_table.copy()
+    w.seqs[0].block_table = good_bt.copy()
+    w.seqs[0].block_table[3] = 64                  # == num_pages: out of range
+    pool, paged, batch, cs = setup_device(w, arr, fill=0xCD)
+    assert kvm.take_faults() == 0
+    kvm.store(paged, batch, workspace=batch.new_store_workspace())
+    assert kvm.take_faults() == 1
+    got = host_chunks(cs[0])
+    exp = oracle.alloc_chunks(oracle_pool(w, arr), 0, 300, BF16)
+    assert oracle.store(oracle_pool(w, arr), good_bt, 0, 300, exp) == 0
+    E, L = w.width, w.num_layers
+    g0 = got[0].view(np.uint16).reshape(L, 2, 256, E)
+    e0 = exp[0].view(np.uint16).reshape(L, 2, 256, E)
+    assert (g0[:, :, 48:64] == 0xCDCD).all()       # the bad page's rows untouched, every other row stored
+    assert np.array_equal(np.delete(g0, range(48, 64), axis=2), np.delete(e0, range(48, 64), axis=2))
+    assert np.array_equal(got[1], exp[1])
+    # a misaligned chunk address: that chunk skipped, the other stored
+    bufs = cs[0][0]
+    bufs[0].fill_(0xCD)
+    bufs[0][cs[0][1][0]:] = 0x5A
+    addrs = torch.tensor([bufs[0].data_ptr() + 8, bufs[1].data_ptr()], dtype=torch.int64).cuda()
+    seq = kvm.Seq(torch.from_numpy(good_bt).cuda(), 0, 300, addrs)
+    b2 = kvm.Batch(paged, [seq])
+    kvm.store(paged, b2, workspace=b2.new_store_workspace())
+    assert kvm.take_faults() == 2
+    assert (bufs[0].cpu().numpy()[: cs[0][1][0]] == 0xCD).all()
+    assert np.array_equal(host_chunks(([bufs[1]], [cs[0][1][1]]))[0], exp[1])
+
+
 # ------------------------------------------------------------------ layerwise
 
 @pytest.mark.parametrize("fmt", **ALL_FMTS)
@@ -906,6 +973,13 @@ def test_odd_page_sizes(pc, fmt):
     _sync()
     assert kvm.take_faults() == 0
     check_store_cachegen(w, arr, cs, kb, vb) if cg else check_store(w, arr, cs, fmt)
+    if not cg:                                       # and through the address plan, over the sentinel
+        for b in cs[0][0] + cs[1][0] + cs[2][0]:
+            b[: b.numel() - 256].fill_(0xCD)
+        kvm.store(paged, batch, fmt, workspace=batch.new_store_workspace(fmt))
+        _sync()
+        assert kvm.take_faults() == 0
+        check_store(w, arr, cs, fmt)
     expect = [2 * C, 2 * C + P + 1 - C, 1]
     forms = ["chunk", "ordered"] if cg else ["chunk", "ordered", "layers"]
     for form in forms:

@@ -37,7 +37,8 @@ def _case(i):
     pages_needed = sum(-(-e // P) for (_, e) in ranges)
     num_pages = pages_needed + int(rng.integers(1, 64))
     fmt = FORMATS[int(rng.integers(0, len(FORMATS)))]
-    store_form = rng.choice(["full", "layers", "layer-range", "layer-range-2s"]) if fmt != kvm.FMT_CACHEGEN \
+    store_form = rng.choice(["full", "planned", "layers", "layer-range", "layer-range-2s"]) \
+        if fmt != kvm.FMT_CACHEGEN \
         else "full"
     retrieve_form = rng.choice(["chunk", "ordered", "layers", "layer-range", "layer-range-2s"]) \
         if fmt != kvm.FMT_CACHEGEN else rng.choice(["chunk", "ordered"])
@@ -62,6 +63,8 @@ def test_random_case(i):
         kvm.store_cachegen(paged, batch, kb, vb, stream=s)
     elif store_form == "full":
         kvm.store(paged, batch, fmt, stream=s)
+    elif store_form == "planned":
+        kvm.store(paged, batch, fmt, stream=s, workspace=batch.new_store_workspace(fmt))
     elif store_form.startswith("layer-range"):
         # every layer in one call, the first at full width and the rest
         # capped; with "-2s" every other layer on a second stream

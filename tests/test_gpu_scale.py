@@ -30,11 +30,13 @@ def _free():
     torch._C._host_emptyCache()     # give back pinned host blocks too
 
 
-def _full_bf16(w, expect_tokens, where="device"):
-    say("case", w.name, "pool GB", w.pool_nbytes() / 1e9, "chunks in", where)
+def _full_bf16(w, expect_tokens, where="device", workspaces=False):
+    # workspaces: the store through its address plan and the retrieve in
+    # pool-address order, as the benchmark runs them
+    say("case", w.name, "pool GB", w.pool_nbytes() / 1e9, "chunks in", where, "workspaces", workspaces)
     pool = wl.device_pool(w)
     pool, paged, batch, chunk_sets = setup_device(w, pool=pool, fill=0xCD, where=where)
-    kvm.store(paged, batch)                       # one launch over every sequence
+    kvm.store(paged, batch, workspace=batch.new_store_workspace() if workspaces else None)
     sync()
     assert kvm.take_faults() == 0
     arr = host_from_dev_pool(pool)
@@ -42,7 +44,7 @@ def _full_bf16(w, expect_tokens, where="device"):
     check_store(w, arr, chunk_sets, BF16)
     del arr
     pool.view(torch.int16).fill_(SENTINEL)
-    n = kvm.retrieve(paged, batch)                # one launch, masks from the workload
+    n = kvm.retrieve(paged, batch, workspace=paged.new_workspace() if workspaces else None)
     sync()
     assert kvm.take_faults() == 0
     assert n == expect_tokens
@@ -68,14 +70,16 @@ def test_full_llama8b_offload_to_host_and_onload():
     _full_bf16(wl.llama8b(), [30 * 256] * 8, where="host")
 
 
-def test_full_llama8b_tp8_share_store_and_30_chunk_retrieve():
+@pytest.mark.parametrize("form", ["plain", "workspaces"])
+def test_full_llama8b_tp8_share_store_and_30_chunk_retrieve(form):
     # one rank's share under 8-way tensor parallelism: one KV head, 4 KiB pages
-    _full_bf16(wl.llama8b_tp8_share(), [30 * 256] * 8)
+    _full_bf16(wl.llama8b_tp8_share(), [30 * 256] * 8, workspaces=form == "workspaces")
 
 
-def test_full_llama70b_store_and_retrieve():
+@pytest.mark.parametrize("form", ["plain", "workspaces"])
+def test_full_llama70b_store_and_retrieve(form):
     # 80 layers, one 32768-token sequence (128 chunks) on a 4096-page pool
-    _full_bf16(wl.llama70b(), [32768])
+    _full_bf16(wl.llama70b(), [32768], workspaces=form == "workspaces")
 
 
 @pytest.mark.parametrize("form", ["per-layer-calls", "per-layer-calls-paced", "one-call", "one-call-two-streams"])
@@ -277,22 +281,8 @@ def test_full_cachegen_8b_every_chunk_and_whole_pool():
     _free()
 
 
-def test_full_llama8b_retrieve_in_pool_address_order():
-    # the headline retrieve (30 hit chunks of 8 x 10000 tokens) through the
-    # ordered scatter, compared in full
-    w = wl.llama8b()
-    say("case", w.name, "ordered retrieve")
-    pool = wl.device_pool(w)
-    pool, paged, batch, chunk_sets = setup_device(w, pool=pool, fill=0xCD)
-    kvm.store(paged, batch)
-    sync()
-    pool.view(torch.int16).fill_(SENTINEL)
-    n = kvm.retrieve(paged, batch, workspace=paged.new_workspace())
-    sync()
-    assert kvm.take_faults() == 0
-    assert n == [30 * 256] * 8
-    got = host_from_dev_pool(pool)
-    before = np.full(got.shape, SENTINEL, np.uint16)
-    assert check_retrieve(w, before, got, chunk_sets, BF16, [s.hit_mask for s in w.seqs], copy=False) == n
-    del got, before, pool, paged, batch, chunk_sets
-    _free()
+def test_full_llama8b_planned_store_and_ordered_retrieve():
+    # the headline step as the benchmark runs it: the store through its
+    # address plan, the retrieve (30 hit chunks of 8 x 10000 tokens) through
+    # the ordered scatter; both compared in full
+    _full_bf16(wl.llama8b(), [30 * 256] * 8, workspaces=True)
