@@ -131,6 +131,34 @@ int main(void)
 
     CHECK_KV(kv_store_chunks(&paged, &seq, 1, KV_FMT_BF16, stream));
     CHECK_HIP(hipStreamSynchronize(stream));
+
+    /* the same store through its address plan (kv_store_chunks_ws): the
+     * chunks, cleared in between, must come out byte for byte the same */
+    const size_t chunk_bytes[2] = {kv_chunk_bytes(&paged, C, KV_FMT_BF16), kv_chunk_bytes(&paged, TOKENS - C, KV_FMT_BF16)};
+    uint8_t* saved[2];
+    for (int c = 0; c < 2; ++c) {
+        saved[c] = (uint8_t*)malloc(chunk_bytes[c]);
+        if (!saved[c]) return 4;
+        CHECK_HIP(hipMemcpy(saved[c], (void*)(uintptr_t)chunk_addr[c], chunk_bytes[c], hipMemcpyDeviceToHost));
+        CHECK_HIP(hipMemset((void*)(uintptr_t)chunk_addr[c], 0xEE, chunk_bytes[c]));
+    }
+    const size_t ws_bytes = kv_store_workspace_bytes(&paged, &seq, 1, KV_FMT_BF16);
+    /* 32 bytes per page unit (every layer's K and V pages), rounded up to 256 */
+    if (ws_bytes != ((size_t)n_bt * L * 2 * 32 + 255) / 256 * 256) { fprintf(stderr, "store workspace %zu bytes\n", ws_bytes); return 5; }
+    void* ws = NULL;
+    CHECK_HIP(hipMalloc(&ws, ws_bytes));
+    CHECK_HIP(hipDeviceSynchronize());
+    CHECK_KV(kv_store_chunks_ws(&paged, &seq, 1, KV_FMT_BF16, ws, ws_bytes, stream));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    for (int c = 0; c < 2; ++c) {
+        uint8_t* again = (uint8_t*)malloc(chunk_bytes[c]);
+        if (!again) return 4;
+        CHECK_HIP(hipMemcpy(again, (void*)(uintptr_t)chunk_addr[c], chunk_bytes[c], hipMemcpyDeviceToHost));
+        if (memcmp(again, saved[c], chunk_bytes[c]) != 0) { fprintf(stderr, "chunk %d differs after the planned store\n", c); return 6; }
+        free(again);
+        free(saved[c]);
+    }
+    CHECK_HIP(hipFree(ws));
     CHECK_HIP(hipMemset(pool, 0, pool_elems * 2));
     CHECK_HIP(hipDeviceSynchronize());
 
@@ -159,7 +187,7 @@ int main(void)
     if (rc != 0) return rc;
     if (kv_take_faults() != 0) { fprintf(stderr, "fault bits after the layer calls\n"); return 6; }
     for (int l = 0; l < L; ++l) CHECK_HIP(hipEventDestroy(done[l]));
-    printf("C ABI round trip: %d tokens x %d layers x K,V restored bit for bit, in one call and layer by layer; "
-           "other rows untouched\n", TOKENS, L);
+    printf("C ABI round trip: %d tokens x %d layers x K,V stored alike with and without the address plan, "
+           "restored bit for bit in one call and layer by layer; other rows untouched\n", TOKENS, L);
     return 0;
 }

@@ -1044,6 +1044,7 @@ def test_store_and_ordered_retrieve_replay_from_a_graph(fmt):
     cg = fmt == kvm.FMT_CACHEGEN
     kb, vb = cachegen_bins(w.num_layers, 461) if cg else (None, None)
     ws = paged.new_workspace()
+    sws = None if cg else batch.new_store_workspace(fmt)    # the store's address plan (bf16 parts)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):                       # warm-up outside capture
@@ -1051,12 +1052,12 @@ def test_store_and_ordered_retrieve_replay_from_a_graph(fmt):
             kvm.store_cachegen(paged, batch, kb, vb)
             kvm.retrieve_cachegen(paged, batch, kb, vb, workspace=ws)
         else:
-            kvm.store(paged, batch, fmt)
+            kvm.store(paged, batch, fmt, workspace=sws)
             kvm.retrieve(paged, batch, fmt=fmt, workspace=ws)
     torch.cuda.synchronize()
     g_store, g_retrieve = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_store, stream=s):
-        kvm.store_cachegen(paged, batch, kb, vb) if cg else kvm.store(paged, batch, fmt)
+        kvm.store_cachegen(paged, batch, kb, vb) if cg else kvm.store(paged, batch, fmt, workspace=sws)
     with torch.cuda.graph(g_retrieve, stream=s):
         if cg:
             n = kvm.retrieve_cachegen(paged, batch, kb, vb, workspace=ws)
@@ -1069,6 +1070,8 @@ def test_store_and_ordered_retrieve_replay_from_a_graph(fmt):
         # new mantissa bits, same exponents: finite values stay finite
         arr = arr0 ^ rng.integers(0, 1 << 7, size=arr0.shape, dtype=np.uint16) if rep else arr0
         pool.copy_(dev_pool_from_host(w, arr))
+        if sws is not None:
+            sws.fill_(0x3A + rep)                        # the plan's contents on entry must not matter
         torch.cuda.synchronize()
         g_store.replay()
         torch.cuda.synchronize()
