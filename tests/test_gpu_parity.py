@@ -707,6 +707,14 @@ def test_host_chunks_offload_and_onload(fmt):
     _sync()
     assert kvm.take_faults() == 0
     check_store(w, arr, cs, fmt)
+    # the offload through the address plan, over a refilled sentinel
+    for bufs, sizes in cs:
+        for b, n in zip(bufs, sizes):
+            b[:n].fill_(0xCD)
+    kvm.store(paged, batch, fmt, workspace=batch.new_store_workspace(fmt))
+    _sync()
+    assert kvm.take_faults() == 0
+    check_store(w, arr, cs, fmt)
     masks = [s.hit_mask for s in w.seqs]
     pool.view(torch.int16).fill_(0x7E57)
     n = kvm.retrieve(paged, batch, fmt=fmt)
