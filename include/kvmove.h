@@ -218,7 +218,9 @@ int kv_store_layer(const kv_paged* paged, const kv_seq* seqs, int n_seqs, kv_fmt
  * the start and the tail of each launch (32 layers of the Llama-3.1-8B
  * workload: 481 us against 561 us on one stream).  It helps only if the two
  * streams are on different hardware queues (GPU_MAX_HW_QUEUES); on one they
- * run in order, still correctly. */
+ * run in order, still correctly.  The fork and the join are event record /
+ * wait pairs, so a capture of stream records the call as a graph with two
+ * branches. */
 int kv_store_layers(const kv_paged* paged, const kv_seq* seqs, int n_seqs, kv_fmt fmt, int32_t layer_begin,
                     int32_t layer_end, const int32_t* max_workgroups, hipStream_t stream, hipStream_t alt_stream,
                     const hipEvent_t* wait_before, const hipEvent_t* layer_done);

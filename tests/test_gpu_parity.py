@@ -1100,6 +1100,39 @@ def test_store_and_ordered_retrieve_replay_from_a_graph(fmt):
         assert counts == [700, 256]
 
 
+def test_layer_range_with_a_second_stream_replays_from_a_graph():
+    # the fork onto the second stream and the join back are event record /
+    # wait pairs, the form a stream capture turns into graph edges: one graph
+    # holds the whole layer-range retrieve on two streams; each replay, after
+    # an eager sentinel fill, must write every layer as the eager call does
+    w = wl.custom("graph-2s", 462, 6, 2, 32, 300, [(0, 1000), (256, 900)],
+                  masks=[np.array([1, 1, 0, 1], np.uint8), np.array([1, 1, 1], np.uint8)])
+    say("case graph replay of a two-stream layer-range retrieve")
+    arr = wl.host_pool(w)
+    pool, paged, batch, cs = setup_device(w, arr)
+    kvm.store(paged, batch)
+    s, alt = torch.cuda.Stream(), torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                       # eager, outside capture: the reference
+        pool.view(torch.int16).fill_(SENTINEL)
+        kvm.retrieve_layers(paged, batch, 0, w.num_layers, stream=s, alt_stream=alt)
+    torch.cuda.synchronize()
+    assert check_retrieve(w, np.full_like(arr, SENTINEL), host_from_dev_pool(pool), cs, BF16,
+                          [sq.hit_mask for sq in w.seqs]) == [512, 644]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        kvm.retrieve_layers(paged, batch, 0, w.num_layers, stream=s, alt_stream=alt)
+    for rep in range(3):
+        pool.view(torch.int16).fill_(SENTINEL + 1 + rep)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert kvm.take_faults() == 0
+        got = host_from_dev_pool(pool)
+        assert check_retrieve(w, np.full_like(arr, SENTINEL + 1 + rep), got, cs, BF16,
+                              [sq.hit_mask for sq in w.seqs]) == [512, 644], rep
+
+
 def test_store_and_retrieve_on_two_streams_at_once():
     # an offload of two sequences on one stream while two others onload on a
     # second stream (disjoint pages, as the pool allocator guarantees): both
