@@ -22,10 +22,13 @@ constexpr int kOnchipMaxPages = 64;
 constexpr uint32_t kOnchipMaxVectors = uint32_t(kOnchipBlock) * (kOnchipRegSlots + kOnchipLdsSlots);
 // dequantising scatter: one-wave workgroups with 4 KiB tiles of bf16 output
 // for a full chunk-major launch (about 1 % faster than 8 KiB tiles of 256
-// threads); 256 threads x 8 KiB for a capped launch and for the
-// pool-address-ordered one, where the one-wave shape measured 2 % slower
+// threads); one-wave 2 KiB tiles for the pool-address-ordered launch (0.4-0.8 %
+// faster than 256 x 8 KiB there, while 4 KiB one-wave tiles were 2 % slower);
+// 256 threads x 8 KiB for a capped launch
 constexpr int kFp8RetrieveBlock = 64;
 constexpr int kFp8RetrieveVpt = 4;
+constexpr int kFp8RetrieveBlockSorted = 64;
+constexpr int kFp8RetrieveVptSorted = 2;
 constexpr int kFp8RetrieveBlockCapped = 256;
 constexpr int kFp8RetrieveVptCapped = 2;
 

@@ -326,13 +326,15 @@ Launch dequantise_shape(bool e5m2, uint32_t kv0, uint32_t n_kv, bool sorted)
     return {k, B, B * V * 16, Unit::Page, kv0, n_kv, ks, true};
 }
 
-// Scatter + dequantise.  The chunk-major launch takes one-wave workgroups;
-// a capped launch, and the pool-address-ordered one (where they measured
-// slower), take 256 threads x 8 KiB.
+// Scatter + dequantise.  The chunk-major and the pool-address-ordered
+// launches take one-wave workgroups (4 KiB and 2 KiB tiles); a capped launch
+// takes 256 threads x 8 KiB and is never ordered.
 Launch dequantise_launch(bool e5m2, uint32_t kv0, uint32_t n_kv, bool capped, bool ordered)
 {
-    if (capped || ordered)
-        return dequantise_shape<kFp8RetrieveBlockCapped, kFp8RetrieveVptCapped>(e5m2, kv0, n_kv, !capped);
+    if (capped)
+        return dequantise_shape<kFp8RetrieveBlockCapped, kFp8RetrieveVptCapped>(e5m2, kv0, n_kv, false);
+    if (ordered)
+        return dequantise_shape<kFp8RetrieveBlockSorted, kFp8RetrieveVptSorted>(e5m2, kv0, n_kv, true);
     return dequantise_shape<kFp8RetrieveBlock, kFp8RetrieveVpt>(e5m2, kv0, n_kv, false);
 }
 
