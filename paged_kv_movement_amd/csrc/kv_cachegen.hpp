@@ -24,6 +24,8 @@ namespace kvmove {
 
 constexpr int kCgBlock = 256;
 constexpr int kCgWaves = kCgBlock / 64;
+// waves (one row each) per workgroup of the pool-address-ordered retrieve
+constexpr int kCgSortedWaves = 1;
 constexpr int kCgMaxLayers = 128;
 constexpr int kCgMaxVpl = 8;            // 16-byte vectors per lane per row: rows up to 4096 elements
 
@@ -298,14 +300,15 @@ __device__ __forceinline__ void retrieve_cachegen_unit(const CgArgs& ca, const P
     }
 }
 
-// Dequantise + scatter tile `tile` of a page unit: kCgWaves rows, one per
-// wave (rows tile * kCgWaves + wave); a.tiles = ceil(page rows / kCgWaves)
-// tiles per unit, one workgroup each (the pool-address-ordered retrieve).  In
-// pool-address order these smaller workgroups measured 5.56 TB/s against 5.39
-// for one workgroup per page at the Llama-3.1-8B shape; in chunk-major order
-// they measured slower (5.08 against 5.33), so that order keeps
-// retrieve_cachegen_unit.  nt + sc1 on both sides (+0.8 % here; -0.4 % in
-// the chunk-major kernel, which keeps nt).
+// Dequantise + scatter tile `tile` of a page unit: kCgSortedWaves rows, one
+// per wave (rows tile * kCgSortedWaves + wave); a.tiles = ceil(page rows /
+// kCgSortedWaves) tiles per unit, one workgroup each (the pool-address-ordered
+// retrieve).  In pool-address order these smaller workgroups measured 5.56
+// TB/s (4 waves) against 5.39 for one workgroup per page at the Llama-3.1-8B
+// shape, and one wave per workgroup 0.5 % faster again than 4 (2 and 8 were
+// slower); in chunk-major order they measured slower (5.08 against 5.33), so
+// that order keeps retrieve_cachegen_unit.  nt + sc1 on both sides (+0.8 %
+// here; -0.4 % in the chunk-major kernel, which keeps nt).
 template <int kVpl>
 __device__ __forceinline__ void retrieve_cachegen_tile(const CgArgs& ca, const PageUnit& u, uint32_t tile)
 {
@@ -313,8 +316,8 @@ __device__ __forceinline__ void retrieve_cachegen_tile(const CgArgs& ca, const P
     // the wave index in a scalar register: row addresses, and the buffer
     // descriptors built from them, are then known to be wave-uniform
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
-    const uint32_t r = tile * kCgWaves + wave;
-    if (tile * kCgWaves >= u.rows) return;                // tile past a short (tail) page: whole workgroup
+    const uint32_t r = tile * kCgSortedWaves + wave;
+    if (tile * kCgSortedWaves >= u.rows) return;                // tile past a short (tail) page: whole workgroup
     if (u.page < 0 || u.page >= a.num_pages) { raise_fault(kFaultPage); return; }
     const uint64_t pool = wave_uniform(gptr<const gu64>(u.kv ? a.v_pages : a.k_pages)[u.l]);
     const uint64_t chunk = wave_uniform(gptr<const gu64>(a.seq[u.s].chunks)[u.c]);
@@ -347,7 +350,7 @@ __global__ __launch_bounds__(kCgBlock) void retrieve_cachegen(CgArgs ca)
 
 // The same in pool-address order (sorted page list, see sorted_unit).
 template <int kVpl>
-__global__ __launch_bounds__(kCgBlock) void retrieve_cachegen_sorted(CgArgs ca, uint64_t list, uint32_t n_list)
+__global__ __launch_bounds__(kCgSortedWaves * 64) void retrieve_cachegen_sorted(CgArgs ca, uint64_t list, uint32_t n_list)
 {
     const uint32_t b = xcd_contiguous(blockIdx.x, gridDim.x);
     const uint32_t unit = b / ca.m.tiles, tile = b - unit * ca.m.tiles;

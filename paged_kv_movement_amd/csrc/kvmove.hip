@@ -572,12 +572,12 @@ int cachegen_setup(const kv_paged* p, const int32_t* key_bins, const int32_t* va
         ko = reinterpret_cast<KernelFn>(&retrieve_cachegen_sorted<8>);
     }
     // the store and the chunk-major retrieve take one workgroup per page
-    // unit; the ordered retrieve one per kCgWaves rows of it (tile_bytes
-    // counts page-side bytes)
+    // unit; the ordered retrieve one per kCgSortedWaves rows of it
+    // (tile_bytes counts page-side bytes), through its sorted kernel only
     const int page_bytes = int(int64_t(p->page_size) * width * 2);
     *store = {ks, kCgBlock, page_bytes, Unit::Page, 0, 2, nullptr};
     *scatter = {kr, kCgBlock, page_bytes, Unit::Page, 0, 2, nullptr};
-    *scatter_ordered = {kr, kCgBlock, int(kCgWaves * width * 2), Unit::Page, 0, 2, ko};
+    *scatter_ordered = {nullptr, kCgSortedWaves * 64, int(kCgSortedWaves * width * 2), Unit::Page, 0, 2, ko};
     return KV_OK;
 }
 
