@@ -2,8 +2,11 @@
  * abi_c_example.c -- the C ABI of libkvmove.so used from plain C (no Python):
  * a two-layer paged pool with a known pattern, one 300-token sequence
  * (a full 256-token chunk and a 44-token tail) on scattered pages, stored
- * into chunks, the pool cleared, the chunks retrieved (in one call, then
- * again layer by layer, one event per layer).  Checks that every
+ * into chunks (plainly and through the store's address plan), the pool
+ * cleared, the chunks retrieved: in one call, layer by layer with one event
+ * per layer, in pool-address order with a workspace and with the library's
+ * scratch, and every layer in one call on two streams; last, every layer
+ * stored in one call on two streams and retrieved.  Checks that every
  * row the sequence owns comes back bit for bit, that the other pages stay
  * clear, that the retrieve reports 300 tokens and that no fault bit is set.
  * Exit status 0 on success.  Built by the package's build step; run by a
@@ -186,8 +189,63 @@ int main(void)
     rc = check_pool(pool, back, host_pool, bt, n_bt, pool_elems, layer_elems, row);
     if (rc != 0) return rc;
     if (kv_take_faults() != 0) { fprintf(stderr, "fault bits after the layer calls\n"); return 6; }
+
+    /* in pool-address order with a workspace (kv_retrieve_chunks_ws), then
+     * with the library's own scratch (kv_retrieve_chunks_noalloc) */
+    const size_t rws_bytes = kv_retrieve_workspace_bytes(&paged);
+    /* the inverse page map and the sorted list, one 32-bit word per pool page each, each rounded up to 256 */
+    if (rws_bytes != 2 * (((size_t)NUM_PAGES * 4 + 255) / 256 * 256)) { fprintf(stderr, "retrieve workspace %zu bytes\n", rws_bytes); return 5; }
+    void* rws = NULL;
+    CHECK_HIP(hipMalloc(&rws, rws_bytes));
+    for (int form = 0; form < 2; ++form) {
+        CHECK_HIP(hipMemset(pool, 0, pool_elems * 2));
+        CHECK_HIP(hipDeviceSynchronize());
+        out_tokens = -1;
+        if (form == 0)
+            CHECK_KV(kv_retrieve_chunks_ws(&paged, &seq, masks, 1, KV_FMT_BF16, &out_tokens, rws, rws_bytes, stream));
+        else
+            CHECK_KV(kv_retrieve_chunks_noalloc(&paged, &seq, masks, 1, KV_FMT_BF16, &out_tokens, stream));
+        CHECK_HIP(hipStreamSynchronize(stream));
+        if (out_tokens != TOKENS) { fprintf(stderr, "ordered form %d: out_tokens %lld\n", form, (long long)out_tokens); return 6; }
+        rc = check_pool(pool, back, host_pool, bt, n_bt, pool_elems, layer_elems, row);
+        if (rc != 0) return rc;
+    }
+    CHECK_HIP(hipFree(rws));
+
+    /* every layer in one call on two streams (kv_retrieve_layers with a
+     * second stream: odd layers on it, joined back into the first); the
+     * host waits on the stream, then checks each layer's event has fired */
+    hipStream_t alt;
+    CHECK_HIP(hipStreamCreate(&alt));
+    CHECK_HIP(hipMemset(pool, 0, pool_elems * 2));
+    CHECK_HIP(hipDeviceSynchronize());
+    out_tokens = -1;
+    CHECK_KV(kv_retrieve_layers(&paged, &seq, masks, 1, KV_FMT_BF16, 0, L, NULL, &out_tokens, stream, alt, done));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    for (int l = 0; l < L; ++l)
+        if (hipEventQuery(done[l]) != hipSuccess) { fprintf(stderr, "layer %d event not complete after the join\n", l); return 6; }
+    if (out_tokens != TOKENS) { fprintf(stderr, "layer range: out_tokens %lld\n", (long long)out_tokens); return 6; }
+    rc = check_pool(pool, back, host_pool, bt, n_bt, pool_elems, layer_elems, row);
+    if (rc != 0) return rc;
+
+    /* the store of every layer in one call on two streams (kv_store_layers)
+     * into cleared chunks, then a retrieve from them */
+    for (int c = 0; c < 2; ++c) CHECK_HIP(hipMemset((void*)(uintptr_t)chunk_addr[c], 0xEE, chunk_bytes[c]));
+    CHECK_HIP(hipMemcpy(pool, host_pool, pool_elems * 2, hipMemcpyHostToDevice));
+    CHECK_HIP(hipDeviceSynchronize());
+    CHECK_KV(kv_store_layers(&paged, &seq, 1, KV_FMT_BF16, 0, L, NULL, stream, alt, NULL, done));
+    CHECK_HIP(hipMemsetAsync(pool, 0, pool_elems * 2, stream));
+    out_tokens = -1;
+    CHECK_KV(kv_retrieve_chunks(&paged, &seq, masks, 1, KV_FMT_BF16, &out_tokens, stream));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    if (out_tokens != TOKENS) { fprintf(stderr, "after the layer-range store: out_tokens %lld\n", (long long)out_tokens); return 6; }
+    rc = check_pool(pool, back, host_pool, bt, n_bt, pool_elems, layer_elems, row);
+    if (rc != 0) return rc;
+    if (kv_take_faults() != 0) { fprintf(stderr, "fault bits after the ordered and layer-range calls\n"); return 6; }
+    CHECK_HIP(hipStreamDestroy(alt));
     for (int l = 0; l < L; ++l) CHECK_HIP(hipEventDestroy(done[l]));
     printf("C ABI round trip: %d tokens x %d layers x K,V stored alike with and without the address plan, "
-           "restored bit for bit in one call and layer by layer; other rows untouched\n", TOKENS, L);
+           "restored bit for bit in one call and layer by layer; other rows untouched; the same in pool-address "
+           "order (workspace, no-allocation), layer ranges on two streams both ways\n", TOKENS, L);
     return 0;
 }

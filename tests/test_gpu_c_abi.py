@@ -1,6 +1,8 @@
 """The C ABI from plain C: tests/abi_c_example.c (built by the build step)
-stores a sequence through kv_store_chunks, clears the pool and restores it
-through kv_retrieve_chunks, checking the rows itself."""
+stores a sequence (kv_store_chunks, kv_store_chunks_ws, kv_store_layers on
+two streams), clears the pool and restores it (kv_retrieve_chunks,
+kv_retrieve_layer, kv_retrieve_chunks_ws, kv_retrieve_chunks_noalloc,
+kv_retrieve_layers on two streams), checking the rows itself."""
 import os
 import subprocess
 
@@ -19,4 +21,4 @@ def test_c_program_round_trip():
     print("case C ABI example", flush=True)
     r = subprocess.run([EXAMPLE], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stdout + r.stderr
-    assert "restored bit for bit" in r.stdout
+    assert "restored bit for bit" in r.stdout and "layer ranges on two streams both ways" in r.stdout
