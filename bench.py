@@ -353,8 +353,18 @@ def bench_llama8b(args):
     n = (store_bytes // 2) // 16 * 16
     copy_ms = timed(stream, lambda: kvm.copy_bytes(arena, src, n, stream=stream), 5)
     copy_gbps = 2 * n / (copy_ms / 1e3) / 1e9
+    # and the same copy with one side in page-sized blocks visited in a
+    # scattered order: the access pattern of the gather (scattered reads) and
+    # of the chunk-major scatter (scattered writes), with no block table
+    page_bytes = w.page_size * w.width * 2
+    nb = n // page_bytes * page_bytes
+    scat = {}
+    for name, side in (("reads", kvm.COPY_SCATTERED_READS), ("writes", kvm.COPY_SCATTERED_WRITES)):
+        t = timed(stream, lambda: kvm.copy_blocks(arena, src, nb, page_bytes, side, stream=stream), 5)
+        scat[name] = 2 * nb / (t / 1e3) / 1e9
     log(f"store {store_ms:.3f} ms ({gather_gbps:.0f} GB/s), retrieve {ret_ms:.3f} ms "
-        f"({scatter_gbps:.0f} GB/s), step {step_s * 1e3:.3f} ms, copy ceiling {copy_gbps:.0f} GB/s")
+        f"({scatter_gbps:.0f} GB/s), step {step_s * 1e3:.3f} ms, copy ceiling {copy_gbps:.0f} GB/s "
+        f"(scattered {page_bytes // 1024} KiB reads {scat['reads']:.0f}, writes {scat['writes']:.0f})")
 
     traffic = read_traffic()
     out = {
@@ -408,6 +418,9 @@ def bench_llama8b(args):
             "store_other_form_ms": round(other_store_ms, 4),
             "store_other_form_GBps": round(store_bytes / (other_store_ms / 1e3) / 1e9, 2),
             "copy_ceiling_GBps": round(copy_gbps, 2),
+            "copy_scattered_reads_GBps": round(scat["reads"], 2),
+            "copy_scattered_writes_GBps": round(scat["writes"], 2),
+            "gather_frac_of_scattered_read_copy": round(gather_gbps / scat["reads"], 4),
             # HBM bytes the counters measured for one gather launch, over this run's launch time
             "gather_counter_GBps": (round(traffic / (store_ms / 1e3) / 1e9, 2) if traffic else None),
             "kernel_source_sha256_16": kernel_source_hash(),
@@ -960,6 +973,19 @@ def bench_simple(args, name, fmt):
     cm_ms = timed(stream, lambda: kvm.retrieve(paged, batch, fmt=fmt, stream=stream), reps)
     assert kvm.take_faults() == 0
     st, rt = st_bytes / (st_ms / 1e3) / 1e9, rt_bytes / (rt_ms / 1e3) / 1e9
+    # bf16: the same-run copies of the gather's payload, contiguous and with
+    # one side in page-sized blocks visited in a scattered order
+    copies = {}
+    page_bytes = w.page_size * w.width * 2
+    if fmt == kvm.FMT_BF16 and page_bytes >= 4096 and page_bytes & (page_bytes - 1) == 0:
+        src = pool.view(-1).view(torch.uint8)
+        nb = (st_bytes // 2) // page_bytes * page_bytes
+        t = timed(stream, lambda: kvm.copy_bytes(arena, src, nb, stream=stream), 5)
+        copies["copy_ceiling_GBps"] = round(2 * nb / (t / 1e3) / 1e9, 2)
+        for key, side in (("reads", kvm.COPY_SCATTERED_READS), ("writes", kvm.COPY_SCATTERED_WRITES)):
+            t = timed(stream, lambda: kvm.copy_blocks(arena, src, nb, page_bytes, side, stream=stream), 5)
+            copies[f"copy_scattered_{key}_GBps"] = round(2 * nb / (t / 1e3) / 1e9, 2)
+        copies["gather_frac_of_scattered_read_copy"] = round(st / copies["copy_scattered_reads_GBps"], 4)
     beside = oracle_beside(w, pool, fmt, 4)
     return {
         "metric": "store / retrieve algorithmic GB/s", "workload": name,
@@ -976,6 +1002,7 @@ def bench_simple(args, name, fmt):
         "store_form": "address plan (kv_store_chunks_ws)" if sws is not None else "kv_store_chunks (no bf16 part)",
         "store_plain_ms": round(plain_ms, 4) if plain_ms else None,
         "store_plain_GBps": round(st_bytes / (plain_ms / 1e3) / 1e9, 2) if plain_ms else None,
+        **copies,
     }
 
 

@@ -358,6 +358,19 @@ int kv_take_faults(void);
  * achievable-copy ceiling and to calibrate HBM traffic counters. */
 int kv_copy_bytes(void* dst, const void* src, size_t bytes, hipStream_t stream);
 
+/* Measurement aid, not part of the movement path: kv_copy_bytes with one
+ * side visited in blocks of block_bytes (a power of two from 4096 to 2^30;
+ * bytes a multiple of it) in a fixed scattered order -- destination block
+ * k <- source block (k * m) mod n_blocks for permute = 1 (scattered reads,
+ * the gather's pattern when block_bytes is the page size), or destination
+ * block (k * m) mod n_blocks <- source block k for permute = 2 (scattered
+ * writes, the chunk-major scatter's), with m a prime the library picks coprime
+ * with n_blocks (7919 unless it divides n_blocks).  Every destination byte is
+ * written once.  The ceiling of each access pattern, with no block table.
+ * Same alignment rules and errors as kv_copy_bytes, plus KV_EINVAL for a bad
+ * block size or permute value. */
+int kv_copy_blocks(void* dst, const void* src, size_t bytes, size_t block_bytes, int permute, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

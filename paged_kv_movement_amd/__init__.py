@@ -110,6 +110,7 @@ def load():
         "kv_last_error": (ctypes.c_char_p, []),
         "kv_take_faults": (ctypes.c_int, []),
         "kv_copy_bytes": (ctypes.c_int, [vp, vp, ctypes.c_size_t, vp]),
+        "kv_copy_blocks": (ctypes.c_int, [vp, vp, ctypes.c_size_t, ctypes.c_size_t, ctypes.c_int, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -567,3 +568,13 @@ def take_faults() -> int:
 def copy_bytes(dst, src, nbytes: int, stream=None) -> None:
     """Plain contiguous device copy (measurement aid)."""
     _check(load().kv_copy_bytes(dst.data_ptr(), src.data_ptr(), nbytes, _stream_handle(stream)))
+
+
+COPY_SCATTERED_READS, COPY_SCATTERED_WRITES = 1, 2
+
+
+def copy_blocks(dst, src, nbytes: int, block_bytes: int, permute: int, stream=None) -> None:
+    """Device copy with one side visited in scattered blocks (measurement aid,
+    kv_copy_blocks): permute = COPY_SCATTERED_READS or COPY_SCATTERED_WRITES."""
+    _check(load().kv_copy_blocks(dst.data_ptr(), src.data_ptr(), nbytes, block_bytes, permute,
+                                 _stream_handle(stream)))

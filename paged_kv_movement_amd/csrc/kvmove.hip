@@ -16,6 +16,7 @@
 #include <string>
 
 #include "kv_cachegen.hpp"
+#include "kv_copy.hpp"
 #include "kv_fp8.hpp"
 #include "kv_move_bf16.hpp"
 #include "kv_order.hpp"
@@ -1010,6 +1011,40 @@ int kv_copy_bytes(void* dst, const void* src, size_t bytes, hipStream_t stream)
     void* args[] = {&s, &d, &n};
     hipError_t e = hipLaunchKernel(reinterpret_cast<KernelFn>(&copy_contiguous<kCopyBlock, kCopyVpt>),
                                    dim3((unsigned)grid), dim3(kCopyBlock), args, 0, stream);
+    if (e != hipSuccess) return fail(KV_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int kv_copy_blocks(void* dst, const void* src, size_t bytes, size_t block_bytes, int permute, hipStream_t stream)
+{
+    if (dst == nullptr || src == nullptr) return fail(KV_EINVAL, "dst / src is NULL");
+    if ((reinterpret_cast<uintptr_t>(dst) & 15) || (reinterpret_cast<uintptr_t>(src) & 15))
+        return fail(KV_EINVAL, "kv_copy_blocks needs 16-byte aligned addresses");
+    const int64_t tile = int64_t(kCopyBlock) * kCopyVpt * 16;
+    if (block_bytes < size_t(tile) || block_bytes > (size_t(1) << 30) || (block_bytes & (block_bytes - 1)) != 0)
+        return fail(KV_EINVAL, "block_bytes must be a power of two from %lld to 2^30 (got %zu)", (long long)tile,
+                    block_bytes);
+    if (bytes % block_bytes != 0) return fail(KV_EINVAL, "bytes (%zu) must be a multiple of block_bytes", bytes);
+    if (permute != 1 && permute != 2)
+        return fail(KV_EINVAL, "permute must be 1 (source blocks) or 2 (destination blocks), got %d", permute);
+    if (bytes == 0) return ok();
+    const int64_t grid = int64_t(bytes) / tile;
+    if (grid > max_blocks(kCopyBlock)) return fail(KV_EINVAL, "copy too large for one launch");
+    // a prime multiplier that does not divide the block count is coprime with
+    // it; at most 2^35 blocks, so at most two of these primes divide it
+    const uint64_t n_blocks = bytes / block_bytes;
+    uint64_t mult = 1;
+    for (uint64_t p : {7919ull, 7927ull, 7933ull})
+        if (n_blocks % p != 0) { mult = p; break; }
+    uint32_t shift = 0;
+    while ((size_t(1) << shift) < block_bytes) ++shift;
+    uint64_t s = reinterpret_cast<uint64_t>(src);
+    uint64_t d = reinterpret_cast<uint64_t>(dst);
+    int64_t n = int64_t(bytes);
+    void* args[] = {&s, &d, &n, &shift, &mult};
+    const KernelFn k = permute == 1 ? reinterpret_cast<KernelFn>(&copy_permuted<kCopyBlock, kCopyVpt, true>)
+                                    : reinterpret_cast<KernelFn>(&copy_permuted<kCopyBlock, kCopyVpt, false>);
+    hipError_t e = hipLaunchKernel(k, dim3((unsigned)grid), dim3(kCopyBlock), args, 0, stream);
     if (e != hipSuccess) return fail(KV_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }

@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ["kv_store_chunks", "kv_store_layer", "kv_store_layers", "kv_retrieve_chunks", "kv_retrieve_layer",
               "kv_retrieve_layer_ex", "kv_retrieve_layers", "kv_chunk_bytes", "kv_num_chunks", "kv_chunk_tokens",
-              "kv_last_error", "kv_take_faults", "kv_copy_bytes"]:
+              "kv_last_error", "kv_take_faults", "kv_copy_bytes", "kv_copy_blocks"]:
         assert n in names
 
 
@@ -199,6 +199,21 @@ def test_copy_bytes_rejections():
     assert L.kv_copy_bytes(0x1008, 0x2000, 32, None) == kvm.KV_EINVAL
     assert L.kv_copy_bytes(None, 0x2000, 32, None) == kvm.KV_EINVAL
     assert L.kv_copy_bytes(0x1000, 0x2000, 0, None) == kvm.KV_OK
+
+
+def test_copy_blocks_rejections():
+    # every case is refused (or is empty) on the host, before any HIP call
+    L = _lib()
+    assert L.kv_copy_blocks(0x1000, 0x2000, 1 << 20, 1000, 1, None) == kvm.KV_EINVAL       # not a power of two
+    assert L.kv_copy_blocks(0x1000, 0x2000, 1 << 20, 2048, 1, None) == kvm.KV_EINVAL       # below the tile
+    assert L.kv_copy_blocks(0x1000, 0x2000, 1 << 20, 1 << 31, 1, None) == kvm.KV_EINVAL    # above 2^30
+    assert L.kv_copy_blocks(0x1000, 0x2000, 45056, 8192, 1, None) == kvm.KV_EINVAL        # not a multiple
+    assert "multiple" in L.kv_last_error().decode()
+    assert L.kv_copy_blocks(0x1000, 0x2000, 1 << 20, 32768, 0, None) == kvm.KV_EINVAL      # permute 0
+    assert L.kv_copy_blocks(0x1000, 0x2000, 1 << 20, 32768, 3, None) == kvm.KV_EINVAL
+    assert L.kv_copy_blocks(0x1008, 0x2000, 1 << 20, 32768, 1, None) == kvm.KV_EINVAL      # misaligned
+    assert L.kv_copy_blocks(None, 0x2000, 1 << 20, 32768, 2, None) == kvm.KV_EINVAL
+    assert L.kv_copy_blocks(0x1000, 0x2000, 0, 32768, 2, None) == kvm.KV_OK                # empty
 
 
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):

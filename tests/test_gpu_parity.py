@@ -593,6 +593,31 @@ def test_copy_bytes_is_a_plain_copy():
     assert (dst[n:] == 7).all()
 
 
+@pytest.mark.parametrize("n_blocks,block,mult", [(37, 8192, 7919), (7919, 4096, 7927), (64, 32768, 7919)])
+@pytest.mark.parametrize("permute", [kvm.COPY_SCATTERED_READS, kvm.COPY_SCATTERED_WRITES], ids=["reads", "writes"])
+def test_copy_blocks_is_a_block_permutation(n_blocks, block, mult, permute):
+    # the measurement aid's order, as its header states it: block k of the
+    # permuted side is block (k * m) mod n_blocks, m the first of 7919, 7927
+    # that does not divide n_blocks; every destination byte written once
+    print("case copy_blocks", n_blocks, block, permute, flush=True)
+    n = n_blocks * block
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.full((n + 4096,), 7, dtype=torch.uint8, device="cuda")
+    kvm.copy_blocks(dst, src, n, block, permute)
+    _sync()
+    perm = (np.arange(n_blocks, dtype=np.int64) * mult) % n_blocks
+    assert np.array_equal(np.sort(perm), np.arange(n_blocks))
+    s_blocks = src.cpu().numpy().reshape(n_blocks, block)
+    want = np.empty_like(s_blocks)
+    if permute == kvm.COPY_SCATTERED_READS:
+        want[:] = s_blocks[perm]
+    else:
+        want[perm] = s_blocks
+    got = dst.cpu().numpy()
+    assert np.array_equal(got[:n].reshape(n_blocks, block), want)
+    assert (got[n:] == 7).all()
+
+
 @pytest.mark.parametrize("fmt", **ALL_FMTS)
 @pytest.mark.parametrize("cap", [0, 5])
 def test_layerwise_store_equals_full_store(fmt, cap):
