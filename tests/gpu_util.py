@@ -164,7 +164,7 @@ def check_retrieve_cachegen(w, pool_before, got_pool, chunk_sets, masks, kb, vb)
     return counts
 
 
-ORACLE_THREADS = 16      # the GPU machine's CPU share
+ORACLE_THREADS = 16      # oracle worker threads (a 16-core share of the host)
 
 
 def _oracle_pool_map(fn, tasks):
