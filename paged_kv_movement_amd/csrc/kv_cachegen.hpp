@@ -22,7 +22,10 @@
 
 namespace kvmove {
 
-constexpr int kCgBlock = 256;
+// threads per workgroup of the store and the chunk-major retrieve (one
+// page unit each): 8 waves measured 2 % faster than 4 for the store (1 and 2
+// slower, 16 much slower) and the same for the retrieve
+constexpr int kCgBlock = 512;
 constexpr int kCgWaves = kCgBlock / 64;
 // waves (one row each) per workgroup of the pool-address-ordered retrieve
 constexpr int kCgSortedWaves = 1;
@@ -30,7 +33,8 @@ constexpr int kCgMaxLayers = 128;
 constexpr int kCgMaxVpl = 8;            // 16-byte vectors per lane per row: rows up to 4096 elements
 
 // Rows a wave loads before it converts the first: as many as keep the data
-// within 8 vectors of 16 bytes per lane, at most 4 (a 16-row page over 4 waves).
+// within 8 vectors of 16 bytes per lane, at most 4 (rows past the unit's end
+// are skipped, so a 16-row page gives each of 8 waves 2).
 template <int kVpl>
 constexpr int kCgRows = kVpl <= 2 ? 4 : 8 / kVpl;
 
