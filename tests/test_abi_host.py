@@ -465,6 +465,31 @@ def test_ordered_retrieve_refuses_more_pages_than_the_pool():
     assert "repeat" in L.kv_last_error().decode()
 
 
+def test_ordered_retrieve_refuses_a_sequence_too_large_for_one_launch():
+    # a launch takes fewer than 2^32 threads, 2^26 - 1 one-wave workgroups:
+    # a sequence of 2^25 pages (K and V: 2^26 units; here 256-byte pages, H=1,
+    # D=8, on a pool of 2^27 pages) is refused on the host before any launch
+    # (the addresses are fake; nothing may reach a device).  This also keeps
+    # every page index within the 26 bits the sorted list packs it in.
+    import numpy as np
+    L = _lib()
+    p = _paged(L=1, H=1, D=8, n=1 << 27)
+    need = L.kv_retrieve_workspace_bytes(ctypes.byref(p))
+    assert need == 2 * (1 << 27) * 4
+    out = (ctypes.c_int64 * 1)()
+    pages = 1 << 25
+    tokens = pages * 16
+    seqs = (kvm._KvSeq * 1)(_seq(0, tokens, pages))
+    m = np.ones(-(-tokens // 256), np.uint8)
+    masks = (ctypes.c_void_p * 1)(m.ctypes.data)
+    for call in (lambda: L.kv_retrieve_chunks_ws(ctypes.byref(p), seqs, masks, 1, kvm.FMT_BF16, out, 0x10000, need,
+                                                 None),
+                 lambda: L.kv_retrieve_chunks(ctypes.byref(p), seqs, masks, 1, kvm.FMT_BF16, out, None),
+                 lambda: L.kv_store_chunks(ctypes.byref(p), seqs, 1, kvm.FMT_BF16, None)):
+        assert call() == kvm.KV_EINVAL
+        assert "exceed one launch" in L.kv_last_error().decode()
+
+
 def test_c_example_builds_against_the_header(tmp_path):
     # a plain C program (tests/abi_c_example.c) compiles against
     # include/kvmove.h and links libkvmove.so; a GPU test runs it
