@@ -259,14 +259,27 @@ __global__ __launch_bounds__(kOnchipBlock) void store_fp8_onchip(MoveArgsLut al)
     if (bad_addr(chunk)) { raise_fault(kFaultChunk); return; }
     const uint32_t first = sq.first_page + g.c * a.pages_per_chunk;
     const uint32_t n_pages = (g.n_c + a.page_size - 1) / a.page_size;
-    if (threadIdx.x < n_pages) pages[threadIdx.x] = gptr<const gi32>(sq.bt)[first + threadIdx.x];
+    const uint32_t page_vecs = a.page_size * (a.width / 8);
+    // The groups of one chunk's layers and parts, which run side by side,
+    // read the same page ids in different layers' pools.  A full group whose
+    // pages hold whole slots visits its pages rotated by spin = (2 l + kv)
+    // mod n_pages, so that they start on different pages (0.2-0.8 % faster):
+    // pages[] lists them rotated, and slot k's codes go to slot
+    // (k + spin * slots per page) mod n_slots of the output.
+    const uint32_t spin = (g.n_c == a.chunk_size && page_vecs % B == 0) ? (g.l * 2 + g.kv) % n_pages : 0u;
+    if (threadIdx.x < n_pages) {
+        uint32_t t = threadIdx.x + spin;
+        if (t >= n_pages) t -= n_pages;
+        pages[threadIdx.x] = gptr<const gi32>(sq.bt)[first + t];
+    }
     __syncthreads();
     for (uint32_t pi = 0; pi < n_pages; ++pi) {       // same verdict in every thread
         if (pages[pi] < 0 || pages[pi] >= a.num_pages) { raise_fault(kFaultPage); return; }
     }
-    const uint32_t page_vecs = a.page_size * (a.width / 8);
     const uint64_t page_bytes = (uint64_t)page_vecs * 16;
     const uint32_t total = g.n_c * (a.width / 8);
+    const uint32_t n_slots = (total + B - 1) / B;
+    const uint32_t slot_shift = spin * (page_vecs / B);   // 0 unless spun: then total = n_slots * B
     const uint32_t wave = threadIdx.x / 64;
 
     // LDS slots: direct-to-LDS loads (each lane's 16 bytes land at
@@ -302,16 +315,23 @@ __global__ __launch_bounds__(kOnchipBlock) void store_fp8_onchip(MoveArgsLut al)
     const float r = 1.0f / scale;
 
     gvec2* dst = reinterpret_cast<gvec2*>(chunk + section_offset(a, g.l, g.kv, g.n_c));
+    // output slot of slot k (k < n_slots, as v < total below); k itself unless spun
+    auto out_slot = [&](uint32_t k) {
+        const uint32_t o = k + slot_shift;
+        return o >= n_slots ? o - n_slots : o;
+    };
 #pragma unroll
     for (int k = 0; k < kOnchipRegSlots; ++k) {
         const uint32_t v = k * B + threadIdx.x;
-        if (v < total) __builtin_nontemporal_store(quantize8<kE5M2>(reg[k], scale, r, fast), dst + v);
+        if (v < total)
+            __builtin_nontemporal_store(quantize8<kE5M2>(reg[k], scale, r, fast), dst + out_slot(k) * B + threadIdx.x);
     }
 #pragma unroll
     for (int k = 0; k < kOnchipLdsSlots; ++k) {
         const uint32_t v = (kOnchipRegSlots + k) * B + threadIdx.x;
         if (v < total)
-            __builtin_nontemporal_store(quantize8<kE5M2>(lds[k * B + threadIdx.x], scale, r, fast), dst + v);
+            __builtin_nontemporal_store(quantize8<kE5M2>(lds[k * B + threadIdx.x], scale, r, fast),
+                                        dst + out_slot(kOnchipRegSlots + k) * B + threadIdx.x);
     }
     if (threadIdx.x == 0) *gptr<gf32>(chunk + scale_offset(a, g.l, g.kv, g.n_c)) = scale;
 }
