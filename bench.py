@@ -127,10 +127,10 @@ def hit_tokens(w):
     return out
 
 
-def timed(stream, fn, reps, warmup=3, stat="mean"):
-    """ms of fn() over reps (mean, or median with stat="median"), HIP events
-    on `stream`, after `warmup` untimed calls (short launches otherwise pay
-    for the first calls' setup)."""
+def timed(stream, fn, reps, warmup=3, stat="median"):
+    """ms of fn() over reps (the median, or the mean with stat="mean"), HIP
+    events on `stream`, after `warmup` untimed calls (short launches otherwise
+    pay for the first calls' setup)."""
     import torch
     for _ in range(warmup):
         fn()
