@@ -268,7 +268,7 @@ int kv_retrieve_chunks_ws(const kv_paged* paged, const kv_seq* seqs, const uint8
  * result and errors as kv_retrieve_chunks, plus: a pool of more than 2^20
  * pages is refused (KV_EINVAL; use kv_retrieve_chunks_ws), and so is a
  * stream that belongs to another device than the current one.  It calls no
- * allocator.  Every call on a GPU shares that GPU's scratch: calls that
+ * allocator, for device or host memory.  Every call on a GPU shares that GPU's scratch: calls that
  * overlap in time on one GPU (on streams not ordered with each other) race
  * and must not be made; calls ordered on one stream are safe. */
 int kv_retrieve_chunks_noalloc(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask,

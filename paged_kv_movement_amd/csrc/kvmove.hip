@@ -475,18 +475,25 @@ int retrieve_ordered(const Launch& L, const Layout& lay, const kv_paged* p, cons
     return pack_units(L, lay, p, seqs, n_tok, n_seqs, layer0, n_layers, flush);
 }
 
-// Tokens each sequence gets back: its leading hit chunks, from tok_start.
+// Tokens sequence i (s, with its hit mask) gets back: its leading hit
+// chunks, from tok_start.
+int seq_hit_tokens(const kv_paged* paged, const kv_seq& s, const uint8_t* mask, int i, int64_t* n_tok)
+{
+    const int64_t n_chunks = ceil_div(s.tok_end - s.tok_start, paged->chunk_size);
+    if (n_chunks > 0 && mask == nullptr) return fail(KV_EINVAL, "seq %d: hit_mask entry is NULL", i);
+    const int64_t n_hit = n_chunks > 0 ? hit_chunks(mask, n_chunks) : 0;
+    const int64_t end = s.tok_start + n_hit * paged->chunk_size;
+    *n_tok = (end < s.tok_end ? end : s.tok_end) - s.tok_start;
+    return KV_OK;
+}
+
 int hit_tokens(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hit_mask, int n_seqs,
                int64_t* n_tok)
 {
     if (n_seqs > 0 && hit_mask == nullptr) return fail(KV_EINVAL, "hit_mask is NULL");
     for (int i = 0; i < n_seqs; ++i) {
-        const kv_seq& s = seqs[i];
-        const int64_t n_chunks = ceil_div(s.tok_end - s.tok_start, paged->chunk_size);
-        if (n_chunks > 0 && hit_mask[i] == nullptr) return fail(KV_EINVAL, "seq %d: hit_mask entry is NULL", i);
-        const int64_t n_hit = n_chunks > 0 ? hit_chunks(hit_mask[i], n_chunks) : 0;
-        const int64_t end = s.tok_start + n_hit * paged->chunk_size;
-        n_tok[i] = (end < s.tok_end ? end : s.tok_end) - s.tok_start;
+        const int rc = seq_hit_tokens(paged, seqs[i], hit_mask[i], i, &n_tok[i]);
+        if (rc != KV_OK) return rc;
     }
     return KV_OK;
 }
@@ -917,14 +924,19 @@ int kv_retrieve_chunks_noalloc(const kv_paged* paged, const kv_seq* seqs, const 
         return fail(KV_EINVAL, "pool of %lld pages: the no-allocation retrieve's scratch holds pools of at most "
                     "%lld pages (use kv_retrieve_chunks_ws with a workspace)", (long long)paged->num_pages,
                     (long long)kScratchMaxPages);
-    {   // the host-side checks of the retrieve itself, before any HIP call
-        int64_t small[64];
-        int64_t* n_tok = n_seqs <= 64 ? small : new int64_t[n_seqs];
-        rc = hit_tokens(paged, seqs, hit_mask, n_seqs, n_tok);
-        if (rc == KV_OK) rc = check_ordered_fits(paged, n_tok, n_seqs);
-        if (n_tok != small) delete[] n_tok;
+    // The host-side checks of the retrieve itself, before any HIP call, one
+    // sequence at a time: this entry point allocates no host memory either.
+    if (n_seqs > 0 && hit_mask == nullptr) return fail(KV_EINVAL, "hit_mask is NULL");
+    int64_t pages = 0;
+    for (int i = 0; i < n_seqs; ++i) {
+        int64_t n = 0;
+        rc = seq_hit_tokens(paged, seqs[i], hit_mask[i], i, &n);
         if (rc != KV_OK) return rc;
+        pages += ceil_div(n, paged->page_size);
     }
+    if (pages > paged->num_pages)
+        return fail(KV_EINVAL, "the call moves %lld pages but the pool holds %lld: page ids repeat",
+                    (long long)pages, (long long)paged->num_pages);
     int dev = -1, sdev = -1;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess && stream != nullptr) e = hipStreamGetDevice(stream, &sdev);
@@ -934,7 +946,14 @@ int kv_retrieve_chunks_noalloc(const kv_paged* paged, const kv_seq* seqs, const 
     void* ws = nullptr;
     rc = scratch_address(&ws);
     if (rc != KV_OK) return rc;
-    rc = retrieve(paged, seqs, hit_mask, n_seqs, fmt, 0, paged->num_layers, out_tokens, stream, 0, ws);
+    // at most 64 sequences per pass, so that the retrieve keeps its token
+    // counts on the stack (a launch packs at most kMaxSeqs of them anyway)
+    static_assert(64 % kMaxSeqs == 0, "passes of 64 sequences pack as one pass would");
+    for (int i0 = 0; i0 < n_seqs && rc == KV_OK; i0 += 64) {
+        const int n = std::min(64, n_seqs - i0);
+        rc = retrieve(paged, seqs + i0, hit_mask + i0, n, fmt, 0, paged->num_layers,
+                      out_tokens != nullptr ? out_tokens + i0 : nullptr, stream, 0, ws);
+    }
     return rc == KV_OK ? ok() : rc;
 }
 

@@ -516,3 +516,24 @@ def test_noalloc_retrieve_refuses_pools_beyond_its_scratch():
     assert L.kv_retrieve_chunks_noalloc(ctypes.byref(p), seqs, None, 1, kvm.FMT_BF16, out, None) == kvm.KV_EINVAL
     bad = (kvm._KvSeq * 1)(_seq(100, 1000, 63))
     assert L.kv_retrieve_chunks_noalloc(ctypes.byref(p), bad, masks, 1, kvm.FMT_BF16, out, None) == kvm.KV_EINVAL
+
+
+def test_noalloc_retrieve_checks_every_sequence_before_any_hip_call():
+    # beyond 64 sequences too (the entry point takes them 64 at a time): a
+    # NULL mask entry of sequence 80, or more pages moved in all than the pool
+    # holds, is refused with KV_EINVAL, not the KV_EHIP a HIP call on this
+    # GPU-less host would give
+    L = _lib()
+    n = 100
+    seqs = (kvm._KvSeq * n)(*[_seq(0, 300, 19) for _ in range(n)])
+    m = (ctypes.c_uint8 * 2)(1, 1)
+    masks = (ctypes.c_void_p * n)(*([ctypes.addressof(m)] * n))
+    out = (ctypes.c_int64 * n)()
+    p = _paged(n=8192)
+    masks[80] = None
+    assert L.kv_retrieve_chunks_noalloc(ctypes.byref(p), seqs, masks, n, kvm.FMT_BF16, out, None) == kvm.KV_EINVAL
+    assert "seq 80" in L.kv_last_error().decode()
+    masks[80] = ctypes.addressof(m)
+    small = _paged(n=100 * 19 - 1)          # 100 sequences x 19 pages moved
+    assert L.kv_retrieve_chunks_noalloc(ctypes.byref(small), seqs, masks, n, kvm.FMT_BF16, out, None) == kvm.KV_EINVAL
+    assert "page ids repeat" in L.kv_last_error().decode()

@@ -88,3 +88,31 @@ def test_noalloc_retrieve_on_a_side_stream_and_zero_hits():
     s.synchronize()
     assert np.array_equal(host_from_dev_pool(pool), ref)
     assert kvm.take_faults() == 0
+
+
+def test_noalloc_retrieve_with_more_sequences_than_one_pass():
+    # 150 sequences: the no-allocation retrieve takes them 64 at a time (its
+    # token counts stay on the stack); the pool is that of one
+    # kv_retrieve_chunks_ws call over all 150
+    rng = np.random.default_rng(606)
+    ranges, masks = [], []
+    for i in range(150):
+        start = 256 * int(rng.integers(0, 2))
+        end = start + int(rng.integers(1, 600))
+        n_chunks = -(-(end - start) // 256)
+        m = np.ones(n_chunks, np.uint8)
+        if i % 5 == 0:
+            m[int(rng.integers(0, n_chunks))] = 0
+        ranges.append((start, end))
+        masks.append(m)
+    w = wl.custom("noalloc-many", 606, 2, 1, 16, 8192, ranges, masks=masks)
+    for fmt in (kvm.FMT_BF16, kvm.FMT_FP8):
+        say("case noalloc many sequences fmt", fmt)
+        pool, paged, batch, ref, n_ref, cs = _case(w, fmt)
+        assert sum(1 for n in n_ref if n > 0) > 100 and any(n > 0 for n in n_ref[128:])
+        assert kvm.retrieve_noalloc(paged, batch, fmt=fmt) == n_ref
+        sync()
+        assert kvm.take_faults() == 0
+        assert np.array_equal(host_from_dev_pool(pool), ref), fmt
+        del pool, paged, batch, cs
+    torch.cuda.empty_cache()
