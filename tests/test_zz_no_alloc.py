@@ -116,3 +116,41 @@ def test_noalloc_retrieve_with_more_sequences_than_one_pass():
         assert np.array_equal(host_from_dev_pool(pool), ref), fmt
         del pool, paged, batch, cs
     torch.cuda.empty_cache()
+
+
+def test_noalloc_retrieve_replays_from_a_graph():
+    # Code under graph capture is one of the callers this entry point is for.
+    # Captured once, the retrieve is replayed three times.  Before each replay
+    # an eager call on another pool (above 32768 pages, so that its inverse
+    # map goes through the scratch) leaves its own contents in the shared
+    # scratch.  Every replay must still give the workspace retrieve's pool.
+    w = wl.custom("noalloc-graph", 607, 2, 2, 32, 300, [(0, 700), (256, 1000)],
+                  masks=[np.array([1, 1, 1], np.uint8), np.array([1, 0, 1], np.uint8)])
+    other = wl.custom("noalloc-graph-other", 608, 1, 1, 8, 40000, [(0, 20000), (0, 9000)])
+    say("case noalloc graph replay")
+    pool, paged, batch, ref, n_ref, cs = _case(w, kvm.FMT_BF16)
+    opool, opaged, obatch, oref, on_ref, ocs = _case(other, kvm.FMT_BF16)
+    assert n_ref == [700, 256]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                       # warm-up outside capture
+        kvm.retrieve_noalloc(paged, batch)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        n = kvm.retrieve_noalloc(paged, batch)
+    assert n == n_ref
+    for rep in range(3):
+        say("replay", rep)
+        opool.view(torch.int16).fill_(SENTINEL)
+        assert kvm.retrieve_noalloc(opaged, obatch) == on_ref
+        sync()
+        assert np.array_equal(host_from_dev_pool(opool), oref)
+        pool.view(torch.int16).fill_(SENTINEL)
+        sync()
+        g.replay()
+        sync()
+        assert kvm.take_faults() == 0
+        assert np.array_equal(host_from_dev_pool(pool), ref), rep
+    del g
+    torch.cuda.empty_cache()
