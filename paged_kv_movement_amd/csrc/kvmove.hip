@@ -281,8 +281,9 @@ int launch_units(const Launch& L, const Layout& lay, const kv_paged* p, const kv
 }
 
 // bf16 mover launch; `capped` (a workgroup cap is given) selects the
-// 256-thread shape, so a cap keeps its meaning in threads.
-Launch bf16_launch(bool to_chunk, uint32_t kv0, uint32_t n_kv, bool capped)
+// 256-thread shape, so a cap keeps its meaning in threads; `whole` (a
+// scatter over every layer at once, uncapped) selects its store policy.
+Launch bf16_launch(bool to_chunk, uint32_t kv0, uint32_t n_kv, bool capped, bool whole = false)
 {
     if (capped) {
         constexpr int B = kMoveBlockCapped;
@@ -294,6 +295,7 @@ Launch bf16_launch(bool to_chunk, uint32_t kv0, uint32_t n_kv, bool capped)
     constexpr int B = kMoveBlock;
     const KernelFn k =
         to_chunk ? reinterpret_cast<KernelFn>(&move_bf16<true, B, kMoveVpt, kGatherAuxLoad, kGatherAuxStore>)
+        : whole  ? reinterpret_cast<KernelFn>(&move_bf16<false, B, kMoveVpt, kScatterAuxLoad, kScatterAuxStoreWhole>)
                  : reinterpret_cast<KernelFn>(&move_bf16<false, B, kMoveVpt, kScatterAuxLoad, kScatterAuxStore>);
     const KernelFn sorted =
         to_chunk ? nullptr
@@ -349,14 +351,16 @@ Plan gather_plan(const kv_paged* p, int fmt, bool capped)
     }
 }
 
-Plan scatter_plan(int fmt, bool capped, bool ordered)
+// The launches of a retrieve; `whole`: every layer in one uncapped launch
+// (the chunk-major scatter's store policy, kScatterAuxStoreWhole).
+Plan scatter_plan(int fmt, bool capped, bool ordered, bool whole = false)
 {
     switch (fmt) {
-    case KV_FMT_BF16: return {{bf16_launch(false, 0, 2, capped)}, 1};
+    case KV_FMT_BF16: return {{bf16_launch(false, 0, 2, capped, whole)}, 1};
     case KV_FMT_FP8_E4M3_SCALED: return {{dequantise_launch(false, 0, 2, capped, ordered)}, 1};
     case KV_FMT_FP8_E5M2_SCALED: return {{dequantise_launch(true, 0, 2, capped, ordered)}, 1};
     default:                                                                                      // K16_V8
-        return {{bf16_launch(false, 0, 1, capped), dequantise_launch(false, 1, 1, capped, ordered)}, 2};
+        return {{bf16_launch(false, 0, 1, capped, whole), dequantise_launch(false, 1, 1, capped, ordered)}, 2};
     }
 }
 
@@ -532,8 +536,8 @@ int retrieve(const kv_paged* paged, const kv_seq* seqs, const uint8_t* const* hi
             rc = retrieve_ordered(plan.part[k], layout_of(fmt), paged, seqs, n_tok, n_seqs, layer0, n_layers,
                                   workspace, stream);
     } else
-        rc = run_plan(scatter_plan(fmt, max_workgroups > 0, false), fmt, paged, seqs, n_tok, n_seqs, layer0, n_layers, stream,
-                      max_workgroups);
+        rc = run_plan(scatter_plan(fmt, max_workgroups > 0, false, max_workgroups == 0 && n_layers == paged->num_layers),
+                      fmt, paged, seqs, n_tok, n_seqs, layer0, n_layers, stream, max_workgroups);
     if (rc == KV_OK && out_tokens != nullptr)
         for (int i = 0; i < n_seqs; ++i) out_tokens[i] = n_tok[i];
     if (n_tok != small) delete[] n_tok;
