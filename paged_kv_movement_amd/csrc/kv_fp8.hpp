@@ -283,14 +283,15 @@ __global__ __launch_bounds__(kOnchipBlock) void store_fp8_onchip(MoveArgsLut al)
     const uint32_t wave = threadIdx.x / 64;
 
     // LDS slots: direct-to-LDS loads (each lane's 16 bytes land at
-    // base + lane * 16, base uniform per wave)
+    // base + lane * 16, base uniform per wave), streaming like the register
+    // slots' loads (nt + sc1: 0.3-0.5 % faster than the default policy)
 #pragma unroll
     for (int k = 0; k < kOnchipLdsSlots; ++k) {
         const uint32_t v = (kOnchipRegSlots + k) * B + threadIdx.x;
         if (v < total)
             __builtin_amdgcn_global_load_lds(group_vector(pool, pages, page_vecs, page_bytes, v),
                                              (__attribute__((address_space(3))) void*)&lds[k * B + wave * 64],
-                                             16, 0, 0);
+                                             16, 0, kCpolNt | kCpolSc1);
     }
     u32x4 reg[kOnchipRegSlots];
 #pragma unroll
