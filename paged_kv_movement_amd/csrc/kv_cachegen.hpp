@@ -210,6 +210,9 @@ __global__ __launch_bounds__(kCgBlock) void store_cachegen(CgArgs ca)
     // issued before the first row is reduced.  A row past the unit's end
     // gets an empty range (loads return zero, nothing is touched).
     constexpr int kRows = kCgRows<kVpl>;
+    // streaming policy with sc1 on the loads and the stores, as the movers
+    // use (0.9 % faster than nt alone at the Llama-3.1-8B shape)
+    constexpr int kAux = kCpolNt | kCpolSc1;
     for (uint32_t r0 = wave; r0 < u.rows; r0 += kCgWaves * kRows) {
         u32x4 v[kRows][kVpl];
 #pragma unroll
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(kCgBlock) void store_cachegen(CgArgs ca)
             const __amdgpu_buffer_rsrc_t rs = byte_range(page_rows + (uint64_t)r * row_bytes, r < u.rows ? row_bytes : 0);
 #pragma unroll
             for (int k = 0; k < kVpl; ++k)
-                v[i][k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (k * 64 + lane) * 16, 0, kCpolNt);
+                v[i][k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (k * 64 + lane) * 16, 0, kAux);
         }
         // the rows' maxima first, so that their cross-lane reductions overlap
         // (a row past the unit's end read zeros and is not used)
@@ -245,12 +248,12 @@ __global__ __launch_bounds__(kCgBlock) void store_cachegen(CgArgs ca)
 #pragma unroll
                 for (int k = 0; k < kVpl; ++k)
                     __builtin_amdgcn_raw_buffer_store_b64(cg_quantise8_fast(v[i][k], factor, qmax), rd,
-                                                          (k * 64 + lane) * 8, 0, kCpolNt);
+                                                          (k * 64 + lane) * 8, 0, kAux);
             } else {
 #pragma unroll
                 for (int k = 0; k < kVpl; ++k)
                     __builtin_amdgcn_raw_buffer_store_b64(cg_quantise8(v[i][k], factor, qmax), rd,
-                                                          (k * 64 + lane) * 8, 0, kCpolNt);
+                                                          (k * 64 + lane) * 8, 0, kAux);
             }
             if (lane == 0) *gptr<gf32>(chunk + cg_max_offset(a, u.l, u.kv, u.n_c, u.j0 + r)) = max1;
         }
